@@ -1,0 +1,19 @@
+"""CPU oracle (test infrastructure only; see moe_ref's header)."""
+from .moe_ref import (  # noqa: F401
+    bf16_to_f64,
+    expert_block_backward,
+    expert_offsets,
+    gmm,
+    gmm_bwd_input,
+    gmm_bwd_weight,
+    moe_layer_forward,
+    permute,
+    permute_maps,
+    round_bf16,
+    sigmoid,
+    swiglu,
+    swiglu_bwd,
+    to_bf16_bits,
+    tokens_per_expert,
+    unpermute,
+)

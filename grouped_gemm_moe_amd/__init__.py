@@ -1,0 +1,207 @@
+"""Routed-expert MoE hot path on AMD MI355X (gfx950): Python binding.
+
+Every function here only marshals torch tensors into the C ABI of
+``libmoegmm.so`` (declared in ``include/moegmm.h``) and enqueues the HIP
+kernels on the current torch stream; no arithmetic of the path runs in
+Python or in PyTorch.  PyTorch provides device memory and streams only.
+
+Names and argument order follow the C ABI:
+    moe_permute, gmm_fwd, gmm_bwd_input, gmm_bwd_weight, swiglu, swiglu_bwd,
+    moe_unpermute
+Outputs are allocated with ``torch.empty`` unless passed via ``out=``; rows
+at or beyond R = sum(group_list) of a permuted-row output are left as they
+were (undefined for a fresh allocation).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as _L
+
+__all__ = [
+    "MoeError", "moe_permute", "gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
+    "swiglu_bwd", "moe_unpermute", "moe_permute_workspace_size", "gmm_workspace_size",
+    "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP",
+]
+
+DEVERR_EXPERT_ID = 1
+DEVERR_GROUP_LIST = 2
+DEVERR_ROW_MAP = 4
+OP_FWD, OP_BWD_INPUT, OP_BWD_WEIGHT = 0, 1, 2
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def library() -> ctypes.CDLL:
+    return _L.load()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = library().moe_status_string(status).decode()
+        raise MoeError(f"{what}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> torch.Tensor:
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    return t
+
+
+def _out(out, shape, dtype, device, name):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(out, name, dtype)
+    if tuple(out.shape) != tuple(shape):
+        raise MoeError(f"{name} must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    return out
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def moe_permute_workspace_size(T: int, top_k: int, E: int) -> int:
+    return int(library().moe_permute_workspace_size(T, top_k, E))
+
+
+def gmm_workspace_size(E: int, M_cap: int, K: int, N: int, op: int) -> int:
+    return int(library().gmm_workspace_size(E, M_cap, K, N, op))
+
+
+def moe_permute(x, topk_ids, num_experts: int, *, out=None, ws=None, dev_err=None):
+    """Histogram + stable permute.  Returns (x_perm, row_id_map, sorted_slot,
+    tokens_per_expert); see moe_permute in include/moegmm.h."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, H = x.shape
+    top_k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise MoeError("topk_ids must be [T, top_k]")
+    S = T * top_k
+    dev = x.device
+    if out is None:
+        out = (None, None, None, None)
+    x_perm = _out(out[0], (S, H), torch.bfloat16, dev, "x_perm")
+    row_id_map = _out(out[1], (S,), torch.int32, dev, "row_id_map")
+    sorted_slot = _out(out[2], (S,), torch.int32, dev, "sorted_slot")
+    tpe = _out(out[3], (num_experts,), torch.int64, dev, "tokens_per_expert")
+    nbytes = moe_permute_workspace_size(T, top_k, num_experts)
+    ws, ws_bytes = _workspace(nbytes, dev, ws)
+    _check(library().moe_permute(_ptr(x), _ptr(topk_ids), T, top_k, H, num_experts, _ptr(x_perm),
+                                 _ptr(row_id_map), _ptr(sorted_slot), _ptr(tpe), _ptr(ws), ws_bytes,
+                                 _ptr(dev_err), _stream(dev)), "moe_permute")
+    return x_perm, row_id_map, sorted_slot, tpe
+
+
+def gmm_fwd(x, w, group_list, *, out=None, ws=None, dev_err=None):
+    """y[rows_e] = x[rows_e] @ w[e] for every expert e."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, K = x.shape
+    E, K2, N = w.shape
+    if K2 != K or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: x [M, K], w [E, K, N], group_list [E]")
+    y = _out(out, (M, N), torch.bfloat16, x.device, "y")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_FWD), x.device, ws)
+    _check(library().gmm_fwd(_ptr(x), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(y), _ptr(ws),
+                             ws_bytes, _ptr(dev_err), _stream(x.device)), "gmm_fwd")
+    return y
+
+
+def gmm_bwd_input(dy, w, group_list, *, out=None, ws=None, dev_err=None):
+    """dx[rows_e] = dy[rows_e] @ w[e]^T."""
+    _dev(dy, "dy", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, N = dy.shape
+    E, K, N2 = w.shape
+    if N2 != N or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: dy [M, N], w [E, K, N], group_list [E]")
+    dx = _out(out, (M, K), torch.bfloat16, dy.device, "dx")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_INPUT), dy.device, ws)
+    _check(library().gmm_bwd_input(_ptr(dy), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(dx),
+                                   _ptr(ws), ws_bytes, _ptr(dev_err), _stream(dy.device)),
+           "gmm_bwd_input")
+    return dx
+
+
+def gmm_bwd_weight(x, dy, group_list, *, out=None, ws=None, dev_err=None):
+    """dw[e] = x[rows_e]^T @ dy[rows_e]; zeros for empty experts."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(dy, "dy", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, K = x.shape
+    M2, N = dy.shape
+    E = group_list.shape[0]
+    if M2 != M:
+        raise MoeError("shape mismatch: x [M, K], dy [M, N]")
+    dw = _out(out, (E, K, N), torch.bfloat16, x.device, "dw")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_WEIGHT), x.device, ws)
+    _check(library().gmm_bwd_weight(_ptr(x), _ptr(dy), _ptr(group_list), E, M, K, N, _ptr(dw),
+                                    _ptr(ws), ws_bytes, _ptr(dev_err), _stream(x.device)),
+           "gmm_bwd_weight")
+    return dw
+
+
+def swiglu(h, group_list, *, out=None):
+    """a = SiLU(h[:, :I]) * h[:, I:] for rows < sum(group_list)."""
+    _dev(h, "h", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, I2 = h.shape
+    I = I2 // 2
+    a = _out(out, (M, I), torch.bfloat16, h.device, "a")
+    _check(library().swiglu(_ptr(h), _ptr(group_list), group_list.shape[0], M, I, _ptr(a),
+                            _stream(h.device)), "swiglu")
+    return a
+
+
+def swiglu_bwd(da, h, group_list, *, out=None):
+    """dh = [dG | dU] for a = SiLU(G) * U."""
+    _dev(da, "da", torch.bfloat16)
+    _dev(h, "h", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, I2 = h.shape
+    I = I2 // 2
+    if tuple(da.shape) != (M, I):
+        raise MoeError("da must be [M, I] for h [M, 2I]")
+    dh = _out(out, (M, I2), torch.bfloat16, h.device, "dh")
+    _check(library().swiglu_bwd(_ptr(da), _ptr(h), _ptr(group_list), group_list.shape[0], M, I,
+                                _ptr(dh), _stream(h.device)), "swiglu_bwd")
+    return dh
+
+
+def moe_unpermute(y_perm, row_id_map, probs, *, out=None, dev_err=None):
+    """out[t] = sum_k probs[t,k] * y_perm[row_id_map[t*K+k]] (fp32, one rounding)."""
+    _dev(y_perm, "y_perm", torch.bfloat16)
+    _dev(row_id_map, "row_id_map", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    T, top_k = probs.shape
+    S, H = y_perm.shape
+    if S != T * top_k or row_id_map.numel() != S:
+        raise MoeError("y_perm must be [T*top_k, H] and row_id_map [T*top_k]")
+    o = _out(out, (T, H), torch.bfloat16, y_perm.device, "out")
+    _check(library().moe_unpermute(_ptr(y_perm), _ptr(row_id_map), _ptr(probs), T, top_k, H,
+                                   _ptr(o), _ptr(dev_err), _stream(y_perm.device)), "moe_unpermute")
+    return o

@@ -1,0 +1,149 @@
+// C ABI of libmoegmm: argument validation, workspace sizing and dispatch to
+// the gfx950 kernels.  Host-checkable problems return a status before
+// anything is enqueued, in the spirit of the two-phase interface of the
+// MoeTokenPermuteWithRoutingMapGrad article (sections 3 and 4.2-4.3: check
+// null and invalid arguments, report a workspace size, then execute), and of
+// "MegaMoE" (constraints: mismatched arguments are rejected, never silently
+// handled another way).
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "moegmm.h"
+
+namespace {
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxTopK = 32;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool dim_ok(int64_t d) { return d > 0 && d % 8 == 0 && d <= (int64_t(1) << 24); }
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status check_gmm_common(const void* a, const void* b, const void* gl, const void* out,
+                            int64_t E, int64_t M_cap, int64_t K, int64_t N, size_t ws_need,
+                            size_t ws_bytes, const void* ws) {
+    if (!gl || (M_cap > 0 && (!a || !out)) || !b) return MOE_ERR_NULL;
+    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(K) || !dim_ok(N))
+        return MOE_ERR_INVALID;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(gl, 8))
+        return MOE_ERR_INVALID;
+    if (M_cap * K > (int64_t(1) << 40) || M_cap * N > (int64_t(1) << 40)) return MOE_ERR_INVALID;
+    if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_INVALID: return "MOE_ERR_INVALID: a size, limit or alignment is out of range";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than the queried size";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: the HIP runtime rejected a launch";
+    }
+    return "unknown moe_status";
+}
+
+int moegmm_abi_version(void) { return 1; }
+
+size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
+    if (T < 0 || top_k < 1 || E < 1) return 0;
+    return moegmm::permute_workspace_bytes(T * top_k, E);
+}
+
+moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                       int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                       int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
+                       size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!tokens_per_expert || !ws) return MOE_ERR_NULL;
+    if (T > 0 && (!x || !topk_ids || !x_perm || !row_id_map || !sorted_slot)) return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || !dim_ok(H))
+        return MOE_ERR_INVALID;
+    if (T * top_k > kMaxRows) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_ids, 4) ||
+        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) || !aligned(tokens_per_expert, 8) ||
+        !aligned(ws, 4))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < moegmm::permute_workspace_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
+    return from_hip(moegmm::launch_permute(x, topk_ids, T, top_k, H, E, x_perm, row_id_map,
+                                           sorted_slot, tokens_per_expert, ws, dev_err,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op) {
+    return moegmm::gmm_workspace_bytes(E, M_cap, K, N, op);
+}
+
+moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list, int64_t E,
+                   int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
+                   int32_t* dev_err, void* stream) {
+    moe_status st = check_gmm_common(x, w, group_list, y, E, M_cap, K, N,
+                                     moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_FWD),
+                                     ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    return from_hip(moegmm::launch_gmm_fwd(x, w, group_list, E, M_cap, K, N, y, ws, dev_err,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
+                         int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx, void* ws,
+                         size_t ws_bytes, int32_t* dev_err, void* stream) {
+    moe_status st = check_gmm_common(
+        dy, w, group_list, dx, E, M_cap, K, N,
+        moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_BWD_INPUT), ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    return from_hip(moegmm::launch_gmm_bwd_input(dy, w, group_list, E, M_cap, K, N, dx, ws, dev_err,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
+                          int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,
+                          size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!dw) return MOE_ERR_NULL;
+    if (M_cap > 0 && !dy) return MOE_ERR_NULL;
+    moe_status st = check_gmm_common(
+        x, dy ? dy : x, group_list, dw, E, M_cap, K, N,
+        moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_BWD_WEIGHT), ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    if (!aligned(dw, 16)) return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_bwd_weight(x, dy, group_list, E, M_cap, K, N, dw, ws,
+                                                  dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                  int64_t I, uint16_t* a, void* stream) {
+    if (!group_list || (M_cap > 0 && (!h || !a))) return MOE_ERR_NULL;
+    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(I)) return MOE_ERR_INVALID;
+    if (!aligned(h, 16) || !aligned(a, 16) || !aligned(group_list, 8)) return MOE_ERR_INVALID;
+    return from_hip(
+        moegmm::launch_swiglu(h, group_list, E, M_cap, I, a, static_cast<hipStream_t>(stream)));
+}
+
+moe_status swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_t* group_list, int64_t E,
+                      int64_t M_cap, int64_t I, uint16_t* dh, void* stream) {
+    if (!group_list || (M_cap > 0 && (!h || !da || !dh))) return MOE_ERR_NULL;
+    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(I)) return MOE_ERR_INVALID;
+    if (!aligned(h, 16) || !aligned(da, 16) || !aligned(dh, 16) || !aligned(group_list, 8))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_swiglu_bwd(da, h, group_list, E, M_cap, I, dh,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, const float* probs,
+                         int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
+                         void* stream) {
+    if (T > 0 && (!y_perm || !row_id_map || !probs || !out)) return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || !dim_ok(H) || T * top_k > kMaxRows)
+        return MOE_ERR_INVALID;
+    if (!aligned(y_perm, 16) || !aligned(out, 16) || !aligned(row_id_map, 4) || !aligned(probs, 4))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

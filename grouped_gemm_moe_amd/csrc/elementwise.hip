@@ -1,0 +1,174 @@
+// SwiGLU, its backward, and the probs-weighted unpermute for gfx950.
+//
+// SwiGLU follows "MegaMoE" (activation formulas: sigma(z) = 1/(1+e^-z),
+// SiLU(z) = z*sigma(z), A = SiLU(G) * U with the clamp unset), with G the
+// first I and U the last I columns of the gate_up output ("NPU Training
+// Operators - GMM", section "Qwen3.5 MoE 路径": one gate_up GMM, then a
+// SwiGLU split).  The backward is derived by calculus (not on the pages).
+//
+// The unpermute follows "MegaMoE" (A16W16 Token Combine: each token sums its
+// top-k expert rows weighted by the gate weights, in token order) and the
+// MoeTokenPermuteWithRoutingMapGrad article (section 6.2: per output token,
+// walk the top-k slots, skip -1, accumulate in FP32, cast back once).  Each
+// token is owned by one workgroup and summed in ascending k, so the result is
+// deterministic with no atomics.
+//
+// All three are HBM-bound streams: 16-byte loads and stores, fp32 math.
+#include "common.h"
+#include "launch.h"
+
+namespace moegmm {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxGrid = 2048;
+
+MOE_DEVICE float silu_sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// Rows r < R (R from group_list), 8 columns of the I outputs per work item.
+__global__ __launch_bounds__(kThreads) void swiglu_kernel(const bf16_t* __restrict__ h,
+                                                          const int64_t* __restrict__ group_list,
+                                                          int E, int64_t M_cap, int64_t I,
+                                                          bf16_t* __restrict__ a) {
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int64_t s_scan[kThreads / 64];
+    const int R = load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, nullptr);
+    const int64_t cpr = I / 8;
+    const int64_t items = (int64_t)R * cpr;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < items;
+         u += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = u / cpr, c = u - r * cpr;
+        const bf16_t* hr = h + r * 2 * I;
+        const u32x4_t g = ld16(hr + c * 8);
+        const u32x4_t up = ld16(hr + I + c * 8);
+        u32x4_t o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const float g0 = bf16_lo(g[d]), g1 = bf16_hi(g[d]);
+            const float u0 = bf16_lo(up[d]), u1 = bf16_hi(up[d]);
+            o[d] = pack_bf16x2(g0 * silu_sigmoid(g0) * u0, g1 * silu_sigmoid(g1) * u1);
+        }
+        st16(a + r * I + c * 8, o);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(
+    const bf16_t* __restrict__ da, const bf16_t* __restrict__ h, const int64_t* __restrict__ group_list,
+    int E, int64_t M_cap, int64_t I, bf16_t* __restrict__ dh) {
+    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int64_t s_scan[kThreads / 64];
+    const int R = load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, nullptr);
+    const int64_t cpr = I / 8;
+    const int64_t items = (int64_t)R * cpr;
+    for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < items;
+         u += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = u / cpr, c = u - r * cpr;
+        const bf16_t* hr = h + r * 2 * I;
+        const u32x4_t g = ld16(hr + c * 8);
+        const u32x4_t up = ld16(hr + I + c * 8);
+        const u32x4_t d = ld16(da + r * I + c * 8);
+        u32x4_t og, ou;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float gv[2] = {bf16_lo(g[q]), bf16_hi(g[q])};
+            float uv[2] = {bf16_lo(up[q]), bf16_hi(up[q])};
+            float dv[2] = {bf16_lo(d[q]), bf16_hi(d[q])};
+            float rg[2], ru[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float s = silu_sigmoid(gv[t]);
+                rg[t] = dv[t] * uv[t] * s * (1.0f + gv[t] * (1.0f - s));
+                ru[t] = dv[t] * gv[t] * s;
+            }
+            og[q] = pack_bf16x2(rg[0], rg[1]);
+            ou[q] = pack_bf16x2(ru[0], ru[1]);
+        }
+        bf16_t* dr = dh + r * 2 * I;
+        st16(dr + c * 8, og);
+        st16(dr + I + c * 8, ou);
+    }
+}
+
+// One workgroup per token; the row ids and gate weights of the token's top_k
+// slots are read once into LDS.  Each thread owns 8 columns per pass.
+constexpr int kMaxTopK = 32;
+
+__global__ __launch_bounds__(kThreads) void unpermute_kernel(
+    const bf16_t* __restrict__ y_perm, const int32_t* __restrict__ row_id_map,
+    const float* __restrict__ probs, int64_t T, int top_k, int64_t H, bf16_t* __restrict__ out,
+    int32_t* dev_err) {
+    __shared__ int32_t s_row[kMaxTopK];
+    __shared__ float s_p[kMaxTopK];
+    const int64_t t = blockIdx.x;
+    const int64_t S = T * top_k;
+    if (threadIdx.x < top_k) {
+        int32_t r = row_id_map[t * top_k + threadIdx.x];
+        if (r < -1 || r >= S) {
+            if (dev_err) atomicOr(dev_err, MOE_DEVERR_ROW_MAP);
+            r = -1;
+        }
+        s_row[threadIdx.x] = r;
+        s_p[threadIdx.x] = probs[t * top_k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < H; c0 += kThreads * 8) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int k = 0; k < top_k; ++k) {
+            const int32_t r = s_row[k];
+            if (r < 0) continue;
+            const float p = s_p[k];
+            const u32x4_t v = ld16(y_perm + (int64_t)r * H + c0);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                acc[2 * d] = __builtin_fmaf(p, bf16_lo(v[d]), acc[2 * d]);
+                acc[2 * d + 1] = __builtin_fmaf(p, bf16_hi(v[d]), acc[2 * d + 1]);
+            }
+        }
+        u32x4_t o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
+        st16(out + t * H + c0, o);
+    }
+}
+
+int64_t elementwise_grid(int64_t M_cap, int64_t I) {
+    int64_t items = M_cap * (I / 8);
+    int64_t g = (items + kThreads - 1) / kThreads;
+    if (g > kMaxGrid) g = kMaxGrid;
+    return g < 1 ? 1 : g;
+}
+
+}  // namespace
+
+hipError_t launch_swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                         int64_t I, uint16_t* a, hipStream_t stream) {
+    if (M_cap == 0) return hipSuccess;
+    hipLaunchKernelGGL(swiglu_kernel, dim3((unsigned)elementwise_grid(M_cap, I)), dim3(kThreads), 0,
+                       stream, h, group_list, (int)E, M_cap, I, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_t* group_list,
+                             int64_t E, int64_t M_cap, int64_t I, uint16_t* dh,
+                             hipStream_t stream) {
+    if (M_cap == 0) return hipSuccess;
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)elementwise_grid(M_cap, I)), dim3(kThreads),
+                       0, stream, da, h, group_list, (int)E, M_cap, I, dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, const float* probs,
+                            int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
+                            hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)T), dim3(kThreads), 0, stream, y_perm,
+                       row_id_map, probs, T, (int)top_k, H, out, dev_err);
+    return hipGetLastError();
+}
+
+}  // namespace moegmm

@@ -1,0 +1,40 @@
+// Internal launchers (host side).  Each enqueues kernels on `stream` and
+// returns hipGetLastError(); argument validation happens in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moegmm {
+
+// permute.hip
+size_t permute_workspace_bytes(int64_t S, int64_t E);
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                          int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                          int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
+                          int32_t* dev_err, hipStream_t stream);
+
+// gmm.hip
+size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
+hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
+                          int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws,
+                          int32_t* dev_err, hipStream_t stream);
+hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
+                                int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx,
+                                void* ws, int32_t* dev_err, hipStream_t stream);
+hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
+                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw,
+                                 void* ws, int32_t* dev_err, hipStream_t stream);
+
+// elementwise.hip
+hipError_t launch_swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                         int64_t I, uint16_t* a, hipStream_t stream);
+hipError_t launch_swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_t* group_list,
+                             int64_t E, int64_t M_cap, int64_t I, uint16_t* dh,
+                             hipStream_t stream);
+hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, const float* probs,
+                            int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
+                            hipStream_t stream);
+
+}  // namespace moegmm

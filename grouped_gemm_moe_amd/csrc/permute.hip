@@ -1,0 +1,218 @@
+// moe_permute on gfx950: histogram of expert ids, stable grouping of slots by
+// expert, and the gather of token rows into expert-contiguous order.
+//
+// What is computed follows "NPU Training Operators - GMM" (section
+// "Qwen3.5 MoE 路径": permute by the selected experts, tokens_per_expert as a
+// histogram of the ids; section 算子语义: the worked example, whose permuted
+// order lists each expert's tokens in token order) and "MegaMoE" (A16W16
+// Dispatch: X_e stacks the tokens routed to e in a fixed order, row(i,k) finds
+// token i in it).  The fixed order chosen here is ascending slot index, which
+// makes every output unique and bit-reproducible; no float is involved.
+//
+// Kernels (all deterministic; the only atomics are integer counts in LDS):
+//   1. hist    -- one block per chunk of slots: per-block expert histogram.
+//   2. scan    -- one block: per expert, an exclusive prefix over blocks, then
+//                 the expert offsets (exclusive scan over experts); writes
+//                 tokens_per_expert and turns the histogram into per-block
+//                 starting rows.
+//   3. scatter -- one block per chunk: each wave ranks its slots within the
+//                 expert in slot order (wave ballots emulate a match-any on
+//                 the expert id) and writes row_id_map and sorted_slot.
+//   4. gather  -- copies token rows to their permuted rows with 16-byte loads
+//                 and stores (coalesced inside each row).
+#include "common.h"
+#include "launch.h"
+
+namespace moegmm {
+
+namespace {
+
+constexpr int kPermThreads = 256;          // 4 waves
+constexpr int kWaves = kPermThreads / 64;
+
+// Slots per block: a multiple of 4*64 so that each wave gets whole groups of
+// 64; grown with S so the number of blocks stays <= 4096.
+int64_t permute_chunk(int64_t S) {
+    const int64_t base = 1024;
+    int64_t mult = (S + base * 4096 - 1) / (base * 4096);
+    if (mult < 1) mult = 1;
+    return base * mult;
+}
+
+MOE_DEVICE bool valid_id(int32_t id, int E) { return id >= 0 && id < E; }
+
+__global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t chunk, int32_t* __restrict__ blk_hist,
+    int32_t* dev_err) {
+    __shared__ int32_t hist[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int64_t s0 = (int64_t)blockIdx.x * chunk;
+    const int64_t s1 = s0 + chunk < S ? s0 + chunk : S;
+    int bad = 0;
+    for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
+        int32_t id = ids[s];
+        if (valid_id(id, E)) atomicAdd(&hist[id], 1);
+        else if (id != -1) bad = 1;
+    }
+    if (bad && dev_err) atomicOr(dev_err, MOE_DEVERR_EXPERT_ID);
+    __syncthreads();
+    int32_t* out = blk_hist + (int64_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
+}
+
+// One block.  Thread i owns experts [i*per, i*per + per) so that the scan
+// over threads runs in ascending expert order.
+__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
+    int32_t* __restrict__ blk_hist, int64_t nblk, int E, int64_t* __restrict__ tokens_per_expert) {
+    __shared__ int64_t scan_tmp[kPermThreads / 64];
+    const int per = (E + blockDim.x - 1) / blockDim.x;
+    const int e0 = threadIdx.x * per;
+    int64_t cnt[4] = {0, 0, 0, 0};
+    int64_t mine = 0;
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        int64_t c = 0;
+        for (int64_t b = 0; b < nblk; ++b) c += blk_hist[b * E + e];
+        cnt[i] = c;
+        mine += c;
+    }
+    int64_t total;
+    int64_t off = block_exclusive_scan<int64_t>(mine, scan_tmp, &total);
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        tokens_per_expert[e] = cnt[i];
+        int64_t run = off;
+        for (int64_t b = 0; b < nblk; ++b) {
+            int32_t v = blk_hist[b * E + e];
+            blk_hist[b * E + e] = (int32_t)run;
+            run += v;
+        }
+        off += cnt[i];
+    }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t chunk,
+    const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_id_map,
+    int32_t* __restrict__ sorted_slot) {
+    __shared__ int32_t next_row[kWaves][kMaxExperts];
+    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
+    __syncthreads();
+
+    const int64_t s0 = (int64_t)blockIdx.x * chunk;
+    const int64_t sub = chunk / kWaves;             // slots per wave, multiple of 64
+    const int64_t w0 = s0 + wid * sub;
+    int64_t w1 = w0 + sub;
+    if (w1 > S) w1 = S;
+
+    // 1. per-wave counts per expert
+    for (int64_t s = w0 + lane; s < w1; s += 64) {
+        int32_t id = ids[s];
+        if (valid_id(id, E)) atomicAdd(&next_row[wid][id], 1);
+    }
+    __syncthreads();
+    // 2. starting row of every wave for every expert
+    const int32_t* base = blk_base + (int64_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t run = base[e];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            int32_t c = next_row[w][e];
+            next_row[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // 3. stable rank within each group of 64 slots, groups in order
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t g = w0; g < w1; g += 64) {
+        const int64_t s = g + lane;
+        int32_t id = (s < w1) ? ids[s] : -1;
+        const bool ok = valid_id(id, E);
+        const int key = ok ? id : 0;
+        uint64_t peers = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (key >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        int32_t row = -1;
+        if (ok) row = next_row[wid][key] + __popcll(peers & lt_mask);
+        // all lanes have read next_row before the leaders update it
+        __builtin_amdgcn_wave_barrier();
+        if (ok && (peers & lt_mask) == 0) next_row[wid][key] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+        if (s < w1) {
+            row_id_map[s] = row;
+            if (ok) sorted_slot[row] = (int32_t)s;
+        }
+    }
+}
+
+constexpr int kGatherSlots = 16;  // slots per block
+
+__global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t S, int top_k,
+    int64_t H, uint16_t* __restrict__ x_perm) {
+    __shared__ int32_t rows[kGatherSlots];
+    const int64_t s0 = (int64_t)blockIdx.x * kGatherSlots;
+    if (threadIdx.x < kGatherSlots) {
+        const int64_t s = s0 + threadIdx.x;
+        int32_t r = (s < S) ? row_id_map[s] : -1;
+        rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
+    }
+    __syncthreads();
+    const int64_t cpr = H / 8;  // 16-byte chunks per row
+    const int64_t total = (int64_t)kGatherSlots * cpr;
+    for (int64_t i = threadIdx.x; i < total; i += blockDim.x) {
+        const int ls = (int)(i / cpr);
+        const int64_t c = i - ls * cpr;
+        const int32_t r = rows[ls];
+        if (r < 0) continue;
+        const int64_t t = (s0 + ls) / top_k;
+        st16(x_perm + (int64_t)r * H + c * 8, ld16(x + t * H + c * 8));
+    }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int64_t S, int64_t E) {
+    const int64_t chunk = permute_chunk(S);
+    const int64_t nblk = (S + chunk - 1) / chunk;
+    size_t bytes = (size_t)(nblk * E) * sizeof(int32_t);
+    bytes = (bytes + 255) / 256 * 256;
+    return bytes < 256 ? 256 : bytes;
+}
+
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                          int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                          int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
+                          int32_t* dev_err, hipStream_t stream) {
+    const int64_t S = T * top_k;
+    const int64_t chunk = permute_chunk(S);
+    const int64_t nblk = (S + chunk - 1) / chunk;
+    int32_t* blk = static_cast<int32_t*>(ws);
+    if (nblk > 0) {
+        hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0, stream,
+                           ids, S, (int)E, chunk, blk, dev_err);
+    }
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
+                       (int)E, tokens_per_expert);
+    if (nblk > 0) {
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
+                           stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
+        const int64_t gblk = (S + kGatherSlots - 1) / kGatherSlots;
+        hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)gblk), dim3(kPermThreads), 0,
+                           stream, x, row_id_map, S, (int)top_k, H, x_perm);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moegmm

@@ -1,0 +1,194 @@
+/*
+ * moegmm.h -- C ABI of the routed-expert MoE hot path for AMD MI355X (gfx950).
+ *
+ * What the calls compute (sources are web pages, cited by title and section):
+ *
+ *   [GMM]       "NPU Training Operators - GMM": section 算子语义 (operator
+ *               semantics) -- the per-expert loop over row ranges taken from
+ *               the cumulative sum of group_list, the input table
+ *               (x[sum(group_list), hidden], weight[num_experts, hidden, out]),
+ *               the worked example with an empty expert, and the two backward
+ *               products right after it; section "Qwen3.5 MoE 路径" -- the
+ *               chain permute -> histc -> gate_up GMM -> SwiGLU -> down GMM ->
+ *               probs-weighted unpermute, and its GMM shape table.
+ *   [MegaMoE]   "MegaMoE" (ops-transformer mc2/mega_moe): section 功能说明,
+ *               activation formulas (SwiGLU), the A16W16 scenario (Dispatch,
+ *               Expert Compute, Token Combine), and the parameter table
+ *               (topkIds int32 in [0, experts), topK in [1, 32]).
+ *   [PermGrad]  "CANN ops-transformer 算子详解：MoeTokenPermuteWithRoutingMapGrad":
+ *               section 3 (size query, then execute with a caller workspace),
+ *               section 4.1 (-1 marks an invalid slot), section 4.3 (null and
+ *               invalid arguments are reported before any work), section 6.2
+ *               (FP32 accumulation over a token's top-k slots, one cast back).
+ *   [MegaBlocks] "03 · grouped GEMM 路径": section 4.2 -- the grouped GEMM
+ *               there needs the group sizes on the host, a device-to-host
+ *               synchronisation this library avoids: group_list stays on the
+ *               device and every kernel builds its own tile schedule from it.
+ *
+ * Conventions for every call below
+ *   - All tensor pointers are DEVICE pointers to row-major, contiguous memory.
+ *     bf16 tensors are arrays of uint16_t bit patterns; bf16 pointers must be
+ *     16-byte aligned.  Other pointers must be aligned to their element size.
+ *   - The caller owns all memory.  The library never allocates device memory
+ *     and never synchronises: each call only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL means the default stream) and returns.
+ *   - Outputs must not alias inputs.
+ *   - Host-checkable problems (NULL required pointer, sizes out of range,
+ *     misalignment, a workspace smaller than the queried size) return an error
+ *     status BEFORE anything is enqueued.
+ *   - Data-dependent problems are reported through `dev_err` (nullable): a
+ *     device int32 the caller zeroes; kernels OR bits into it
+ *     (MOE_DEVERR_*).  Kernels clamp offending values so that they never read
+ *     or write out of bounds; outputs are unspecified when a bit is set.  Read
+ *     it after synchronising the stream.
+ *   - Row counts: `group_list` (a.k.a. tokens_per_expert) is a DEVICE int64
+ *     array of per-expert COUNTS n_e; expert e owns rows off_e .. off_e+n_e-1
+ *     where off_e = n_0 + ... + n_{e-1}.  An empty expert owns no row and does
+ *     not shift later offsets.  R = sum(n_e) must not exceed M_cap; rows at or
+ *     beyond R are neither read for results nor written (except as stated).
+ *   - Limits: 1 <= E <= 1024; 1 <= top_k <= 32; T*top_k < 2^31;
+ *     hidden / intermediate / K / N are positive multiples of 8.
+ */
+#ifndef MOEGMM_H
+#define MOEGMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    MOE_ERR_INVALID = 2,   /* a size, limit or alignment is out of range        */
+    MOE_ERR_WORKSPACE = 3, /* ws_bytes is below the size the query returned     */
+    MOE_ERR_LAUNCH = 4     /* the HIP runtime rejected a launch                 */
+} moe_status;
+
+/* bits OR-ed into *dev_err by the kernels */
+#define MOE_DEVERR_EXPERT_ID 1  /* an expert id outside [-1, E)               */
+#define MOE_DEVERR_GROUP_LIST 2 /* a negative count, or sum(group_list) > M_cap */
+#define MOE_DEVERR_ROW_MAP 4    /* a row_id_map entry outside [-1, T*top_k)   */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* ABI version of this header; bumped on any signature change. */
+int moegmm_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- histogram + stable permute of token rows by expert.
+ * [GMM] "Qwen3.5 MoE 路径": token permute by selected experts, and
+ * tokens_per_expert as a histogram of the selected ids; worked example in
+ * 算子语义.  [MegaMoE] A16W16 Dispatch: X_e stacks the tokens routed to e in a
+ * fixed order and row(i,k) locates token i in it.  [PermGrad] 4.1: id -1
+ * marks a slot that takes no part.
+ *
+ *   x          [T, H] bf16             token rows
+ *   topk_ids   [T, top_k] int32        expert of each slot s = t*top_k + k, or -1
+ *   x_perm     [T*top_k, H] bf16  OUT  row r = x[sorted_slot[r] / top_k], r < R;
+ *                                      rows >= R untouched
+ *   row_id_map [T*top_k] int32    OUT  slot -> row, -1 for a masked slot
+ *   sorted_slot[T*top_k] int32    OUT  row -> slot for r < R; entries >= R untouched
+ *   tokens_per_expert [E] int64   OUT  n_e (this is the group_list of the GMMs)
+ *   ws / ws_bytes                      caller workspace, >= moe_permute_workspace_size
+ * Rows are grouped by expert in ascending expert order and, inside an expert,
+ * in ascending slot order -- so the result is unique and bit-reproducible.
+ * Ids outside [-1, E) set MOE_DEVERR_EXPERT_ID and are treated as masked.
+ * T == 0 is allowed (tokens_per_expert is zeroed).
+ * ---------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E);
+moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                       int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                       int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
+                       size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_fwd -- grouped matmul  y[off_e + i, :] = x[off_e + i, :] @ w[e]  for
+ * every expert e and 0 <= i < n_e.   [GMM] 算子语义: the per-expert loop and
+ * its input table; [MegaMoE] Expert Compute: H_e = X_e W1[e], Y_e = A_e W2[e].
+ *
+ *   x [M_cap, K] bf16, w [E, K, N] bf16, group_list [E] int64 (device),
+ *   y [M_cap, N] bf16 OUT (rows < R written; rows >= R untouched).
+ * bf16 products accumulate in fp32; each output is rounded once (RNE).
+ * w[e] of an empty expert is never read.
+ * ---------------------------------------------------------------------- */
+size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
+#define MOE_GMM_OP_FWD 0
+#define MOE_GMM_OP_BWD_INPUT 1
+#define MOE_GMM_OP_BWD_WEIGHT 2
+moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list, int64_t E,
+                   int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
+                   int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_bwd_input -- dx[off_e + i, :] = dy[off_e + i, :] @ w[e]^T.
+ * [GMM] 算子语义, backward: the input gradient is the output gradient times
+ * the transposed weight, over the same group boundaries.
+ *
+ *   dy [M_cap, N] bf16, w [E, K, N] bf16, group_list [E] int64,
+ *   dx [M_cap, K] bf16 OUT (rows < R written; rows >= R untouched).
+ * ---------------------------------------------------------------------- */
+moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
+                         int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx, void* ws,
+                         size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_bwd_weight -- dw[e] = x[rows_e]^T @ dy[rows_e]   (sum over the n_e rows).
+ * [GMM] 算子语义, backward: the weight gradient of each expert is its input
+ * rows transposed times its output-gradient rows.
+ *
+ *   x [M_cap, K] bf16, dy [M_cap, N] bf16, group_list [E] int64,
+ *   dw [E, K, N] bf16 OUT -- every expert written; exact zeros for n_e == 0.
+ * The reduction order is fixed, so the result is bit-reproducible.
+ * ---------------------------------------------------------------------- */
+moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
+                          int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,
+                          size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * swiglu -- a[r, j] = SiLU(h[r, j]) * h[r, I + j],  SiLU(z) = z / (1 + e^-z),
+ * for rows r < R = sum(group_list) (clamped to M_cap).  gate = first I
+ * columns, up = last I columns; no clamp.  [MegaMoE] activation formulas,
+ * swiglu with the clamp unset; [GMM] "Qwen3.5 MoE 路径": one gate_up GMM then
+ * a SwiGLU split.
+ *
+ *   h [M_cap, 2I] bf16, a [M_cap, I] bf16 OUT (rows >= R untouched).
+ * fp32 arithmetic, one RNE rounding per output.
+ * ---------------------------------------------------------------------- */
+moe_status swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                  int64_t I, uint16_t* a, void* stream);
+
+/* ------------------------------------------------------------------------
+ * swiglu_bwd -- derivative of swiglu (derived by calculus; not on the pages):
+ *   s = sigma(G);  dG = dA * U * s * (1 + G (1 - s));  dU = dA * G * s;
+ *   dh = [dG | dU]  for rows r < R.
+ *
+ *   da [M_cap, I] bf16, h [M_cap, 2I] bf16, dh [M_cap, 2I] bf16 OUT.
+ * ---------------------------------------------------------------------- */
+moe_status swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_t* group_list, int64_t E,
+                      int64_t M_cap, int64_t I, uint16_t* dh, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_unpermute -- probs-weighted combine back to token order:
+ *   out[t, :] = sum over k = 0..top_k-1 with row_id_map[t*top_k+k] >= 0 of
+ *               probs[t, k] * y_perm[row_id_map[t*top_k + k], :]
+ * accumulated in fp32 in ascending k, rounded once (RNE); a token with no
+ * valid slot gets zeros.  [MegaMoE] Token Combine; [PermGrad] 6.2.
+ *
+ *   y_perm [T*top_k, H] bf16, row_id_map [T*top_k] int32, probs [T, top_k] fp32,
+ *   out [T, H] bf16 OUT.
+ * Entries of row_id_map outside [-1, T*top_k) set MOE_DEVERR_ROW_MAP and are
+ * skipped.  Deterministic: no atomics.
+ * ---------------------------------------------------------------------- */
+moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, const float* probs,
+                         int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEGMM_H */

@@ -1,0 +1,125 @@
+"""C-ABI boundary checks that need no GPU.
+
+* libmoegmm.so loads and exports every function include/moegmm.h declares.
+* Host-side validation returns an error status before anything is enqueued
+  (null pointers, sizes out of range, misalignment, small workspace); these
+  calls never reach the HIP runtime.
+* Workspace size queries.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from grouped_gemm_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moegmm.h")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID, MOE_ERR_WORKSPACE = 0, 1, 2, 3
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_bwd_input",
+              "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
+              "moe_status_string", "moegmm_abi_version"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in _declared_functions():
+        assert n in exported, f"{n} declared in moegmm.h but not exported"
+        assert hasattr(lib, n)
+    assert set(_lib.SIGNATURES) == set(_declared_functions())
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moegmm_abi_version() == _lib.ABI_VERSION
+    for s in range(5):
+        assert lib.moe_status_string(s).decode().startswith("MOE_")
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_workspace_queries(lib):
+    assert lib.moe_permute_workspace_size(4096, 8, 128) >= 32 * 128 * 4
+    assert lib.moe_permute_workspace_size(0, 8, 128) >= 0
+    assert lib.moe_permute_workspace_size(-1, 8, 128) == 0
+    for op in range(3):
+        assert lib.gmm_workspace_size(32, 16384, 4096, 3072, op) >= 0
+
+
+# fake but aligned non-null device addresses: validation must reject the call
+# before any of them is touched
+A16 = ctypes.c_void_p(0x10000)
+A16b = ctypes.c_void_p(0x20000)
+A16c = ctypes.c_void_p(0x30000)
+MIS = ctypes.c_void_p(0x10002)
+
+
+def test_gmm_rejects_bad_arguments(lib):
+    ws = ctypes.c_void_p(0x40000)
+    # null weight / group_list
+    assert lib.gmm_fwd(A16, None, A16b, 4, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_NULL
+    assert lib.gmm_fwd(A16, A16b, None, 4, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_NULL
+    # E out of range, K not a multiple of 8, negative M_cap
+    assert lib.gmm_fwd(A16, A16b, A16c, 0, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd(A16, A16b, A16c, 1025, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd(A16, A16b, A16c, 4, 64, 60, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd(A16, A16b, A16c, 4, -1, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    # misaligned bf16 pointer
+    assert lib.gmm_fwd(MIS, A16b, A16c, 4, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_bwd_input(A16, MIS, A16c, 4, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, None, ws, 0, None, None) == MOE_ERR_NULL
+    assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, MIS, ws, 0, None, None) == MOE_ERR_INVALID
+
+
+def test_permute_rejects_bad_arguments(lib):
+    need = lib.moe_permute_workspace_size(64, 8, 256)
+    ws = ctypes.c_void_p(0x50000)
+    args = dict(x=A16, ids=A16b, T=64, k=8, H=2048, E=256, xp=A16c, rmap=A16, ss=A16b, tpe=A16c)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_permute(a["x"], a["ids"], a["T"], a["k"], a["H"], a["E"], a["xp"], a["rmap"],
+                               a["ss"], a["tpe"], kw.get("ws", ws), kw.get("wsb", need), None, None)
+
+    assert call(x=None) == MOE_ERR_NULL
+    assert call(tpe=None) == MOE_ERR_NULL
+    assert call(ws=None) == MOE_ERR_NULL
+    assert call(k=0) == MOE_ERR_INVALID
+    assert call(k=33) == MOE_ERR_INVALID
+    assert call(E=0) == MOE_ERR_INVALID
+    assert call(E=1025) == MOE_ERR_INVALID
+    assert call(H=100) == MOE_ERR_INVALID
+    assert call(T=-1) == MOE_ERR_INVALID
+    assert call(x=MIS) == MOE_ERR_INVALID
+    assert call(wsb=need - 1) == MOE_ERR_WORKSPACE
+
+
+def test_elementwise_reject_bad_arguments(lib):
+    assert lib.swiglu(A16, None, 4, 64, 64, A16b, None) == MOE_ERR_NULL
+    assert lib.swiglu(A16, A16c, 4, 64, 60, A16b, None) == MOE_ERR_INVALID
+    assert lib.swiglu(MIS, A16c, 4, 64, 64, A16b, None) == MOE_ERR_INVALID
+    assert lib.swiglu_bwd(A16, A16b, A16c, 4, 64, 64, None, None) == MOE_ERR_NULL
+    assert lib.moe_unpermute(A16, None, A16b, 4, 2, 64, A16c, None, None) == MOE_ERR_NULL
+    assert lib.moe_unpermute(A16, A16b, A16c, 4, 33, 64, A16c, None, None) == MOE_ERR_INVALID
+    assert lib.moe_unpermute(A16, A16b, A16c, 4, 2, 12, A16c, None, None) == MOE_ERR_INVALID

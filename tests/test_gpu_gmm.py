@@ -1,0 +1,253 @@
+"""gmm_fwd / gmm_bwd_input / gmm_bwd_weight on the GPU vs the oracle.
+
+Tolerance: rtol = atol = 1e-2 elementwise (the bf16 fused-vs-eager tolerance
+of "NPU Training Operators - GMM", conclusions and verification table).
+Only rows < R = sum(group_list) are compared; rows >= R must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import grouped_gemm_moe_amd as moe
+import oracle
+import workloads
+from tests.gpu_util import assert_close, bf16_dev, dev_bits, dev_f64, f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SENT = np.uint16(0x7FC1)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _gl(dev, gl):
+    return torch.from_numpy(np.asarray(gl, dtype=np.int64)).to(dev)
+
+
+def _sentinel(dev, shape):
+    return bf16_dev(np.full(shape, SENT, dtype=np.uint16), dev)
+
+
+def run_all(dev, x_bits, w_bits, dy_bits, gl, tag):
+    """Run fwd, dX and dW; return host arrays (float64) and the error word."""
+    M, K = x_bits.shape
+    E, _, N = w_bits.shape
+    print(f"gmm {tag}: E={E} M={M} K={K} N={N} R={int(np.sum(gl))}", flush=True)
+    x, w, dy, g = bf16_dev(x_bits, dev), bf16_dev(w_bits, dev), bf16_dev(dy_bits, dev), _gl(dev, gl)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = moe.gmm_fwd(x, w, g, out=_sentinel(dev, (M, N)), dev_err=err)
+    dx = moe.gmm_bwd_input(dy, w, g, out=_sentinel(dev, (M, K)), dev_err=err)
+    dw = moe.gmm_bwd_weight(x, dy, g, out=_sentinel(dev, (E, K, N)), dev_err=err)
+    torch.cuda.synchronize()
+    return dev_bits(y), dev_bits(dx), dev_bits(dw), int(err.item())
+
+
+def check_all(dev, x_bits, w_bits, dy_bits, gl, tag):
+    y, dx, dw, err = run_all(dev, x_bits, w_bits, dy_bits, gl, tag)
+    assert err == 0
+    R = int(np.sum(gl))
+    x, w, dy = f64(x_bits), f64(w_bits), f64(dy_bits)
+    assert_close(f64(y)[:R], oracle.gmm(x, w, gl)[:R], f"{tag} fwd")
+    assert_close(f64(dx)[:R], oracle.gmm_bwd_input(dy, w, gl)[:R], f"{tag} dX")
+    assert_close(f64(dw), oracle.gmm_bwd_weight(x, dy, gl), f"{tag} dW")
+    assert (y[R:] == SENT).all() and (dx[R:] == SENT).all(), f"{tag}: rows >= R were written"
+    for e in np.nonzero(np.asarray(gl) == 0)[0]:
+        assert (dw[e] == 0).all(), f"{tag}: dW of empty expert {e} not exactly zero"
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2])
+def test_sweep(dev, variant):
+    wl = workloads.sweep(variant)
+    check_all(dev, wl["x"], wl["w"], wl["dy"], wl["group_list"], f"sweep{variant}")
+
+
+def test_worked_example_shapes(dev):
+    wl = workloads.tiny()
+    rng = np.random.default_rng(0)
+    x = workloads.normal_bf16(rng, (5, 64))
+    dy = workloads.normal_bf16(rng, (5, 64))
+    check_all(dev, x, wl["w1"], dy, [1, 2, 0, 2], "tiny")
+
+
+@pytest.mark.parametrize("M,K,N,gl", [
+    (300, 200, 136, [300]),                   # E=1: dense, ragged tiles in every dim
+    (777, 72, 264, [0, 777, 0]),              # all rows in one expert
+    (513, 520, 128, [1, 0, 255, 0, 0, 257]),  # group sizes around the tile size
+    (129, 8, 8, [64, 1, 64]),                 # tiny K and N
+    (64, 4096, 64, [31, 33]),                 # long reduction, short everything else
+])
+def test_ragged_shapes(dev, M, K, N, gl):
+    rng = np.random.default_rng(M + K + N)
+    E = len(gl)
+    x = workloads.normal_bf16(rng, (M, K))
+    w = workloads.normal_bf16(rng, (E, K, N), 0.05)
+    dy = workloads.normal_bf16(rng, (M, N))
+    check_all(dev, x, w, dy, np.array(gl, dtype=np.int64), f"ragged{M}x{K}x{N}")
+
+
+def test_rows_beyond_R_hold_nan(dev):
+    """Capacity rows past R are undefined memory: NaN there must not leak."""
+    rng = np.random.default_rng(3)
+    M, K, N = 640, 256, 192
+    gl = np.array([100, 0, 200, 57], dtype=np.int64)
+    R = int(gl.sum())
+    x = workloads.normal_bf16(rng, (M, K))
+    dy = workloads.normal_bf16(rng, (M, N))
+    x[R:] = SENT
+    dy[R:] = SENT
+    w = workloads.normal_bf16(rng, (4, K, N), 0.05)
+    check_all(dev, x, w, dy, gl, "nan-tail")
+
+
+def test_empty_expert_weights_never_read(dev):
+    rng = np.random.default_rng(4)
+    M, K, N = 512, 128, 256
+    gl = np.array([0, 200, 0, 0, 312, 0], dtype=np.int64)
+    x = workloads.normal_bf16(rng, (M, K))
+    dy = workloads.normal_bf16(rng, (M, N))
+    w = workloads.normal_bf16(rng, (6, K, N), 0.05)
+    w[gl == 0] = SENT
+    y, dx, dw, err = run_all(dev, x, w, dy, gl, "nan-empty-weights")
+    assert err == 0
+    wf = f64(w)
+    wf[gl == 0] = 0.0
+    assert_close(f64(y), oracle.gmm(f64(x), wf, gl), "fwd with NaN empty weights")
+    assert_close(f64(dx), oracle.gmm_bwd_input(f64(dy), wf, gl), "dX with NaN empty weights")
+    assert (dw[gl == 0] == 0).all()
+
+
+def test_all_experts_empty(dev):
+    rng = np.random.default_rng(5)
+    M, K, N = 128, 64, 64
+    gl = np.zeros(4, dtype=np.int64)
+    x = workloads.normal_bf16(rng, (M, K))
+    dy = workloads.normal_bf16(rng, (M, N))
+    w = workloads.normal_bf16(rng, (4, K, N))
+    y, dx, dw, err = run_all(dev, x, w, dy, gl, "all-empty")
+    assert err == 0 and (y == SENT).all() and (dx == SENT).all() and (dw == 0).all()
+
+
+@pytest.mark.parametrize("skew", [False, True])
+def test_decode_shaped_forward(dev, skew):
+    """E=256, 512 rows: the weight-streaming forward."""
+    wl = workloads.decode(with_weights=True)
+    gl = oracle.tokens_per_expert(wl["topk_ids"], 256)
+    if skew:  # one expert with many rows (several streaming passes)
+        gl = gl.copy()
+        gl[17] += 40
+        gl[200] = 0
+    M = int(gl.sum()) + 7
+    rng = np.random.default_rng(6)
+    x = workloads.normal_bf16(rng, (M, 2048))
+    print(f"decode fwd skew={skew} R={int(gl.sum())}", flush=True)
+    y = moe.gmm_fwd(bf16_dev(x, dev), bf16_dev(wl["w1"], dev), _gl(dev, gl),
+                    out=_sentinel(dev, (M, 1024)))
+    y2 = moe.gmm_fwd(bf16_dev(x[:, :512].copy(), dev), bf16_dev(wl["w2"], dev), _gl(dev, gl),
+                     out=_sentinel(dev, (M, 2048)))
+    torch.cuda.synchronize()
+    R = int(gl.sum())
+    assert_close(dev_f64(y)[:R], oracle.gmm(f64(x), f64(wl["w1"]), gl)[:R], "decode gate_up")
+    assert_close(dev_f64(y2)[:R], oracle.gmm(f64(x[:, :512]), f64(wl["w2"]), gl)[:R], "decode down")
+    assert (dev_bits(y)[R:] == SENT).all()
+
+
+def test_group_list_errors_reported(dev):
+    """sum(group_list) > M_cap and negative counts set the error bit; the
+    kernels clamp to the buffer, so the call itself is safe."""
+    rng = np.random.default_rng(7)
+    M, K, N = 256, 64, 64
+    x = bf16_dev(workloads.normal_bf16(rng, (M, K)), dev)
+    dy = bf16_dev(workloads.normal_bf16(rng, (M, N)), dev)
+    w = bf16_dev(workloads.normal_bf16(rng, (3, K, N)), dev)
+    for gl in ([200, 100, 10], [-5, 100, 10], [0, 0, 1000]):
+        print(f"group_list error case {gl}", flush=True)
+        for fn in ("fwd", "dx", "dw"):
+            err = torch.zeros(1, dtype=torch.int32, device=dev)
+            g = _gl(dev, gl)
+            if fn == "fwd":
+                moe.gmm_fwd(x, w, g, dev_err=err)
+            elif fn == "dx":
+                moe.gmm_bwd_input(dy, w, g, dev_err=err)
+            else:
+                moe.gmm_bwd_weight(x, dy, g, dev_err=err)
+            torch.cuda.synchronize()
+            assert int(err.item()) & moe.DEVERR_GROUP_LIST, (gl, fn)
+
+
+def test_deterministic_repeat(dev):
+    wl = workloads.sweep(1)
+    a = run_all(dev, wl["x"], wl["w"], wl["dy"], wl["group_list"], "repeat-a")
+    b = run_all(dev, wl["x"], wl["w"], wl["dy"], wl["group_list"], "repeat-b")
+    for u, v in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# full size: one expert-parallel rank's share (E=32, H=4096, I=1536, 16384
+# rows, Zipf group sizes with empty experts), sampled outputs computed by the
+# oracle one row / one weight row at a time
+# ---------------------------------------------------------------------------
+
+
+def _sample_rows(gl, rng, per_expert=3):
+    off = oracle.expert_offsets(gl)
+    rows = []
+    for e in range(len(gl)):
+        if gl[e] == 0:
+            continue
+        rows += [off[e], off[e + 1] - 1]
+        rows += list(rng.integers(off[e], off[e + 1], per_expert))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def _expert_of(gl):
+    return np.repeat(np.arange(len(gl)), gl)
+
+
+def test_ep_full_size_sampled(dev):
+    wl = workloads.ep_slice()
+    gl = wl["group_list"]
+    R, E, H, I = 16384, 32, 4096, 1536
+    rng = np.random.default_rng(55)
+    x_b, dy_b = wl["x"], wl["dyp"]
+    dh_b = workloads.normal_bf16(rng, (R, 2 * I))
+    g = _gl(dev, gl)
+    x, dyp, dh = bf16_dev(x_b, dev), bf16_dev(dy_b, dev), bf16_dev(dh_b, dev)
+    w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
+    print("ep full size: fwd(W1), dX(W2), dX(W1), dW1", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = moe.gmm_fwd(x, w1, g, dev_err=err)            # [R, 3072]
+    da = moe.gmm_bwd_input(dyp, w2, g, dev_err=err)   # [R, 1536]
+    dx = moe.gmm_bwd_input(dh, w1, g, dev_err=err)    # [R, 4096]
+    dw1 = moe.gmm_bwd_weight(x, dh, g, dev_err=err)   # [32, 4096, 3072]
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    rows = _sample_rows(gl, rng)
+    eo = _expert_of(gl)
+    xs, w1f, w2f = f64(x_b[rows]), wl["w1"], wl["w2"]
+    y_s = dev_f64(y[torch.from_numpy(rows).to(dev)])
+    da_s = dev_f64(da[torch.from_numpy(rows).to(dev)])
+    dx_s = dev_f64(dx[torch.from_numpy(rows).to(dev)])
+    dys, dhs = f64(dy_b[rows]), f64(dh_b[rows])
+    for i, r in enumerate(rows):
+        e = eo[r]
+        assert_close(y_s[i], xs[i] @ f64(w1f[e]), f"ep fwd row {r}")
+        assert_close(da_s[i], dys[i] @ f64(w2f[e]).T, f"ep dX(W2) row {r}")
+        assert_close(dx_s[i], dhs[i] @ f64(w1f[e]).T, f"ep dX(W1) row {r}")
+    # weight gradient: sampled weight rows k of sampled experts, all columns
+    off = oracle.expert_offsets(gl)
+    dw_host = {}
+    for e in range(E):
+        ks = rng.integers(0, H, 4)
+        got = dev_f64(dw1[e, torch.from_numpy(ks).to(dev)])
+        if gl[e] == 0:
+            assert (got == 0).all(), f"dW1 of empty expert {e}"
+            continue
+        xe = f64(x_b[off[e]:off[e + 1]][:, ks])        # [n_e, 4]
+        dhe = f64(dh_b[off[e]:off[e + 1]])             # [n_e, 3072]
+        assert_close(got, xe.T @ dhe, f"ep dW1 expert {e} rows {ks.tolist()}")
+        dw_host[e] = True
+    assert len(dw_host) == int((gl > 0).sum())

@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE hot path on one MI355X.
+
+Headline (one JSON line on stdout): GMM fwd+bwd TFLOP/s on one expert-parallel
+rank's share -- E=32 local experts, hidden 4096, intermediate 1536, 16384
+received rows with Zipf(1.2) group sizes and 3 empty experts.  One step is
+one pass of the whole hot path:
+
+    moe_permute (top_k=1 local re-routing, histogram) -> gmm_fwd(W1)
+    -> swiglu -> gmm_fwd(W2) -> moe_unpermute
+    -> gmm_bwd_input(W2) -> gmm_bwd_weight(dW2) -> swiglu_bwd
+    -> gmm_bwd_input(W1) -> gmm_bwd_weight(dW1)
+
+``value`` = algorithmic GEMM FLOPs of the step (real rows only, 6 GEMMs)
+divided by the wall time of the whole step, inputs resident in HBM.
+
+Also in the line:
+  roofline     -- the dominant kernel (largest share of step time), its
+                  algorithmic FLOPs per launch over its mean launch time
+                  from HIP events recorded on the launch stream;
+  decode       -- the decode-shaped layer forward (T=64, top-8, E=256,
+                  hidden 2048, intermediate 512) in HBM GB/s;
+  cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--cpu-budget", type=float, default=12.0,
+                   help="seconds of oracle work for the CPU baseline (0 = skip)")
+    p.add_argument("--skip-decode", action="store_true")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class KernelTimer:
+    """Records a pair of HIP events (torch.cuda.Event on the current stream --
+    the stream every libmoegmm call is enqueued on) around each call."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+
+    def __call__(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        self.pending.append((name, ev0, ev1))
+
+    def collect(self):
+        out = {}
+        for name, a, b in self.pending:
+            out.setdefault(name, []).append(a.elapsed_time(b))
+        self.pending = []
+        return out
+
+
+def bf16_dev(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+# ---------------------------------------------------------------------------
+# expert-parallel rank share: fwd + bwd
+# ---------------------------------------------------------------------------
+
+def ep_gemm_flops(gl, H, I):
+    R = int(np.sum(gl))
+    fwd1 = 2.0 * R * H * 2 * I
+    fwd2 = 2.0 * R * I * H
+    return {"gmm_fwd_gate_up": fwd1, "gmm_fwd_down": fwd2,
+            "gmm_bwd_input_down": fwd2, "gmm_bwd_weight_down": fwd2,
+            "gmm_bwd_input_gate_up": fwd1, "gmm_bwd_weight_gate_up": fwd1}
+
+
+# libmoegmm kernel behind each call of the step (kernel symbol -> calls)
+EP_KERNELS = {
+    "gmm_rows_kernel<fwd>": ["gmm_fwd_gate_up", "gmm_fwd_down"],
+    "gmm_rows_kernel<dX>": ["gmm_bwd_input_down", "gmm_bwd_input_gate_up"],
+    "gmm_dw_kernel": ["gmm_bwd_weight_down", "gmm_bwd_weight_gate_up"],
+}
+
+
+def run_ep(torch, dev, args):
+    import workloads
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
+
+    t0 = time.time()
+    wl = workloads.ep_slice()
+    log(f"ep inputs generated in {time.time() - t0:.1f}s; group_list={wl['group_list'].tolist()}")
+    d = wl.dims
+    H, I, E, R = d["H"], d["I"], d["E"], d["R"]
+    x = bf16_dev(torch, wl["x"], dev)
+    dyp = bf16_dev(torch, wl["dyp"], dev)
+    w1 = bf16_dev(torch, wl["w1"], dev)
+    w2 = bf16_dev(torch, wl["w2"], dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    layer = MoeLayer(LayerShape(R, 1, E, H, I), dev, with_backward=True)
+    timer = KernelTimer(torch)
+    g = layer.tokens_per_expert
+
+    from grouped_gemm_moe_amd import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, moe_unpermute,
+                                      swiglu, swiglu_bwd)
+
+    def step(t):
+        t("moe_permute", lambda: layer.permute(x, ids))
+        t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h, dev_err=layer.dev_err))
+        t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
+        t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp, dev_err=layer.dev_err))
+        t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out,
+                                                 dev_err=layer.dev_err))
+        t("gmm_bwd_input_down", lambda: gmm_bwd_input(dyp, w2, g, out=layer.da, dev_err=layer.dev_err))
+        t("gmm_bwd_weight_down", lambda: gmm_bwd_weight(layer.a, dyp, g, out=layer.dw2,
+                                                        dev_err=layer.dev_err))
+        t("swiglu_bwd", lambda: swiglu_bwd(layer.da, layer.h, g, out=layer.dh))
+        t("gmm_bwd_input_gate_up", lambda: gmm_bwd_input(layer.dh, w1, g, out=layer.dx,
+                                                         dev_err=layer.dev_err))
+        t("gmm_bwd_weight_gate_up", lambda: gmm_bwd_weight(layer.x_perm, layer.dh, g, out=layer.dw1,
+                                                           dev_err=layer.dev_err))
+
+    plain = lambda name, fn: fn()  # noqa: E731
+    for _ in range(args.warmup):
+        step(plain)
+    torch.cuda.synchronize()
+    timer.collect()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = timer.collect()
+    assert int(layer.dev_err.item()) == 0, "device error word set during the bench"
+    ms_per_step = wall * 1e3 / args.steps
+    flops = ep_gemm_flops(wl["group_list"], H, I)
+    total_flops = sum(flops.values())
+    mean_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    gmm_ms = sum(mean_ms[k] for k in flops)
+    # dominant kernel: the kernel symbol with the largest time per step
+    kern_ms = {k: sum(mean_ms[c] for c in calls) for k, calls in EP_KERNELS.items()}
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_calls = EP_KERNELS[dom]
+    dom_flops_per_launch = sum(flops[c] for c in dom_calls) / len(dom_calls)
+    dom_ms_per_launch = kern_ms[dom] / len(dom_calls)
+    achieved = dom_flops_per_launch / (dom_ms_per_launch * 1e-3) / 1e12
+    res = dict(
+        ms_per_step=ms_per_step,
+        value=total_flops / (ms_per_step * 1e-3) / 1e12,
+        gmm_only_tflops=total_flops / (gmm_ms * 1e-3) / 1e12,
+        gemm_gflop_per_step=total_flops / 1e9,
+        per_call_us={k: round(v * 1e3, 2) for k, v in mean_ms.items()},
+        roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
+                      peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                      flops_per_launch=dom_flops_per_launch,
+                      mean_launch_us=round(dom_ms_per_launch * 1e3, 2)),
+    )
+    return res, wl
+
+
+# ---------------------------------------------------------------------------
+# decode-shaped layer forward: HBM GB/s
+# ---------------------------------------------------------------------------
+
+def decode_bytes(gl, T, K, H, I):
+    """Algorithmic bytes of one layer forward: weights of experts with rows,
+    once; every activation tensor written once and read once; indices."""
+    n_active = int(np.sum(np.asarray(gl) > 0))
+    S = int(np.sum(gl))
+    w = n_active * (H * 2 * I + I * H) * 2
+    act = (T * H * 2            # x read by permute
+           + S * H * 2 * 2      # x_perm written, read
+           + S * 2 * I * 2 * 2  # h written, read
+           + S * I * 2 * 2      # a written, read
+           + S * H * 2 * 2      # yp written, read
+           + T * H * 2)         # out written
+    idx = T * K * 4 * 3 + T * K * 4 + len(gl) * 8
+    return w + act + idx, n_active
+
+
+def run_decode(torch, dev, args):
+    import workloads
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
+
+    wl = workloads.decode()
+    d = wl.dims
+    T, K, E, H, I = d["T"], d["K"], d["E"], d["H"], d["I"]
+    x = bf16_dev(torch, wl["x"], dev)
+    w1 = bf16_dev(torch, wl["w1"], dev)
+    w2 = bf16_dev(torch, wl["w2"], dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    layer = MoeLayer(LayerShape(T, K, E, H, I), dev)
+    timer = KernelTimer(torch)
+    from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu
+    g = layer.tokens_per_expert
+
+    def step(t):
+        t("moe_permute", lambda: layer.permute(x, ids))
+        t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h))
+        t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
+        t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp))
+        t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out))
+
+    plain = lambda name, fn: fn()  # noqa: E731
+    for _ in range(10):
+        step(plain)
+    torch.cuda.synchronize()
+    # wall time without events, then a pass with per-call events
+    t0 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        step(plain)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.decode_steps
+    for _ in range(min(50, args.decode_steps)):
+        step(timer)
+    torch.cuda.synchronize()
+    per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
+    gl = layer.tokens_per_expert.cpu().numpy()
+    nbytes, n_active = decode_bytes(gl, T, K, H, I)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    wbytes = {k: n_active * (H * 2 * I if k == "gmm_fwd_gate_up" else I * H) * 2
+              for k in ("gmm_fwd_gate_up", "gmm_fwd_down")}
+    return dict(
+        metric="decode MoE layer HBM GB/s",
+        workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
+                 "intermediate 512; permute -> gate_up -> SwiGLU -> down -> unpermute",
+        value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4),
+        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=nbytes,
+        active_experts=n_active,
+        per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
+        gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
+    )
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, on a bounded sample of the ep step
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, budget_s):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    gl = wl["group_list"]
+    H, I = wl.dims["H"], wl.dims["I"]
+    ss, _, _ = oracle.permute_maps(wl["topk_ids"], len(gl))
+    off = oracle.expert_offsets(gl)
+    flops = 0.0
+    rows = 0
+    done = []
+    t0 = time.perf_counter()
+    for e in np.nonzero(gl > 0)[0]:
+        n = int(gl[e])
+        sl = slice(off[e], off[e + 1])
+        xe = oracle.bf16_to_f64(wl["x"][ss[sl]])
+        dye = oracle.bf16_to_f64(wl["dyp"][sl])
+        w1e = oracle.bf16_to_f64(wl["w1"][e:e + 1])
+        w2e = oracle.bf16_to_f64(wl["w2"][e:e + 1])
+        h = oracle.round_bf16(oracle.gmm(xe, w1e, [n]))
+        a = oracle.round_bf16(oracle.swiglu(h))
+        oracle.round_bf16(oracle.gmm(a, w2e, [n]))
+        oracle.expert_block_backward(xe, h, a, dye, w1e, w2e, [n])
+        flops += 3 * (2.0 * n * H * 2 * I + 2.0 * n * I * H)
+        rows += n
+        done.append(int(e))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"oracle (NumPy float64) expert-block fwd+bwd GEMM chain of experts {done} "
+                       f"({rows} of {int(gl.sum())} rows), {flops / 1e9:.1f} GFLOP in {el:.1f} s",
+                seconds=round(el, 2))
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import grouped_gemm_moe_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.library()
+    dev = torch.device("cuda:0")
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    ep, wl = run_ep(torch, dev, args)
+    log(f"ep: {ep['ms_per_step']:.3f} ms/step, {ep['value']:.1f} TFLOP/s; per call {ep['per_call_us']}")
+    decode = None
+    if not args.skip_decode:
+        decode = run_decode(torch, dev, args)
+        log(f"decode: {decode['ms_per_layer']:.4f} ms, {decode['value']:.0f} GB/s; {decode['per_call_us']}")
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(wl, args.cpu_budget)
+        log(f"cpu baseline: {cpu}")
+    line = {
+        "metric": "GMM fwd+bwd TFLOP/s & % bf16 MFMA peak; decode MoE layer HBM GB/s",
+        "value": round(ep["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ep["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "one expert-parallel rank's share, fwd+bwd: E=32 local experts, hidden 4096, "
+                        "intermediate 1536, 16384 received rows (top_k=1 local re-routing), Zipf(1.2) "
+                        "group sizes with 3 empty experts; permute -> gate_up GMM -> SwiGLU -> down GMM "
+                        "-> unpermute -> expert-block backward (dX and dW of both GMMs)",
+            "experts": 32, "hidden": 4096, "intermediate": 1536, "rows": 16384,
+            "gemm_gflop_per_step": round(ep["gemm_gflop_per_step"], 1),
+        },
+        "pct_bf16_mfma_peak": round(100.0 * ep["value"] / MFMA_BF16_PEAK_TFLOPS, 2),
+        "gmm_only_tflops": round(ep["gmm_only_tflops"], 2),
+        "per_call_us": ep["per_call_us"],
+        "roofline": ep["roofline"],
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,96 @@
+"""The routed-expert MoE layer as a chain of C-ABI calls on preallocated buffers.
+
+Forward ("NPU Training Operators - GMM", section "Qwen3.5 MoE 路径"):
+    moe_permute -> gmm_fwd(W1) -> swiglu -> gmm_fwd(W2) -> moe_unpermute
+Backward of the expert block, from the gradient dYp at the down-GMM output
+(permuted row order):
+    dA = gmm_bwd_input(dYp, W2); dW2 = gmm_bwd_weight(A, dYp);
+    dH = swiglu_bwd(dA, H);      dX  = gmm_bwd_input(dH, W1);
+    dW1 = gmm_bwd_weight(X_perm, dH)
+
+Every step runs in the HIP kernels of libmoegmm; this module only owns the
+buffers and the call order.  group_list (tokens_per_expert) stays on the
+device between the calls.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_workspace_size, moe_permute,
+               moe_permute_workspace_size, moe_unpermute, swiglu, swiglu_bwd)
+
+
+@dataclass
+class LayerShape:
+    T: int
+    top_k: int
+    E: int
+    H: int
+    I: int
+
+    @property
+    def S(self) -> int:
+        return self.T * self.top_k
+
+
+class MoeLayer:
+    """Buffers for one layer shape; forward() and backward() enqueue on the
+    current torch stream and never synchronise."""
+
+    def __init__(self, shape: LayerShape, device, with_backward: bool = False):
+        s = shape
+        self.shape = s
+        d = device
+        bf = torch.bfloat16
+        S = s.S
+        self.x_perm = torch.empty((S, s.H), dtype=bf, device=d)
+        self.row_id_map = torch.empty(S, dtype=torch.int32, device=d)
+        self.sorted_slot = torch.empty(S, dtype=torch.int32, device=d)
+        self.tokens_per_expert = torch.empty(s.E, dtype=torch.int64, device=d)
+        self.h = torch.empty((S, 2 * s.I), dtype=bf, device=d)
+        self.a = torch.empty((S, s.I), dtype=bf, device=d)
+        self.yp = torch.empty((S, s.H), dtype=bf, device=d)
+        self.out = torch.empty((s.T, s.H), dtype=bf, device=d)
+        self.dev_err = torch.zeros(1, dtype=torch.int32, device=d)
+        self.ws_perm = torch.empty(max(1, moe_permute_workspace_size(s.T, s.top_k, s.E)),
+                                   dtype=torch.uint8, device=d)
+        ws = max(gmm_workspace_size(s.E, S, k, n, op)
+                 for (k, n) in ((s.H, 2 * s.I), (s.I, s.H)) for op in (0, 1, 2))
+        self.ws_gmm = torch.empty(ws, dtype=torch.uint8, device=d) if ws > 0 else None
+        if with_backward:
+            self.da = torch.empty((S, s.I), dtype=bf, device=d)
+            self.dh = torch.empty((S, 2 * s.I), dtype=bf, device=d)
+            self.dx = torch.empty((S, s.H), dtype=bf, device=d)
+            self.dw1 = torch.empty((s.E, s.H, 2 * s.I), dtype=bf, device=d)
+            self.dw2 = torch.empty((s.E, s.I, s.H), dtype=bf, device=d)
+
+    # -- forward ---------------------------------------------------------
+    def permute(self, x, topk_ids):
+        moe_permute(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
+                    out=(self.x_perm, self.row_id_map, self.sorted_slot, self.tokens_per_expert))
+
+    def experts_forward(self, w1, w2):
+        g = self.tokens_per_expert
+        gmm_fwd(self.x_perm, w1, g, out=self.h, ws=self.ws_gmm, dev_err=self.dev_err)
+        swiglu(self.h, g, out=self.a)
+        gmm_fwd(self.a, w2, g, out=self.yp, ws=self.ws_gmm, dev_err=self.dev_err)
+
+    def unpermute(self, probs):
+        moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
+
+    def forward(self, x, topk_ids, probs, w1, w2):
+        self.permute(x, topk_ids)
+        self.experts_forward(w1, w2)
+        self.unpermute(probs)
+        return self.out
+
+    # -- backward of the expert block --------------------------------------
+    def backward(self, dyp, w1, w2):
+        g = self.tokens_per_expert
+        gmm_bwd_input(dyp, w2, g, out=self.da, ws=self.ws_gmm, dev_err=self.dev_err)
+        gmm_bwd_weight(self.a, dyp, g, out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
+        swiglu_bwd(self.da, self.h, g, out=self.dh)
+        gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
+        gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)

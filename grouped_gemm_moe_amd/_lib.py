@@ -8,7 +8,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoegmm.so")
+LIB_PATH = os.environ.get("MOEGMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libmoegmm.so")
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64

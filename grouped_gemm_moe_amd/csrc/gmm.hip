@@ -10,28 +10,32 @@
 //
 // Design (MI355X-first):
 //  * group_list never leaves the device.  Every workgroup reads it, scans it
-//    in LDS and finds its own tile: a row-grouped tile list for fwd / dX
-//    (sum over experts of ceil(n_e/BM) M-tiles times the N-tiles) and an
-//    expert-major (e, k-tile, n-tile) list for dW.  The grid is sized from
-//    host-known bounds (M_cap, E); surplus workgroups exit at once.
-//  * One MFMA tile engine: v_mfma_f32_32x32x16_bf16 on 64-wide waves, fp32
-//    accumulation, a BK=64 reduction step staged through double-buffered LDS.
-//    In LDS every operand tile is stored reduction-contiguous ([outer][64],
-//    128-byte rows, 16-byte chunks XOR-swizzled by row), which is the layout
-//    the MFMA operands want.  An operand that is reduction-contiguous in HBM
-//    (x for fwd, dy and w for dX) is copied 16 bytes at a time; one that is
-//    outer-contiguous (w for fwd, x and dy for dW) is loaded as 4x8 blocks and
-//    transposed in registers before the LDS store.
+//    in LDS and finds its own tile: a row-grouped tile list for fwd / dX (sum
+//    over experts of ceil(n_e/BM) M-tiles times the N-tiles, walked in an
+//    XCD-aware order so neighbouring tiles share an L2) and an (expert,
+//    k-tile, n-tile) list for dW, largest experts first.  The grid is sized
+//    from host-known bounds; surplus workgroups exit at once.
+//  * One MFMA engine: 256x256 output tile per workgroup, 4 waves of 128x128,
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators, a 64-deep reduction step.
+//  * Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+//    VGPR staging).  Lanes whose element lies outside the problem (ragged
+//    rows, reduction tails, rows past an expert) get an out-of-range buffer
+//    offset, which loads zeros -- so partial tiles need no special path.
+//  * Each operand keeps its HBM orientation in LDS.  A reduction-contiguous
+//    tile ([outer][64], 128-byte rows) is read with ds_read_b128; an
+//    outer-contiguous tile ([64][outer]) is read with ds_read_b64_tr_b16,
+//    the gfx950 transposing LDS read, which hands each lane 4 consecutive
+//    reduction elements of one column.  16-byte chunks are XOR-swizzled per
+//    row so both reads hit every LDS bank pair at most twice per pass.
+//  * Two LDS stages (2 x 64 KiB): the loads for step s+1 fly while step s
+//    runs its MFMAs; one barrier per step.
 //  * The MFMA is issued with operands swapped (B fragment as the hardware A
-//    operand) so that every lane ends up owning four consecutive output
-//    columns; the epilogue packs them to bf16 (RNE), stages the tile in LDS
-//    and writes 16-byte coalesced rows, masked to the expert's rows.
-//  * A second forward kernel streams the weights for decode-shaped calls
-//    (a few rows per expert): each workgroup owns one expert's 256-column
-//    slice, reads every weight once with 16-byte loads and does the few-row
-//    products on the vector ALUs, where MFMA tiles would idle.
+//    operand) so each lane holds 4 consecutive output columns; the epilogue
+//    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
 #include "common.h"
 #include "launch.h"
+
+#define LDS_AS __attribute__((address_space(3)))
 
 namespace moegmm {
 
@@ -40,467 +44,437 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int BK = 64;         // reduction step
 
-// ---------------------------------------------------------------------------
-// LDS operand tiles: [BO][BK] bf16, 8 chunks of 16 bytes per row; chunk c of
-// row o lives at chunk c ^ swz(o).  The swizzle spreads both the MFMA reads
-// (32 consecutive rows, same chunk) and the transposed writes (rows 8 apart)
-// over the banks.
-// ---------------------------------------------------------------------------
-MOE_DEVICE int swz(int o) { return (o ^ (o >> 3)) & 7; }
-MOE_DEVICE int lds_off(int o, int c) { return o * BK + ((c ^ swz(o)) << 3); }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
-// Operand stored reduction-contiguous in HBM: element (o, q) at base[o*ld + q].
+// Buffer resource covering the whole 31-bit offset range from `base`; every
+// lane's offset is computed in bounds or set to kOOB, which the hardware
+// range check turns into a zero load.
+constexpr int kNumRecords = 0x7FFFFFF0;
+constexpr uint32_t kOOB = 0x7FFFFFF0u;
+
+MOE_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords,
+                                             0x00020000);
+}
+
+// Wave index as a scalar (the LDS-DMA destination must be wave-uniform).
+MOE_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// LDS swizzles (16-byte chunk index XOR) for the two tile orientations.
+MOE_DEVICE int swz_k(int o) { return (o ^ (o >> 3)) & 7; }   // [outer][64] tiles
+MOE_DEVICE int swz_mn(int k) { return (k & 3) << 2; }         // [64][outer] tiles
+
+// ---------------------------------------------------------------------------
+// HBM -> LDS copies of one operand tile per reduction step.  A wave
+// instruction moves 1 KiB: lane l's 16 bytes land at LDS byte 16*l of it, so
+// the lane -> global-address map decides the LDS layout (and the swizzle).
+// ---------------------------------------------------------------------------
+template <int BO, bool KMAJOR>
+struct Dma;
+
+// Reduction-contiguous operand: element (o, q) at base[o*ld + q].
+// LDS tile [BO][BK]; one instruction fills 8 rows of 128 bytes.
 template <int BO>
-struct KMajorLoader {
-    static constexpr int kN = BO * (BK / 8) / kThreads;
-    static_assert(kN >= 1 && BO * (BK / 8) % kThreads == 0, "tile/threads mismatch");
-    u32x4_t v[kN];
+struct Dma<BO, true> {
+    static constexpr int kInst = BO / 8 / 4;  // per wave
+    uint32_t off[kInst];
+    int red[kInst];
+    uint32_t ok_mask;
 
-    MOE_DEVICE void load(const bf16_t* __restrict__ base, int64_t ld, int o_lim, int q0, int q_lim) {
+    MOE_DEVICE void init(int64_t ld, int outer_lim) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
 #pragma unroll
-        for (int i = 0; i < kN; ++i) {
-            const int u = threadIdx.x + kThreads * i;
-            const int o = u >> 3, c = u & 7;
-            const int q = q0 + c * 8;
-            if (o < o_lim && q < q_lim)
-                v[i] = ld16(base + (int64_t)o * ld + q);
-            else
-                v[i] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kInst; ++i) {
+            const int o = (wid * kInst + i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz_k(o);
+            off[i] = (uint32_t)(((int64_t)o * ld + c * 8) * 2);
+            red[i] = c * 8;
+            if (o < outer_lim) ok_mask |= 1u << i;
         }
     }
-    MOE_DEVICE void store(bf16_t* lds) const {
+    // stage_base: element (0, s*BK); red_left: valid reduction length from there
+    MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(stage_base);
+        const int wid = wave_id();
 #pragma unroll
-        for (int i = 0; i < kN; ++i) {
-            const int u = threadIdx.x + kThreads * i;
-            const int o = u >> 3, c = u & 7;
-            *reinterpret_cast<u32x4_t*>(lds + lds_off(o, c)) = v[i];
+        for (int i = 0; i < kInst; ++i) {
+            const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (LDS_AS void*)(lds + (wid * kInst + i) * 512), 16, v, 0, 0, 0);
         }
+    }
+    static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t, int s) { return base + s * BK; }
+};
+
+// Outer-contiguous operand: element (o, q) at base[q*ld + o].
+// LDS tile [BK][BO]; one instruction fills 1024 / (2*BO) rows.
+template <int BO>
+struct Dma<BO, false> {
+    static constexpr int kChunks = BO / 8;
+    static constexpr int kRowsPerInst = 64 / kChunks;
+    static constexpr int kInst = BK / kRowsPerInst / 4;  // per wave
+    static_assert(kChunks >= 16 && 64 % kChunks == 0 && kInst >= 1, "outer tile must be 128 or 256");
+    uint32_t off[kInst];
+    int red[kInst];
+    uint32_t ok_mask;
+
+    MOE_DEVICE void init(int64_t ld, int outer_lim) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int k = (wid * kInst + i) * kRowsPerInst + lane / kChunks;
+            const int col = ((lane % kChunks) ^ swz_mn(k)) * 8;
+            off[i] = (uint32_t)(((int64_t)k * ld + col) * 2);
+            red[i] = k;
+            if (col < outer_lim) ok_mask |= 1u << i;
+        }
+    }
+    MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(stage_base);
+        const int wid = wave_id();
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (LDS_AS void*)(lds + (wid * kInst + i) * 512), 16, v, 0, 0, 0);
+        }
+    }
+    static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t ld, int s) {
+        return base + (int64_t)s * BK * ld;
     }
 };
 
-// Operand stored outer-contiguous in HBM: element (q, o) at base[q*ld + o].
-// Each unit is 4 reduction rows x 8 outer columns, transposed in registers.
-template <int BO>
-struct MNMajorLoader {
-    static constexpr int kUnitsO = BO / 8;
-    static constexpr int kN = (BK / 4) * kUnitsO / kThreads;
-    static_assert(kN >= 1 && (BK / 4) * kUnitsO % kThreads == 0, "tile/threads mismatch");
-    u32x4_t v[kN][4];
-
-    MOE_DEVICE void load(const bf16_t* __restrict__ base, int64_t ld, int o_lim, int q0, int q_lim) {
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-            const int u = threadIdx.x + kThreads * i;
-            const int ob = u % kUnitsO, qb = u / kUnitsO;
-            const int o = ob * 8;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = q0 + qb * 4 + j;
-                if (o < o_lim && q < q_lim)
-                    v[i][j] = ld16(base + (int64_t)q * ld + o);
-                else
-                    v[i][j] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    }
-    MOE_DEVICE void store(bf16_t* lds) const {
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-            const int u = threadIdx.x + kThreads * i;
-            const int ob = u % kUnitsO, qb = u / kUnitsO;
-            const int c = qb >> 1, half = qb & 1;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const int d = p >> 1;
-                uint32_t w0, w1;
-                if ((p & 1) == 0) {
-                    w0 = (v[i][0][d] & 0xffffu) | (v[i][1][d] << 16);
-                    w1 = (v[i][2][d] & 0xffffu) | (v[i][3][d] << 16);
-                } else {
-                    w0 = (v[i][0][d] >> 16) | (v[i][1][d] & 0xffff0000u);
-                    w1 = (v[i][2][d] >> 16) | (v[i][3][d] & 0xffff0000u);
-                }
-                const int o = ob * 8 + p;
-                *reinterpret_cast<u32x2_t*>(lds + lds_off(o, c) + half * 4) = u32x2_t{w0, w1};
-            }
-        }
-    }
-};
+// ---------------------------------------------------------------------------
+// MFMA operand fragments: lane l gets T[o0 + l%32][k0 + 8*(l/32) + 0..7].
+//
+// The reads are issued as inline asm on purpose: the loads of the next
+// reduction step are in flight into the other LDS stage while these run, and
+// the compiler, unable to prove the two stages apart through computed
+// addresses, would otherwise wait for those loads first.  The caller waits
+// for the reads itself (lds_wait) before feeding the fragments to MFMAs.
+// ---------------------------------------------------------------------------
+MOE_DEVICE uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
 
 template <int BO, bool KMAJOR>
-struct LoaderSel;
+struct Frag;
+
 template <int BO>
-struct LoaderSel<BO, true> { using type = KMajorLoader<BO>; };
+struct Frag<BO, true> {
+    static MOE_DEVICE void load(bf16x8_t& v, const bf16_t* lds, int o0, int k0) {
+        const int lane = threadIdx.x & 63;
+        const int o = o0 + (lane & 31);
+        const int c = (k0 >> 3) + (lane >> 5);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(lds_addr(lds + o * BK + ((c ^ swz_k(o)) << 3))));
+    }
+};
+
+// ds_read_b64_tr_b16 over a 16-lane group: lane s supplies the address of 4
+// consecutive columns (o .. o+3) of reduction row kb + s/4; lane L receives
+// column ob + L of rows kb .. kb+3.  Two such reads (rows +0..3 and +4..7)
+// give the 8 reduction elements of one MFMA operand lane.
 template <int BO>
-struct LoaderSel<BO, false> { using type = MNMajorLoader<BO>; };
+struct Frag<BO, false> {
+    static MOE_DEVICE void load(bf16x8_t& v, const bf16_t* lds, int o0, int k0) {
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, s = lane & 15;
+        const int o = o0 + ((g & 1) << 4) + ((s & 3) << 2);
+        const int k = k0 + ((g >> 1) << 3) + (s >> 2);
+        const int cc = ((o >> 3) ^ swz_mn(k)) << 3;   // swz_mn(k) == swz_mn(k + 4)
+        const uint32_t a = lds_addr(lds + k * BO + cc + (o & 7));
+        u32x2_t lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(4 * BO * 2));
+        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        v = __builtin_bit_cast(bf16x8_t, w);
+    }
+};
+
+// Wait for every outstanding LDS read; the fragments pass through the asm so
+// that no use of them can be scheduled above the wait.
+template <int TM, int TN>
+MOE_DEVICE void lds_wait(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(a[t]));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(b[t]));
+}
 
 // ---------------------------------------------------------------------------
-// MFMA tile engine.  A: [BM][BK] (outer = output rows), B: [BN][BK] (outer =
-// output columns), both reduction-contiguous in LDS.  Waves form a WM x WN
-// grid; each wave owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA tiles.
+// The tile engine: C[BM][BN] = A[BM][red] * B[red][BN], fp32 accumulation.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
-struct MfmaTile {
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR>
+struct Engine {
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static_assert(WM * WN == kThreads / 64, "wave grid");
-    static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(WM * WN == kThreads / 64 && TM >= 1 && TN >= 1, "wave grid");
     f32x16_t acc[TM][TN];
 
     MOE_DEVICE void zero() {
-#pragma unroll
-        for (int a = 0; a < TM; ++a)
-#pragma unroll
-            for (int b = 0; b < TN; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    }
-
-    MOE_DEVICE void step(const bf16_t* ldsA, const bf16_t* ldsB) {
-        const int lane = threadIdx.x & 63;
-        const int wid = threadIdx.x >> 6;
-        const int wm = wid / WN, wn = wid % WN;
-        const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t a[TM], b[TN];
-            const int c = ks * 2 + hi;
-#pragma unroll
-            for (int t = 0; t < TM; ++t)
-                a[t] = *reinterpret_cast<const bf16x8_t*>(ldsA + lds_off(wm * WTM + t * 32 + l32, c));
-#pragma unroll
-            for (int t = 0; t < TN; ++t)
-                b[t] = *reinterpret_cast<const bf16x8_t*>(ldsB + lds_off(wn * WTN + t * 32 + l32, c));
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-        }
-    }
-
-    // Write the tile to out[row*ld + col] for row < rows_valid, col < cols_valid
-    // (both relative to the tile origin), via an LDS staging buffer of
-    // BM x (BN + 8) bf16.
-    MOE_DEVICE void store(bf16_t* lds_c, bf16_t* __restrict__ out, int64_t ld, int rows_valid,
-                          int cols_valid) const {
-        constexpr int LDC = BN + 8;
-        const int lane = threadIdx.x & 63;
-        const int wid = threadIdx.x >> 6;
-        const int wm = wid / WN, wn = wid % WN;
-        const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+
+    MOE_DEVICE void load_frags(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN], const bf16_t* la, const bf16_t* lb,
+                               int ks) const {
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) Frag<BM, A_KMAJOR>::load(a[t], la, wm * WTM + t * 32, ks * 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) Frag<BN, B_KMAJOR>::load(b[t], lb, wn * WTN + t * 32, ks * 16);
+    }
+
+    MOE_DEVICE void mfmas(const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+
+    // One reduction step from LDS: fragments of sub-step ks+1 are read while
+    // the MFMAs of sub-step ks run.
+    MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb) {
+        bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+        load_frags(a0, b0, la, lb, 0);
+        lds_wait(a0, b0);
+        load_frags(a1, b1, la, lb, 1);
+        mfmas(a0, b0);
+        lds_wait(a1, b1);
+        load_frags(a0, b0, la, lb, 2);
+        mfmas(a1, b1);
+        lds_wait(a0, b0);
+        load_frags(a1, b1, la, lb, 3);
+        mfmas(a0, b0);
+        lds_wait(a1, b1);
+        mfmas(a1, b1);
+    }
+
+    // lane holds rows (l%32) and 4 consecutive columns per (i, j, g)
+    MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid) const {
+        const int lane = threadIdx.x & 63;
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            if (row >= rows_valid) continue;
+            bf16_t* orow = out + (int64_t)row * ld;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int row = wm * WTM + i * 32 + l32;
-                    const int col = wn * WTN + j * 32 + g * 8 + hi * 4;
-                    u32x2_t pk;
-                    pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                    pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    *reinterpret_cast<u32x2_t*>(lds_c + row * LDC + col) = pk;
+                    const int col = wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    if (col < cols_valid) {
+                        u32x2_t pk;
+                        pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                        pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                        *reinterpret_cast<u32x2_t*>(orow + col) = pk;
+                    }
                 }
-        __syncthreads();
-        constexpr int CPR = BN / 8;
-        for (int u = threadIdx.x; u < BM * CPR; u += kThreads) {
-            const int row = u / CPR, c = u % CPR;
-            if (row < rows_valid && c * 8 < cols_valid)
-                st16(out + (int64_t)row * ld + c * 8, ld16(lds_c + row * LDC + c * 8));
         }
     }
 };
 
-template <int BM, int BN>
-constexpr int tile_lds_elems() {
-    // two stages of A and B, or the epilogue staging buffer, whichever is larger
-    return (2 * (BM + BN) * BK) > (BM * (BN + 8)) ? (2 * (BM + BN) * BK) : (BM * (BN + 8));
+// One output tile: two LDS stages, statically named so the compiler can tell
+// which outstanding LDS-DMA a read depends on.
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR>
+MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
+                          int64_t ldb, int b_olim, int red_len, bf16_t* out, int64_t ldo,
+                          int rows_valid, int cols_valid, bf16_t* lA0, bf16_t* lB0, bf16_t* lA1,
+                          bf16_t* lB1) {
+    using DA = Dma<BM, A_KMAJOR>;
+    using DB = Dma<BN, B_KMAJOR>;
+    DA da;
+    DB db;
+    da.init(lda, a_olim);
+    db.init(ldb, b_olim);
+    Engine<BM, BN, WM, WN, A_KMAJOR, B_KMAJOR> eng;
+    eng.zero();
+    const int nk = (red_len + BK - 1) / BK;
+    da.issue(DA::stage(a_base, lda, 0), lA0, red_len);
+    db.issue(DB::stage(b_base, ldb, 0), lB0, red_len);
+    // pairs of steps: stage s in buffer 0, stage s+1 in buffer 1
+    int s = 0;
+    for (; s + 1 < nk; s += 2) {
+        __syncthreads();  // stage s landed (every wave waited for its own copies); s-1 consumed
+        da.issue(DA::stage(a_base, lda, s + 1), lA1, red_len - (s + 1) * BK);
+        db.issue(DB::stage(b_base, ldb, s + 1), lB1, red_len - (s + 1) * BK);
+        eng.compute(lA0, lB0);
+        __syncthreads();  // stage s+1 landed; stage s consumed
+        if (s + 2 < nk) {
+            da.issue(DA::stage(a_base, lda, s + 2), lA0, red_len - (s + 2) * BK);
+            db.issue(DB::stage(b_base, ldb, s + 2), lB0, red_len - (s + 2) * BK);
+        }
+        eng.compute(lA1, lB1);
+    }
+    if (s < nk) {  // odd number of steps: the last one sits in buffer 0
+        __syncthreads();
+        eng.compute(lA0, lB0);
+    }
+    eng.store(out, ldo, rows_valid, cols_valid);
 }
 
-// Shared memory of one workgroup: the tile buffers, overlapped at start-up by
-// the per-expert schedule arrays (dead before the first tile load).
-template <int BM, int BN>
-struct GmmSmem {
-    static constexpr int kTileBytes = tile_lds_elems<BM, BN>() * 2;
-    static constexpr int kSchedBytes = 3 * kMaxExperts * 4;
-    static constexpr int kBytes = kTileBytes > kSchedBytes ? kTileBytes : kSchedBytes;
-};
+// Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
+// contiguous range of logical tiles so tiles that share operands share an L2.
+MOE_DEVICE int xcd_remap(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, j = bid >> 3;
+    return x * q + (x < r ? x : r) + j;
+}
+
+#ifndef MOEGMM_BM
+#define MOEGMM_BM 256
+#endif
+#ifndef MOEGMM_BN
+#define MOEGMM_BN 256
+#endif
+#ifndef MOEGMM_WM
+#define MOEGMM_WM 2
+#endif
+#ifndef MOEGMM_WN
+#define MOEGMM_WN 2
+#endif
+constexpr int kBM = MOEGMM_BM, kBN = MOEGMM_BN, kWM = MOEGMM_WM, kWN = MOEGMM_WN;
+static_assert(kBM * BK * 2 >= 12 * 1024, "schedule arrays live in an A stage");
 
 // ---------------------------------------------------------------------------
 // Row-grouped GEMM: forward (IS_DX = false) and input gradient (IS_DX = true).
-//   fwd: A = x [M_cap, K] (K-major, ld K), B(q, j) = w[e][q][j] (N-major, ld N),
-//        out y [M_cap, N]; reduction length K, output columns N.
+//   fwd: A = x [M_cap, K] (reduction-contiguous, ld K), B(q, j) = w[e][q][j]
+//        (outer-contiguous, ld N); out y [M_cap, N]; reduction K.
 //   dX:  A = dy [M_cap, N] (ld N), B(q, j) = w[e][j][q] (reduction-contiguous,
-//        ld N), out dx [M_cap, K]; reduction length N, output columns K.
+//        ld N); out dx [M_cap, K]; reduction N.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool IS_DX>
+template <bool IS_DX>
 __global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
-    using SM = GmmSmem<BM, BN>;
-    __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+    __shared__ __attribute__((aligned(1024))) bf16_t lA0[kBM * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lB0[kBN * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lA1[kBM * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lB1[kBN * BK];
     __shared__ int64_t s_scan[kThreads / 64];
-    int* s_off = reinterpret_cast<int*>(smem);
+    int* s_off = reinterpret_cast<int*>(lA1);
     int* s_cnt = s_off + kMaxExperts;
     int* s_tst = s_cnt + kMaxExperts;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    // exclusive scan of M-tiles per expert (thread owns <= 4 consecutive experts)
     const int per = (E + kThreads - 1) / kThreads;
     const int e0 = threadIdx.x * per;
     int64_t my_tiles = 0;
     for (int i = 0; i < per; ++i)
-        if (e0 + i < E) my_tiles += (s_cnt[e0 + i] + BM - 1) / BM;
+        if (e0 + i < E) my_tiles += (s_cnt[e0 + i] + kBM - 1) / kBM;
     int64_t total_mt;
     int64_t run = block_exclusive_scan<int64_t>(my_tiles, s_scan, &total_mt);
     for (int i = 0; i < per; ++i)
         if (e0 + i < E) {
             s_tst[e0 + i] = (int)run;
-            run += (s_cnt[e0 + i] + BM - 1) / BM;
+            run += (s_cnt[e0 + i] + kBM - 1) / kBM;
         }
     __syncthreads();
 
-    const int Ncols = IS_DX ? K : N;   // output columns
-    const int Kred = IS_DX ? N : K;    // reduction length
-    const int NT = (Ncols + BN - 1) / BN;
-    const int mt = blockIdx.x / NT, nt = blockIdx.x % NT;
-    if (mt >= total_mt) return;  // uniform across the block
-    // last expert whose first tile is <= mt (empty experts share the start of
-    // the next one, so the last match is the non-empty owner)
-    int lo = 0, hi = E - 1;
+    const int Ncols = IS_DX ? K : N;  // output columns
+    const int Kred = IS_DX ? N : K;   // reduction length
+    const int NT = (Ncols + kBN - 1) / kBN;
+    const int ntiles = (int)total_mt * NT;
+    if ((int)blockIdx.x >= ntiles) return;  // uniform across the block
+    const int t = xcd_remap(blockIdx.x, ntiles);
+    const int mt = t / NT, nt = t % NT;
+    int lo = 0, hi = E - 1;  // last expert whose first tile is <= mt
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_tst[mid] <= mt) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int row0 = s_off[e] + (mt - s_tst[e]) * BM;
-    const int row_end = s_off[e] + s_cnt[e];
-    const int rows_valid = row_end - row0 < BM ? row_end - row0 : BM;
-    const int n0 = nt * BN;
-    __syncthreads();  // schedule arrays are dead from here on
-
-    bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
-    bf16_t* ldsA[2] = {lds, lds + (BM + BN) * BK};
-    bf16_t* ldsB[2] = {lds + BM * BK, lds + (BM + BN) * BK + BM * BK};
+    // block-uniform values read from LDS: keep them in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int row0 = __builtin_amdgcn_readfirstlane(s_off[e] + (mt - s_tst[e]) * kBM);
+    const int row_end = __builtin_amdgcn_readfirstlane(s_off[e] + s_cnt[e]);
+    const int rows_valid = row_end - row0 < kBM ? row_end - row0 : kBM;
+    const int n0 = __builtin_amdgcn_readfirstlane(nt * kBN);
+    __syncthreads();  // schedule arrays (inside lA1) are dead from here on
 
     const int64_t lda = IS_DX ? N : K;
-    const bf16_t* Abase = A + (int64_t)row0 * lda;
     const bf16_t* We = W + (int64_t)e * K * N;
-    // B operand base / leading dimension / outer limit
-    const bf16_t* Bbase = IS_DX ? We + (int64_t)n0 * N : We + n0;
-    const int64_t ldb = N;
-    const int b_olim = Ncols - n0;
-
-    KMajorLoader<BM> la;
-    typename LoaderSel<BN, IS_DX>::type lb;
-    MfmaTile<BM, BN, WM, WN> tile;
-    tile.zero();
-
-    const int nk = (Kred + BK - 1) / BK;
-    la.load(Abase, lda, rows_valid, 0, Kred);
-    lb.load(Bbase, ldb, b_olim, 0, Kred);
-    la.store(ldsA[0]);
-    lb.store(ldsB[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(Abase, lda, rows_valid, (kt + 1) * BK, Kred);
-            lb.load(Bbase, ldb, b_olim, (kt + 1) * BK, Kred);
-        }
-        tile.step(ldsA[cur], ldsB[cur]);
-        if (more) {
-            la.store(ldsA[cur ^ 1]);
-            lb.store(ldsB[cur ^ 1]);
-        }
-        __syncthreads();
-    }
-    tile.store(lds, Y + (int64_t)row0 * Ncols + n0, Ncols, rows_valid, Ncols - n0);
+    gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
+        A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N, Ncols - n0,
+        Kred, Y + (int64_t)row0 * Ncols + n0, Ncols, rows_valid, Ncols - n0, lA0, lB0, lA1, lB1);
 }
 
 // ---------------------------------------------------------------------------
-// Weight gradient: dw[e] = x[rows_e]^T @ dy[rows_e].  Tiles (e, k-tile,
-// n-tile) in expert-major order; the reduction runs over the expert's rows in
-// steps of BK with rows past the end zero-filled in BOTH operands (rows past
-// R are undefined memory).  Empty experts write zeros.
+// Weight gradient: dw[e] = x[rows_e]^T @ dy[rows_e].  Tiles (expert, k-tile,
+// n-tile), experts in descending row count (ties by index) so the longest
+// reductions start first.  Both operands are outer-contiguous; the reduction
+// runs over the expert's rows, zero-filled past its last row.  Empty experts
+// write zeros.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
+constexpr int kMaxRankedExperts = 256;  // beyond this, experts run in index order
+
 __global__ __launch_bounds__(kThreads) void gmm_dw_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int32_t* dev_err) {
-    using SM = GmmSmem<BM, BN>;
-    __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+    __shared__ __attribute__((aligned(1024))) bf16_t lA0[kBM * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lB0[kBN * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lA1[kBM * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t lB1[kBN * BK];
     __shared__ int64_t s_scan[kThreads / 64];
-    int* s_off = reinterpret_cast<int*>(smem);
+    __shared__ int s_pick;
+    int* s_off = reinterpret_cast<int*>(lA1);
     int* s_cnt = s_off + kMaxExperts;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int KT = (K + BM - 1) / BM, NT = (N + BN - 1) / BN;
-    const int e = blockIdx.x / (KT * NT);
+    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
+    const int rank = blockIdx.x / (KT * NT);
     const int rem = blockIdx.x % (KT * NT);
-    const int kt_out = rem / NT, nt = rem % NT;
-    const int k0 = kt_out * BM, n0 = nt * BN;
-    const int off = s_off[e], cnt = s_cnt[e];
+    if (E <= kMaxRankedExperts) {
+        // the expert whose (count desc, index asc) rank is `rank`
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            const int c = s_cnt[e];
+            int r = 0;
+            for (int f = 0; f < E; ++f) {
+                const int cf = s_cnt[f];
+                r += (cf > c) || (cf == c && f < e);
+            }
+            if (r == rank) s_pick = e;
+        }
+    } else if (threadIdx.x == 0) {
+        s_pick = rank;
+    }
     __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(s_pick);
+    const int kt_out = rem / NT, nt = rem % NT;
+    const int k0 = kt_out * kBM, n0 = nt * kBN;
+    const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+    __syncthreads();  // schedule arrays (inside lA1) are dead from here on
 
-    const int rows_valid = K - k0 < BM ? K - k0 : BM;
-    const int cols_valid = N - n0 < BN ? N - n0 : BN;
+    const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
+    const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
     bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
     if (cnt == 0) {
-        constexpr int CPR = BN / 8;
-        for (int u = threadIdx.x; u < BM * CPR; u += kThreads) {
+        constexpr int CPR = kBN / 8;
+        for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
             const int row = u / CPR, c = u % CPR;
             if (row < rows_valid && c * 8 < cols_valid)
                 st16(out + (int64_t)row * N + c * 8, u32x4_t{0u, 0u, 0u, 0u});
         }
         return;
     }
-
-    bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
-    bf16_t* ldsA[2] = {lds, lds + (BM + BN) * BK};
-    bf16_t* ldsB[2] = {lds + BM * BK, lds + (BM + BN) * BK + BM * BK};
-    const bf16_t* Abase = X + (int64_t)off * K + k0;   // (q=row, o=k) at q*K + o
-    const bf16_t* Bbase = DY + (int64_t)off * N + n0;  // (q=row, o=n) at q*N + o
-
-    MNMajorLoader<BM> la;
-    MNMajorLoader<BN> lb;
-    MfmaTile<BM, BN, WM, WN> tile;
-    tile.zero();
-
-    const int nk = (cnt + BK - 1) / BK;
-    la.load(Abase, K, rows_valid, 0, cnt);
-    lb.load(Bbase, N, cols_valid, 0, cnt);
-    la.store(ldsA[0]);
-    lb.store(ldsB[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(Abase, K, rows_valid, (kt + 1) * BK, cnt);
-            lb.load(Bbase, N, cols_valid, (kt + 1) * BK, cnt);
-        }
-        tile.step(ldsA[cur], ldsB[cur]);
-        if (more) {
-            la.store(ldsA[cur ^ 1]);
-            lb.store(ldsB[cur ^ 1]);
-        }
-        __syncthreads();
-    }
-    tile.store(lds, out, N, rows_valid, cols_valid);
+    gemm_tile<kBM, kBN, kWM, kWN, false, false>(X + (int64_t)off * K + k0, K, rows_valid,
+                                                DY + (int64_t)off * N + n0, N, cols_valid, cnt, out, N,
+                                                rows_valid, cols_valid, lA0, lB0, lA1, lB1);
 }
-
-// ---------------------------------------------------------------------------
-// Decode-shaped forward: weight streaming.  Block = (expert e, 256-column
-// slice).  256 threads = 8 k-groups x 32 column lanes; lane owns 8 columns,
-// k-group g walks k-chunks of 8 starting at 8g with stride 64.  Rows of the
-// expert are processed kStreamRows at a time (one weight pass each), staged in
-// LDS as bf16; partial sums over k-groups meet in LDS.
-// ---------------------------------------------------------------------------
-constexpr int kStreamCols = 256;
-constexpr int kStreamRows = 4;
-constexpr int kStreamKGroups = kThreads / 32;
-
-__global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
-    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
-    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
-    extern __shared__ __attribute__((aligned(16))) char dsmem[];
-    __shared__ int s_off[kMaxExperts];
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int64_t s_scan[kThreads / 64];
-    __shared__ float red[kStreamKGroups][kStreamRows][kStreamCols];
-    bf16_t* xs = reinterpret_cast<bf16_t*>(dsmem);  // [kStreamRows][K]
-
-    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int NB = (N + kStreamCols - 1) / kStreamCols;
-    const int e = blockIdx.x / NB, nb = blockIdx.x % NB;
-    const int off = s_off[e], cnt = s_cnt[e];
-    if (cnt == 0) return;  // uniform
-
-    const int kg = threadIdx.x >> 5, cl = threadIdx.x & 31;
-    const int col = nb * kStreamCols + cl * 8;
-    const bool col_ok = col < N;
-    const bf16_t* We = W + (int64_t)e * K * N + col;
-
-    for (int r0 = 0; r0 < cnt; r0 += kStreamRows) {
-        const int rows = cnt - r0 < kStreamRows ? cnt - r0 : kStreamRows;
-        const int cpr = K / 8;
-        for (int u = threadIdx.x; u < kStreamRows * cpr; u += kThreads) {
-            const int r = u / cpr, c = u % cpr;
-            u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-            if (r < rows) v = ld16(X + (int64_t)(off + r0 + r) * K + c * 8);
-            *reinterpret_cast<u32x4_t*>(xs + r * K + c * 8) = v;
-        }
-        __syncthreads();
-
-        float acc[kStreamRows][8];
-#pragma unroll
-        for (int r = 0; r < kStreamRows; ++r)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-
-        if (col_ok) {
-#pragma unroll 2
-            for (int k = kg * 8; k < K; k += 8 * kStreamKGroups) {
-                u32x4_t wv[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) wv[j] = ld16(We + (int64_t)(k + j) * N);
-#pragma unroll
-                for (int r = 0; r < kStreamRows; ++r) {
-                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + r * K + k);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t xp = xv[j >> 1];
-                        const float xf = (j & 1) ? bf16_hi(xp) : bf16_lo(xp);
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) {
-                            const uint32_t wp = wv[j][c >> 1];
-                            const float wf = (c & 1) ? bf16_hi(wp) : bf16_lo(wp);
-                            acc[r][c] = __builtin_fmaf(xf, wf, acc[r][c]);
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < kStreamRows; ++r)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) red[kg][r][cl * 8 + c] = acc[r][c];
-        __syncthreads();
-        // 4 rows x 32 chunks of 8 columns; fixed summation order over k-groups
-        if (threadIdx.x < kStreamRows * (kStreamCols / 8)) {
-            const int r = threadIdx.x / (kStreamCols / 8);
-            const int c8 = threadIdx.x % (kStreamCols / 8);
-            const int gcol = nb * kStreamCols + c8 * 8;
-            if (r < rows && gcol < N) {
-                float s[8];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) s[c] = 0.f;
-                for (int g = 0; g < kStreamKGroups; ++g)
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) s[c] += red[g][r][c8 * 8 + c];
-                u32x4_t o;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(s[2 * c], s[2 * c + 1]);
-                st16(Y + (int64_t)(off + r0 + r) * N + gcol, o);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// tile shapes of the first version
-constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;
 
 int64_t row_tiles_bound(int64_t M_cap, int64_t E, int bm) { return (M_cap + bm - 1) / bm + E; }
-
-bool use_stream(int64_t E, int64_t M_cap, int64_t K) {
-    // a few rows per expert on average, and the staged x rows keep the
-    // kernel's total LDS (40 KiB static) within 64 KiB
-    return M_cap <= 8 * E && K * kStreamRows * 2 <= 24 * 1024;
-}
 
 }  // namespace
 
@@ -510,18 +484,12 @@ hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* g
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void*,
                           int32_t* dev_err, hipStream_t stream) {
     if (M_cap == 0) return hipSuccess;
-    if (use_stream(E, M_cap, K)) {
-        const int64_t NB = (N + kStreamCols - 1) / kStreamCols;
-        const size_t shmem = (size_t)K * kStreamRows * 2;
-        hipLaunchKernelGGL(gmm_stream_kernel, dim3((unsigned)(E * NB)), dim3(kThreads), shmem, stream,
-                           x, w, group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
-        return hipGetLastError();
-    }
+    if (gmm_stream_applies(E, M_cap, K))
+        return launch_gmm_stream(x, w, group_list, E, M_cap, K, N, y, dev_err, stream);
     const int64_t NT = (N + kBN - 1) / kBN;
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
-    hipLaunchKernelGGL((gmm_rows_kernel<kBM, kBN, kWM, kWN, false>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, x, w, group_list, (int)E, M_cap, (int)K, (int)N, y,
-                       dev_err);
+    hipLaunchKernelGGL(gmm_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
+                       group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
     return hipGetLastError();
 }
 
@@ -531,9 +499,8 @@ hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int
     if (M_cap == 0) return hipSuccess;
     const int64_t NT = (K + kBN - 1) / kBN;
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
-    hipLaunchKernelGGL((gmm_rows_kernel<kBM, kBN, kWM, kWN, true>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, dy, w, group_list, (int)E, M_cap, (int)K, (int)N,
-                       dx, dev_err);
+    hipLaunchKernelGGL(gmm_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, dy, w,
+                       group_list, (int)E, M_cap, (int)K, (int)N, dx, dev_err);
     return hipGetLastError();
 }
 
@@ -541,8 +508,8 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
                                  int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw,
                                  void*, int32_t* dev_err, hipStream_t stream) {
     const int64_t grid = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL((gmm_dw_kernel<kBM, kBN, kWM, kWN>), dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, x, dy, group_list, (int)E, M_cap, (int)K, (int)N, dw, dev_err);
+    hipLaunchKernelGGL(gmm_dw_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, dy,
+                       group_list, (int)E, M_cap, (int)K, (int)N, dw, dev_err);
     return hipGetLastError();
 }
 

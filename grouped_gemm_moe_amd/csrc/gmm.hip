@@ -16,19 +16,21 @@
 //    k-tile, n-tile) list for dW, largest experts first.  The grid is sized
 //    from host-known bounds; surplus workgroups exit at once.
 //  * One MFMA engine: 256x256 output tile per workgroup, 4 waves of 128x128,
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators, a 64-deep reduction step.
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //  * Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
 //    VGPR staging).  Lanes whose element lies outside the problem (ragged
 //    rows, reduction tails, rows past an expert) get an out-of-range buffer
 //    offset, which loads zeros -- so partial tiles need no special path.
 //  * Each operand keeps its HBM orientation in LDS.  A reduction-contiguous
-//    tile ([outer][64], 128-byte rows) is read with ds_read_b128; an
-//    outer-contiguous tile ([64][outer]) is read with ds_read_b64_tr_b16,
+//    tile ([outer][BK]) is read with ds_read_b128; an outer-contiguous tile
+//    ([BK][outer]) is read with ds_read_b64_tr_b16,
 //    the gfx950 transposing LDS read, which hands each lane 4 consecutive
 //    reduction elements of one column.  16-byte chunks are XOR-swizzled per
 //    row so both reads hit every LDS bank pair at most twice per pass.
-//  * Two LDS stages (2 x 64 KiB): the loads for step s+1 fly while step s
-//    runs its MFMAs; one barrier per step.
+//  * A ring of NST LDS stages (4 x 32 KiB, BK = 32): the loads of the next
+//    NST-1 steps fly while a step runs its MFMAs -- deep enough to cover
+//    HBM latency with one workgroup per CU.  One barrier per step; each wave
+//    waits only for its own loads of the step about to be read.
 //  * The MFMA is issued with operands swapped (B fragment as the hardware A
 //    operand) so each lane holds 4 consecutive output columns; the epilogue
 //    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
@@ -42,7 +44,17 @@ namespace moegmm {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
-constexpr int BK = 64;         // reduction step
+
+#ifndef MOEGMM_BK
+#define MOEGMM_BK 32
+#endif
+#ifndef MOEGMM_NST
+#define MOEGMM_NST 4
+#endif
+constexpr int BK = MOEGMM_BK;     // reduction depth of one LDS stage
+constexpr int kNST = MOEGMM_NST;  // LDS stages in the ring
+static_assert(BK == 32 || BK == 64, "stage depth");
+static_assert(kNST >= 2 && kNST <= 6, "stage count");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -62,7 +74,9 @@ MOE_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 MOE_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // LDS swizzles (16-byte chunk index XOR) for the two tile orientations.
-MOE_DEVICE int swz_k(int o) { return (o ^ (o >> 3)) & 7; }   // [outer][64] tiles
+// [outer][BK] tiles: 16 consecutive rows read at one logical chunk must land
+// on distinct bank groups (64 banks x 4 bytes).
+MOE_DEVICE int swz_k(int o) { return BK == 64 ? ((o ^ (o >> 3)) & 7) : ((o >> 2) & 3); }
 MOE_DEVICE int swz_mn(int k) { return (k & 3) << 2; }         // [64][outer] tiles
 
 // ---------------------------------------------------------------------------
@@ -74,10 +88,13 @@ template <int BO, bool KMAJOR>
 struct Dma;
 
 // Reduction-contiguous operand: element (o, q) at base[o*ld + q].
-// LDS tile [BO][BK]; one instruction fills 8 rows of 128 bytes.
+// LDS tile [BO][BK]; one instruction fills 1024 / (2*BK) rows.
 template <int BO>
 struct Dma<BO, true> {
-    static constexpr int kInst = BO / 8 / 4;  // per wave
+    static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
+    static constexpr int kRowsPerInst = 64 / kCPR;
+    static constexpr int kInst = BO / kRowsPerInst / 4;  // per wave
+    static_assert(kInst >= 1, "tile/threads mismatch");
     uint32_t off[kInst];
     int red[kInst];
     uint32_t ok_mask;
@@ -87,8 +104,8 @@ struct Dma<BO, true> {
         ok_mask = 0;
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
-            const int o = (wid * kInst + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz_k(o);
+            const int o = (wid * kInst + i) * kRowsPerInst + lane / kCPR;
+            const int c = (lane % kCPR) ^ swz_k(o);
             off[i] = (uint32_t)(((int64_t)o * ld + c * 8) * 2);
             red[i] = c * 8;
             if (o < outer_lim) ok_mask |= 1u << i;
@@ -106,6 +123,12 @@ struct Dma<BO, true> {
         }
     }
     static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t, int s) { return base + s * BK; }
+    // instruction i of this wave's share of one stage
+    MOE_DEVICE void issue_one(int i, __amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, int red_left) const {
+        const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (LDS_AS void*)(lds + (wave_id() * kInst + i) * 512), 16, v, 0, 0, 0);
+    }
 };
 
 // Outer-contiguous operand: element (o, q) at base[q*ld + o].
@@ -144,6 +167,12 @@ struct Dma<BO, false> {
     }
     static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t ld, int s) {
         return base + (int64_t)s * BK * ld;
+    }
+    // instruction i of this wave's share of one stage
+    MOE_DEVICE void issue_one(int i, __amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, int red_left) const {
+        const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (LDS_AS void*)(lds + (wave_id() * kInst + i) * 512), 16, v, 0, 0, 0);
     }
 };
 
@@ -234,30 +263,41 @@ struct Engine {
         for (int t = 0; t < TN; ++t) Frag<BN, B_KMAJOR>::load(b[t], lb, wn * WTN + t * 32, ks * 16);
     }
 
-    MOE_DEVICE void mfmas(const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN]) {
+    // MFMAs of one sub-step; hook(m) runs after the m-th MFMA of the step
+    // (m counts across sub-steps), so loads can be spread between MFMAs.
+    template <class Hook>
+    MOE_DEVICE void mfmas(const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN], int ks, Hook& hook) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+                hook(ks * TM * TN + i * TN + j);
+            }
     }
 
     // One reduction step from LDS: fragments of sub-step ks+1 are read while
     // the MFMAs of sub-step ks run.
-    MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb) {
+    template <class Hook>
+    MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb, Hook& hook) {
+        static_assert(BK / 16 == 2 || BK / 16 == 4, "sub-steps");
         bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
         load_frags(a0, b0, la, lb, 0);
         lds_wait(a0, b0);
         load_frags(a1, b1, la, lb, 1);
-        mfmas(a0, b0);
+        mfmas(a0, b0, 0, hook);
         lds_wait(a1, b1);
-        load_frags(a0, b0, la, lb, 2);
-        mfmas(a1, b1);
-        lds_wait(a0, b0);
-        load_frags(a1, b1, la, lb, 3);
-        mfmas(a0, b0);
-        lds_wait(a1, b1);
-        mfmas(a1, b1);
+        if constexpr (BK / 16 == 4) {
+            load_frags(a0, b0, la, lb, 2);
+            mfmas(a1, b1, 1, hook);
+            lds_wait(a0, b0);
+            load_frags(a1, b1, la, lb, 3);
+            mfmas(a0, b0, 2, hook);
+            lds_wait(a1, b1);
+            mfmas(a1, b1, 3, hook);
+        } else {
+            mfmas(a1, b1, 1, hook);
+        }
     }
 
     // lane holds rows (l%32) and 4 consecutive columns per (i, j, g)
@@ -286,15 +326,29 @@ struct Engine {
     }
 };
 
-// One output tile: two LDS stages, statically named so the compiler can tell
-// which outstanding LDS-DMA a read depends on.
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+MOE_DEVICE void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// One output tile over a ring of kNST LDS stages.  Per step s: wait for this
+// wave's copies of step s (the kNST-2 later steps stay in flight), barrier
+// (all copies of step s landed; step s-1 fully read), then run step s while
+// refilling the stage read at step s-1 with step s+kNST-1, one load after
+// every few MFMAs so the memory pipe and the MFMA pipe work side by side.
+// Steps past the end still "load", with every lane out of range: that only
+// writes zeros into a stage nobody reads again, and keeps the number of
+// loads in flight constant (no data-dependent wait counts, no branches).
+// `smem` holds kNST stages of [A tile | B tile].
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR>
 MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
                           int64_t ldb, int b_olim, int red_len, bf16_t* out, int64_t ldo,
-                          int rows_valid, int cols_valid, bf16_t* lA0, bf16_t* lB0, bf16_t* lA1,
-                          bf16_t* lB1) {
+                          int rows_valid, int cols_valid, bf16_t* smem) {
     using DA = Dma<BM, A_KMAJOR>;
     using DB = Dma<BN, B_KMAJOR>;
+    constexpr int kStage = (BM + BN) * BK;       // elements per stage
+    constexpr int kPer = DA::kInst + DB::kInst;  // loads per wave per stage
     DA da;
     DB db;
     da.init(lda, a_olim);
@@ -302,26 +356,38 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     Engine<BM, BN, WM, WN, A_KMAJOR, B_KMAJOR> eng;
     eng.zero();
     const int nk = (red_len + BK - 1) / BK;
-    da.issue(DA::stage(a_base, lda, 0), lA0, red_len);
-    db.issue(DB::stage(b_base, ldb, 0), lB0, red_len);
-    // pairs of steps: stage s in buffer 0, stage s+1 in buffer 1
-    int s = 0;
-    for (; s + 1 < nk; s += 2) {
-        __syncthreads();  // stage s landed (every wave waited for its own copies); s-1 consumed
-        da.issue(DA::stage(a_base, lda, s + 1), lA1, red_len - (s + 1) * BK);
-        db.issue(DB::stage(b_base, ldb, s + 1), lB1, red_len - (s + 1) * BK);
-        eng.compute(lA0, lB0);
-        __syncthreads();  // stage s+1 landed; stage s consumed
-        if (s + 2 < nk) {
-            da.issue(DA::stage(a_base, lda, s + 2), lA0, red_len - (s + 2) * BK);
-            db.issue(DB::stage(b_base, ldb, s + 2), lB0, red_len - (s + 2) * BK);
-        }
-        eng.compute(lA1, lB1);
+    auto issue = [&](int step) {
+        bf16_t* st = smem + (step % kNST) * kStage;
+        da.issue(DA::stage(a_base, lda, step), st, red_len - step * BK);
+        db.issue(DB::stage(b_base, ldb, step), st + BM * BK, red_len - step * BK);
+    };
+    // the MFMAs of one step, and how many of them separate two loads
+    constexpr int kMfmaPerStep = (BK / 16) * (BM / WM / 32) * (BN / WN / 32);
+    constexpr int kStride = kMfmaPerStep / kPer;
+    static_assert(kStride >= 1 && kMfmaPerStep % kPer == 0, "load spacing");
+#pragma unroll
+    for (int p = 0; p < kNST - 1; ++p) issue(p);
+    for (int s = 0; s < nk; ++s) {
+        wait_vmcnt<(kNST - 2) * kPer>();
+        __builtin_amdgcn_s_barrier();
+        // loads of step s+kNST-1 into the stage read at step s-1, one after
+        // every kStride MFMAs of step s
+        const int nxt = s + kNST - 1;
+        bf16_t* nst = smem + (nxt % kNST) * kStage;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(DA::stage(a_base, lda, nxt));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b_base, ldb, nxt));
+        const int left = red_len - nxt * BK;  // <= 0 past the end: all lanes out of range
+        auto hook = [&](int m) {
+            if ((m % kStride) == kStride - 1) {
+                const int q = m / kStride;
+                if (q < DA::kInst) da.issue_one(q, ra, nst, left);
+                else db.issue_one(q - DA::kInst, rb, nst + BM * BK, left);
+            }
+        };
+        const bf16_t* st = smem + (s % kNST) * kStage;
+        eng.compute(st, st + BM * BK, hook);
     }
-    if (s < nk) {  // odd number of steps: the last one sits in buffer 0
-        __syncthreads();
-        eng.compute(lA0, lB0);
-    }
+    wait_vmcnt<0>();  // no LDS write may outlive the workgroup
     eng.store(out, ldo, rows_valid, cols_valid);
 }
 
@@ -346,7 +412,8 @@ MOE_DEVICE int xcd_remap(int bid, int n) {
 #define MOEGMM_WN 2
 #endif
 constexpr int kBM = MOEGMM_BM, kBN = MOEGMM_BN, kWM = MOEGMM_WM, kWN = MOEGMM_WN;
-static_assert(kBM * BK * 2 >= 12 * 1024, "schedule arrays live in an A stage");
+constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
+static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the last stage");
 
 // ---------------------------------------------------------------------------
 // Row-grouped GEMM: forward (IS_DX = false) and input gradient (IS_DX = true).
@@ -359,12 +426,11 @@ template <bool IS_DX>
 __global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
-    __shared__ __attribute__((aligned(1024))) bf16_t lA0[kBM * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lB0[kBN * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lA1[kBM * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lB1[kBN * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
-    int* s_off = reinterpret_cast<int*>(lA1);
+    // schedule arrays: in the last stage, which no load touches before the
+    // first barrier of the main loop
+    int* s_off = reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK);
     int* s_cnt = s_off + kMaxExperts;
     int* s_tst = s_cnt + kMaxExperts;
 
@@ -401,13 +467,13 @@ __global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
     const int row_end = __builtin_amdgcn_readfirstlane(s_off[e] + s_cnt[e]);
     const int rows_valid = row_end - row0 < kBM ? row_end - row0 : kBM;
     const int n0 = __builtin_amdgcn_readfirstlane(nt * kBN);
-    __syncthreads();  // schedule arrays (inside lA1) are dead from here on
+    __syncthreads();  // schedule arrays are dead from here on
 
     const int64_t lda = IS_DX ? N : K;
     const bf16_t* We = W + (int64_t)e * K * N;
     gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
         A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N, Ncols - n0,
-        Kred, Y + (int64_t)row0 * Ncols + n0, Ncols, rows_valid, Ncols - n0, lA0, lB0, lA1, lB1);
+        Kred, Y + (int64_t)row0 * Ncols + n0, Ncols, rows_valid, Ncols - n0, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,13 +488,12 @@ constexpr int kMaxRankedExperts = 256;  // beyond this, experts run in index ord
 __global__ __launch_bounds__(kThreads) void gmm_dw_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int32_t* dev_err) {
-    __shared__ __attribute__((aligned(1024))) bf16_t lA0[kBM * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lB0[kBN * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lA1[kBM * BK];
-    __shared__ __attribute__((aligned(1024))) bf16_t lB1[kBN * BK];
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_pick;
-    int* s_off = reinterpret_cast<int*>(lA1);
+    // schedule arrays: in the last stage, which no load touches before the
+    // first barrier of the main loop
+    int* s_off = reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK);
     int* s_cnt = s_off + kMaxExperts;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
@@ -455,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void gmm_dw_kernel(
     const int k0 = kt_out * kBM, n0 = nt * kBN;
     const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
     const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
-    __syncthreads();  // schedule arrays (inside lA1) are dead from here on
+    __syncthreads();  // schedule arrays are dead from here on
 
     const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
     const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
@@ -471,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void gmm_dw_kernel(
     }
     gemm_tile<kBM, kBN, kWM, kWN, false, false>(X + (int64_t)off * K + k0, K, rows_valid,
                                                 DY + (int64_t)off * N + n0, N, cols_valid, cnt, out, N,
-                                                rows_valid, cols_valid, lA0, lB0, lA1, lB1);
+                                                rows_valid, cols_valid, smem);
 }
 
 int64_t row_tiles_bound(int64_t M_cap, int64_t E, int bm) { return (M_cap + bm - 1) / bm + E; }

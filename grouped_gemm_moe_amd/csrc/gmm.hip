@@ -15,7 +15,8 @@
 //    XCD-aware order so neighbouring tiles share an L2) and an (expert,
 //    k-tile, n-tile) list for dW, largest experts first.  The grid is sized
 //    from host-known bounds; surplus workgroups exit at once.
-//  * One MFMA engine: 256x256 output tile per workgroup, 4 waves of 128x128,
+//  * One MFMA engine: 256x256 output tile per workgroup, 8 waves (two per
+//    SIMD, so one hides the other's waits) of 128x64 each,
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 //  * Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
 //    VGPR staging).  Lanes whose element lies outside the problem (ragged
@@ -28,9 +29,8 @@
 //    reduction elements of one column.  16-byte chunks are XOR-swizzled per
 //    row so both reads hit every LDS bank pair at most twice per pass.
 //  * A ring of NST LDS stages (4 x 32 KiB, BK = 32): the loads of the next
-//    NST-1 steps fly while a step runs its MFMAs -- deep enough to cover
-//    HBM latency with one workgroup per CU.  One barrier per step; each wave
-//    waits only for its own loads of the step about to be read.
+//    NST-1 steps fly while a step runs its MFMAs.  One barrier per step;
+//    each wave waits only for its own loads of the step about to be read.
 //  * The MFMA is issued with operands swapped (B fragment as the hardware A
 //    operand) so each lane holds 4 consecutive output columns; the epilogue
 //    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
@@ -43,7 +43,11 @@ namespace moegmm {
 
 namespace {
 
-constexpr int kThreads = 256;  // 4 waves
+#ifndef MOEGMM_THREADS
+#define MOEGMM_THREADS 512
+#endif
+constexpr int kThreads = MOEGMM_THREADS;  // 4 or 8 waves
+constexpr int kWaves = kThreads / 64;
 
 #ifndef MOEGMM_BK
 #define MOEGMM_BK 32
@@ -93,8 +97,8 @@ template <int BO>
 struct Dma<BO, true> {
     static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
     static constexpr int kRowsPerInst = 64 / kCPR;
-    static constexpr int kInst = BO / kRowsPerInst / 4;  // per wave
-    static_assert(kInst >= 1, "tile/threads mismatch");
+    static constexpr int kInst = BO / kRowsPerInst / kWaves;  // per wave
+    static_assert(kInst >= 1 && BO % (kRowsPerInst * kWaves) == 0, "tile/threads mismatch");
     uint32_t off[kInst];
     int red[kInst];
     uint32_t ok_mask;
@@ -137,8 +141,9 @@ template <int BO>
 struct Dma<BO, false> {
     static constexpr int kChunks = BO / 8;
     static constexpr int kRowsPerInst = 64 / kChunks;
-    static constexpr int kInst = BK / kRowsPerInst / 4;  // per wave
-    static_assert(kChunks >= 16 && 64 % kChunks == 0 && kInst >= 1, "outer tile must be 128 or 256");
+    static constexpr int kInst = BK / kRowsPerInst / kWaves;  // per wave
+    static_assert(kChunks >= 16 && 64 % kChunks == 0 && kInst >= 1 &&
+                      BK % (kRowsPerInst * kWaves) == 0, "outer tile must be 128 or 256");
     uint32_t off[kInst];
     int red[kInst];
     uint32_t ok_mask;
@@ -361,10 +366,9 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
         da.issue(DA::stage(a_base, lda, step), st, red_len - step * BK);
         db.issue(DB::stage(b_base, ldb, step), st + BM * BK, red_len - step * BK);
     };
-    // the MFMAs of one step, and how many of them separate two loads
+    // the MFMAs of one step; load q goes after MFMA (q+1)*kMfmaPerStep/kPer - 1
     constexpr int kMfmaPerStep = (BK / 16) * (BM / WM / 32) * (BN / WN / 32);
-    constexpr int kStride = kMfmaPerStep / kPer;
-    static_assert(kStride >= 1 && kMfmaPerStep % kPer == 0, "load spacing");
+    static_assert(kMfmaPerStep >= kPer, "load spacing");
 #pragma unroll
     for (int p = 0; p < kNST - 1; ++p) issue(p);
     for (int s = 0; s < nk; ++s) {
@@ -378,10 +382,12 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b_base, ldb, nxt));
         const int left = red_len - nxt * BK;  // <= 0 past the end: all lanes out of range
         auto hook = [&](int m) {
-            if ((m % kStride) == kStride - 1) {
-                const int q = m / kStride;
-                if (q < DA::kInst) da.issue_one(q, ra, nst, left);
-                else db.issue_one(q - DA::kInst, rb, nst + BM * BK, left);
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                if (m == (q + 1) * kMfmaPerStep / kPer - 1) {
+                    if (q < DA::kInst) da.issue_one(q, ra, nst, left);
+                    else db.issue_one(q - DA::kInst, rb, nst + BM * BK, left);
+                }
             }
         };
         const bf16_t* st = smem + (s % kNST) * kStage;
@@ -409,10 +415,14 @@ MOE_DEVICE int xcd_remap(int bid, int n) {
 #define MOEGMM_WM 2
 #endif
 #ifndef MOEGMM_WN
-#define MOEGMM_WN 2
+#define MOEGMM_WN 4
 #endif
 constexpr int kBM = MOEGMM_BM, kBN = MOEGMM_BN, kWM = MOEGMM_WM, kWN = MOEGMM_WN;
 constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
+// two workgroups per CU when the LDS ring and the accumulators allow it: one
+// workgroup's epilogue and first loads then overlap the other's MFMAs
+constexpr int kAccRegs = (kBM / kWM) * (kBN / kWN) / 64;
+constexpr int kOccupancy = (kSmemElems * 2 <= 80 * 1024 && kAccRegs <= 128) ? 2 : 1;
 static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the last stage");
 
 // ---------------------------------------------------------------------------
@@ -423,7 +433,7 @@ static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the la
 //        ld N); out dx [M_cap, K]; reduction N.
 // ---------------------------------------------------------------------------
 template <bool IS_DX>
-__global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
+__global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
@@ -454,7 +464,11 @@ __global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
     const int NT = (Ncols + kBN - 1) / kBN;
     const int ntiles = (int)total_mt * NT;
     if ((int)blockIdx.x >= ntiles) return;  // uniform across the block
+#if defined(MOEGMM_NO_XCD_REMAP)
+    const int t = blockIdx.x;
+#else
     const int t = xcd_remap(blockIdx.x, ntiles);
+#endif
     const int mt = t / NT, nt = t % NT;
     int lo = 0, hi = E - 1;  // last expert whose first tile is <= mt
     while (lo < hi) {
@@ -485,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void gmm_rows_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMaxRankedExperts = 256;  // beyond this, experts run in index order
 
-__global__ __launch_bounds__(kThreads) void gmm_dw_kernel(
+__global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int32_t* dev_err) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];

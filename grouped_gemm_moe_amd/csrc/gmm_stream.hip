@@ -16,34 +16,71 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// Decode-shaped forward: weight streaming.  Block = (expert e, 256-column
-// slice).  256 threads = 8 k-groups x 32 column lanes; lane owns 8 columns,
-// k-group g walks k-chunks of 8 starting at 8g with stride 64.  Rows of the
-// expert are processed kStreamRows at a time (one weight pass each), staged in
-// LDS as bf16; partial sums over k-groups meet in LDS.
+// Block = (expert e, slice of COLS columns).  A wave holds 64/(COLS/8)
+// k-groups of COLS/8 column lanes; a lane owns 8 columns and walks k-chunks
+// of 8 rows, so each step is eight 16-byte weight loads feeding 8x8xROWS fp32
+// FMAs.  The expert's rows are staged in LDS (bf16) kStreamRows at a time,
+// one pass over the weights per group of rows.  Partial sums meet first
+// across the k-groups of a wave (shuffles), then across waves in LDS, always
+// in the same order.
 // ---------------------------------------------------------------------------
-constexpr int kStreamCols = 256;
+#ifndef MOEGMM_STREAM_COLS
+#define MOEGMM_STREAM_COLS 256
+#endif
+constexpr int kStreamCols = MOEGMM_STREAM_COLS;
 constexpr int kStreamRows = 4;
-constexpr int kStreamKGroups = kThreads / 32;
+constexpr int kWaves = kThreads / 64;
 
+template <int COLS, int ROWS>
+MOE_DEVICE void stream_rows(const bf16_t* __restrict__ We, const bf16_t* xs, int K, int N, int kg,
+                            float (&acc)[kStreamRows][8]) {
+    constexpr int kGroups = (64 / (COLS / 8)) * kWaves;
+#pragma unroll 2
+    for (int k = kg * 8; k < K; k += 8 * kGroups) {
+        u32x4_t wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[j] = ld16(We + (int64_t)(k + j) * N);
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + r * K + k);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t xp = xv[j >> 1];
+                const float xf = (j & 1) ? bf16_hi(xp) : bf16_lo(xp);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t wp = wv[j][c >> 1];
+                    const float wf = (c & 1) ? bf16_hi(wp) : bf16_lo(wp);
+                    acc[r][c] = __builtin_fmaf(xf, wf, acc[r][c]);
+                }
+            }
+        }
+    }
+}
+
+template <int COLS>
 __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
+    constexpr int kLanes = COLS / 8;          // column lanes of one k-group
+    constexpr int kGPW = 64 / kLanes;         // k-groups per wave
     extern __shared__ __attribute__((aligned(16))) char dsmem[];
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int64_t s_scan[kThreads / 64];
-    __shared__ float red[kStreamKGroups][kStreamRows][kStreamCols];
+    __shared__ float red[kWaves][kStreamRows][COLS];
     bf16_t* xs = reinterpret_cast<bf16_t*>(dsmem);  // [kStreamRows][K]
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int NB = (N + kStreamCols - 1) / kStreamCols;
+    const int NB = (N + COLS - 1) / COLS;
     const int e = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int off = s_off[e], cnt = s_cnt[e];
     if (cnt == 0) return;  // uniform
 
-    const int kg = threadIdx.x >> 5, cl = threadIdx.x & 31;
-    const int col = nb * kStreamCols + cl * 8;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int cl = lane % kLanes;
+    const int kg = wid * kGPW + lane / kLanes;
+    const int col = nb * COLS + cl * 8;
     const bool col_ok = col < N;
     const bf16_t* We = W + (int64_t)e * K * N + col;
 
@@ -63,50 +100,39 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
         for (int r = 0; r < kStreamRows; ++r)
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-
         if (col_ok) {
-#pragma unroll 2
-            for (int k = kg * 8; k < K; k += 8 * kStreamKGroups) {
-                u32x4_t wv[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) wv[j] = ld16(We + (int64_t)(k + j) * N);
-#pragma unroll
-                for (int r = 0; r < kStreamRows; ++r) {
-                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xs + r * K + k);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t xp = xv[j >> 1];
-                        const float xf = (j & 1) ? bf16_hi(xp) : bf16_lo(xp);
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) {
-                            const uint32_t wp = wv[j][c >> 1];
-                            const float wf = (c & 1) ? bf16_hi(wp) : bf16_lo(wp);
-                            acc[r][c] = __builtin_fmaf(xf, wf, acc[r][c]);
-                        }
-                    }
-                }
-            }
+            if (rows == 1) stream_rows<COLS, 1>(We, xs, K, N, kg, acc);
+            else if (rows == 2) stream_rows<COLS, 2>(We, xs, K, N, kg, acc);
+            else stream_rows<COLS, 4>(We, xs, K, N, kg, acc);  // a third row is zero-padded
         }
+        // k-groups of this wave, then waves, in a fixed order
 #pragma unroll
-        for (int r = 0; r < kStreamRows; ++r)
+        for (int o = kLanes; o < 64; o <<= 1)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) red[kg][r][cl * 8 + c] = acc[r][c];
+            for (int r = 0; r < kStreamRows; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[r][c] += __shfl_xor(acc[r][c], o, 64);
+        if (lane < kLanes) {
+#pragma unroll
+            for (int r = 0; r < kStreamRows; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) red[wid][r][cl * 8 + c] = acc[r][c];
+        }
         __syncthreads();
-        // 4 rows x 32 chunks of 8 columns; fixed summation order over k-groups
-        if (threadIdx.x < kStreamRows * (kStreamCols / 8)) {
-            const int r = threadIdx.x / (kStreamCols / 8);
-            const int c8 = threadIdx.x % (kStreamCols / 8);
-            const int gcol = nb * kStreamCols + c8 * 8;
+        if (threadIdx.x < kStreamRows * kLanes) {
+            const int r = threadIdx.x / kLanes, c8 = threadIdx.x % kLanes;
+            const int gcol = nb * COLS + c8 * 8;
             if (r < rows && gcol < N) {
-                float s[8];
+                float sum[8];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) s[c] = 0.f;
-                for (int g = 0; g < kStreamKGroups; ++g)
+                for (int c = 0; c < 8; ++c) sum[c] = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) s[c] += red[g][r][c8 * 8 + c];
+                for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) sum[c] += red[w][r][c8 * 8 + c];
                 u32x4_t o;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(s[2 * c], s[2 * c + 1]);
+                for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(sum[2 * c], sum[2 * c + 1]);
                 st16(Y + (int64_t)(off + r0 + r) * N + gcol, o);
             }
         }
@@ -114,13 +140,12 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     }
 }
 
-
 }  // namespace
 
 bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K) {
     // a few rows per expert on average, and the staged x rows keep the
-    // kernel's total LDS (40 KiB static) within 64 KiB
-    return M_cap <= 8 * E && K * kStreamRows * 2 <= 24 * 1024;
+    // kernel's total LDS (at most 24 KiB static) within 64 KiB
+    return M_cap <= 8 * E && K * kStreamRows * 2 <= 32 * 1024;
 }
 
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
@@ -128,8 +153,8 @@ hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t
                              int32_t* dev_err, hipStream_t stream) {
     const int64_t NB = (N + kStreamCols - 1) / kStreamCols;
     const size_t shmem = (size_t)K * kStreamRows * 2;
-    hipLaunchKernelGGL(gmm_stream_kernel, dim3((unsigned)(E * NB)), dim3(kThreads), shmem, stream, x,
-                       w, group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
+    hipLaunchKernelGGL(gmm_stream_kernel<kStreamCols>, dim3((unsigned)(E * NB)), dim3(kThreads), shmem,
+                       stream, x, w, group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
     return hipGetLastError();
 }
 

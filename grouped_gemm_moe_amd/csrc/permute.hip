@@ -19,7 +19,10 @@
 //                 expert in slot order (wave ballots emulate a match-any on
 //                 the expert id) and writes row_id_map and sorted_slot.
 //   4. gather  -- copies token rows to their permuted rows with 16-byte loads
-//                 and stores (coalesced inside each row).
+//                 and stores (coalesced inside each row), four loads in
+//                 flight per thread.
+// For at most 4096 slots (decode-sized calls) steps 1-3 run as one
+// single-workgroup kernel, so the whole permute is two launches.
 #include "common.h"
 #include "launch.h"
 
@@ -29,6 +32,7 @@ namespace {
 
 constexpr int kPermThreads = 256;          // 4 waves
 constexpr int kWaves = kPermThreads / 64;
+constexpr int64_t kSmallSlots = 4096;      // single-workgroup path up to this many slots
 
 // Slots per block: a multiple of 4*64 so that each wave gets whole groups of
 // 64; grown with S so the number of blocks stays <= 4096.
@@ -94,49 +98,34 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     }
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t S, int E, int64_t chunk,
-    const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_id_map,
-    int32_t* __restrict__ sorted_slot) {
-    __shared__ int32_t next_row[kWaves][kMaxExperts];
-    const int wid = threadIdx.x >> 6;
+// Per-wave pieces shared by the multi-block and the single-block paths.  Each
+// wave owns the slot range [w0, w1) (consecutive ranges in wave order).
+
+// counts per expert of the wave's slots into cnt (LDS, zeroed by the caller)
+MOE_DEVICE void wave_counts(const int32_t* __restrict__ ids, int64_t w0, int64_t w1, int E,
+                            int32_t* cnt) {
     const int lane = threadIdx.x & 63;
-    for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
-    __syncthreads();
-
-    const int64_t s0 = (int64_t)blockIdx.x * chunk;
-    const int64_t sub = chunk / kWaves;             // slots per wave, multiple of 64
-    const int64_t w0 = s0 + wid * sub;
-    int64_t w1 = w0 + sub;
-    if (w1 > S) w1 = S;
-
-    // 1. per-wave counts per expert
     for (int64_t s = w0 + lane; s < w1; s += 64) {
-        int32_t id = ids[s];
-        if (valid_id(id, E)) atomicAdd(&next_row[wid][id], 1);
+        const int32_t id = ids[s];
+        if (valid_id(id, E)) atomicAdd(&cnt[id], 1);
     }
-    __syncthreads();
-    // 2. starting row of every wave for every expert
-    const int32_t* base = blk_base + (int64_t)blockIdx.x * E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t run = base[e];
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            int32_t c = next_row[w][e];
-            next_row[w][e] = run;
-            run += c;
-        }
-    }
-    __syncthreads();
-    // 3. stable rank within each group of 64 slots, groups in order
+}
+
+// Stable rank of every slot within its expert, groups of 64 slots in order.
+// next_row[e] holds the wave's first row for expert e and is advanced.
+MOE_DEVICE void wave_rank_scatter(const int32_t* __restrict__ ids, int64_t w0, int64_t w1, int E,
+                                  int32_t* next_row, int32_t* __restrict__ row_id_map,
+                                  int32_t* __restrict__ sorted_slot) {
+    const int lane = threadIdx.x & 63;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int64_t g = w0; g < w1; g += 64) {
         const int64_t s = g + lane;
-        int32_t id = (s < w1) ? ids[s] : -1;
+        const int32_t id = (s < w1) ? ids[s] : -1;
         const bool ok = valid_id(id, E);
         const int key = ok ? id : 0;
+        // peers = lanes with the same expert (match-any built from ballots)
         uint64_t peers = __ballot(ok);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (key >> b) & 1;
@@ -144,10 +133,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
             peers &= bit ? m : ~m;
         }
         int32_t row = -1;
-        if (ok) row = next_row[wid][key] + __popcll(peers & lt_mask);
+        if (ok) row = next_row[key] + __popcll(peers & lt_mask);
         // all lanes have read next_row before the leaders update it
         __builtin_amdgcn_wave_barrier();
-        if (ok && (peers & lt_mask) == 0) next_row[wid][key] += __popcll(peers);
+        if (ok && (peers & lt_mask) == 0) next_row[key] += __popcll(peers);
         __builtin_amdgcn_wave_barrier();
         if (s < w1) {
             row_id_map[s] = row;
@@ -156,7 +145,90 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     }
 }
 
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t chunk,
+    const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_id_map,
+    int32_t* __restrict__ sorted_slot) {
+    __shared__ int32_t next_row[kWaves][kMaxExperts];
+    const int wid = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
+    __syncthreads();
+
+    const int64_t s0 = (int64_t)blockIdx.x * chunk;
+    const int64_t sub = chunk / kWaves;  // slots per wave, multiple of 64
+    const int64_t w0 = s0 + wid * sub;
+    const int64_t w1 = w0 + sub < S ? w0 + sub : S;
+
+    wave_counts(ids, w0, w1, E, next_row[wid]);
+    __syncthreads();
+    // starting row of every wave for every expert
+    const int32_t* base = blk_base + (int64_t)blockIdx.x * E;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t run = base[e];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = next_row[w][e];
+            next_row[w][e] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    wave_rank_scatter(ids, w0, w1, E, next_row[wid], row_id_map, sorted_slot);
+}
+
+// All of histogram, expert offsets and ranking in one workgroup, for inputs
+// of at most one chunk (decode-sized calls: one launch instead of three).
+__global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t* __restrict__ tokens_per_expert,
+    int32_t* __restrict__ row_id_map, int32_t* __restrict__ sorted_slot, int32_t* dev_err) {
+    __shared__ int32_t next_row[kWaves][kMaxExperts];
+    __shared__ int64_t scan_tmp[kPermThreads / 64];
+    const int wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t sub = (S + kWaves * 64 - 1) / (kWaves * 64) * 64;  // multiple of 64
+    const int64_t w0 = wid * sub < S ? wid * sub : S;
+    const int64_t w1 = w0 + sub < S ? w0 + sub : S;
+    int bad = 0;
+    for (int64_t s = w0 + lane; s < w1; s += 64) {
+        const int32_t id = ids[s];
+        if (!valid_id(id, E) && id != -1) bad = 1;
+    }
+    if (bad && dev_err) atomicOr(dev_err, MOE_DEVERR_EXPERT_ID);
+    wave_counts(ids, w0, w1, E, next_row[wid]);
+    __syncthreads();
+    // per-expert totals, scanned in expert order (thread owns <= 4 experts)
+    const int per = (E + kPermThreads - 1) / kPermThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t tot[4] = {0, 0, 0, 0};
+    int64_t mine = 0;
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        for (int w = 0; w < kWaves; ++w) tot[i] += next_row[w][e];
+        mine += tot[i];
+    }
+    int64_t total;
+    int64_t off = block_exclusive_scan<int64_t>(mine, scan_tmp, &total);
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        tokens_per_expert[e] = tot[i];
+        int32_t run = (int32_t)off;
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = next_row[w][e];
+            next_row[w][e] = run;
+            run += c;
+        }
+        off += tot[i];
+    }
+    __syncthreads();
+    wave_rank_scatter(ids, w0, w1, E, next_row[wid], row_id_map, sorted_slot);
+}
+
 constexpr int kGatherSlots = 16;  // slots per block
+constexpr int kGatherUnroll = 4;  // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t S, int top_k,
@@ -165,19 +237,33 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
     const int64_t s0 = (int64_t)blockIdx.x * kGatherSlots;
     if (threadIdx.x < kGatherSlots) {
         const int64_t s = s0 + threadIdx.x;
-        int32_t r = (s < S) ? row_id_map[s] : -1;
+        const int32_t r = (s < S) ? row_id_map[s] : -1;
         rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
     }
     __syncthreads();
     const int64_t cpr = H / 8;  // 16-byte chunks per row
     const int64_t total = (int64_t)kGatherSlots * cpr;
-    for (int64_t i = threadIdx.x; i < total; i += blockDim.x) {
-        const int ls = (int)(i / cpr);
-        const int64_t c = i - ls * cpr;
-        const int32_t r = rows[ls];
-        if (r < 0) continue;
-        const int64_t t = (s0 + ls) / top_k;
-        st16(x_perm + (int64_t)r * H + c * 8, ld16(x + t * H + c * 8));
+    for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)kPermThreads * kGatherUnroll) {
+        u32x4_t v[kGatherUnroll];
+        int64_t dst[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            dst[u] = -1;
+            if (i < total) {
+                const int ls = (int)(i / cpr);
+                const int64_t c = i - ls * cpr;
+                const int32_t r = rows[ls];
+                if (r >= 0) {
+                    const int64_t t = (s0 + ls) / top_k;
+                    v[u] = ld16(x + t * H + c * 8);
+                    dst[u] = (int64_t)r * H + c * 8;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u)
+            if (dst[u] >= 0) st16(x_perm + dst[u], v[u]);
     }
 }
 
@@ -199,15 +285,20 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
     const int64_t chunk = permute_chunk(S);
     const int64_t nblk = (S + chunk - 1) / chunk;
     int32_t* blk = static_cast<int32_t*>(ws);
-    if (nblk > 0) {
-        hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0, stream,
-                           ids, S, (int)E, chunk, blk, dev_err);
+    if (S > 0 && S <= kSmallSlots) {
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, stream, ids, S,
+                           (int)E, tokens_per_expert, row_id_map, sorted_slot, dev_err);
+    } else {
+        if (nblk > 0)
+            hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
+                               stream, ids, S, (int)E, chunk, blk, dev_err);
+        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
+                           (int)E, tokens_per_expert);
+        if (nblk > 0)
+            hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
+                               stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
     }
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
-                       (int)E, tokens_per_expert);
     if (nblk > 0) {
-        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
-                           stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
         const int64_t gblk = (S + kGatherSlots - 1) / kGatherSlots;
         hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)gblk), dim3(kPermThreads), 0,
                            stream, x, row_id_map, S, (int)top_k, H, x_perm);

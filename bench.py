@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -47,6 +48,9 @@ def parse_args():
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline (0 = skip)")
     p.add_argument("--skip-decode", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="finish with three 512 MiB device copies (the reference kernel that scales "
+                        "the FETCH_SIZE / WRITE_SIZE counters into bytes)")
     return p.parse_args()
 
 
@@ -76,6 +80,33 @@ class KernelTimer:
             out.setdefault(name, []).append(a.elapsed_time(b))
         self.pending = []
         return out
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gmm_dw_kernel_hbm_traffic_ep_rank.md")
+KERNEL_SOURCES = ["grouped_gemm_moe_amd/csrc/gmm.hip", "grouped_gemm_moe_amd/csrc/common.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if it is missing or was taken on different kernel source."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^- (\w+): `([^`]+)`", text, flags=re.M))
+    if vals.get("kernel") != kernel or vals.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(vals["hbm_bytes_per_launch"])
 
 
 def bf16_dev(torch, bits, dev):
@@ -165,6 +196,7 @@ def run_ep(torch, dev, args):
     dom_flops_per_launch = sum(flops[c] for c in dom_calls) / len(dom_calls)
     dom_ms_per_launch = kern_ms[dom] / len(dom_calls)
     achieved = dom_flops_per_launch / (dom_ms_per_launch * 1e-3) / 1e12
+    traffic = measured_traffic(dom)
     res = dict(
         ms_per_step=ms_per_step,
         value=total_flops / (ms_per_step * 1e-3) / 1e12,
@@ -173,7 +205,8 @@ def run_ep(torch, dev, args):
         per_call_us={k: round(v * 1e3, 2) for k, v in mean_ms.items()},
         roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
                       peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                      frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
+                      traffic_unit="bytes per launch (HBM read + write)",
                       flops_per_launch=dom_flops_per_launch,
                       mean_launch_us=round(dom_ms_per_launch * 1e3, 2)),
     )
@@ -354,6 +387,13 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 512 MiB device copies done")
 
 
 if __name__ == "__main__":

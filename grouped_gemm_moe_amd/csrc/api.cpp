@@ -18,6 +18,9 @@ constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool dim_ok(int64_t d) { return d > 0 && d % 8 == 0 && d <= (int64_t(1) << 24); }
+// GMM operand tiles address up to 256 rows of a matrix with 32-bit byte
+// offsets, which bounds the row length (K or N) at 2^21 elements.
+constexpr int64_t kMaxGmmDim = int64_t(1) << 21;
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
@@ -25,11 +28,14 @@ moe_status check_gmm_common(const void* a, const void* b, const void* gl, const 
                             int64_t E, int64_t M_cap, int64_t K, int64_t N, size_t ws_need,
                             size_t ws_bytes, const void* ws) {
     if (!gl || (M_cap > 0 && (!a || !out)) || !b) return MOE_ERR_NULL;
-    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(K) || !dim_ok(N))
+    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(K) || !dim_ok(N) ||
+        K > kMaxGmmDim || N > kMaxGmmDim)
         return MOE_ERR_INVALID;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16) || !aligned(gl, 8))
         return MOE_ERR_INVALID;
-    if (M_cap * K > (int64_t(1) << 40) || M_cap * N > (int64_t(1) << 40)) return MOE_ERR_INVALID;
+    if (M_cap * K > (int64_t(1) << 40) || M_cap * N > (int64_t(1) << 40) ||
+        E * K * N > (int64_t(1) << 40))
+        return MOE_ERR_INVALID;
     if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return MOE_ERR_WORKSPACE;
     return MOE_OK;
 }

@@ -17,7 +17,10 @@
 //    from host-known bounds; surplus workgroups exit at once.
 //  * One MFMA engine: 256x256 output tile per workgroup, 8 waves (two per
 //    SIMD, so one hides the other's waits) of 128x64 each,
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave whose
+//    sub-tile lies wholly past the tile's valid rows or columns (the last
+//    row tile of an expert) skips its LDS reads and MFMAs and only issues
+//    its share of the loads.
 //  * Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
 //    VGPR staging).  Lanes whose element lies outside the problem (ragged
 //    rows, reduction tails, rows past an expert) get an out-of-range buffer
@@ -34,6 +37,8 @@
 //  * The MFMA is issued with operands swapped (B fragment as the hardware A
 //    operand) so each lane holds 4 consecutive output columns; the epilogue
 //    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -371,16 +376,18 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     static_assert(kMfmaPerStep >= kPer, "load spacing");
 #pragma unroll
     for (int p = 0; p < kNST - 1; ++p) issue(p);
+    // this wave's corner of the output tile; two copies of the step loop
+    // (active and idle wave), so the common one carries no branch
+    const int wrow0 = (wave_id() / WN) * (BM / WM), wcol0 = (wave_id() % WN) * (BN / WN);
+    auto run_steps = [&](auto active_tag) {
     for (int s = 0; s < nk; ++s) {
         wait_vmcnt<(kNST - 2) * kPer>();
         __builtin_amdgcn_s_barrier();
-        // loads of step s+kNST-1 into the stage read at step s-1, one after
-        // every kStride MFMAs of step s
         const int nxt = s + kNST - 1;
         bf16_t* nst = smem + (nxt % kNST) * kStage;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(DA::stage(a_base, lda, nxt));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b_base, ldb, nxt));
-        const int left = red_len - nxt * BK;  // <= 0 past the end: all lanes out of range
+        const int left = red_len - nxt * BK;
         auto hook = [&](int m) {
 #pragma unroll
             for (int q = 0; q < kPer; ++q) {
@@ -390,9 +397,17 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
                 }
             }
         };
-        const bf16_t* st = smem + (s % kNST) * kStage;
-        eng.compute(st, st + BM * BK, hook);
+        if constexpr (decltype(active_tag)::value) {
+            const bf16_t* st = smem + (s % kNST) * kStage;
+            eng.compute(st, st + BM * BK, hook);
+        } else {
+#pragma unroll
+            for (int m = 0; m < kMfmaPerStep; ++m) hook(m);
+        }
     }
+    };
+    if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
+    else run_steps(std::false_type{});
     wait_vmcnt<0>();  // no LDS write may outlive the workgroup
     eng.store(out, ldo, rows_valid, cols_valid);
 }

@@ -47,7 +47,9 @@
  *     not shift later offsets.  R = sum(n_e) must not exceed M_cap; rows at or
  *     beyond R are neither read for results nor written (except as stated).
  *   - Limits: 1 <= E <= 1024; 1 <= top_k <= 32; T*top_k < 2^31;
- *     hidden / intermediate / K / N are positive multiples of 8.
+ *     hidden / intermediate / K / N are positive multiples of 8, at most
+ *     2^24 (hidden, intermediate) and 2^21 (the GMM's K and N);
+ *     E*K*N, M_cap*K and M_cap*N are at most 2^40.
  */
 #ifndef MOEGMM_H
 #define MOEGMM_H
@@ -115,6 +117,10 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
  * bf16 products accumulate in fp32; each output is rounded once (RNE).
  * w[e] of an empty expert is never read.
  * ---------------------------------------------------------------------- */
+/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  Every op currently needs
+ * none (0): each workgroup derives its tile from group_list in LDS.  Callers
+ * pass a workspace of the queried size (NULL for 0) so that a future kernel
+ * needing one does not change the calls. */
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
 #define MOE_GMM_OP_FWD 0
 #define MOE_GMM_OP_BWD_INPUT 1
@@ -142,7 +148,8 @@ moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* g
  *
  *   x [M_cap, K] bf16, dy [M_cap, N] bf16, group_list [E] int64,
  *   dw [E, K, N] bf16 OUT -- every expert written; exact zeros for n_e == 0.
- * The reduction order is fixed, so the result is bit-reproducible.
+ * The reduction order of every output is fixed, so the result is
+ * bit-reproducible whatever order the tiles run in.
  * ---------------------------------------------------------------------- */
 moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,

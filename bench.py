@@ -20,6 +20,9 @@ Also in the line:
                   from HIP events recorded on the launch stream;
   decode       -- the decode-shaped layer forward (T=64, top-8, E=256,
                   hidden 2048, intermediate 512) in HBM GB/s;
+  prefill      -- the prefill-shaped layer forward (T=4096, top-8, E=128,
+                  hidden 2048, intermediate 512) as a fraction of its
+                  attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak);
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -45,9 +48,10 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--prefill-steps", type=int, default=50)
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline (0 = skip)")
-    p.add_argument("--skip-decode", action="store_true")
+    p.add_argument("--skip-decode", action="store_true", help="skip the decode and prefill layer legs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="finish with three 512 MiB device copies (the reference kernel that scales "
                         "the FETCH_SIZE / WRITE_SIZE counters into bytes)")
@@ -233,11 +237,11 @@ def decode_bytes(gl, T, K, H, I):
     return w + act + idx, n_active
 
 
-def run_decode(torch, dev, args):
-    import workloads
+def layer_forward(torch, dev, wl, steps):
+    """Time the layer forward (permute -> gate_up -> SwiGLU -> down ->
+    unpermute) on workload `wl`: wall ms per layer and per-call means."""
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
 
-    wl = workloads.decode()
     d = wl.dims
     T, K, E, H, I = d["T"], d["K"], d["E"], d["H"], d["I"]
     x = bf16_dev(torch, wl["x"], dev)
@@ -263,16 +267,42 @@ def run_decode(torch, dev, args):
     torch.cuda.synchronize()
     # wall time without events, then a pass with per-call events
     t0 = time.perf_counter()
-    for _ in range(args.decode_steps):
+    for _ in range(steps):
         step(plain)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.decode_steps
-    for _ in range(min(50, args.decode_steps)):
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    for _ in range(min(50, steps)):
         step(timer)
     torch.cuda.synchronize()
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     gl = layer.tokens_per_expert.cpu().numpy()
+    return ms, per, gl
+
+
+def layer_roofline(gl, T, K, H, I, ms):
+    """Algorithmic bytes and FLOPs of one layer forward and the fraction of
+    the attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak) that the
+    measured time reaches."""
     nbytes, n_active = decode_bytes(gl, T, K, H, I)
+    S = int(np.sum(gl))
+    flops = 2.0 * S * H * 2 * I + 2.0 * S * I * H
+    t_mem = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    roof_ms = max(t_mem, t_mfma) * 1e3
+    return dict(bytes_per_layer=nbytes, active_experts=n_active, gflop_per_layer=round(flops / 1e9, 2),
+                bound="hbm" if t_mem >= t_mfma else "mfma", roofline_ms=round(roof_ms, 4),
+                frac_of_attainable=round(roof_ms / ms, 4))
+
+
+def run_decode(torch, dev, args):
+    import workloads
+
+    wl = workloads.decode()
+    d = wl.dims
+    T, K, H, I = d["T"], d["K"], d["H"], d["I"]
+    ms, per, gl = layer_forward(torch, dev, wl, args.decode_steps)
+    roof = layer_roofline(gl, T, K, H, I, ms)
+    nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
     gbs = nbytes / (ms * 1e-3) / 1e9
     wbytes = {k: n_active * (H * 2 * I if k == "gmm_fwd_gate_up" else I * H) * 2
               for k in ("gmm_fwd_gate_up", "gmm_fwd_down")}
@@ -282,9 +312,31 @@ def run_decode(torch, dev, args):
                  "intermediate 512; permute -> gate_up -> SwiGLU -> down -> unpermute",
         value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4),
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=nbytes,
-        active_experts=n_active,
+        active_experts=n_active, frac_of_attainable=roof["frac_of_attainable"],
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
         gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
+    )
+
+
+def run_prefill(torch, dev, args):
+    import workloads
+
+    wl = workloads.prefill()
+    d = wl.dims
+    T, K, H, I = d["T"], d["K"], d["H"], d["I"]
+    ms, per, gl = layer_forward(torch, dev, wl, args.prefill_steps)
+    roof = layer_roofline(gl, T, K, H, I, ms)
+    gbs = roof["bytes_per_layer"] / (ms * 1e-3) / 1e9
+    tflops = roof["gflop_per_layer"] * 1e9 / (ms * 1e-3) / 1e12
+    return dict(
+        metric="prefill MoE layer forward: % of attainable roofline",
+        workload="prefill layer forward: T=4096 tokens, top-8 of E=128, hidden 2048, "
+                 "intermediate 512; permute -> gate_up -> SwiGLU -> down -> unpermute",
+        value=round(100.0 * roof["frac_of_attainable"], 2), unit="% of attainable roofline",
+        ms_per_layer=round(ms, 4), gb_per_s=round(gbs, 1), tflops=round(tflops, 2),
+        pct_bf16_mfma_peak=round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **roof,
+        per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
     )
 
 
@@ -350,10 +402,13 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     ep, wl = run_ep(torch, dev, args)
     log(f"ep: {ep['ms_per_step']:.3f} ms/step, {ep['value']:.1f} TFLOP/s; per call {ep['per_call_us']}")
-    decode = None
+    decode = prefill = None
     if not args.skip_decode:
         decode = run_decode(torch, dev, args)
         log(f"decode: {decode['ms_per_layer']:.4f} ms, {decode['value']:.0f} GB/s; {decode['per_call_us']}")
+        prefill = run_prefill(torch, dev, args)
+        log(f"prefill: {prefill['ms_per_layer']:.4f} ms, {prefill['value']:.1f} % of attainable "
+            f"({prefill['bound']}-bound); {prefill['per_call_us']}")
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(wl, args.cpu_budget)
@@ -384,6 +439,7 @@ def main():
         "per_call_us": ep["per_call_us"],
         "roofline": ep["roofline"],
         "decode": decode,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

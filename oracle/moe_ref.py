@@ -21,9 +21,11 @@ Sources (web pages, cited by title and section):
              Expert Compute (H_e = X_e W1[e], split into G|U, Y_e = A_e W2[e]),
              Token Combine (y_i = sum_k w_k Y_{e_ik}[row(i,k)]).
 * [PermGrad] "CANN ops-transformer 算子详解：MoeTokenPermuteWithRoutingMapGrad"
-             (mhpq.cn): section 4.1 (-1 marks an invalid slot that takes no
-             part), section 6.2 (each output token walks its top-k slots and
-             accumulates in FP32, cast back once).
+             (mhpq.cn): section 2.2 (the probs gradient), section 2.3 (the
+             token gradient: an index-add of the permuted rows' gradients
+             back onto their tokens), section 4.1 (-1 marks an invalid slot
+             that takes no part), section 6.2 (each output token walks its
+             top-k slots and accumulates in FP32, cast back once).
 * [MegaBlocks] "03 · grouped GEMM 路径" (MegaBlocks chapter 3): section 2
              (rows of all groups concatenated, weight [groups, k, n], a list of
              per-group row counts).
@@ -39,6 +41,9 @@ Readings where the pages are silent or ambiguous (each listed in the design doc):
   once, round-to-nearest-even, from the exact value; the layer chain rounds at
   those same points so a layer comparison measures kernel error only.
 * SwiGLU backward is not on the pages; it is derived by calculus.
+* The backward of the weighted unpermute (dYp, dprobs) is the derivative of
+  the Token Combine formula; the permute backward sums each token's slot
+  rows in ascending k (the per-token walk of [PermGrad] 6.2).
 """
 from __future__ import annotations
 
@@ -233,6 +238,50 @@ def unpermute(y_perm, row_id_map, probs) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# backward of the two ends of the path: the weighted unpermute (Token Combine)
+# and the permute  [MegaMoE: Token Combine; PermGrad: 2.2, 2.3, 6.2]
+# ---------------------------------------------------------------------------
+
+
+def unpermute_bwd(dout, y_perm, row_id_map, probs):
+    """Gradients of out[t] = sum_k probs[t,k] * y_perm[row(t,k)].
+
+    dy_perm[row(t,k)] = probs[t,k] * dout[t]   (rows no slot points at: 0)
+    dprobs[t,k]       = <dout[t], y_perm[row(t,k)]>   (0 for a masked slot)
+    """
+    dout = np.asarray(dout, dtype=np.float64)
+    y_perm = np.asarray(y_perm, dtype=np.float64)
+    probs = np.asarray(probs, dtype=np.float64)
+    T, K = probs.shape
+    rmap = np.asarray(row_id_map, dtype=np.int64).reshape(T, K)
+    dy_perm = np.zeros_like(y_perm)
+    dprobs = np.zeros((T, K), dtype=np.float64)
+    for k in range(K):
+        valid = rmap[:, k] >= 0
+        rows = rmap[valid, k]
+        dy_perm[rows] = probs[valid, k:k + 1] * dout[valid]
+        dprobs[valid, k] = np.sum(dout[valid] * y_perm[rows], axis=1)
+    return dy_perm, dprobs
+
+
+def permute_bwd(dx_perm, row_id_map, num_tokens: int):
+    """dx[t] = sum over valid k, ascending, of dx_perm[row(t,k)].
+
+    The gradient of the gather x_perm[r] = x[token(r)]: every permuted row
+    hands its gradient back to the token it was copied from, and a token
+    copied into several rows (top_k > 1) receives their sum.  Masked slots add
+    nothing; a token with no valid slot gets zeros.
+    """
+    dx_perm = np.asarray(dx_perm, dtype=np.float64)
+    rmap = np.asarray(row_id_map, dtype=np.int64).reshape(num_tokens, -1)
+    dx = np.zeros((num_tokens, dx_perm.shape[1]), dtype=np.float64)
+    for k in range(rmap.shape[1]):
+        valid = rmap[:, k] >= 0
+        dx[valid] += dx_perm[rmap[valid, k]]
+    return dx
+
+
+# ---------------------------------------------------------------------------
 # chains (rounding at the library boundary)
 # ---------------------------------------------------------------------------
 
@@ -271,3 +320,23 @@ def expert_block_backward(x_perm, h, a, dyp, w1, w2, group_list,
     dx = gmm_bwd_input(dh, w1, group_list)
     dw1 = gmm_bwd_weight(x_perm, dh, group_list)
     return dict(da=da, dw2=dw2, dh=dh, dx=dx, dw1=dw1)
+
+
+def moe_layer_backward(fwd, dout, probs, w1, w2, rounding=round_bf16) -> dict:
+    """Full layer backward from dout, given the forward dict ``fwd``.
+
+    unpermute_bwd -> expert block backward -> permute_bwd.  dYp and dX_perm
+    are rounded to bf16 as they cross the boundary (``rounding``; ``None``
+    for the exact chain); dprobs (fp32 on the device) and dx are returned
+    exact.
+    """
+    rnd = rounding if rounding is not None else (lambda v: v)
+    T = np.asarray(dout).shape[0]
+    dyp, dprobs = unpermute_bwd(dout, fwd["yp"], fwd["row_id_map"], probs)
+    dyp = rnd(dyp)
+    blk = expert_block_backward(fwd["x_perm"], fwd["h"], fwd["a"], dyp, w1, w2,
+                                fwd["tokens_per_expert"], rounding=rounding)
+    dx_perm = rnd(blk["dx"])
+    dx = permute_bwd(dx_perm, fwd["row_id_map"], T)
+    return dict(dyp=dyp, dprobs=dprobs, da=blk["da"], dw2=blk["dw2"], dh=blk["dh"],
+                dx_perm=dx_perm, dw1=blk["dw1"], dx=dx)

@@ -468,6 +468,151 @@ def test_empty_expert_weights_never_read():
 
 
 # ---------------------------------------------------------------------------
+# pin 11: permute backward -- the worked example, the adjoint of the gather,
+#         a brute-force walk
+# ---------------------------------------------------------------------------
+
+
+def check_permute_bwd_worked(g, permute_bwd):
+    """With dX_perm = the identity rows, dx[t] marks exactly the permuted rows
+    copied from token t (the page's rows, laid out by readings 2-3)."""
+    rmap = np.asarray(g["from_readings"]["row_id_map"])
+    src = g["from_readings"]["permuted_source_tokens"]
+    R = len(src)
+    dx = permute_bwd(np.eye(R), rmap, 4)
+    for t in range(4):
+        np.testing.assert_array_equal(dx[t], [1.0 if src[r] == t else 0.0 for r in range(R)])
+
+
+def check_permute_adjoint(permute, permute_bwd):
+    """<permute(x), g> == <x, permute_bwd(g)> for every x and g: the permute
+    backward is the adjoint of the gather, masked slots included."""
+    rng = _rng(21)
+    for (T, K, E, H) in [(6, 2, 3, 5), (20, 4, 7, 3), (9, 8, 12, 4), (4, 1, 2, 6)]:
+        ids = _random_ids(rng, T, K, E, mask_frac=0.25)
+        x = rng.standard_normal((T, H))
+        x_perm, rmap, _, _ = permute(x, ids, E)
+        gr = rng.standard_normal(x_perm.shape)
+        lhs = float(np.sum(x_perm * gr))
+        rhs = float(np.sum(x * permute_bwd(gr, rmap, T)))
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (T, K, lhs, rhs)
+
+
+def check_permute_bwd_brute(permute_bwd):
+    rng = _rng(22)
+    T, K, H, R = 7, 3, 4, 12
+    rmap = np.full(T * K, -1, dtype=np.int64)
+    slots = rng.choice(T * K, size=R, replace=False)
+    rmap[slots] = rng.permutation(R)
+    gr = rng.standard_normal((R, H))
+    got = permute_bwd(gr, rmap, T)
+    for t in range(T):
+        ref = np.zeros(H)
+        for k in range(K):
+            r = rmap[t * K + k]
+            if r >= 0:
+                ref = ref + gr[r]
+        np.testing.assert_allclose(got[t], ref, rtol=0, atol=1e-14)
+
+
+def test_permute_bwd_worked_example(golden_dir):
+    check_permute_bwd_worked(_load_worked(golden_dir), oracle.permute_bwd)
+
+
+def test_permute_bwd_adjoint():
+    check_permute_adjoint(oracle.permute, oracle.permute_bwd)
+
+
+def test_permute_bwd_bruteforce():
+    check_permute_bwd_brute(oracle.permute_bwd)
+
+
+# ---------------------------------------------------------------------------
+# pin 12: unpermute backward -- L = <dout, unpermute(Yp, probs)> is linear in
+#         Yp and in probs, so <dYp, Yp> = L = <dprobs, probs>, and a one-
+#         coordinate difference quotient is the derivative exactly
+# ---------------------------------------------------------------------------
+
+
+def check_unpermute_bwd(permute, unpermute, unpermute_bwd):
+    rng = _rng(23)
+    for (T, K, E, H) in [(8, 2, 4, 6), (15, 4, 9, 3), (5, 8, 10, 4)]:
+        ids = _random_ids(rng, T, K, E, mask_frac=0.25)
+        x = rng.standard_normal((T, H))
+        _, rmap, _, _ = permute(x, ids, E)
+        R = int(np.sum(ids >= 0))
+        yp = rng.standard_normal((R, H))
+        probs = rng.random((T, K))
+        dout = rng.standard_normal((T, H))
+
+        def loss(y, p):
+            return float(np.sum(dout * unpermute(y, rmap, p)))
+
+        L = loss(yp, probs)
+        dyp, dprobs = unpermute_bwd(dout, yp, rmap, probs)
+        assert dyp.shape == yp.shape and dprobs.shape == probs.shape
+        assert abs(float(np.sum(dyp * yp)) - L) <= 1e-12 * max(1.0, abs(L))
+        assert abs(float(np.sum(dprobs * probs)) - L) <= 1e-12 * max(1.0, abs(L))
+        flat = ids.reshape(-1)
+        assert np.all(dprobs.reshape(-1)[flat < 0] == 0.0)
+        for _ in range(6):
+            i, j = rng.integers(R), rng.integers(H)
+            y2 = yp.copy()
+            y2[i, j] += 1.0
+            assert abs((loss(y2, probs) - L) - dyp[i, j]) <= 1e-12 * max(1.0, abs(L))
+            t, k = rng.integers(T), rng.integers(K)
+            p2 = probs.copy()
+            p2[t, k] += 1.0
+            assert abs((loss(yp, p2) - L) - dprobs[t, k]) <= 1e-12 * max(1.0, abs(L))
+
+
+def test_unpermute_bwd_identities():
+    check_unpermute_bwd(oracle.permute, oracle.unpermute, oracle.unpermute_bwd)
+
+
+# ---------------------------------------------------------------------------
+# pin 13: the whole layer backward (dx, dprobs, dW1, dW2) by central finite
+#         differences of f = <dout, layer(x, probs, W1, W2)>, exact chain
+# ---------------------------------------------------------------------------
+
+
+def check_layer_backward_fd(layer_forward, layer_backward):
+    rng = _rng(24)
+    T, K, E, H, I = 6, 2, 3, 4, 3
+    ids = _random_ids(rng, T, K, E, mask_frac=0.2)
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, H, 2 * I)) * 0.5
+    w2 = rng.standard_normal((E, I, H)) * 0.5
+    probs = rng.random((T, K))
+    dout = rng.standard_normal((T, H))
+
+    def f(xx, pp, a1, a2):
+        return float(np.sum(dout * layer_forward(xx, ids, pp, a1, a2, E, rounding=None)["out"]))
+
+    fwd = layer_forward(x, ids, probs, w1, w2, E, rounding=None)
+    g = layer_backward(fwd, dout, probs, w1, w2, rounding=None)
+    eps = 1e-6
+    args = dict(x=x, probs=probs, w1=w1, w2=w2)
+    grads = dict(x=g["dx"], probs=g["dprobs"], w1=g["dw1"], w2=g["dw2"])
+    for name in ("x", "probs", "w1", "w2"):
+        arr = args[name]
+        for _ in range(8):
+            idx = tuple(int(rng.integers(n)) for n in arr.shape)
+            vals = []
+            for sgn in (1, -1):
+                a = dict(args)
+                a[name] = arr.copy()
+                a[name][idx] += sgn * eps
+                vals.append(f(a["x"], a["probs"], a["w1"], a["w2"]))
+            fd = (vals[0] - vals[1]) / (2 * eps)
+            assert abs(fd - grads[name][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grads[name][idx])
+
+
+def test_layer_backward_finite_differences():
+    check_layer_backward_fd(oracle.moe_layer_forward, oracle.moe_layer_backward)
+
+
+# ---------------------------------------------------------------------------
 # mutation tests: a planted mistake in a copy of an oracle function must trip
 # at least one pin (run on the CPU only)
 # ---------------------------------------------------------------------------
@@ -557,6 +702,37 @@ def _mut_hist_counts_masked(ids, E):
     return np.bincount(np.where(ids < 0, 0, ids), minlength=E).astype(np.int64)
 
 
+def _mut_unpermute_bwd_no_probs(dout, y_perm, row_id_map, probs):
+    _, dprobs = oracle.unpermute_bwd(dout, y_perm, row_id_map, probs)
+    dyp, _ = oracle.unpermute_bwd(dout, y_perm, row_id_map, np.ones_like(probs))
+    return dyp, dprobs  # dYp forgets the probs factor
+
+
+def _mut_unpermute_bwd_next_slot(dout, y_perm, row_id_map, probs):
+    dyp, dprobs = oracle.unpermute_bwd(dout, y_perm, row_id_map, probs)
+    return dyp, np.roll(dprobs, 1, axis=1)  # dprobs paired with the wrong slot
+
+
+def _mut_permute_bwd_masked(dx_perm, row_id_map, num_tokens):
+    rmap = np.asarray(row_id_map, dtype=np.int64).reshape(num_tokens, -1)
+    dx = np.zeros((num_tokens, np.asarray(dx_perm).shape[1]))
+    for k in range(rmap.shape[1]):
+        dx += np.asarray(dx_perm)[rmap[:, k]]  # -1 indexes the last row
+    return dx
+
+
+def _mut_permute_bwd_first_slot(dx_perm, row_id_map, num_tokens):
+    rmap = np.asarray(row_id_map, dtype=np.int64).reshape(num_tokens, -1)
+    return oracle.permute_bwd(dx_perm, rmap[:, :1].reshape(-1), num_tokens)
+
+
+def _mut_layer_bwd_dprobs_doubled(fwd, dout, probs, w1, w2, rounding=None):
+    g = oracle.moe_layer_backward(fwd, dout, probs, w1, w2, rounding=rounding)
+    g = dict(g)
+    g["dprobs"] = g["dprobs"] * 2.0  # double-counted combine weight
+    return g
+
+
 def _mut_round_truncate(a):
     f = np.asarray(a, dtype=np.float32)
     u = f.view(np.uint32) & np.uint32(0xFFFF0000)
@@ -584,6 +760,15 @@ def test_mutants_are_caught(golden_dir):
         "hist_counts_masked": _fails(check_worked_example, g, oracle.permute_maps,
                                      _mut_hist_counts_masked, oracle.gmm),
         "round_truncate": _fails(check_bf16_rounding, _mut_round_truncate),
+        "unpermute_bwd_no_probs": _fails(check_unpermute_bwd, oracle.permute, oracle.unpermute,
+                                         _mut_unpermute_bwd_no_probs),
+        "unpermute_bwd_next_slot": _fails(check_unpermute_bwd, oracle.permute, oracle.unpermute,
+                                          _mut_unpermute_bwd_next_slot),
+        "permute_bwd_masked": _fails(check_permute_adjoint, oracle.permute, _mut_permute_bwd_masked),
+        "permute_bwd_first_slot": _fails(check_permute_bwd_worked, g, _mut_permute_bwd_first_slot)
+        or _fails(check_permute_adjoint, oracle.permute, _mut_permute_bwd_first_slot),
+        "layer_bwd_dprobs_doubled": _fails(check_layer_backward_fd, oracle.moe_layer_forward,
+                                           _mut_layer_bwd_dprobs_doubled),
     }
     missed = [k for k, v in caught.items() if not v]
     assert not missed, f"mutants not caught by any pin: {missed}"

@@ -22,7 +22,9 @@ Also in the line:
                   hidden 2048, intermediate 512) in HBM GB/s;
   prefill      -- the prefill-shaped layer forward (T=4096, top-8, E=128,
                   hidden 2048, intermediate 512) as a fraction of its
-                  attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak);
+                  attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak),
+                  and the backward of the two ends (moe_unpermute_bwd,
+                  moe_permute_bwd) on its buffers in HBM GB/s;
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -276,7 +278,47 @@ def layer_forward(torch, dev, wl, steps):
     torch.cuda.synchronize()
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     gl = layer.tokens_per_expert.cpu().numpy()
-    return ms, per, gl
+    return ms, per, gl, (layer, probs)
+
+
+def end_backward(torch, dev, layer, probs, steps=20):
+    """Time the backward of the two ends on a forward's buffers: the
+    unpermute backward (dYp and dprobs from a synthetic dout) and the permute
+    backward (dx from a synthetic dX_perm), in GB/s of algorithmic bytes."""
+    from grouped_gemm_moe_amd import moe_permute_bwd, moe_unpermute_bwd
+
+    s = layer.shape
+    T, K, H = s.T, s.top_k, s.H
+    R = int(layer.tokens_per_expert.sum().item())
+    g = torch.Generator(device=dev).manual_seed(9)
+    dout = torch.randn((T, H), generator=g, device=dev).to(torch.bfloat16)
+    dxp = torch.randn((s.S, H), generator=g, device=dev).to(torch.bfloat16)
+    dyp = torch.empty((s.S, H), dtype=torch.bfloat16, device=dev)
+    dp = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    calls = {
+        "moe_unpermute_bwd": (lambda: moe_unpermute_bwd(dout, layer.yp, layer.row_id_map, probs,
+                                                        out=(dyp, dp)),
+                              T * H * 2 + 2 * R * H * 2 + 2 * T * K * 4 + s.S * 4),
+        "moe_permute_bwd": (lambda: moe_permute_bwd(dxp, layer.row_id_map, T, out=dx),
+                            R * H * 2 + T * H * 2 + s.S * 4),
+    }
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = dict(us=round(us, 2), bytes=nbytes, gb_per_s=round(gbs, 1),
+                         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+    return res
 
 
 def layer_roofline(gl, T, K, H, I, ms):
@@ -300,7 +342,7 @@ def run_decode(torch, dev, args):
     wl = workloads.decode()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl = layer_forward(torch, dev, wl, args.decode_steps)
+    ms, per, gl, _ = layer_forward(torch, dev, wl, args.decode_steps)
     roof = layer_roofline(gl, T, K, H, I, ms)
     nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -324,8 +366,9 @@ def run_prefill(torch, dev, args):
     wl = workloads.prefill()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl = layer_forward(torch, dev, wl, args.prefill_steps)
+    ms, per, gl, (layer, probs) = layer_forward(torch, dev, wl, args.prefill_steps)
     roof = layer_roofline(gl, T, K, H, I, ms)
+    ends = end_backward(torch, dev, layer, probs)
     gbs = roof["bytes_per_layer"] / (ms * 1e-3) / 1e9
     tflops = roof["gflop_per_layer"] * 1e9 / (ms * 1e-3) / 1e12
     return dict(
@@ -337,6 +380,7 @@ def run_prefill(torch, dev, args):
         pct_bf16_mfma_peak=round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **roof,
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
+        end_backward=ends,
     )
 
 

@@ -22,7 +22,8 @@ from . import _lib as _L
 
 __all__ = [
     "MoeError", "moe_permute", "gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
-    "swiglu_bwd", "moe_unpermute", "moe_permute_workspace_size", "gmm_workspace_size",
+    "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
+    "moe_permute_workspace_size", "gmm_workspace_size",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP",
 ]
 
@@ -205,3 +206,39 @@ def moe_unpermute(y_perm, row_id_map, probs, *, out=None, dev_err=None):
     _check(library().moe_unpermute(_ptr(y_perm), _ptr(row_id_map), _ptr(probs), T, top_k, H,
                                    _ptr(o), _ptr(dev_err), _stream(y_perm.device)), "moe_unpermute")
     return o
+
+
+def moe_unpermute_bwd(dout, y_perm, row_id_map, probs, *, out=None, dev_err=None):
+    """Gradients of moe_unpermute: dy_perm[row(t,k)] = probs[t,k] * dout[t] and
+    dprobs[t,k] = <dout[t], y_perm[row(t,k)]> (fp32).  Returns (dy_perm, dprobs);
+    ``out`` may pass both buffers as a pair."""
+    _dev(dout, "dout", torch.bfloat16)
+    _dev(y_perm, "y_perm", torch.bfloat16)
+    _dev(row_id_map, "row_id_map", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    T, top_k = probs.shape
+    S, H = y_perm.shape
+    if S != T * top_k or row_id_map.numel() != S or tuple(dout.shape) != (T, H):
+        raise MoeError("dout must be [T, H], y_perm [T*top_k, H] and row_id_map [T*top_k]")
+    dyp_out, dp_out = out if out is not None else (None, None)
+    dyp = _out(dyp_out, (S, H), torch.bfloat16, y_perm.device, "dy_perm")
+    dp = _out(dp_out, (T, top_k), torch.float32, y_perm.device, "dprobs")
+    _check(library().moe_unpermute_bwd(_ptr(dout), _ptr(y_perm), _ptr(row_id_map), _ptr(probs), T,
+                                       top_k, H, _ptr(dyp), _ptr(dp), _ptr(dev_err),
+                                       _stream(y_perm.device)), "moe_unpermute_bwd")
+    return dyp, dp
+
+
+def moe_permute_bwd(dx_perm, row_id_map, num_tokens: int, *, out=None, dev_err=None):
+    """dx[t] = sum over valid k, ascending, of dx_perm[row_id_map[t*K+k]] (fp32, one rounding)."""
+    _dev(dx_perm, "dx_perm", torch.bfloat16)
+    _dev(row_id_map, "row_id_map", torch.int32)
+    S, H = dx_perm.shape
+    T = int(num_tokens)
+    if T <= 0 or S % T != 0 or row_id_map.numel() != S:
+        raise MoeError("dx_perm must be [T*top_k, H] and row_id_map [T*top_k]")
+    top_k = S // T
+    dx = _out(out, (T, H), torch.bfloat16, dx_perm.device, "dx")
+    _check(library().moe_permute_bwd(_ptr(dx_perm), _ptr(row_id_map), T, top_k, H, _ptr(dx),
+                                     _ptr(dev_err), _stream(dx_perm.device)), "moe_permute_bwd")
+    return dx

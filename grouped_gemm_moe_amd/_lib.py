@@ -29,9 +29,11 @@ SIGNATURES = {
     "swiglu": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
     "swiglu_bwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "moe_unpermute": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "moe_unpermute_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "moe_permute_bwd": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 

@@ -55,7 +55,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 1; }
+int moegmm_abi_version(void) { return 2; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -150,6 +150,34 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, cons
         return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err,
                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,
+                             const int32_t* row_id_map, const float* probs, int64_t T,
+                             int64_t top_k, int64_t H, uint16_t* dy_perm, float* dprobs,
+                             int32_t* dev_err, void* stream) {
+    if (T > 0 && (!dout || !y_perm || !row_id_map || !probs || !dy_perm || !dprobs))
+        return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || !dim_ok(H) || T * top_k > kMaxRows)
+        return MOE_ERR_INVALID;
+    if (!aligned(dout, 16) || !aligned(y_perm, 16) || !aligned(dy_perm, 16) ||
+        !aligned(row_id_map, 4) || !aligned(probs, 4) || !aligned(dprobs, 4))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_unpermute_bwd(dout, y_perm, row_id_map, probs, T, top_k, H,
+                                                 dy_perm, dprobs, dev_err,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, int64_t T,
+                           int64_t top_k, int64_t H, uint16_t* dx, int32_t* dev_err,
+                           void* stream) {
+    if (T > 0 && (!dx_perm || !row_id_map || !dx)) return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || !dim_ok(H) || T * top_k > kMaxRows)
+        return MOE_ERR_INVALID;
+    if (!aligned(dx_perm, 16) || !aligned(dx, 16) || !aligned(row_id_map, 4))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_permute_bwd(dx_perm, row_id_map, T, top_k, H, dx, dev_err,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -13,7 +13,16 @@
 // token is owned by one workgroup and summed in ascending k, so the result is
 // deterministic with no atomics.
 //
-// All three are HBM-bound streams: 16-byte loads and stores, fp32 math.
+// The same per-token walk, with unit weights, is the permute backward: the
+// article's token gradient (section 2.3) adds every permuted row's gradient
+// back onto the token it was copied from.  The backward of the weighted
+// unpermute is the derivative of the Token Combine formula:
+//   dy_perm[row(t,k)] = probs[t,k] * dout[t],
+//   dprobs[t,k]       = <dout[t], y_perm[row(t,k)]>   (0 for a masked slot),
+// both from one pass over a token's rows, the dot products reduced in a fixed
+// order (lane shuffles, then the waves in order), so again deterministic.
+//
+// All are HBM-bound streams: 16-byte loads and stores, fp32 math.
 #include "common.h"
 #include "launch.h"
 
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
             r = -1;
         }
         s_row[threadIdx.x] = r;
-        s_p[threadIdx.x] = probs[t * top_k + threadIdx.x];
+        s_p[threadIdx.x] = probs ? probs[t * top_k + threadIdx.x] : 1.0f;  // no probs: plain sum
     }
     __syncthreads();
     for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < H; c0 += kThreads * 8) {
@@ -133,6 +142,78 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[2 * d], acc[2 * d + 1]);
         st16(out + t * H + c0, o);
+    }
+}
+
+// One workgroup per token; KMAX >= top_k is a compile-time bound so the
+// per-slot partial dot products stay in registers.
+template <int KMAX>
+__global__ __launch_bounds__(kThreads) void unpermute_bwd_kernel(
+    const bf16_t* __restrict__ dout, const bf16_t* __restrict__ y_perm,
+    const int32_t* __restrict__ row_id_map, const float* __restrict__ probs, int64_t T, int top_k,
+    int64_t H, bf16_t* __restrict__ dy_perm, float* __restrict__ dprobs, int32_t* dev_err) {
+    __shared__ int32_t s_row[KMAX];
+    __shared__ float s_p[KMAX];
+    __shared__ float s_red[kThreads / 64][KMAX];
+    const int64_t t = blockIdx.x;
+    const int64_t S = T * top_k;
+    if (threadIdx.x < KMAX) {
+        int32_t r = -1;
+        float p = 0.f;
+        if ((int)threadIdx.x < top_k) {
+            r = row_id_map[t * top_k + threadIdx.x];
+            if (r < -1 || r >= S) {
+                if (dev_err) atomicOr(dev_err, MOE_DEVERR_ROW_MAP);
+                r = -1;
+            }
+            p = probs[t * top_k + threadIdx.x];
+        }
+        s_row[threadIdx.x] = r;
+        s_p[threadIdx.x] = p;
+    }
+    __syncthreads();
+    float part[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) part[k] = 0.f;
+    for (int64_t c0 = (int64_t)threadIdx.x * 8; c0 < H; c0 += kThreads * 8) {
+        const u32x4_t g = ld16(dout + t * H + c0);
+        float gv[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            gv[2 * d] = bf16_lo(g[d]);
+            gv[2 * d + 1] = bf16_hi(g[d]);
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int32_t r = s_row[k];
+            if (r < 0) continue;
+            const u32x4_t y = ld16(y_perm + (int64_t)r * H + c0);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                part[k] = __builtin_fmaf(gv[2 * d], bf16_lo(y[d]), part[k]);
+                part[k] = __builtin_fmaf(gv[2 * d + 1], bf16_hi(y[d]), part[k]);
+            }
+            const float p = s_p[k];
+            u32x4_t o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(p * gv[2 * d], p * gv[2 * d + 1]);
+            st16(dy_perm + (int64_t)r * H + c0, o);
+        }
+    }
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        float v = part[k];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0) s_red[wid][k] = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < top_k) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) sum += s_red[w][threadIdx.x];
+        dprobs[t * top_k + threadIdx.x] = s_row[threadIdx.x] >= 0 ? sum : 0.f;
     }
 }
 
@@ -168,6 +249,34 @@ hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, c
     if (T == 0) return hipSuccess;
     hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)T), dim3(kThreads), 0, stream, y_perm,
                        row_id_map, probs, T, (int)top_k, H, out, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, int64_t T,
+                              int64_t top_k, int64_t H, uint16_t* dx, int32_t* dev_err,
+                              hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)T), dim3(kThreads), 0, stream, dx_perm,
+                       row_id_map, nullptr, T, (int)top_k, H, dx, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,
+                                const int32_t* row_id_map, const float* probs, int64_t T,
+                                int64_t top_k, int64_t H, uint16_t* dy_perm, float* dprobs,
+                                int32_t* dev_err, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((unsigned)T), block(kThreads);
+#define MOE_UNPERMUTE_BWD(KMAX)                                                                 \
+    hipLaunchKernelGGL(unpermute_bwd_kernel<KMAX>, grid, block, 0, stream, dout, y_perm,        \
+                       row_id_map, probs, T, (int)top_k, H, dy_perm, dprobs, dev_err)
+    if (top_k <= 1) MOE_UNPERMUTE_BWD(1);
+    else if (top_k <= 2) MOE_UNPERMUTE_BWD(2);
+    else if (top_k <= 4) MOE_UNPERMUTE_BWD(4);
+    else if (top_k <= 8) MOE_UNPERMUTE_BWD(8);
+    else if (top_k <= 16) MOE_UNPERMUTE_BWD(16);
+    else MOE_UNPERMUTE_BWD(32);
+#undef MOE_UNPERMUTE_BWD
     return hipGetLastError();
 }
 

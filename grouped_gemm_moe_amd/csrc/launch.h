@@ -42,5 +42,12 @@ hipError_t launch_swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_
 hipError_t launch_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, const float* probs,
                             int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
                             hipStream_t stream);
+hipError_t launch_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, int64_t T,
+                              int64_t top_k, int64_t H, uint16_t* dx, int32_t* dev_err,
+                              hipStream_t stream);
+hipError_t launch_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,
+                                const int32_t* row_id_map, const float* probs, int64_t T,
+                                int64_t top_k, int64_t H, uint16_t* dy_perm, float* dprobs,
+                                int32_t* dev_err, hipStream_t stream);
 
 }  // namespace moegmm

@@ -8,6 +8,10 @@ Backward of the expert block, from the gradient dYp at the down-GMM output
     dH = swiglu_bwd(dA, H);      dX  = gmm_bwd_input(dH, W1);
     dW1 = gmm_bwd_weight(X_perm, dH)
 
+Backward of the whole layer from dout (the gradient at the layer output):
+    dYp, dprobs = moe_unpermute_bwd(dout, Yp, probs); the expert block as
+    above; dx = moe_permute_bwd(dX_perm)
+
 Every step runs in the HIP kernels of libmoegmm; this module only owns the
 buffers and the call order.  group_list (tokens_per_expert) stays on the
 device between the calls.
@@ -19,7 +23,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_workspace_size, moe_permute,
-               moe_permute_workspace_size, moe_unpermute, swiglu, swiglu_bwd)
+               moe_permute_bwd, moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd,
+               swiglu, swiglu_bwd)
 
 
 @dataclass
@@ -65,6 +70,9 @@ class MoeLayer:
             self.dx = torch.empty((S, s.H), dtype=bf, device=d)
             self.dw1 = torch.empty((s.E, s.H, 2 * s.I), dtype=bf, device=d)
             self.dw2 = torch.empty((s.E, s.I, s.H), dtype=bf, device=d)
+            self.dyp = torch.empty((S, s.H), dtype=bf, device=d)
+            self.dprobs = torch.empty((s.T, s.top_k), dtype=torch.float32, device=d)
+            self.dx_tokens = torch.empty((s.T, s.H), dtype=bf, device=d)
 
     # -- forward ---------------------------------------------------------
     def permute(self, x, topk_ids):
@@ -94,3 +102,18 @@ class MoeLayer:
         swiglu_bwd(self.da, self.h, g, out=self.dh)
         gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
         gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)
+
+    # -- backward of the two ends and of the whole layer --------------------
+    def unpermute_backward(self, dout, probs):
+        moe_unpermute_bwd(dout, self.yp, self.row_id_map, probs, out=(self.dyp, self.dprobs),
+                          dev_err=self.dev_err)
+
+    def permute_backward(self):
+        moe_permute_bwd(self.dx, self.row_id_map, self.shape.T, out=self.dx_tokens,
+                        dev_err=self.dev_err)
+
+    def backward_full(self, dout, probs, w1, w2):
+        """dout -> (dx_tokens, dprobs, dw1, dw2), every intermediate kept."""
+        self.unpermute_backward(dout, probs)
+        self.backward(self.dyp, w1, w2)
+        self.permute_backward()

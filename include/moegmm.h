@@ -194,6 +194,46 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, cons
                          int64_t T, int64_t top_k, int64_t H, uint16_t* out, int32_t* dev_err,
                          void* stream);
 
+/* ------------------------------------------------------------------------
+ * moe_unpermute_bwd -- gradients of moe_unpermute with respect to y_perm and
+ * probs, given dout = d(loss)/d(out):
+ *   dy_perm[row(t,k), :] = probs[t, k] * dout[t, :]        (rounded once, RNE)
+ *   dprobs[t, k]         = sum_h dout[t, h] * y_perm[row(t,k), h]   (fp32)
+ * with row(t,k) = row_id_map[t*top_k + k]; a masked slot (-1) gets
+ * dprobs = 0 and writes no row.  [MegaMoE] Token Combine, differentiated:
+ * the combine is linear in each of y_perm and probs.
+ *
+ *   dout [T, H] bf16, y_perm [T*top_k, H] bf16, row_id_map [T*top_k] int32,
+ *   probs [T, top_k] fp32; dy_perm [T*top_k, H] bf16 OUT (the rows that some
+ *   valid slot points at are written, the others untouched), dprobs
+ *   [T, top_k] fp32 OUT.
+ * Entries of row_id_map outside [-1, T*top_k) set MOE_DEVERR_ROW_MAP and are
+ * skipped.  Deterministic: every sum runs in a fixed order, no atomics.
+ * ---------------------------------------------------------------------- */
+moe_status moe_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,
+                             const int32_t* row_id_map, const float* probs, int64_t T,
+                             int64_t top_k, int64_t H, uint16_t* dy_perm, float* dprobs,
+                             int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_bwd -- the token gradient of moe_permute:
+ *   dx[t, :] = sum over k = 0..top_k-1 with row_id_map[t*top_k+k] >= 0 of
+ *              dx_perm[row_id_map[t*top_k + k], :]
+ * accumulated in fp32 in ascending k, rounded once (RNE); a token with no
+ * valid slot gets zeros.  [PermGrad] section 2.3 (each permuted row's
+ * gradient is added back onto the token it was copied from) and section 6.2
+ * (a token walks its top-k slots, skips -1, accumulates in FP32, casts back
+ * once).
+ *
+ *   dx_perm [T*top_k, H] bf16, row_id_map [T*top_k] int32 (as written by
+ *   moe_permute), dx [T, H] bf16 OUT.
+ * Entries of row_id_map outside [-1, T*top_k) set MOE_DEVERR_ROW_MAP and are
+ * skipped.  Deterministic: no atomics.
+ * ---------------------------------------------------------------------- */
+moe_status moe_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, int64_t T,
+                           int64_t top_k, int64_t H, uint16_t* dx, int32_t* dev_err,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

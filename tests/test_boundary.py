@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_bwd_input",
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
-              "moe_status_string", "moegmm_abi_version"]:
+              "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version"]:
         assert n in names, n
 
 
@@ -128,3 +128,29 @@ def test_elementwise_reject_bad_arguments(lib):
     assert lib.moe_unpermute(A16, None, A16b, 4, 2, 64, A16c, None, None) == MOE_ERR_NULL
     assert lib.moe_unpermute(A16, A16b, A16c, 4, 33, 64, A16c, None, None) == MOE_ERR_INVALID
     assert lib.moe_unpermute(A16, A16b, A16c, 4, 2, 12, A16c, None, None) == MOE_ERR_INVALID
+
+
+def test_end_backward_calls_reject_bad_arguments(lib):
+    # moe_unpermute_bwd(dout, y_perm, row_id_map, probs, T, top_k, H, dy_perm, dprobs, dev_err, stream)
+    good = dict(dout=A16, yp=A16b, rmap=A16c, probs=A16, T=8, k=2, H=64, dyp=A16b, dp=A16c)
+
+    def ub(**kw):
+        a = dict(good, **kw)
+        return lib.moe_unpermute_bwd(a["dout"], a["yp"], a["rmap"], a["probs"], a["T"], a["k"], a["H"],
+                                     a["dyp"], a["dp"], None, None)
+
+    assert ub(dout=None) == MOE_ERR_NULL
+    assert ub(dp=None) == MOE_ERR_NULL
+    assert ub(k=0) == MOE_ERR_INVALID
+    assert ub(k=33) == MOE_ERR_INVALID
+    assert ub(H=100) == MOE_ERR_INVALID
+    assert ub(T=-1) == MOE_ERR_INVALID
+    assert ub(dyp=MIS) == MOE_ERR_INVALID
+    assert ub(T=0, dout=None, yp=None, rmap=None, probs=None, dyp=None, dp=None) == MOE_OK
+    # moe_permute_bwd(dx_perm, row_id_map, T, top_k, H, dx, dev_err, stream)
+    assert lib.moe_permute_bwd(None, A16c, 8, 2, 64, A16, None, None) == MOE_ERR_NULL
+    assert lib.moe_permute_bwd(A16, A16c, 8, 2, 64, None, None, None) == MOE_ERR_NULL
+    assert lib.moe_permute_bwd(A16, A16c, 8, 0, 64, A16b, None, None) == MOE_ERR_INVALID
+    assert lib.moe_permute_bwd(A16, A16c, 8, 2, 12, A16b, None, None) == MOE_ERR_INVALID
+    assert lib.moe_permute_bwd(MIS, A16c, 8, 2, 64, A16b, None, None) == MOE_ERR_INVALID
+    assert lib.moe_permute_bwd(None, None, 0, 2, 64, None, None, None) == MOE_OK

@@ -81,6 +81,7 @@ def tiny(seed: int = 0) -> Workload:
         w2=normal_bf16(rng, (E, I, H), 0.05),
         probs=rng.uniform(0.0, 1.0, size=(T, K)).astype(np.float32),
         dyp=normal_bf16(rng, (5, H)),
+        dout=normal_bf16(rng, (T, H)),  # drawn last: the arrays above keep their values
     )
     return Workload("tiny", dict(T=T, K=K, E=E, H=H, I=I), arrays)
 

@@ -508,9 +508,11 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
 // ---------------------------------------------------------------------------
 // Weight gradient: dw[e] = x[rows_e]^T @ dy[rows_e].  Tiles (expert, k-tile,
 // n-tile), experts in descending row count (ties by index) so the longest
-// reductions start first.  Both operands are outer-contiguous; the reduction
-// runs over the expert's rows, zero-filled past its last row.  Empty experts
-// write zeros.
+// reductions start first.  Inside an expert, each of the 8 XCDs takes one
+// rectangle of the (k-tile, n-tile) grid, so its L2 streams a few x and dy
+// panels rather than nearly all of them.  Both operands are outer-contiguous;
+// the reduction runs over the expert's rows, zero-filled past its last row.
+// Empty experts write zeros.
 // ---------------------------------------------------------------------------
 constexpr int kMaxRankedExperts = 256;  // beyond this, experts run in index order
 
@@ -545,7 +547,32 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
     }
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_pick);
-    const int kt_out = rem / NT, nt = rem % NT;
+    // Workgroup ids go round-robin to the 8 XCDs and every expert's tile
+    // range starts at a multiple of 8 (KT*NT % 8 == 0): give XCD rem % 8 one
+    // rectangle of the expert's (k-tile, n-tile) grid, kx x (8/kx) rectangles
+    // chosen to minimise the x and dy panels each XCD reads.
+    int kx = 0;
+    {
+        int best = 0x7fffffff;
+        for (int c = 1; c <= 8; c *= 2) {
+            const int ny = 8 / c;
+            if (KT % c == 0 && NT % ny == 0 && KT / c + NT / ny < best) {
+                best = KT / c + NT / ny;
+                kx = c;
+            }
+        }
+    }
+    int kt_out, nt;
+    if (kx) {
+        const int ny = 8 / kx, KTr = KT / kx, NTr = NT / ny;
+        const int x = rem & 7, p = rem >> 3;
+        kt_out = (x / ny) * KTr + p / NTr;
+        nt = (x % ny) * NTr + p % NTr;
+    } else {
+        kt_out = rem / NT;
+        nt = rem % NT;
+    }
+
     const int k0 = kt_out * kBM, n0 = nt * kBN;
     const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
     const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);

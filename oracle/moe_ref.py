@@ -237,6 +237,16 @@ def unpermute(y_perm, row_id_map, probs) -> np.ndarray:
     return out
 
 
+def gmm_swiglu(x, w1, group_list) -> np.ndarray:
+    """A = SiLU(G) * U with [G | U] = the gate_up GMM x @ w1[e] over each
+    expert's rows, with no rounding in between.
+
+    [MegaMoE: Expert Compute -- H_e = X_e W1[e] split along its columns into
+    G and U, then the activation.]  The fused call rounds only A.
+    """
+    return swiglu(gmm(x, w1, group_list))
+
+
 # ---------------------------------------------------------------------------
 # backward of the two ends of the path: the weighted unpermute (Token Combine)
 # and the permute  [MegaMoE: Token Combine; PermGrad: 2.2, 2.3, 6.2]

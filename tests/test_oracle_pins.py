@@ -613,6 +613,35 @@ def test_layer_backward_finite_differences():
 
 
 # ---------------------------------------------------------------------------
+# pin 14: the fused gate_up GMM + SwiGLU, row by row with explicit loops
+# ---------------------------------------------------------------------------
+
+
+def check_gmm_swiglu_brute(gmm_swiglu):
+    rng = _rng(25)
+    gl = np.array([3, 0, 2, 1])
+    K, I = 5, 3
+    M = int(gl.sum())
+    x = rng.standard_normal((M, K))
+    w1 = rng.standard_normal((4, K, 2 * I))
+    got = gmm_swiglu(x, w1, gl)
+    assert got.shape == (M, I)
+    r = 0
+    for e, n in enumerate(gl):
+        for _ in range(n):
+            for j in range(I):
+                g = sum(x[r, q] * w1[e, q, j] for q in range(K))
+                u = sum(x[r, q] * w1[e, q, I + j] for q in range(K))
+                ref = g / (1.0 + np.exp(-g)) * u
+                assert abs(got[r, j] - ref) <= 1e-12 * max(1.0, abs(ref)), (r, j)
+            r += 1
+
+
+def test_gmm_swiglu_bruteforce():
+    check_gmm_swiglu_brute(oracle.gmm_swiglu)
+
+
+# ---------------------------------------------------------------------------
 # mutation tests: a planted mistake in a copy of an oracle function must trip
 # at least one pin (run on the CPU only)
 # ---------------------------------------------------------------------------
@@ -733,6 +762,12 @@ def _mut_layer_bwd_dprobs_doubled(fwd, dout, probs, w1, w2, rounding=None):
     return g
 
 
+def _mut_gmm_swiglu_up_gate(x, w1, gl):
+    I = np.asarray(w1).shape[2] // 2
+    w = np.concatenate([np.asarray(w1)[:, :, I:], np.asarray(w1)[:, :, :I]], axis=2)
+    return oracle.gmm_swiglu(x, w, gl)  # gate and up halves swapped
+
+
 def _mut_round_truncate(a):
     f = np.asarray(a, dtype=np.float32)
     u = f.view(np.uint32) & np.uint32(0xFFFF0000)
@@ -769,6 +804,7 @@ def test_mutants_are_caught(golden_dir):
         or _fails(check_permute_adjoint, oracle.permute, _mut_permute_bwd_first_slot),
         "layer_bwd_dprobs_doubled": _fails(check_layer_backward_fd, oracle.moe_layer_forward,
                                            _mut_layer_bwd_dprobs_doubled),
+        "gmm_swiglu_up_gate": _fails(check_gmm_swiglu_brute, _mut_gmm_swiglu_up_gate),
     }
     missed = [k for k, v in caught.items() if not v]
     assert not missed, f"mutants not caught by any pin: {missed}"

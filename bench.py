@@ -6,8 +6,9 @@ rank's share -- E=32 local experts, hidden 4096, intermediate 1536, 16384
 received rows with Zipf(1.2) group sizes and 3 empty experts.  One step is
 one pass of the whole hot path:
 
-    moe_permute (top_k=1 local re-routing, histogram) -> gmm_fwd(W1)
-    -> swiglu -> gmm_fwd(W2) -> moe_unpermute
+    moe_permute (top_k=1 local re-routing, histogram)
+    -> gmm_fwd_swiglu(W1; writes A and, for the backward, H) -> gmm_fwd(W2)
+    -> moe_unpermute
     -> gmm_bwd_input(W2) -> gmm_bwd_weight(dW2) -> swiglu_bwd
     -> gmm_bwd_input(W1) -> gmm_bwd_weight(dW1)
 
@@ -127,14 +128,15 @@ def ep_gemm_flops(gl, H, I):
     R = int(np.sum(gl))
     fwd1 = 2.0 * R * H * 2 * I
     fwd2 = 2.0 * R * I * H
-    return {"gmm_fwd_gate_up": fwd1, "gmm_fwd_down": fwd2,
+    return {"gmm_fwd_swiglu": fwd1, "gmm_fwd_down": fwd2,
             "gmm_bwd_input_down": fwd2, "gmm_bwd_weight_down": fwd2,
             "gmm_bwd_input_gate_up": fwd1, "gmm_bwd_weight_gate_up": fwd1}
 
 
 # libmoegmm kernel behind each call of the step (kernel symbol -> calls)
 EP_KERNELS = {
-    "gmm_rows_kernel<fwd>": ["gmm_fwd_gate_up", "gmm_fwd_down"],
+    "gmm_rows_kernel<fwd+swiglu>": ["gmm_fwd_swiglu"],
+    "gmm_rows_kernel<fwd>": ["gmm_fwd_down"],
     "gmm_rows_kernel<dX>": ["gmm_bwd_input_down", "gmm_bwd_input_gate_up"],
     "gmm_dw_kernel": ["gmm_bwd_weight_down", "gmm_bwd_weight_gate_up"],
 }
@@ -159,13 +161,14 @@ def run_ep(torch, dev, args):
     timer = KernelTimer(torch)
     g = layer.tokens_per_expert
 
-    from grouped_gemm_moe_amd import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, moe_unpermute,
-                                      swiglu, swiglu_bwd)
+    from grouped_gemm_moe_amd import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu,
+                                      moe_unpermute, swiglu_bwd)
 
     def step(t):
         t("moe_permute", lambda: layer.permute(x, ids))
-        t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h, dev_err=layer.dev_err))
-        t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
+        # gate_up GMM fused with SwiGLU; H is kept for the SwiGLU backward
+        t("gmm_fwd_swiglu", lambda: gmm_fwd_swiglu(layer.x_perm, w1, g, out=layer.a, h_out=layer.h,
+                                                   dev_err=layer.dev_err))
         t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp, dev_err=layer.dev_err))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out,
                                                  dev_err=layer.dev_err))
@@ -223,15 +226,17 @@ def run_ep(torch, dev, args):
 # decode-shaped layer forward: HBM GB/s
 # ---------------------------------------------------------------------------
 
-def decode_bytes(gl, T, K, H, I):
+def decode_bytes(gl, T, K, H, I, fused=True):
     """Algorithmic bytes of one layer forward: weights of experts with rows,
-    once; every activation tensor written once and read once; indices."""
+    once; every activation tensor the path materialises written once and read
+    once (x_perm, A, Yp; H too when gate_up and SwiGLU run unfused);
+    indices."""
     n_active = int(np.sum(np.asarray(gl) > 0))
     S = int(np.sum(gl))
     w = n_active * (H * 2 * I + I * H) * 2
     act = (T * H * 2            # x read by permute
            + S * H * 2 * 2      # x_perm written, read
-           + S * 2 * I * 2 * 2  # h written, read
+           + (0 if fused else S * 2 * I * 2 * 2)  # h written, read
            + S * I * 2 * 2      # a written, read
            + S * H * 2 * 2      # yp written, read
            + T * H * 2)         # out written
@@ -240,8 +245,10 @@ def decode_bytes(gl, T, K, H, I):
 
 
 def layer_forward(torch, dev, wl, steps):
-    """Time the layer forward (permute -> gate_up -> SwiGLU -> down ->
-    unpermute) on workload `wl`: wall ms per layer and per-call means."""
+    """Time the layer forward on workload `wl` -- permute -> gate_up GMM and
+    SwiGLU (fused into one call, no H, except for decode-shaped calls where
+    the weight-streaming gate_up + swiglu pair is faster) -> down GMM ->
+    unpermute: wall ms per layer, per-call means, and whether it fused."""
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
 
     d = wl.dims
@@ -253,13 +260,17 @@ def layer_forward(torch, dev, wl, steps):
     probs = torch.from_numpy(wl["probs"]).to(dev)
     layer = MoeLayer(LayerShape(T, K, E, H, I), dev)
     timer = KernelTimer(torch)
-    from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu
+    from grouped_gemm_moe_amd import gmm_fwd, gmm_fwd_swiglu, moe_unpermute, swiglu
     g = layer.tokens_per_expert
+    fused = layer.use_fused("auto")
 
     def step(t):
         t("moe_permute", lambda: layer.permute(x, ids))
-        t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h))
-        t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
+        if fused:
+            t("gmm_fwd_swiglu", lambda: gmm_fwd_swiglu(layer.x_perm, w1, g, out=layer.a))
+        else:
+            t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h))
+            t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
         t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out))
 
@@ -278,7 +289,7 @@ def layer_forward(torch, dev, wl, steps):
     torch.cuda.synchronize()
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     gl = layer.tokens_per_expert.cpu().numpy()
-    return ms, per, gl, (layer, probs)
+    return ms, per, gl, (layer, probs, fused)
 
 
 def end_backward(torch, dev, layer, probs, steps=20):
@@ -321,11 +332,11 @@ def end_backward(torch, dev, layer, probs, steps=20):
     return res
 
 
-def layer_roofline(gl, T, K, H, I, ms):
+def layer_roofline(gl, T, K, H, I, ms, fused=True):
     """Algorithmic bytes and FLOPs of one layer forward and the fraction of
     the attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak) that the
     measured time reaches."""
-    nbytes, n_active = decode_bytes(gl, T, K, H, I)
+    nbytes, n_active = decode_bytes(gl, T, K, H, I, fused)
     S = int(np.sum(gl))
     flops = 2.0 * S * H * 2 * I + 2.0 * S * I * H
     t_mem = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -342,16 +353,16 @@ def run_decode(torch, dev, args):
     wl = workloads.decode()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl, _ = layer_forward(torch, dev, wl, args.decode_steps)
-    roof = layer_roofline(gl, T, K, H, I, ms)
+    ms, per, gl, (_, _, fused) = layer_forward(torch, dev, wl, args.decode_steps)
+    roof = layer_roofline(gl, T, K, H, I, ms, fused)
     nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
     gbs = nbytes / (ms * 1e-3) / 1e9
-    wbytes = {k: n_active * (H * 2 * I if k == "gmm_fwd_gate_up" else I * H) * 2
-              for k in ("gmm_fwd_gate_up", "gmm_fwd_down")}
+    gate_up = "gmm_fwd_swiglu" if fused else "gmm_fwd_gate_up"
+    wbytes = {k: n_active * (H * 2 * I if k == gate_up else I * H) * 2 for k in (gate_up, "gmm_fwd_down")}
     return dict(
         metric="decode MoE layer HBM GB/s",
         workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
-                 "intermediate 512; permute -> gate_up -> SwiGLU -> down -> unpermute",
+                 "intermediate 512; permute -> gate_up (weight streaming) -> SwiGLU -> down -> unpermute",
         value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4),
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=nbytes,
         active_experts=n_active, frac_of_attainable=roof["frac_of_attainable"],
@@ -366,15 +377,15 @@ def run_prefill(torch, dev, args):
     wl = workloads.prefill()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl, (layer, probs) = layer_forward(torch, dev, wl, args.prefill_steps)
-    roof = layer_roofline(gl, T, K, H, I, ms)
+    ms, per, gl, (layer, probs, fused) = layer_forward(torch, dev, wl, args.prefill_steps)
+    roof = layer_roofline(gl, T, K, H, I, ms, fused)
     ends = end_backward(torch, dev, layer, probs)
     gbs = roof["bytes_per_layer"] / (ms * 1e-3) / 1e9
     tflops = roof["gflop_per_layer"] * 1e9 / (ms * 1e-3) / 1e12
     return dict(
         metric="prefill MoE layer forward: % of attainable roofline",
         workload="prefill layer forward: T=4096 tokens, top-8 of E=128, hidden 2048, "
-                 "intermediate 512; permute -> gate_up -> SwiGLU -> down -> unpermute",
+                 "intermediate 512; permute -> gate_up GMM fused with SwiGLU -> down -> unpermute",
         value=round(100.0 * roof["frac_of_attainable"], 2), unit="% of attainable roofline",
         ms_per_layer=round(ms, 4), gb_per_s=round(gbs, 1), tflops=round(tflops, 2),
         pct_bf16_mfma_peak=round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
@@ -473,7 +484,7 @@ def main():
         "config": {
             "workload": "one expert-parallel rank's share, fwd+bwd: E=32 local experts, hidden 4096, "
                         "intermediate 1536, 16384 received rows (top_k=1 local re-routing), Zipf(1.2) "
-                        "group sizes with 3 empty experts; permute -> gate_up GMM -> SwiGLU -> down GMM "
+                        "group sizes with 3 empty experts; permute -> gate_up GMM fused with SwiGLU -> down GMM "
                         "-> unpermute -> expert-block backward (dX and dW of both GMMs)",
             "experts": 32, "hidden": 4096, "intermediate": 1536, "rows": 16384,
             "gemm_gflop_per_step": round(ep["gemm_gflop_per_step"], 1),

@@ -21,7 +21,7 @@ import torch
 from . import _lib as _L
 
 __all__ = [
-    "MoeError", "moe_permute", "gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
+    "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
     "moe_permute_workspace_size", "gmm_workspace_size",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP",
@@ -129,6 +129,27 @@ def gmm_fwd(x, w, group_list, *, out=None, ws=None, dev_err=None):
     _check(library().gmm_fwd(_ptr(x), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(y), _ptr(ws),
                              ws_bytes, _ptr(dev_err), _stream(x.device)), "gmm_fwd")
     return y
+
+
+def gmm_fwd_swiglu(x, w1, group_list, *, out=None, h_out=None, ws=None, dev_err=None):
+    """a = SiLU(G) * U with [G | U] = x[rows_e] @ w1[e], from the fp32
+    accumulators; ``h_out`` ([M, 2I], optional) also receives [G | U]."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(w1, "w1", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, K = x.shape
+    E, K2, N2 = w1.shape
+    if K2 != K or N2 % 2 or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: x [M, K], w1 [E, K, 2I], group_list [E]")
+    I = N2 // 2
+    a = _out(out, (M, I), torch.bfloat16, x.device, "a")
+    if h_out is not None:
+        _out(h_out, (M, N2), torch.bfloat16, x.device, "h_out")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N2, OP_FWD), x.device, ws)
+    _check(library().gmm_fwd_swiglu(_ptr(x), _ptr(w1), _ptr(group_list), E, M, K, I, _ptr(a),
+                                    _ptr(h_out), _ptr(ws), ws_bytes, _ptr(dev_err),
+                                    _stream(x.device)), "gmm_fwd_swiglu")
+    return a
 
 
 def gmm_bwd_input(dy, w, group_list, *, out=None, ws=None, dev_err=None):

@@ -24,6 +24,7 @@ SIGNATURES = {
     "moe_permute": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "gmm_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
     "gmm_fwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
+    "gmm_fwd_swiglu": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
     "gmm_bwd_input": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd_weight": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "swiglu": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
@@ -33,7 +34,7 @@ SIGNATURES = {
     "moe_permute_bwd": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 

@@ -55,7 +55,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 2; }
+int moegmm_abi_version(void) { return 3; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -94,6 +94,20 @@ moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_li
     if (st != MOE_OK) return st;
     return from_hip(moegmm::launch_gmm_fwd(x, w, group_list, E, M_cap, K, N, y, ws, dev_err,
                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
+                          int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
+                          uint16_t* h, void* ws, size_t ws_bytes, int32_t* dev_err,
+                          void* stream) {
+    if (!dim_ok(I)) return MOE_ERR_INVALID;
+    moe_status st = check_gmm_common(x, w1, group_list, a, E, M_cap, K, 2 * I,
+                                     moegmm::gmm_workspace_bytes(E, M_cap, K, 2 * I, MOE_GMM_OP_FWD),
+                                     ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    if (!aligned(h, 16)) return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_fwd_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, ws,
+                                                  dev_err, static_cast<hipStream_t>(stream)));
 }
 
 moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,

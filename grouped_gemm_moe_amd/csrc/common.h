@@ -33,6 +33,10 @@ MOE_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// sigma(g) = 1 / (1 + e^-g), the gate of SiLU(g) = g * sigma(g) ("MegaMoE",
+// activation formulas).
+MOE_DEVICE float silu_sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
 // Vector loads/stores of 16 bytes.
 MOE_DEVICE u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 MOE_DEVICE void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }

@@ -33,8 +33,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxGrid = 2048;
 
-MOE_DEVICE float silu_sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
-
 // Rows r < R (R from group_list), 8 columns of the I outputs per work item.
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const bf16_t* __restrict__ h,
                                                           const int64_t* __restrict__ group_list,

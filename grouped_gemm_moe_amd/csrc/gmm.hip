@@ -108,7 +108,7 @@ struct Dma<BO, true> {
     int red[kInst];
     uint32_t ok_mask;
 
-    MOE_DEVICE void init(int64_t ld, int outer_lim) {
+    MOE_DEVICE void init(int64_t ld, int outer_lim, int = 0) {
         const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
         ok_mask = 0;
 #pragma unroll
@@ -153,16 +153,25 @@ struct Dma<BO, false> {
     int red[kInst];
     uint32_t ok_mask;
 
-    MOE_DEVICE void init(int64_t ld, int outer_lim) {
+    // pair > 0: the tile's columns are 32-wide groups taken alternately from
+    // column c and column pair + c of the operand (gate and up halves of a
+    // gate_up weight), so that tile groups 2g and 2g+1 hold the same
+    // output columns 32g..32g+31; outer_lim then bounds c.
+    MOE_DEVICE void init(int64_t ld, int outer_lim, int pair = 0) {
         const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
         ok_mask = 0;
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
             const int k = (wid * kInst + i) * kRowsPerInst + lane / kChunks;
             const int col = ((lane % kChunks) ^ swz_mn(k)) * 8;
-            off[i] = (uint32_t)(((int64_t)k * ld + col) * 2);
+            int vc = col, gc = col;
+            if (pair > 0) {
+                vc = (col >> 6) * 32 + (col & 31);
+                gc = ((col >> 5) & 1) * pair + vc;
+            }
+            off[i] = (uint32_t)(((int64_t)k * ld + gc) * 2);
             red[i] = k;
-            if (col < outer_lim) ok_mask |= 1u << i;
+            if (vc < outer_lim) ok_mask |= 1u << i;
         }
     }
     MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
@@ -334,6 +343,49 @@ struct Engine {
                 }
         }
     }
+
+    // Gate_up tile with paired columns (see Dma::init): fragment 0 of a wave
+    // holds the gate values G and fragment 1 the up values U of the same 32
+    // output columns.  Writes A = SiLU(G) * U (rounded once, from the fp32
+    // accumulators) and, when h is given, G and U themselves to h[:, c] and
+    // h[:, pair + c].
+    MOE_DEVICE void store_swiglu(bf16_t* __restrict__ a, int64_t lda, bf16_t* __restrict__ h,
+                                 int64_t ldh, int pair, int rows_valid, int cols_valid) const {
+        static_assert(TN == 2, "one gate and one up fragment per wave");
+        const int lane = threadIdx.x & 63;
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            if (row >= rows_valid) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = wn * 32 + g * 8 + (lane >> 5) * 4;
+                if (col >= cols_valid) continue;
+                float av[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float gv = acc[i][0][4 * g + c], uv = acc[i][1][4 * g + c];
+                    av[c] = gv * silu_sigmoid(gv) * uv;
+                }
+                u32x2_t pk;
+                pk[0] = pack_bf16x2(av[0], av[1]);
+                pk[1] = pack_bf16x2(av[2], av[3]);
+                *reinterpret_cast<u32x2_t*>(a + (int64_t)row * lda + col) = pk;
+                if (h) {
+                    u32x2_t pg, pu;
+                    pg[0] = pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]);
+                    pg[1] = pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]);
+                    pu[0] = pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]);
+                    pu[1] = pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]);
+                    bf16_t* hr = h + (int64_t)row * ldh + col;
+                    *reinterpret_cast<u32x2_t*>(hr) = pg;
+                    *reinterpret_cast<u32x2_t*>(hr + pair) = pu;
+                }
+            }
+        }
+    }
 };
 
 // Wait until at most N of this wave's vector-memory loads are outstanding.
@@ -351,10 +403,12 @@ MOE_DEVICE void wait_vmcnt() {
 // writes zeros into a stage nobody reads again, and keeps the number of
 // loads in flight constant (no data-dependent wait counts, no branches).
 // `smem` holds kNST stages of [A tile | B tile].
-template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR>
+// `store(eng)` writes the result; rows_valid / cols_valid (in tile columns)
+// decide which waves have any work.
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Store>
 MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
-                          int64_t ldb, int b_olim, int red_len, bf16_t* out, int64_t ldo,
-                          int rows_valid, int cols_valid, bf16_t* smem) {
+                          int64_t ldb, int b_olim, int b_pair, int red_len, int rows_valid,
+                          int cols_valid, bf16_t* smem, const Store& store) {
     using DA = Dma<BM, A_KMAJOR>;
     using DB = Dma<BN, B_KMAJOR>;
     constexpr int kStage = (BM + BN) * BK;       // elements per stage
@@ -362,7 +416,7 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     DA da;
     DB db;
     da.init(lda, a_olim);
-    db.init(ldb, b_olim);
+    db.init(ldb, b_olim, b_pair);
     Engine<BM, BN, WM, WN, A_KMAJOR, B_KMAJOR> eng;
     eng.zero();
     const int nk = (red_len + BK - 1) / BK;
@@ -409,7 +463,7 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
     else run_steps(std::false_type{});
     wait_vmcnt<0>();  // no LDS write may outlive the workgroup
-    eng.store(out, ldo, rows_valid, cols_valid);
+    store(eng);
 }
 
 // Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
@@ -441,16 +495,24 @@ constexpr int kOccupancy = (kSmemElems * 2 <= 80 * 1024 && kAccRegs <= 128) ? 2 
 static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the last stage");
 
 // ---------------------------------------------------------------------------
-// Row-grouped GEMM: forward (IS_DX = false) and input gradient (IS_DX = true).
-//   fwd: A = x [M_cap, K] (reduction-contiguous, ld K), B(q, j) = w[e][q][j]
-//        (outer-contiguous, ld N); out y [M_cap, N]; reduction K.
-//   dX:  A = dy [M_cap, N] (ld N), B(q, j) = w[e][j][q] (reduction-contiguous,
-//        ld N); out dx [M_cap, K]; reduction N.
+// Row-grouped GEMM, three modes:
+//   kFwd:    A = x [M_cap, K] (reduction-contiguous, ld K), B(q, j) = w[e][q][j]
+//            (outer-contiguous, ld N); out y [M_cap, N]; reduction K.
+//   kDx:     A = dy [M_cap, N] (ld N), B(q, j) = w[e][j][q] (reduction-
+//            contiguous, ld N); out dx [M_cap, K]; reduction N.
+//   kSwiGLU: the gate_up forward with N = 2I fused with SwiGLU: a tile covers
+//            kBN/2 output columns c of a [M_cap, I], reading gate columns c
+//            and up columns I + c of w[e]; optionally h [M_cap, 2I] too.
 // ---------------------------------------------------------------------------
-template <bool IS_DX>
+enum RowsMode { kFwd = 0, kDx = 1, kSwiGLU = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
-    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
+    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
+    int32_t* dev_err) {
+    constexpr bool IS_DX = MODE == kDx;
+    constexpr int kCols = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     // schedule arrays: in the last stage, which no load touches before the
@@ -474,9 +536,9 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
         }
     __syncthreads();
 
-    const int Ncols = IS_DX ? K : N;  // output columns
-    const int Kred = IS_DX ? N : K;   // reduction length
-    const int NT = (Ncols + kBN - 1) / kBN;
+    const int Ncols = IS_DX ? K : (MODE == kSwiGLU ? N / 2 : N);  // output columns
+    const int Kred = IS_DX ? N : K;                                 // reduction length
+    const int NT = (Ncols + kCols - 1) / kCols;
     const int ntiles = (int)total_mt * NT;
     if ((int)blockIdx.x >= ntiles) return;  // uniform across the block
 #if defined(MOEGMM_NO_XCD_REMAP)
@@ -495,14 +557,28 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const int row0 = __builtin_amdgcn_readfirstlane(s_off[e] + (mt - s_tst[e]) * kBM);
     const int row_end = __builtin_amdgcn_readfirstlane(s_off[e] + s_cnt[e]);
     const int rows_valid = row_end - row0 < kBM ? row_end - row0 : kBM;
-    const int n0 = __builtin_amdgcn_readfirstlane(nt * kBN);
+    const int n0 = __builtin_amdgcn_readfirstlane(nt * kCols);
     __syncthreads();  // schedule arrays are dead from here on
 
     const int64_t lda = IS_DX ? N : K;
     const bf16_t* We = W + (int64_t)e * K * N;
-    gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
-        A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N, Ncols - n0,
-        Kred, Y + (int64_t)row0 * Ncols + n0, Ncols, rows_valid, Ncols - n0, smem);
+    const int cols_left = Ncols - n0;
+    if constexpr (MODE == kSwiGLU) {
+        bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
+        bf16_t* h = Hout ? Hout + (int64_t)row0 * N + n0 : nullptr;
+        const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
+        gemm_tile<kBM, kBN, kWM, kWN, true, false>(
+            A + (int64_t)row0 * lda, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid,
+            tile_cols, smem, [&](const auto& eng) {
+                eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left);
+            });
+    } else {
+        bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
+        gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
+            A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N,
+            cols_left, 0, Kred, rows_valid, cols_left, smem,
+            [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left); });
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -590,9 +666,9 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
         }
         return;
     }
-    gemm_tile<kBM, kBN, kWM, kWN, false, false>(X + (int64_t)off * K + k0, K, rows_valid,
-                                                DY + (int64_t)off * N + n0, N, cols_valid, cnt, out, N,
-                                                rows_valid, cols_valid, smem);
+    gemm_tile<kBM, kBN, kWM, kWN, false, false>(
+        X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0, cnt,
+        rows_valid, cols_valid, smem, [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid); });
 }
 
 int64_t row_tiles_bound(int64_t M_cap, int64_t E, int bm) { return (M_cap + bm - 1) / bm + E; }
@@ -609,8 +685,8 @@ hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* g
         return launch_gmm_stream(x, w, group_list, E, M_cap, K, N, y, dev_err, stream);
     const int64_t NT = (N + kBN - 1) / kBN;
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
-    hipLaunchKernelGGL(gmm_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
-                       group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
+    hipLaunchKernelGGL(gmm_rows_kernel<kFwd>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
+                       group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err);
     return hipGetLastError();
 }
 
@@ -620,8 +696,8 @@ hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int
     if (M_cap == 0) return hipSuccess;
     const int64_t NT = (K + kBN - 1) / kBN;
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
-    hipLaunchKernelGGL(gmm_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, dy, w,
-                       group_list, (int)E, M_cap, (int)K, (int)N, dx, dev_err);
+    hipLaunchKernelGGL(gmm_rows_kernel<kDx>, dim3((unsigned)grid), dim3(kThreads), 0, stream, dy, w,
+                       group_list, (int)E, M_cap, (int)K, (int)N, dx, nullptr, dev_err);
     return hipGetLastError();
 }
 
@@ -631,6 +707,19 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
     const int64_t grid = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     hipLaunchKernelGGL(gmm_dw_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, dy,
                        group_list, (int)E, M_cap, (int)K, (int)N, dw, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
+                                 int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
+                                 uint16_t* h, void*, int32_t* dev_err, hipStream_t stream) {
+    if (M_cap == 0) return hipSuccess;
+    if (gmm_stream_applies(E, M_cap, K))
+        return launch_gmm_stream_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, dev_err, stream);
+    const int64_t NT = (I + kBN / 2 - 1) / (kBN / 2);
+    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    hipLaunchKernelGGL(gmm_rows_kernel<kSwiGLU>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x,
+                       w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h, dev_err);
     return hipGetLastError();
 }
 

@@ -23,6 +23,12 @@ constexpr int kThreads = 256;
 // one pass over the weights per group of rows.  Partial sums meet first
 // across the k-groups of a wave (shuffles), then across waves in LDS, always
 // in the same order.
+//
+// SWIGLU: the gate_up forward (N = 2I) fused with SwiGLU.  The block's
+// column lanes are split in two halves: the first streams gate columns
+// c0 .. c0+COLS/2-1, the second the up columns I+c0 .. of the same outputs,
+// and the epilogue writes a = SiLU(G) * U for COLS/2 output columns (and,
+// when h is given, G and U too).
 // ---------------------------------------------------------------------------
 #ifndef MOEGMM_STREAM_COLS
 #define MOEGMM_STREAM_COLS 256
@@ -58,12 +64,14 @@ MOE_DEVICE void stream_rows(const bf16_t* __restrict__ We, const bf16_t* xs, int
     }
 }
 
-template <int COLS>
+template <int COLS, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
-    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, int32_t* dev_err) {
+    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
+    int32_t* dev_err) {
     constexpr int kLanes = COLS / 8;          // column lanes of one k-group
     constexpr int kGPW = 64 / kLanes;         // k-groups per wave
+    constexpr int kOutCols = SWIGLU ? COLS / 2 : COLS;  // output columns per block
     extern __shared__ __attribute__((aligned(16))) char dsmem[];
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
@@ -72,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     bf16_t* xs = reinterpret_cast<bf16_t*>(dsmem);  // [kStreamRows][K]
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int NB = (N + COLS - 1) / COLS;
+    const int Nout = SWIGLU ? N / 2 : N;  // output columns
+    const int NB = (Nout + kOutCols - 1) / kOutCols;
     const int e = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int off = s_off[e], cnt = s_cnt[e];
     if (cnt == 0) return;  // uniform
@@ -80,8 +89,10 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int cl = lane % kLanes;
     const int kg = wid * kGPW + lane / kLanes;
-    const int col = nb * COLS + cl * 8;
-    const bool col_ok = col < N;
+    // the output column of this lane's 8 columns, and its weight column
+    const int ocol = nb * kOutCols + (SWIGLU ? cl % (kLanes / 2) : cl) * 8;
+    const int col = SWIGLU && cl >= kLanes / 2 ? Nout + ocol : ocol;
+    const bool col_ok = ocol < Nout;
     const bf16_t* We = W + (int64_t)e * K * N + col;
 
     for (int r0 = 0; r0 < cnt; r0 += kStreamRows) {
@@ -119,7 +130,42 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
                 for (int c = 0; c < 8; ++c) red[wid][r][cl * 8 + c] = acc[r][c];
         }
         __syncthreads();
-        if (threadIdx.x < kStreamRows * kLanes) {
+        if constexpr (SWIGLU) {
+            // 4 output columns per thread (as many threads as the plain
+            // epilogue uses): gate sums from columns j, up sums from
+            // kOutCols + j of the block's partials
+            constexpr int kQuads = kOutCols / 4;
+            if (threadIdx.x < kStreamRows * kQuads) {
+                const int r = threadIdx.x / kQuads, c4 = threadIdx.x % kQuads;
+                const int gcol = nb * kOutCols + c4 * 4;
+                if (r < rows && gcol < Nout) {
+                    float gs[4], us[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) gs[c] = us[c] = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            gs[c] += red[w][r][c4 * 4 + c];
+                            us[c] += red[w][r][kOutCols + c4 * 4 + c];
+                        }
+                    const int64_t orow = off + r0 + r;
+                    u32x2_t o;
+                    o[0] = pack_bf16x2(gs[0] * silu_sigmoid(gs[0]) * us[0], gs[1] * silu_sigmoid(gs[1]) * us[1]);
+                    o[1] = pack_bf16x2(gs[2] * silu_sigmoid(gs[2]) * us[2], gs[3] * silu_sigmoid(gs[3]) * us[3]);
+                    *reinterpret_cast<u32x2_t*>(Y + orow * Nout + gcol) = o;
+                    if (Hout) {
+                        u32x2_t og, ou;
+                        og[0] = pack_bf16x2(gs[0], gs[1]);
+                        og[1] = pack_bf16x2(gs[2], gs[3]);
+                        ou[0] = pack_bf16x2(us[0], us[1]);
+                        ou[1] = pack_bf16x2(us[2], us[3]);
+                        *reinterpret_cast<u32x2_t*>(Hout + orow * N + gcol) = og;
+                        *reinterpret_cast<u32x2_t*>(Hout + orow * N + Nout + gcol) = ou;
+                    }
+                }
+            }
+        } else if (threadIdx.x < kStreamRows * kLanes) {
             const int r = threadIdx.x / kLanes, c8 = threadIdx.x % kLanes;
             const int gcol = nb * COLS + c8 * 8;
             if (r < rows && gcol < N) {
@@ -153,8 +199,21 @@ hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t
                              int32_t* dev_err, hipStream_t stream) {
     const int64_t NB = (N + kStreamCols - 1) / kStreamCols;
     const size_t shmem = (size_t)K * kStreamRows * 2;
-    hipLaunchKernelGGL(gmm_stream_kernel<kStreamCols>, dim3((unsigned)(E * NB)), dim3(kThreads), shmem,
-                       stream, x, w, group_list, (int)E, M_cap, (int)K, (int)N, y, dev_err);
+    hipLaunchKernelGGL((gmm_stream_kernel<kStreamCols, false>), dim3((unsigned)(E * NB)), dim3(kThreads),
+                       shmem, stream, x, w, group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr,
+                       dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,
+                                    const int64_t* group_list, int64_t E, int64_t M_cap,
+                                    int64_t K, int64_t I, uint16_t* a, uint16_t* h,
+                                    int32_t* dev_err, hipStream_t stream) {
+    const int64_t NB = (I + kStreamCols / 2 - 1) / (kStreamCols / 2);
+    const size_t shmem = (size_t)K * kStreamRows * 2;
+    hipLaunchKernelGGL((gmm_stream_kernel<kStreamCols, true>), dim3((unsigned)(E * NB)), dim3(kThreads),
+                       shmem, stream, x, w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h,
+                       dev_err);
     return hipGetLastError();
 }
 

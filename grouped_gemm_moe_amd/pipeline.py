@@ -2,6 +2,8 @@
 
 Forward ("NPU Training Operators - GMM", section "Qwen3.5 MoE 路径"):
     moe_permute -> gmm_fwd(W1) -> swiglu -> gmm_fwd(W2) -> moe_unpermute
+or, fused, moe_permute -> gmm_fwd_swiglu(W1) -> gmm_fwd(W2) -> moe_unpermute
+(H written only when a backward will need it)
 Backward of the expert block, from the gradient dYp at the down-GMM output
 (permuted row order):
     dA = gmm_bwd_input(dYp, W2); dW2 = gmm_bwd_weight(A, dYp);
@@ -22,7 +24,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_workspace_size, moe_permute,
+from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_workspace_size, moe_permute,
                moe_permute_bwd, moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd,
                swiglu, swiglu_bwd)
 
@@ -79,18 +81,33 @@ class MoeLayer:
         moe_permute(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
                     out=(self.x_perm, self.row_id_map, self.sorted_slot, self.tokens_per_expert))
 
-    def experts_forward(self, w1, w2):
+    def use_fused(self, fused) -> bool:
+        """fused="auto": the fused gate_up + SwiGLU call unless the shape is
+        decode-like (at most 8 rows per expert), where the weight-streaming
+        gate_up followed by swiglu measures faster."""
+        if fused == "auto":
+            return self.shape.S > 8 * self.shape.E
+        return bool(fused)
+
+    def experts_forward(self, w1, w2, fused=False, keep_h=True):
+        """fused: one gate_up GMM + SwiGLU call writes A (and H only when
+        keep_h, as the backward needs it); otherwise gate_up GMM -> H ->
+        swiglu -> A.  fused may be "auto" (see use_fused)."""
         g = self.tokens_per_expert
-        gmm_fwd(self.x_perm, w1, g, out=self.h, ws=self.ws_gmm, dev_err=self.dev_err)
-        swiglu(self.h, g, out=self.a)
+        if self.use_fused(fused):
+            gmm_fwd_swiglu(self.x_perm, w1, g, out=self.a, h_out=self.h if keep_h else None,
+                           ws=self.ws_gmm, dev_err=self.dev_err)
+        else:
+            gmm_fwd(self.x_perm, w1, g, out=self.h, ws=self.ws_gmm, dev_err=self.dev_err)
+            swiglu(self.h, g, out=self.a)
         gmm_fwd(self.a, w2, g, out=self.yp, ws=self.ws_gmm, dev_err=self.dev_err)
 
     def unpermute(self, probs):
         moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
 
-    def forward(self, x, topk_ids, probs, w1, w2):
+    def forward(self, x, topk_ids, probs, w1, w2, fused=False, keep_h=True):
         self.permute(x, topk_ids)
-        self.experts_forward(w1, w2)
+        self.experts_forward(w1, w2, fused=fused, keep_h=keep_h)
         self.unpermute(probs)
         return self.out
 

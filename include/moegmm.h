@@ -130,6 +130,26 @@ moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_li
                    int32_t* dev_err, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gmm_fwd_swiglu -- the gate_up grouped matmul fused with SwiGLU:
+ *   [G | U] = x[off_e + i, :] @ w1[e]   (G = first I columns, U = last I)
+ *   a[off_e + i, j] = SiLU(G[j]) * U[j],  SiLU(z) = z / (1 + e^-z)
+ * computed from the fp32 accumulators and rounded once (RNE); G and U are not
+ * rounded in between.  [MegaMoE] Expert Compute (H_e = X_e W1[e], split along
+ * its columns into G and U, then the activation) with the clamp unset;
+ * [GMM] "Qwen3.5 MoE 路径" (gate_up GMM, then SwiGLU).
+ *
+ *   x [M_cap, K] bf16, w1 [E, K, 2I] bf16, group_list [E] int64,
+ *   a [M_cap, I] bf16 OUT (rows < R written; rows >= R untouched),
+ *   h [M_cap, 2I] bf16 OUT or NULL: when given, also gets [G | U] rounded
+ *   once, exactly as gmm_fwd would write them (for the SwiGLU backward).
+ * Workspace: gmm_workspace_size(E, M_cap, K, 2I, MOE_GMM_OP_FWD).
+ * ---------------------------------------------------------------------- */
+moe_status gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
+                          int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
+                          uint16_t* h, void* ws, size_t ws_bytes, int32_t* dev_err,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
  * gmm_bwd_input -- dx[off_e + i, :] = dy[off_e + i, :] @ w[e]^T.
  * [GMM] 算子语义, backward: the input gradient is the output gradient times
  * the transposed weight, over the same group boundaries.

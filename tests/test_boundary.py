@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_bwd_input",
+    for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input",
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version"]:
         assert n in names, n
@@ -154,3 +154,13 @@ def test_end_backward_calls_reject_bad_arguments(lib):
     assert lib.moe_permute_bwd(A16, A16c, 8, 2, 12, A16b, None, None) == MOE_ERR_INVALID
     assert lib.moe_permute_bwd(MIS, A16c, 8, 2, 64, A16b, None, None) == MOE_ERR_INVALID
     assert lib.moe_permute_bwd(None, None, 0, 2, 64, None, None, None) == MOE_OK
+
+
+def test_fused_swiglu_rejects_bad_arguments(lib):
+    ws = ctypes.c_void_p(0x40000)
+    # gmm_fwd_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, ws, ws_bytes, dev_err, stream)
+    assert lib.gmm_fwd_swiglu(A16, None, A16c, 4, 64, 64, 32, A16b, None, ws, 0, None, None) == MOE_ERR_NULL
+    assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 12, A16b, None, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 1 << 21, A16b, None, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 32, MIS, None, ws, 0, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 32, A16b, MIS, ws, 0, None, None) == MOE_ERR_INVALID

@@ -19,8 +19,9 @@
 //                 expert in slot order (wave ballots emulate a match-any on
 //                 the expert id) and writes row_id_map and sorted_slot.
 //   4. gather  -- copies token rows to their permuted rows with 16-byte loads
-//                 and stores (coalesced inside each row), four loads in
-//                 flight per thread.
+//                 and stores (coalesced inside each row): each piece of a
+//                 token row is loaded once and stored to all of the token's
+//                 slot rows; four loads in flight per thread.
 // For at most 4096 slots (decode-sized calls) steps 1-3 run as one
 // single-workgroup kernel, so the whole permute is two launches.
 #include "common.h"
@@ -66,10 +67,22 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(
 }
 
 // One block.  Thread i owns experts [i*per, i*per + per) so that the scan
-// over threads runs in ascending expert order.
+// over threads runs in ascending expert order.  The per-block histograms are
+// first staged in LDS with one coalesced pass when they fit (so the column
+// sums below read LDS instead of walking global memory one load at a time).
+constexpr int64_t kScanLdsInts = 12288;  // 48 KiB
+
 __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
     int32_t* __restrict__ blk_hist, int64_t nblk, int E, int64_t* __restrict__ tokens_per_expert) {
     __shared__ int64_t scan_tmp[kPermThreads / 64];
+    __shared__ int32_t s_hist[kScanLdsInts];
+    const int64_t n = nblk * E;
+    const bool staged = n <= kScanLdsInts;  // uniform
+    if (staged) {
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s_hist[i] = blk_hist[i];
+        __syncthreads();
+    }
+    auto count = [&](int64_t i) { return staged ? s_hist[i] : blk_hist[i]; };
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
     int64_t cnt[4] = {0, 0, 0, 0};
@@ -78,7 +91,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
         const int e = e0 + i;
         if (e >= E) break;
         int64_t c = 0;
-        for (int64_t b = 0; b < nblk; ++b) c += blk_hist[b * E + e];
+        for (int64_t b = 0; b < nblk; ++b) c += count(b * E + e);
         cnt[i] = c;
         mine += c;
     }
@@ -90,7 +103,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
         tokens_per_expert[e] = cnt[i];
         int64_t run = off;
         for (int64_t b = 0; b < nblk; ++b) {
-            int32_t v = blk_hist[b * E + e];
+            const int32_t v = count(b * E + e);
             blk_hist[b * E + e] = (int32_t)run;
             run += v;
         }
@@ -227,44 +240,64 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
     wave_rank_scatter(ids, w0, w1, E, next_row[wid], row_id_map, sorted_slot);
 }
 
-constexpr int kGatherSlots = 16;  // slots per block
-constexpr int kGatherUnroll = 4;  // 16-byte loads in flight per thread
+// Gather, token by token: a block owns tpb consecutive tokens, loads each
+// 16-byte piece of a token row once and stores it to every row its valid
+// slots map to (top_k stores per load), so a top-8 permute reads x once.
+#ifndef MOEGMM_GATHER_SLOTS
+#define MOEGMM_GATHER_SLOTS 16
+#endif
+constexpr int kGatherMaxSlots = MOEGMM_GATHER_SLOTS;  // tpb * top_k <= max(this, top_k)
+constexpr int kGatherUnroll = 4;     // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t S, int top_k,
-    int64_t H, uint16_t* __restrict__ x_perm) {
-    __shared__ int32_t rows[kGatherSlots];
-    const int64_t s0 = (int64_t)blockIdx.x * kGatherSlots;
-    if (threadIdx.x < kGatherSlots) {
-        const int64_t s = s0 + threadIdx.x;
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t T, int top_k,
+    int64_t H, int tpb, uint16_t* __restrict__ x_perm) {
+    __shared__ int32_t rows[kGatherMaxSlots > 32 ? kGatherMaxSlots : 32];  // top_k <= 32
+    const int64_t S = T * top_k;
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int nslots = tpb * top_k;
+    if ((int)threadIdx.x < nslots) {
+        const int64_t s = t0 * top_k + threadIdx.x;
         const int32_t r = (s < S) ? row_id_map[s] : -1;
         rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
     }
     __syncthreads();
     const int64_t cpr = H / 8;  // 16-byte chunks per row
-    const int64_t total = (int64_t)kGatherSlots * cpr;
+    const int64_t tok = T - t0 < tpb ? T - t0 : tpb;
+    const int64_t total = tok * cpr;
     for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)kPermThreads * kGatherUnroll) {
         u32x4_t v[kGatherUnroll];
-        int64_t dst[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
             const int64_t i = i0 + (int64_t)u * kPermThreads;
-            dst[u] = -1;
             if (i < total) {
-                const int ls = (int)(i / cpr);
-                const int64_t c = i - ls * cpr;
-                const int32_t r = rows[ls];
-                if (r >= 0) {
-                    const int64_t t = (s0 + ls) / top_k;
-                    v[u] = ld16(x + t * H + c * 8);
-                    dst[u] = (int64_t)r * H + c * 8;
-                }
+                const int64_t tt = i / cpr, c = i - tt * cpr;
+                v[u] = ld16(x + (t0 + tt) * H + c * 8);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u)
-            if (dst[u] >= 0) st16(x_perm + dst[u], v[u]);
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            if (i < total) {
+                const int64_t tt = i / cpr, c = i - tt * cpr;
+                for (int k = 0; k < top_k; ++k) {
+                    const int32_t r = rows[tt * top_k + k];
+                    if (r >= 0) st16(x_perm + (int64_t)r * H + c * 8, v[u]);
+                }
+            }
+        }
     }
+}
+
+// Tokens per gather block: up to kGatherMaxSlots slots, but at most T/256
+// tokens so that the launch still has some 256 blocks to spread.  (16 slots
+// measured best on the decode, prefill and top-1 EP shapes; 32 and 64 lose
+// up to 50 % on the EP shape.)
+int gather_tokens_per_block(int64_t T, int64_t top_k) {
+    int64_t tpb = kGatherMaxSlots / top_k;
+    const int64_t cap = T / 256;
+    if (tpb > cap) tpb = cap;
+    return tpb < 1 ? 1 : (int)tpb;
 }
 
 }  // namespace
@@ -299,9 +332,10 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                                stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
     }
     if (nblk > 0) {
-        const int64_t gblk = (S + kGatherSlots - 1) / kGatherSlots;
+        const int tpb = gather_tokens_per_block(T, top_k);
+        const int64_t gblk = (T + tpb - 1) / tpb;
         hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)gblk), dim3(kPermThreads), 0,
-                           stream, x, row_id_map, S, (int)top_k, H, x_perm);
+                           stream, x, row_id_map, T, (int)top_k, H, tpb, x_perm);
     }
     return hipGetLastError();
 }

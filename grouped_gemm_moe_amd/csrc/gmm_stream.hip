@@ -34,6 +34,9 @@ constexpr int kThreads = 256;
 #define MOEGMM_STREAM_COLS 256
 #endif
 constexpr int kStreamCols = MOEGMM_STREAM_COLS;
+#ifndef MOEGMM_STREAM_UNROLL
+#define MOEGMM_STREAM_UNROLL 2
+#endif
 constexpr int kStreamRows = 4;
 constexpr int kWaves = kThreads / 64;
 
@@ -41,7 +44,7 @@ template <int COLS, int ROWS>
 MOE_DEVICE void stream_rows(const bf16_t* __restrict__ We, const bf16_t* xs, int K, int N, int kg,
                             float (&acc)[kStreamRows][8]) {
     constexpr int kGroups = (64 / (COLS / 8)) * kWaves;
-#pragma unroll 2
+#pragma unroll MOEGMM_STREAM_UNROLL
     for (int k = kg * 8; k < K; k += 8 * kGroups) {
         u32x4_t wv[8];
 #pragma unroll

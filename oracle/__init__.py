@@ -21,3 +21,4 @@ from .moe_ref import (  # noqa: F401
     unpermute,
     unpermute_bwd,
 )
+from . import mx_ref  # noqa: F401,E402

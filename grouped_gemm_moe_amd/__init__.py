@@ -7,7 +7,9 @@ Python or in PyTorch.  PyTorch provides device memory and streams only.
 
 Names and argument order follow the C ABI:
     moe_permute, gmm_fwd, gmm_bwd_input, gmm_bwd_weight, swiglu, swiglu_bwd,
-    moe_unpermute
+    moe_unpermute, and the MXFP8 calls mx_quantize, moe_permute_mx,
+    gmm_mx_fwd, gmm_mx_fwd_swiglu (an MX tensor is a pair of uint8 tensors:
+    codes [rows, K] and scales [rows, mx_scale_ld(K)])
 Outputs are allocated with ``torch.empty`` unless passed via ``out=``; rows
 at or beyond R = sum(group_list) of a permuted-row output are left as they
 were (undefined for a fresh allocation).
@@ -23,7 +25,8 @@ from . import _lib as _L
 __all__ = [
     "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
-    "moe_permute_workspace_size", "gmm_workspace_size",
+    "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
+    "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP",
 ]
 
@@ -263,3 +266,104 @@ def moe_permute_bwd(dx_perm, row_id_map, num_tokens: int, *, out=None, dev_err=N
     _check(library().moe_permute_bwd(_ptr(dx_perm), _ptr(row_id_map), T, top_k, H, _ptr(dx),
                                      _ptr(dev_err), _stream(dx_perm.device)), "moe_permute_bwd")
     return dx
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (A8W8-FP)
+# ---------------------------------------------------------------------------
+
+
+def mx_scale_ld(K: int) -> int:
+    """Scale row stride for K codes: ceil(K/32) rounded up to 16 bytes."""
+    g = (K + 31) // 32
+    return (g + 15) // 16 * 16
+
+
+def mx_quantize(x, *, out=None):
+    """Q_MX of every row (last dimension) of a bf16 tensor; returns
+    (codes uint8 like x, scales uint8 [..., mx_scale_ld(K)])."""
+    _dev(x, "x", torch.bfloat16)
+    K = x.shape[-1]
+    rows = x.numel() // K if K else 0
+    ld = mx_scale_ld(K)
+    if out is None:
+        out = (None, None)
+    q = _out(out[0], tuple(x.shape), torch.uint8, x.device, "q")
+    sc = _out(out[1], tuple(x.shape[:-1]) + (ld,), torch.uint8, x.device, "scales")
+    _check(library().mx_quantize(_ptr(x), rows, K, ld, _ptr(q), _ptr(sc), _stream(x.device)),
+           "mx_quantize")
+    return q, sc
+
+
+def moe_permute_mx(x, topk_ids, num_experts: int, *, out=None, ws=None, dev_err=None):
+    """moe_permute whose gather writes Q_MX of each row.  Returns (xq, xs,
+    row_id_map, sorted_slot, tokens_per_expert)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, H = x.shape
+    top_k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise MoeError("topk_ids must be [T, top_k]")
+    S = T * top_k
+    dev = x.device
+    ld = mx_scale_ld(H)
+    if out is None:
+        out = (None,) * 5
+    xq = _out(out[0], (S, H), torch.uint8, dev, "xq")
+    xs = _out(out[1], (S, ld), torch.uint8, dev, "xs")
+    row_id_map = _out(out[2], (S,), torch.int32, dev, "row_id_map")
+    sorted_slot = _out(out[3], (S,), torch.int32, dev, "sorted_slot")
+    tpe = _out(out[4], (num_experts,), torch.int64, dev, "tokens_per_expert")
+    nbytes = moe_permute_workspace_size(T, top_k, num_experts)
+    ws, ws_bytes = _workspace(nbytes, dev, ws)
+    _check(library().moe_permute_mx(_ptr(x), _ptr(topk_ids), T, top_k, H, num_experts, _ptr(xq),
+                                    _ptr(xs), ld, _ptr(row_id_map), _ptr(sorted_slot), _ptr(tpe),
+                                    _ptr(ws), ws_bytes, _ptr(dev_err), _stream(dev)),
+           "moe_permute_mx")
+    return xq, xs, row_id_map, sorted_slot, tpe
+
+
+def _mx_pair(q, s, name):
+    _dev(q, name + " codes", torch.uint8)
+    _dev(s, name + " scales", torch.uint8)
+    if tuple(q.shape[:-1]) != tuple(s.shape[:-1]):
+        raise MoeError(f"{name}: codes and scales disagree on the row shape")
+    return q.shape[-1], s.shape[-1]
+
+
+def gmm_mx_fwd(xq, xs, wq, wsc, group_list, *, out=None, dev_err=None):
+    """y[rows_e] = DQ(x)[rows_e] @ DQ(w[e])^T with w stored [E, N, K]; bf16 y."""
+    K, ld_x = _mx_pair(xq, xs, "x")
+    K2, ld_w = _mx_pair(wq, wsc, "w")
+    _dev(group_list, "group_list", torch.int64)
+    M = xq.shape[0]
+    E, N, _ = wq.shape
+    if K2 != K or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: x [M, K], w [E, N, K], group_list [E]")
+    y = _out(out, (M, N), torch.bfloat16, xq.device, "y")
+    _check(library().gmm_mx_fwd(_ptr(xq), _ptr(xs), ld_x, _ptr(wq), _ptr(wsc), ld_w,
+                                _ptr(group_list), E, M, K, N, _ptr(y), _ptr(dev_err),
+                                _stream(xq.device)), "gmm_mx_fwd")
+    return y
+
+
+def gmm_mx_fwd_swiglu(xq, xs, w1q, w1s, group_list, *, out=None, dev_err=None):
+    """GMM1 + SwiGLU + Q_MX: returns (aq [M, I], as [M, mx_scale_ld(I)]) with
+    w1 stored [E, 2I, K] (gate rows, then up rows)."""
+    K, ld_x = _mx_pair(xq, xs, "x")
+    K2, ld_w = _mx_pair(w1q, w1s, "w1")
+    _dev(group_list, "group_list", torch.int64)
+    M = xq.shape[0]
+    E, N2, _ = w1q.shape
+    if K2 != K or group_list.shape[0] != E or N2 % 2:
+        raise MoeError("shape mismatch: x [M, K], w1 [E, 2I, K], group_list [E]")
+    I = N2 // 2
+    ld_a = mx_scale_ld(I)
+    if out is None:
+        out = (None, None)
+    aq = _out(out[0], (M, I), torch.uint8, xq.device, "aq")
+    asc = _out(out[1], (M, ld_a), torch.uint8, xq.device, "as")
+    _check(library().gmm_mx_fwd_swiglu(_ptr(xq), _ptr(xs), ld_x, _ptr(w1q), _ptr(w1s), ld_w,
+                                       _ptr(group_list), E, M, K, I, _ptr(aq), _ptr(asc), ld_a,
+                                       _ptr(dev_err), _stream(xq.device)), "gmm_mx_fwd_swiglu")
+    return aq, asc

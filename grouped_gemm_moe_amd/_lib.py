@@ -32,9 +32,15 @@ SIGNATURES = {
     "moe_unpermute": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]),
     "moe_unpermute_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "moe_permute_bwd": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "mx_quantize": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
+    "moe_permute_mx": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _sz,
+                              _p, _p]),
+    "gmm_mx_fwd": (_int, [_p, _p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p, _p]),
+    "gmm_mx_fwd_swiglu": (_int, [_p, _p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p,
+                                 _i64, _p, _p]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 

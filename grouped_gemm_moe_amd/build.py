@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoegmm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "permute.hip", "gmm.hip", "gmm_stream.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "permute.hip", "gmm.hip", "gmm_stream.hip", "gmm_mx.hip", "mx_quant.hip",
+           "elementwise.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

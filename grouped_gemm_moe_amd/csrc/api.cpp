@@ -24,6 +24,27 @@ constexpr int64_t kMaxGmmDim = int64_t(1) << 21;
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// An MX tensor's scale rows: at least ceil(K/32) bytes, padded to 16.
+bool mx_ld_ok(int64_t ld_s, int64_t K) { return ld_s >= (K + 31) / 32 && ld_s % 16 == 0; }
+
+moe_status check_gmm_mx(const void* xq, const void* xs, int64_t ld_xs, const void* wq,
+                        const void* ws, int64_t ld_ws, const void* gl, int64_t E, int64_t M_cap,
+                        int64_t K, int64_t N) {
+    if (!gl || !wq || !ws || (M_cap > 0 && (!xq || !xs))) return MOE_ERR_NULL;
+    if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(K) || !dim_ok(N) ||
+        K % 32 != 0 || K > kMaxGmmDim || N > kMaxGmmDim)
+        return MOE_ERR_INVALID;
+    if (!mx_ld_ok(ld_xs, K) || !mx_ld_ok(ld_ws, K)) return MOE_ERR_INVALID;
+    if (!aligned(xq, 16) || !aligned(xs, 16) || !aligned(wq, 16) || !aligned(ws, 16) ||
+        !aligned(gl, 8))
+        return MOE_ERR_INVALID;
+    if (M_cap * K > (int64_t(1) << 40) || M_cap * N > (int64_t(1) << 40) ||
+        E * K * N > (int64_t(1) << 40) || M_cap * ld_xs > (int64_t(1) << 40) ||
+        E * N * ld_ws > (int64_t(1) << 40))
+        return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
 moe_status check_gmm_common(const void* a, const void* b, const void* gl, const void* out,
                             int64_t E, int64_t M_cap, int64_t K, int64_t N, size_t ws_need,
                             size_t ws_bytes, const void* ws) {
@@ -55,7 +76,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 3; }
+int moegmm_abi_version(void) { return 4; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -76,9 +97,9 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
         !aligned(ws, 4))
         return MOE_ERR_INVALID;
     if (ws_bytes < moegmm::permute_workspace_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
-    return from_hip(moegmm::launch_permute(x, topk_ids, T, top_k, H, E, x_perm, row_id_map,
-                                           sorted_slot, tokens_per_expert, ws, dev_err,
-                                           static_cast<hipStream_t>(stream)));
+    return from_hip(moegmm::launch_permute(x, topk_ids, T, top_k, H, E, x_perm, nullptr, nullptr,
+                                           0, row_id_map, sorted_slot, tokens_per_expert, ws,
+                                           dev_err, static_cast<hipStream_t>(stream)));
 }
 
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op) {
@@ -192,6 +213,67 @@ moe_status moe_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, i
         return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_permute_bwd(dx_perm, row_id_map, T, top_k, H, dx, dev_err,
                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status mx_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ld_s, uint8_t* q,
+                       uint8_t* s, void* stream) {
+    if (rows > 0 && (!x || !q || !s)) return MOE_ERR_NULL;
+    if (rows < 0 || rows > kMaxRows || K <= 0 || K % 32 != 0 || K > (int64_t(1) << 24) ||
+        !mx_ld_ok(ld_s, K) || rows * K > (int64_t(1) << 40))
+        return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(q, 16)) return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_mx_quantize(x, rows, K, ld_s, q, s,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute_mx(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                          int64_t H, int64_t E, uint8_t* xq, uint8_t* xs, int64_t ld_xs,
+                          int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                          void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!tokens_per_expert || !ws) return MOE_ERR_NULL;
+    if (T > 0 && (!x || !topk_ids || !xq || !xs || !row_id_map || !sorted_slot))
+        return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || !dim_ok(H) ||
+        H % 32 != 0 || !mx_ld_ok(ld_xs, H))
+        return MOE_ERR_INVALID;
+    if (T * top_k > kMaxRows) return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(topk_ids, 4) ||
+        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) || !aligned(tokens_per_expert, 8) ||
+        !aligned(ws, 4))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < moegmm::permute_workspace_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
+    return from_hip(moegmm::launch_permute(x, topk_ids, T, top_k, H, E, nullptr, xq, xs, ld_xs,
+                                           row_id_map, sorted_slot, tokens_per_expert, ws,
+                                           dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
+                      const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
+                      int64_t M_cap, int64_t K, int64_t N, uint16_t* y, int32_t* dev_err,
+                      void* stream) {
+    moe_status st = check_gmm_mx(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap, K, N);
+    if (st != MOE_OK) return st;
+    if (M_cap > 0 && !y) return MOE_ERR_NULL;
+    if (!aligned(y, 16)) return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_mx_fwd(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap,
+                                              K, N, y, dev_err,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                             const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                             const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                             int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                             int32_t* dev_err, void* stream) {
+    if (!dim_ok(I) || I % 32 != 0 || !mx_ld_ok(ld_as, I)) return MOE_ERR_INVALID;
+    moe_status st = check_gmm_mx(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, E, M_cap, K, 2 * I);
+    if (st != MOE_OK) return st;
+    if (M_cap > 0 && (!aq || !as)) return MOE_ERR_NULL;
+    if (!aligned(aq, 16) || !aligned(as, 16) || M_cap * ld_as > (int64_t(1) << 40))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_mx_fwd_swiglu(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list,
+                                                     E, M_cap, K, I, aq, as, ld_as, dev_err,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,560 @@
+// The MFMA tile engine of the grouped matmul kernels (gfx950): HBM -> LDS
+// operand staging, the LDS ring, MFMA fragments and the tile epilogues,
+// shared by the bf16 kernels (gmm.hip) and the MXFP8 kernels (gmm_mx.hip).
+//
+// Design (MI355X-first):
+//  * group_list never leaves the device.  Every workgroup reads it, scans it
+//    in LDS and finds its own tile: a row-grouped tile list for fwd / dX (sum
+//    over experts of ceil(n_e/BM) M-tiles times the N-tiles, walked in an
+//    XCD-aware order so neighbouring tiles share an L2) and an (expert,
+//    k-tile, n-tile) list for dW, largest experts first.  The grid is sized
+//    from host-known bounds; surplus workgroups exit at once.
+//  * One MFMA engine: 256x256 output tile per workgroup, 8 waves (two per
+//    SIMD, so one hides the other's waits) of 128x64 each,
+//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave whose
+//    sub-tile lies wholly past the tile's valid rows or columns (the last
+//    row tile of an expert) skips its LDS reads and MFMAs and only issues
+//    its share of the loads.
+//  * Operands go HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+//    VGPR staging).  Lanes whose element lies outside the problem (ragged
+//    rows, reduction tails, rows past an expert) get an out-of-range buffer
+//    offset, which loads zeros -- so partial tiles need no special path.
+//  * Each operand keeps its HBM orientation in LDS.  A reduction-contiguous
+//    tile ([outer][BK]) is read with ds_read_b128; an outer-contiguous tile
+//    ([BK][outer]) is read with ds_read_b64_tr_b16,
+//    the gfx950 transposing LDS read, which hands each lane 4 consecutive
+//    reduction elements of one column.  16-byte chunks are XOR-swizzled per
+//    row so both reads hit every LDS bank pair at most twice per pass.
+//  * A ring of NST LDS stages (4 x 32 KiB, BK = 32): the loads of the next
+//    NST-1 steps fly while a step runs its MFMAs.  One barrier per step;
+//    each wave waits only for its own loads of the step about to be read.
+//  * The MFMA is issued with operands swapped (B fragment as the hardware A
+//    operand) so each lane holds 4 consecutive output columns; the epilogue
+//    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace moegmm {
+
+namespace {
+
+#ifndef MOEGMM_THREADS
+#define MOEGMM_THREADS 512
+#endif
+constexpr int kThreads = MOEGMM_THREADS;  // 4 or 8 waves
+constexpr int kWaves = kThreads / 64;
+
+#ifndef MOEGMM_BK
+#define MOEGMM_BK 32
+#endif
+#ifndef MOEGMM_NST
+#define MOEGMM_NST 4
+#endif
+constexpr int BK = MOEGMM_BK;     // reduction depth of one LDS stage
+constexpr int kNST = MOEGMM_NST;  // LDS stages in the ring
+static_assert(BK == 32 || BK == 64, "stage depth");
+static_assert(kNST >= 2 && kNST <= 6, "stage count");
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+// Buffer resource covering the whole 31-bit offset range from `base`; every
+// lane's offset is computed in bounds or set to kOOB, which the hardware
+// range check turns into a zero load.
+constexpr int kNumRecords = 0x7FFFFFF0;
+constexpr uint32_t kOOB = 0x7FFFFFF0u;
+
+MOE_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, kNumRecords,
+                                             0x00020000);
+}
+
+// Wave index as a scalar (the LDS-DMA destination must be wave-uniform).
+MOE_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// LDS swizzles (16-byte chunk index XOR) for the two tile orientations.
+// [outer][BK] tiles: 16 consecutive rows read at one logical chunk must land
+// on distinct bank groups (64 banks x 4 bytes).
+MOE_DEVICE int swz_k(int o) { return BK == 64 ? ((o ^ (o >> 3)) & 7) : ((o >> 2) & 3); }
+MOE_DEVICE int swz_mn(int k) { return (k & 3) << 2; }         // [64][outer] tiles
+
+// ---------------------------------------------------------------------------
+// HBM -> LDS copies of one operand tile per reduction step.  A wave
+// instruction moves 1 KiB: lane l's 16 bytes land at LDS byte 16*l of it, so
+// the lane -> global-address map decides the LDS layout (and the swizzle).
+// ---------------------------------------------------------------------------
+template <int BO, bool KMAJOR>
+struct Dma;
+
+// Reduction-contiguous operand: element (o, q) at base[o*ld + q].
+// LDS tile [BO][BK]; one instruction fills 1024 / (2*BK) rows.
+template <int BO>
+struct Dma<BO, true> {
+    static constexpr int kCPR = BK / 8;                  // 16-byte chunks per row
+    static constexpr int kRowsPerInst = 64 / kCPR;
+    static constexpr int kInst = BO / kRowsPerInst / kWaves;  // per wave
+    static_assert(kInst >= 1 && BO % (kRowsPerInst * kWaves) == 0, "tile/threads mismatch");
+    uint32_t off[kInst];
+    int red[kInst];
+    uint32_t ok_mask;
+
+    // pair > 0: tile rows are 32-row groups taken alternately from operand
+    // row r and row pair + r (gate and up halves of a gate_up weight), as in
+    // the outer-contiguous case below; outer_lim then bounds r.
+    MOE_DEVICE void init(int64_t ld, int outer_lim, int pair = 0) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int o = (wid * kInst + i) * kRowsPerInst + lane / kCPR;
+            const int c = (lane % kCPR) ^ swz_k(o);
+            int vo = o, go = o;
+            if (pair > 0) {
+                vo = (o >> 6) * 32 + (o & 31);
+                go = ((o >> 5) & 1) * pair + vo;
+            }
+            off[i] = (uint32_t)(((int64_t)go * ld + c * 8) * 2);
+            red[i] = c * 8;
+            if (vo < outer_lim) ok_mask |= 1u << i;
+        }
+    }
+    // stage_base: element (0, s*BK); red_left: valid reduction length from there
+    MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(stage_base);
+        const int wid = wave_id();
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (LDS_AS void*)(lds + (wid * kInst + i) * 512), 16, v, 0, 0, 0);
+        }
+    }
+    static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t, int s) { return base + s * BK; }
+    // instruction i of this wave's share of one stage
+    MOE_DEVICE void issue_one(int i, __amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, int red_left) const {
+        const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (LDS_AS void*)(lds + (wave_id() * kInst + i) * 512), 16, v, 0, 0, 0);
+    }
+};
+
+// Outer-contiguous operand: element (o, q) at base[q*ld + o].
+// LDS tile [BK][BO]; one instruction fills 1024 / (2*BO) rows.
+template <int BO>
+struct Dma<BO, false> {
+    static constexpr int kChunks = BO / 8;
+    static constexpr int kRowsPerInst = 64 / kChunks;
+    static constexpr int kInst = BK / kRowsPerInst / kWaves;  // per wave
+    static_assert(kChunks >= 16 && 64 % kChunks == 0 && kInst >= 1 &&
+                      BK % (kRowsPerInst * kWaves) == 0, "outer tile must be 128 or 256");
+    uint32_t off[kInst];
+    int red[kInst];
+    uint32_t ok_mask;
+
+    // pair > 0: the tile's columns are 32-wide groups taken alternately from
+    // column c and column pair + c of the operand (gate and up halves of a
+    // gate_up weight), so that tile groups 2g and 2g+1 hold the same
+    // output columns 32g..32g+31; outer_lim then bounds c.
+    MOE_DEVICE void init(int64_t ld, int outer_lim, int pair = 0) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int k = (wid * kInst + i) * kRowsPerInst + lane / kChunks;
+            const int col = ((lane % kChunks) ^ swz_mn(k)) * 8;
+            int vc = col, gc = col;
+            if (pair > 0) {
+                vc = (col >> 6) * 32 + (col & 31);
+                gc = ((col >> 5) & 1) * pair + vc;
+            }
+            off[i] = (uint32_t)(((int64_t)k * ld + gc) * 2);
+            red[i] = k;
+            if (vc < outer_lim) ok_mask |= 1u << i;
+        }
+    }
+    MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(stage_base);
+        const int wid = wave_id();
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (LDS_AS void*)(lds + (wid * kInst + i) * 512), 16, v, 0, 0, 0);
+        }
+    }
+    static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t ld, int s) {
+        return base + (int64_t)s * BK * ld;
+    }
+    // instruction i of this wave's share of one stage
+    MOE_DEVICE void issue_one(int i, __amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, int red_left) const {
+        const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (LDS_AS void*)(lds + (wave_id() * kInst + i) * 512), 16, v, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA operand fragments: lane l gets T[o0 + l%32][k0 + 8*(l/32) + 0..7].
+//
+// The reads are issued as inline asm on purpose: the loads of the next
+// reduction step are in flight into the other LDS stage while these run, and
+// the compiler, unable to prove the two stages apart through computed
+// addresses, would otherwise wait for those loads first.  The caller waits
+// for the reads itself (lds_wait) before feeding the fragments to MFMAs.
+// ---------------------------------------------------------------------------
+MOE_DEVICE uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+template <int BO, bool KMAJOR>
+struct Frag;
+
+template <int BO>
+struct Frag<BO, true> {
+    static MOE_DEVICE void load(bf16x8_t& v, const bf16_t* lds, int o0, int k0) {
+        const int lane = threadIdx.x & 63;
+        const int o = o0 + (lane & 31);
+        const int c = (k0 >> 3) + (lane >> 5);
+        asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(lds_addr(lds + o * BK + ((c ^ swz_k(o)) << 3))));
+    }
+};
+
+// ds_read_b64_tr_b16 over a 16-lane group: lane s supplies the address of 4
+// consecutive columns (o .. o+3) of reduction row kb + s/4; lane L receives
+// column ob + L of rows kb .. kb+3.  Two such reads (rows +0..3 and +4..7)
+// give the 8 reduction elements of one MFMA operand lane.
+template <int BO>
+struct Frag<BO, false> {
+    static MOE_DEVICE void load(bf16x8_t& v, const bf16_t* lds, int o0, int k0) {
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, s = lane & 15;
+        const int o = o0 + ((g & 1) << 4) + ((s & 3) << 2);
+        const int k = k0 + ((g >> 1) << 3) + (s >> 2);
+        const int cc = ((o >> 3) ^ swz_mn(k)) << 3;   // swz_mn(k) == swz_mn(k + 4)
+        const uint32_t a = lds_addr(lds + k * BO + cc + (o & 7));
+        u32x2_t lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a), "i"(4 * BO * 2));
+        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        v = __builtin_bit_cast(bf16x8_t, w);
+    }
+};
+
+// Wait for every outstanding LDS read; the fragments pass through the asm so
+// that no use of them can be scheduled above the wait.
+template <int TM, int TN>
+MOE_DEVICE void lds_wait(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(a[t]));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(b[t]));
+}
+
+// ---------------------------------------------------------------------------
+// The tile engine: C[BM][BN] = A[BM][red] * B[red][BN], fp32 accumulation.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR>
+struct Engine {
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(WM * WN == kThreads / 64 && TM >= 1 && TN >= 1, "wave grid");
+    f32x16_t acc[TM][TN];
+
+    MOE_DEVICE void zero() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+
+    MOE_DEVICE void load_frags(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN], const bf16_t* la, const bf16_t* lb,
+                               int ks) const {
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) Frag<BM, A_KMAJOR>::load(a[t], la, wm * WTM + t * 32, ks * 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) Frag<BN, B_KMAJOR>::load(b[t], lb, wn * WTN + t * 32, ks * 16);
+    }
+
+    // MFMAs of one sub-step; hook(m) runs after the m-th MFMA of the step
+    // (m counts across sub-steps), so loads can be spread between MFMAs.
+    template <class Hook>
+    MOE_DEVICE void mfmas(const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN], int ks, Hook& hook) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+                hook(ks * TM * TN + i * TN + j);
+            }
+    }
+
+    // One reduction step from LDS: fragments of sub-step ks+1 are read while
+    // the MFMAs of sub-step ks run.
+    template <class Hook>
+    MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb, Hook& hook) {
+        static_assert(BK / 16 == 2 || BK / 16 == 4, "sub-steps");
+        bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+        load_frags(a0, b0, la, lb, 0);
+        lds_wait(a0, b0);
+        load_frags(a1, b1, la, lb, 1);
+        mfmas(a0, b0, 0, hook);
+        lds_wait(a1, b1);
+        if constexpr (BK / 16 == 4) {
+            load_frags(a0, b0, la, lb, 2);
+            mfmas(a1, b1, 1, hook);
+            lds_wait(a0, b0);
+            load_frags(a1, b1, la, lb, 3);
+            mfmas(a0, b0, 2, hook);
+            lds_wait(a1, b1);
+            mfmas(a1, b1, 3, hook);
+        } else {
+            mfmas(a1, b1, 1, hook);
+        }
+    }
+
+    // lane holds rows (l%32) and 4 consecutive columns per (i, j, g)
+    MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid) const {
+        const int lane = threadIdx.x & 63;
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            if (row >= rows_valid) continue;
+            bf16_t* orow = out + (int64_t)row * ld;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    if (col < cols_valid) {
+                        u32x2_t pk;
+                        pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                        pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                        *reinterpret_cast<u32x2_t*>(orow + col) = pk;
+                    }
+                }
+        }
+    }
+
+    // Gate_up tile with paired columns (see Dma::init): fragment 0 of a wave
+    // holds the gate values G and fragment 1 the up values U of the same 32
+    // output columns.  Writes A = SiLU(G) * U (rounded once, from the fp32
+    // accumulators) and, when h is given, G and U themselves to h[:, c] and
+    // h[:, pair + c].
+    MOE_DEVICE void store_swiglu(bf16_t* __restrict__ a, int64_t lda, bf16_t* __restrict__ h,
+                                 int64_t ldh, int pair, int rows_valid, int cols_valid) const {
+        static_assert(TN == 2, "one gate and one up fragment per wave");
+        const int lane = threadIdx.x & 63;
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            if (row >= rows_valid) continue;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = wn * 32 + g * 8 + (lane >> 5) * 4;
+                if (col >= cols_valid) continue;
+                float av[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float gv = acc[i][0][4 * g + c], uv = acc[i][1][4 * g + c];
+                    av[c] = gv * silu_sigmoid(gv) * uv;
+                }
+                u32x2_t pk;
+                pk[0] = pack_bf16x2(av[0], av[1]);
+                pk[1] = pack_bf16x2(av[2], av[3]);
+                *reinterpret_cast<u32x2_t*>(a + (int64_t)row * lda + col) = pk;
+                if (h) {
+                    u32x2_t pg, pu;
+                    pg[0] = pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]);
+                    pg[1] = pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]);
+                    pu[0] = pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]);
+                    pu[1] = pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]);
+                    bf16_t* hr = h + (int64_t)row * ldh + col;
+                    *reinterpret_cast<u32x2_t*>(hr) = pg;
+                    *reinterpret_cast<u32x2_t*>(hr + pair) = pu;
+                }
+            }
+        }
+    }
+};
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+MOE_DEVICE void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// One output tile over a ring of kNST LDS stages.  Per step s: wait for this
+// wave's copies of step s (the kNST-2 later steps stay in flight), barrier
+// (all copies of step s landed; step s-1 fully read), then run step s while
+// refilling the stage read at step s-1 with step s+kNST-1, one load after
+// every few MFMAs so the memory pipe and the MFMA pipe work side by side.
+// Steps past the end still "load", with every lane out of range: that only
+// writes zeros into a stage nobody reads again, and keeps the number of
+// loads in flight constant (no data-dependent wait counts, no branches).
+// `smem` holds kNST stages of [A tile | B tile].
+// `store(eng)` writes the result; rows_valid / cols_valid (in tile columns)
+// decide which waves have any work.
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Store>
+MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
+                          int64_t ldb, int b_olim, int b_pair, int red_len, int rows_valid,
+                          int cols_valid, bf16_t* smem, const Store& store) {
+    using DA = Dma<BM, A_KMAJOR>;
+    using DB = Dma<BN, B_KMAJOR>;
+    constexpr int kStage = (BM + BN) * BK;       // elements per stage
+    constexpr int kPer = DA::kInst + DB::kInst;  // loads per wave per stage
+    DA da;
+    DB db;
+    da.init(lda, a_olim);
+    db.init(ldb, b_olim, b_pair);
+    Engine<BM, BN, WM, WN, A_KMAJOR, B_KMAJOR> eng;
+    eng.zero();
+    const int nk = (red_len + BK - 1) / BK;
+    auto issue = [&](int step) {
+        bf16_t* st = smem + (step % kNST) * kStage;
+        da.issue(DA::stage(a_base, lda, step), st, red_len - step * BK);
+        db.issue(DB::stage(b_base, ldb, step), st + BM * BK, red_len - step * BK);
+    };
+    // the MFMAs of one step; load q goes after MFMA (q+1)*kMfmaPerStep/kPer - 1
+    constexpr int kMfmaPerStep = (BK / 16) * (BM / WM / 32) * (BN / WN / 32);
+    static_assert(kMfmaPerStep >= kPer, "load spacing");
+#pragma unroll
+    for (int p = 0; p < kNST - 1; ++p) issue(p);
+    // this wave's corner of the output tile; two copies of the step loop
+    // (active and idle wave), so the common one carries no branch
+    const int wrow0 = (wave_id() / WN) * (BM / WM), wcol0 = (wave_id() % WN) * (BN / WN);
+    auto run_steps = [&](auto active_tag) {
+    for (int s = 0; s < nk; ++s) {
+        wait_vmcnt<(kNST - 2) * kPer>();
+        __builtin_amdgcn_s_barrier();
+        const int nxt = s + kNST - 1;
+        bf16_t* nst = smem + (nxt % kNST) * kStage;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(DA::stage(a_base, lda, nxt));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b_base, ldb, nxt));
+        const int left = red_len - nxt * BK;
+        auto hook = [&](int m) {
+#pragma unroll
+            for (int q = 0; q < kPer; ++q) {
+                if (m == (q + 1) * kMfmaPerStep / kPer - 1) {
+                    if (q < DA::kInst) da.issue_one(q, ra, nst, left);
+                    else db.issue_one(q - DA::kInst, rb, nst + BM * BK, left);
+                }
+            }
+        };
+        if constexpr (decltype(active_tag)::value) {
+            const bf16_t* st = smem + (s % kNST) * kStage;
+            eng.compute(st, st + BM * BK, hook);
+        } else {
+#pragma unroll
+            for (int m = 0; m < kMfmaPerStep; ++m) hook(m);
+        }
+    }
+    };
+    if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
+    else run_steps(std::false_type{});
+    wait_vmcnt<0>();  // no LDS write may outlive the workgroup
+    store(eng);
+}
+
+// Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
+// contiguous range of logical tiles so tiles that share operands share an L2.
+MOE_DEVICE int xcd_remap(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, j = bid >> 3;
+    return x * q + (x < r ? x : r) + j;
+}
+
+#ifndef MOEGMM_BM
+#define MOEGMM_BM 256
+#endif
+#ifndef MOEGMM_BN
+#define MOEGMM_BN 256
+#endif
+#ifndef MOEGMM_WM
+#define MOEGMM_WM 2
+#endif
+#ifndef MOEGMM_WN
+#define MOEGMM_WN 4
+#endif
+constexpr int kBM = MOEGMM_BM, kBN = MOEGMM_BN, kWM = MOEGMM_WM, kWN = MOEGMM_WN;
+constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
+// two workgroups per CU when the LDS ring and the accumulators allow it: one
+// workgroup's epilogue and first loads then overlap the other's MFMAs
+constexpr int kAccRegs = (kBM / kWM) * (kBN / kWN) / 64;
+constexpr int kOccupancy = (kSmemElems * 2 <= 80 * 1024 && kAccRegs <= 128) ? 2 : 1;
+static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the last stage");
+
+// ---------------------------------------------------------------------------
+// The output tile of this workgroup in a row-grouped GEMM.  Tiles are
+// (expert M-tile, N-tile) pairs: sum over experts of ceil(n_e/BM) M-tiles
+// times NT N-tiles, in logical order expert-major, then walked XCD-aware.
+// `sched` is LDS for 3*kMaxExperts ints (dead once this returns).  Returns
+// false, uniformly across the block, for surplus workgroups.
+// ---------------------------------------------------------------------------
+struct RowTile {
+    int e, row0, rows_valid, nt;
+};
+
+template <int BM>
+MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int64_t M_cap, int NT,
+                              int* sched, int64_t* s_scan, int32_t* dev_err, RowTile& rt) {
+    int* s_off = sched;
+    int* s_cnt = s_off + kMaxExperts;
+    int* s_tst = s_cnt + kMaxExperts;
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t my_tiles = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) my_tiles += (s_cnt[e0 + i] + BM - 1) / BM;
+    int64_t total_mt;
+    int64_t run = block_exclusive_scan<int64_t>(my_tiles, s_scan, &total_mt);
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) {
+            s_tst[e0 + i] = (int)run;
+            run += (s_cnt[e0 + i] + BM - 1) / BM;
+        }
+    __syncthreads();
+
+    const int ntiles = (int)total_mt * NT;
+    if ((int)blockIdx.x >= ntiles) return false;  // uniform across the block
+#if defined(MOEGMM_NO_XCD_REMAP)
+    const int t = blockIdx.x;
+#else
+    const int t = xcd_remap(blockIdx.x, ntiles);
+#endif
+    const int mt = t / NT;
+    int lo = 0, hi = E - 1;  // last expert whose first tile is <= mt
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tst[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    // block-uniform values read from LDS: keep them in scalar registers
+    rt.e = __builtin_amdgcn_readfirstlane(lo);
+    rt.row0 = __builtin_amdgcn_readfirstlane(s_off[rt.e] + (mt - s_tst[rt.e]) * BM);
+    const int row_end = __builtin_amdgcn_readfirstlane(s_off[rt.e] + s_cnt[rt.e]);
+    rt.rows_valid = row_end - rt.row0 < BM ? row_end - rt.row0 : BM;
+    rt.nt = t % NT;
+    __syncthreads();  // schedule arrays are dead from here on
+    return true;
+}
+
+// Grid bound for a row-grouped launch: every expert may end in a partial tile.
+inline int64_t row_tiles_bound(int64_t M_cap, int64_t E, int bm) { return (M_cap + bm - 1) / bm + E; }
+
+}  // namespace
+
+}  // namespace moegmm

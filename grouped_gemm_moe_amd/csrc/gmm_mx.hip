@@ -1,0 +1,364 @@
+// MXFP8 grouped matmul kernels for gfx950 (the A8W8-FP variant of the
+// expert block).
+//
+// What is computed ("MegaMoE", A8W8-FP scenario): operands are MX-quantised
+// in groups of 32 along the reduction dimension -- E4M3 codes plus one E8M0
+// scale per group -- and the matmul dequantises inside:
+//   gmm_mx        y[rows_e]  = DQ(x[rows_e]) @ DQ(w[e])^T          (bf16 out)
+//   gmm_mx_swiglu [G | U]    = DQ(x[rows_e]) @ DQ(w1[e])^T,
+//                 A = SiLU(G) * U,  (aq, as) = Q_MX(A)     (MX out, for GMM2)
+// Weights are stored reduction-contiguous, w[e] as [N][K] codes with scales
+// [N][ld] (the parameter table of that scenario gives the hidden size as the
+// last dimension of weight1); x is [M][K] codes with scales [M][ld].  Scale
+// rows are padded to a multiple of 16 bytes; bytes past ceil(K/32) are never
+// used.  For gmm_mx_swiglu, w1[e] holds the I gate rows, then the I up rows.
+//
+// Design: the bf16 tile engine (gmm_engine.h) carries over with fp8 bytes in
+// place of bf16 pairs.  A 64-byte LDS row of one stage holds 64 reduction
+// elements -- two MX groups -- and feeds one v_mfma_scale_f32_32x32x64_f8f6f4
+// per fragment pair: lane l holds half of each of the two groups of row
+// l%32 (two ds_read_b128) and passes the scale byte of group l/32 to the
+// MFMA, which applies both operands' 2^(s-127) to the exact fp8 products.  So a stage
+// moves the same bytes as a bf16 stage and the MFMAs take the same time, for
+// twice the flops.  Scales travel HBM -> LDS as their own 16-byte-per-lane DMA
+// (one instruction per wave every 8 steps covers 16 groups of all 256 A rows
+// and 256 B rows) into a two-slot ring beside the operand ring.
+#include "gmm_engine.h"
+#include "launch.h"
+#include "mx.h"
+
+namespace moegmm {
+
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+static_assert(BK == 32, "an MX stage is 64 bytes: two scale groups");
+static_assert(kThreads == kBM + kBN, "one scale row per thread");
+constexpr int kStepsPerScaleLoad = 8;                    // 16 groups of 32 = 8 steps of 64
+constexpr int kScaleSlot = (kBM + kBN) * 16;             // bytes per scale slot
+
+// ---------------------------------------------------------------------------
+// Scale rows HBM -> LDS.  Thread t < kBM loads 16 scale bytes of A row t,
+// thread kBM + t those of B row t (with the gate/up pairing of Dma::init);
+// LDS slot layout: [kBM A rows][16] then [kBN B rows][16].
+// ---------------------------------------------------------------------------
+struct ScaleDma {
+    uint32_t off;
+    bool ok;
+
+    MOE_DEVICE void init(int64_t ld_a, int a_olim, int64_t ld_b, int b_olim, int b_pair) {
+        const int t = threadIdx.x;
+        if (t < kBM) {
+            off = (uint32_t)(t * ld_a);
+            ok = t < a_olim;
+        } else {
+            const int o = t - kBM;
+            int vo = o, go = o;
+            if (b_pair > 0) {
+                vo = (o >> 6) * 32 + (o & 31);
+                go = ((o >> 5) & 1) * b_pair + vo;
+            }
+            off = (uint32_t)(go * ld_b);
+            ok = vo < b_olim;
+        }
+    }
+    // group g: scale bytes 16g .. 16g+15 of every row; nblocks = ceil(K/32)
+    MOE_DEVICE void issue(const uint8_t* a_sc, const uint8_t* b_sc, int g, int nblocks,
+                          uint8_t* slot) const {
+        const int wid = wave_id();
+        const uint8_t* base = (wid < kBM / 64 ? a_sc : b_sc) + 16 * g;
+        const uint32_t v = ok && 16 * g < nblocks ? off : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base), (LDS_AS void*)(slot + wid * 1024),
+                                                 16, v, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The MX engine: the bf16 engine's accumulators and epilogues, fed by scaled
+// fp8 MFMAs.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN>
+struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
+    using Base = Engine<BM, BN, WM, WN, true, true>;
+    static constexpr int TM = Base::TM, TN = Base::TN, WTM = Base::WTM, WTN = Base::WTN;
+    static_assert(TM % 2 == 0, "fragments are read in two halves");
+
+    // The operand layout of the 32x32x64 fp8 MFMA: lane l holds row l%32,
+    // reduction elements 16*(l/32) .. +15 in its first four registers and
+    // 32 + 16*(l/32) .. +15 in the last four; the scale lane l passes is
+    // that of group l/32 of its row (elements 32*(l/32) .. +31), which lanes
+    // l and l^32 share.  So lane l reads logical 16-byte chunks l/32 and
+    // l/32 + 2 of the 64-byte stage row -- the chunks the bf16 engine reads
+    // for its two 16-deep sub-steps.
+    static MOE_DEVICE void frag(i32x8_t& v, const bf16_t* lds, int o0) {
+        const int lane = threadIdx.x & 63;
+        const int o = o0 + (lane & 31);
+        const int c = lane >> 5;
+        const int sw = swz_k(o);
+        u32x4_t lo, hi;
+        asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(lds_addr(lds + o * BK + ((c ^ sw) << 3))));
+        asm volatile("ds_read_b128 %0, %1"
+                     : "=v"(hi)
+                     : "v"(lds_addr(lds + o * BK + (((c + 2) ^ sw) << 3))));
+        v = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+    static MOE_DEVICE void scale(uint32_t& s, const uint8_t* sl, int o0, int kb) {
+        const int o = o0 + (threadIdx.x & 31);
+        asm volatile("ds_read_u8 %0, %1" : "=v"(s) : "v"(lds_addr(sl + o * 16 + kb)));
+    }
+
+    // One 64-element step.  kb: this lane's group within the scale slot;
+    // kb_ok false for a group past ceil(K/32) (its codes are zero; its scale
+    // byte, padding, is replaced by 2^0).
+    template <class Hook>
+    MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb, const uint8_t* sla, const uint8_t* slb,
+                            int kb, bool kb_ok, Hook& hook) {
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+        i32x8_t a[TM], b[TN];
+        uint32_t sa[TM], sb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            frag(b[j], lb, wn * WTN + j * 32);
+            scale(sb[j], slb, wn * WTN + j * 32, kb);
+        }
+#pragma unroll
+        for (int i = 0; i < TM / 2; ++i) {
+            frag(a[i], la, wm * WTM + i * 32);
+            scale(sa[i], sla, wm * WTM + i * 32, kb);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(b[j]), "+v"(sb[j]));
+#pragma unroll
+        for (int i = 0; i < TM / 2; ++i) asm volatile("" : "+v"(a[i]), "+v"(sa[i]));
+#pragma unroll
+        for (int i = TM / 2; i < TM; ++i) {
+            frag(a[i], la, wm * WTM + i * 32);
+            scale(sa[i], sla, wm * WTM + i * 32, kb);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sb[j] = kb_ok ? sb[j] : 127u;
+#pragma unroll
+        for (int i = 0; i < TM / 2; ++i) sa[i] = kb_ok ? sa[i] : 127u;
+        mfmas(a, b, sa, sb, 0, TM / 2, hook);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = TM / 2; i < TM; ++i) {
+            asm volatile("" : "+v"(a[i]), "+v"(sa[i]));
+            sa[i] = kb_ok ? sa[i] : 127u;
+        }
+        mfmas(a, b, sa, sb, TM / 2, TM, hook);
+    }
+
+    template <class Hook>
+    MOE_DEVICE void mfmas(const i32x8_t (&a)[TM], const i32x8_t (&b)[TN], const uint32_t (&sa)[TM],
+                          const uint32_t (&sb)[TN], int i0, int i1, Hook& hook) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                // operands swapped, as in the bf16 engine: B is the hardware A
+                this->acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    b[j], a[i], this->acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+                hook(i * TN + j);
+            }
+    }
+
+    // Gate_up tile with paired rows: A = SiLU(G) * U in fp32, then Q_MX over
+    // each row's 32 columns of this wave (one MX group: this lane's 16 values
+    // and those of lane l^32).  Writes codes to aq (ld bytes) and the group's
+    // scale byte to as[row][blk0 + wn].
+    MOE_DEVICE void store_swiglu_mx(uint8_t* __restrict__ aq, int64_t ldq, uint8_t* __restrict__ as,
+                                    int64_t ld_as, int blk0, int rows_valid, int cols_valid) const {
+        static_assert(TN == 2, "one gate and one up fragment per wave");
+        const int lane = threadIdx.x & 63;
+        const int wid = threadIdx.x >> 6;
+        const int wm = wid / WN, wn = wid % WN;
+        if (wn * 32 >= cols_valid) return;  // uniform across the wave
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + (lane & 31);
+            float av[16];
+            float amax = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float gv = this->acc[i][0][r], uv = this->acc[i][1][r];
+                av[r] = gv * silu_sigmoid(gv) * uv;
+                amax = fmaxf(amax, fabsf(av[r]));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+            const uint32_t sbyte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(sbyte);
+            if (row < rows_valid) {
+                uint8_t* orow = aq + (int64_t)row * ldq + wn * 32 + (lane >> 5) * 4;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<uint32_t*>(orow + g * 8) =
+                        e4m3_pack4(av[4 * g] * inv, av[4 * g + 1] * inv, av[4 * g + 2] * inv,
+                                   av[4 * g + 3] * inv);
+                if (lane < 32) as[(int64_t)row * ld_as + blk0 + wn] = (uint8_t)sbyte;
+            }
+        }
+    }
+};
+
+// One output tile over the ring, as gemm_tile (gmm_engine.h), plus the scale
+// ring: the scale group of step s (s/8) sits in slot (s/8)&1, loaded ahead
+// with the operands of its first step.  Every wave issues the same loads in
+// the same order, so the vmcnt wait of gemm_tile still covers step s: a
+// scale load among the newer loads only makes that wait conservative.
+template <int BM, int BN, int WM, int WN, class Store>
+MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a_sc, int64_t ld_as,
+                             const uint8_t* b_base, int b_olim, int b_pair, const uint8_t* b_sc,
+                             int64_t ld_bs, int K, int rows_valid, int cols_valid, bf16_t* smem,
+                             uint8_t* ssc, const Store& store) {
+    using DA = Dma<BM, true>;
+    using DB = Dma<BN, true>;
+    constexpr int kStage = (BM + BN) * BK;
+    constexpr int kPer = DA::kInst + DB::kInst;
+    const bf16_t* a16 = reinterpret_cast<const bf16_t*>(a_base);
+    const bf16_t* b16 = reinterpret_cast<const bf16_t*>(b_base);
+    const int64_t ld16 = K / 2;  // row length in 2-byte units
+    const int red = K / 2;
+    const int nblocks = K / kMxGroup;
+    DA da;
+    DB db;
+    ScaleDma sd;
+    da.init(ld16, a_olim);
+    db.init(ld16, b_olim, b_pair);
+    sd.init(ld_as, a_olim, ld_bs, b_olim, b_pair);
+    EngineMx<BM, BN, WM, WN> eng;
+    eng.zero();
+    const int nk = (red + BK - 1) / BK;
+    auto issue = [&](int step) {
+        bf16_t* st = smem + (step % kNST) * kStage;
+        da.issue(DA::stage(a16, ld16, step), st, red - step * BK);
+        db.issue(DB::stage(b16, ld16, step), st + BM * BK, red - step * BK);
+    };
+    constexpr int kMfmaPerStep = EngineMx<BM, BN, WM, WN>::TM * EngineMx<BM, BN, WM, WN>::TN;
+    static_assert(kMfmaPerStep >= kPer, "load spacing");
+    sd.issue(a_sc, b_sc, 0, nblocks, ssc);
+#pragma unroll
+    for (int p = 0; p < kNST - 1; ++p) issue(p);
+    const int lane_grp = (threadIdx.x >> 5) & 1;
+    const int wrow0 = (wave_id() / WN) * (BM / WM), wcol0 = (wave_id() % WN) * (BN / WN);
+    auto run_steps = [&](auto active_tag) {
+        for (int s = 0; s < nk; ++s) {
+            wait_vmcnt<(kNST - 2) * kPer>();
+            __builtin_amdgcn_s_barrier();
+            const int nxt = s + kNST - 1;
+            if (nxt % kStepsPerScaleLoad == 0) {
+                const int g = nxt / kStepsPerScaleLoad;
+                sd.issue(a_sc, b_sc, g, nblocks, ssc + (g & 1) * kScaleSlot);
+            }
+            bf16_t* nst = smem + (nxt % kNST) * kStage;
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(DA::stage(a16, ld16, nxt));
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b16, ld16, nxt));
+            const int left = red - nxt * BK;
+            auto hook = [&](int m) {
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    if (m == (q + 1) * kMfmaPerStep / kPer - 1) {
+                        if (q < DA::kInst) da.issue_one(q, ra, nst, left);
+                        else db.issue_one(q - DA::kInst, rb, nst + BM * BK, left);
+                    }
+                }
+            };
+            if constexpr (decltype(active_tag)::value) {
+                const bf16_t* st = smem + (s % kNST) * kStage;
+                const uint8_t* sl = ssc + ((s / kStepsPerScaleLoad) & 1) * kScaleSlot;
+                const int kb = 2 * s + lane_grp;
+                eng.compute(st, st + BM * BK, sl, sl + BM * 16, kb & 15, kb < nblocks, hook);
+            } else {
+#pragma unroll
+                for (int m = 0; m < kMfmaPerStep; ++m) hook(m);
+            }
+        }
+    };
+    if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
+    else run_steps(std::false_type{});
+    wait_vmcnt<0>();  // no LDS write may outlive the workgroup
+    store(eng);
+}
+
+// ---------------------------------------------------------------------------
+// Row-grouped MX GEMM: tiles (expert M-tile, N-tile) as in gmm_rows_kernel.
+//   SWIGLU false: y [M_cap, N] bf16 = DQ(x) @ DQ(w[e])^T, w[e] [N][K].
+//   SWIGLU true:  N = 2I weight rows; a tile covers kBN/2 output columns c,
+//                 reading gate rows c and up rows I + c; writes (aq, as).
+// ---------------------------------------------------------------------------
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
+    const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, int64_t ld_xs,
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ WS, int64_t ld_ws,
+    const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
+    bf16_t* __restrict__ Y, uint8_t* __restrict__ AQ, uint8_t* __restrict__ AS, int64_t ld_as,
+    int32_t* dev_err) {
+    constexpr int kCols = SWIGLU ? kBN / 2 : kBN;  // output columns per tile
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
+    __shared__ __attribute__((aligned(16))) uint8_t ssc[2 * kScaleSlot];
+    __shared__ int64_t s_scan[kThreads / 64];
+    const int Ncols = SWIGLU ? N / 2 : N;
+    const int NT = (Ncols + kCols - 1) / kCols;
+    RowTile rt;
+    if (!find_row_tile<kBM>(group_list, E, M_cap, NT,
+                            reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK), s_scan,
+                            dev_err, rt))
+        return;
+    const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
+    const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
+    const int cols_left = Ncols - n0;
+    const uint8_t* We = W + ((int64_t)e * N + n0) * K;
+    const uint8_t* Se = WS + ((int64_t)e * N + n0) * ld_ws;
+    const uint8_t* Xt = X + (int64_t)row0 * K;
+    const uint8_t* XSt = XS + (int64_t)row0 * ld_xs;
+    if constexpr (SWIGLU) {
+        const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
+        gemm_tile_mx<kBM, kBN, kWM, kWN>(
+            Xt, rows_valid, XSt, ld_xs, We, cols_left, Ncols, Se, ld_ws, K, rows_valid, tile_cols,
+            smem, ssc, [&](const auto& eng) {
+                eng.store_swiglu_mx(AQ + (int64_t)row0 * Ncols + n0, Ncols,
+                                    AS + (int64_t)row0 * ld_as, ld_as, n0 / kMxGroup, rows_valid,
+                                    cols_left);
+            });
+    } else {
+        bf16_t* y = Y + (int64_t)row0 * N + n0;
+        gemm_tile_mx<kBM, kBN, kWM, kWN>(
+            Xt, rows_valid, XSt, ld_xs, We, cols_left, 0, Se, ld_ws, K, rows_valid, cols_left, smem,
+            ssc, [&](const auto& eng) { eng.store(y, N, rows_valid, cols_left); });
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
+                             const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
+                             int64_t M_cap, int64_t K, int64_t N, uint16_t* y, int32_t* dev_err,
+                             hipStream_t stream) {
+    if (M_cap == 0) return hipSuccess;
+    const int64_t NT = (N + kBN - 1) / kBN;
+    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    hipLaunchKernelGGL(gmm_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       xq, xs, ld_xs, wq, ws, ld_ws, group_list, (int)E, M_cap, (int)K, (int)N, y,
+                       nullptr, nullptr, (int64_t)0, dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                                    const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                                    const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                                    int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                                    int32_t* dev_err, hipStream_t stream) {
+    if (M_cap == 0) return hipSuccess;
+    const int64_t NT = (I + kBN / 2 - 1) / (kBN / 2);
+    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
+                       (int)(2 * I), nullptr, aq, as, ld_as, dev_err);
+    return hipGetLastError();
+}
+
+}  // namespace moegmm

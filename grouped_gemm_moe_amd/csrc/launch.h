@@ -10,10 +10,13 @@ namespace moegmm {
 
 // permute.hip
 size_t permute_workspace_bytes(int64_t S, int64_t E);
+// The gather writes bf16 rows to x_perm, or, when xq is given, their MX
+// quantisation to xq (codes) and xs (scales, row stride ld_xs).
 hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
-                          int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
-                          int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
-                          int32_t* dev_err, hipStream_t stream);
+                          int64_t H, int64_t E, uint16_t* x_perm, uint8_t* xq, uint8_t* xs,
+                          int64_t ld_xs, int32_t* row_id_map, int32_t* sorted_slot,
+                          int64_t* tokens_per_expert, void* ws, int32_t* dev_err,
+                          hipStream_t stream);
 
 // gmm.hip
 size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
@@ -40,6 +43,21 @@ hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,
                                     const int64_t* group_list, int64_t E, int64_t M_cap,
                                     int64_t K, int64_t I, uint16_t* a, uint16_t* h,
                                     int32_t* dev_err, hipStream_t stream);
+
+// gmm_mx.hip (MXFP8)
+hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
+                             const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
+                             int64_t M_cap, int64_t K, int64_t N, uint16_t* y, int32_t* dev_err,
+                             hipStream_t stream);
+hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                                    const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                                    const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                                    int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                                    int32_t* dev_err, hipStream_t stream);
+
+// mx_quant.hip
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ld_s, uint8_t* q,
+                              uint8_t* s, hipStream_t stream);
 
 // elementwise.hip
 hipError_t launch_swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,

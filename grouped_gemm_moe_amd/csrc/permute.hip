@@ -21,11 +21,14 @@
 //   4. gather  -- copies token rows to their permuted rows with 16-byte loads
 //                 and stores (coalesced inside each row): each piece of a
 //                 token row is loaded once and stored to all of the token's
-//                 slot rows; four loads in flight per thread.
+//                 slot rows; four loads in flight per thread.  The MXFP8
+//                 variant quantises the row as it goes (E4M3 codes + E8M0
+//                 scales).
 // For at most 4096 slots (decode-sized calls) steps 1-3 run as one
 // single-workgroup kernel, so the whole permute is two launches.
 #include "common.h"
 #include "launch.h"
+#include "mx.h"
 
 namespace moegmm {
 
@@ -289,6 +292,75 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
     }
 }
 
+// The same gather with MX quantisation of each token row on the way (row-wise
+// Q_MX commutes with the gather, so a top-k token is quantised once): four
+// lanes own one group of 32 (16 bytes of bf16 each) and meet on its maximum
+// with two xor shuffles; each lane stores 8 codes, and the quad's first lane
+// the scale byte, to every slot row of the token.
+__global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t T, int top_k,
+    int64_t H, int tpb, int64_t ld_s, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+    __shared__ int32_t rows[kGatherMaxSlots > 32 ? kGatherMaxSlots : 32];  // top_k <= 32
+    const int64_t S = T * top_k;
+    const int64_t t0 = (int64_t)blockIdx.x * tpb;
+    const int nslots = tpb * top_k;
+    if ((int)threadIdx.x < nslots) {
+        const int64_t s = t0 * top_k + threadIdx.x;
+        const int32_t r = (s < S) ? row_id_map[s] : -1;
+        rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
+    }
+    __syncthreads();
+    const int64_t cpr = H / 8;  // 16-byte pieces per row, a multiple of 4
+    const int64_t tok = T - t0 < tpb ? T - t0 : tpb;
+    const int64_t total = tok * cpr;
+    // every lane runs the same number of iterations (shuffles need the quad)
+    constexpr int64_t kStep = (int64_t)kPermThreads * kGatherUnroll;
+    const int64_t iters = (total + kStep - 1) / kStep;
+    for (int64_t it = 0; it < iters; ++it) {
+        const int64_t i0 = it * kStep + threadIdx.x;
+        u32x4_t v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            v[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (i < total) {
+                const int64_t tt = i / cpr, c = i - tt * cpr;
+                v[u] = ld16(x + (t0 + tt) * H + c * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            float f[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                f[2 * c] = bf16_lo(v[u][c]);
+                f[2 * c + 1] = bf16_hi(v[u][c]);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            if (i < total) {  // whole quads agree: total % 4 == 0
+                const uint32_t sb = mx_scale_byte(amax);
+                const float inv = mx_inv_scale(sb);
+                u32x2_t o;
+                o[0] = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+                o[1] = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+                const int64_t tt = i / cpr, c = i - tt * cpr;
+                for (int k = 0; k < top_k; ++k) {
+                    const int32_t r = rows[tt * top_k + k];
+                    if (r >= 0) {
+                        *reinterpret_cast<u32x2_t*>(xq + (int64_t)r * H + c * 8) = o;
+                        if ((c & 3) == 0) xs[(int64_t)r * ld_s + (c >> 2)] = (uint8_t)sb;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Tokens per gather block: up to kGatherMaxSlots slots, but at most T/256
 // tokens so that the launch still has some 256 blocks to spread.  (16 slots
 // measured best on the decode, prefill and top-1 EP shapes; 32 and 64 lose
@@ -311,9 +383,10 @@ size_t permute_workspace_bytes(int64_t S, int64_t E) {
 }
 
 hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
-                          int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
-                          int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
-                          int32_t* dev_err, hipStream_t stream) {
+                          int64_t H, int64_t E, uint16_t* x_perm, uint8_t* xq, uint8_t* xs,
+                          int64_t ld_xs, int32_t* row_id_map, int32_t* sorted_slot,
+                          int64_t* tokens_per_expert, void* ws, int32_t* dev_err,
+                          hipStream_t stream) {
     const int64_t S = T * top_k;
     const int64_t chunk = permute_chunk(S);
     const int64_t nblk = (S + chunk - 1) / chunk;
@@ -334,8 +407,12 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
     if (nblk > 0) {
         const int tpb = gather_tokens_per_block(T, top_k);
         const int64_t gblk = (T + tpb - 1) / tpb;
-        hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)gblk), dim3(kPermThreads), 0,
-                           stream, x, row_id_map, T, (int)top_k, H, tpb, x_perm);
+        if (xq)
+            hipLaunchKernelGGL(permute_gather_mx_kernel, dim3((unsigned)gblk), dim3(kPermThreads),
+                               0, stream, x, row_id_map, T, (int)top_k, H, tpb, ld_xs, xq, xs);
+        else
+            hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)gblk), dim3(kPermThreads), 0,
+                               stream, x, row_id_map, T, (int)top_k, H, tpb, x_perm);
     }
     return hipGetLastError();
 }

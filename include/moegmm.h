@@ -20,6 +20,16 @@
  *               section 4.1 (-1 marks an invalid slot), section 4.3 (null and
  *               invalid arguments are reported before any work), section 6.2
  *               (FP32 accumulation over a token's top-k slots, one cast back).
+ *   [MX]        "MegaMoE": the A8W8-FP scenario -- tokens gathered per expert
+ *               are MX-quantised (groups of 32, FP8 elements, FLOAT8_E8M0
+ *               scales), GMM1 dequantises inside the matmul, the activation
+ *               output is MX-quantised again for GMM2; its parameter table
+ *               (activation scales of shape (rows, CeilDiv(H, 32)), weights
+ *               with the hidden size as the last dimension).  The group
+ *               quantiser itself follows the OCP Microscaling (MX) v1.0
+ *               definition: shared exponent floor(log2(max|v|)) - 8 (clamped
+ *               to >= -127; an all-zero group takes -127), E4M3 elements
+ *               rounded to nearest even and saturated at +-448.
  *   [MegaBlocks] "03 · grouped GEMM 路径": section 4.2 -- the grouped GEMM
  *               there needs the group sizes on the host, a device-to-host
  *               synchronisation this library avoids: group_list stays on the
@@ -253,6 +263,79 @@ moe_status moe_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,
 moe_status moe_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, int64_t T,
                            int64_t top_k, int64_t H, uint16_t* dx, int32_t* dev_err,
                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * MXFP8 (A8W8-FP) calls.  [MX]
+ *
+ * An MX tensor is a pair: codes [rows, K] uint8 (E4M3FN bit patterns,
+ * row-major) and scales [rows, ld_s] uint8 (E8M0: byte b means 2^(b-127)),
+ * one scale per group of 32 consecutive codes of a row.  The scale row
+ * stride ld_s is at least ceil(K/32) and a multiple of 16; scale bytes past
+ * ceil(K/32) are padding, never read as scales and never written.  K must be
+ * a multiple of 32.  Codes and scale pointers must be 16-byte aligned.
+ * Weights are stored reduction-contiguous: w[e] is [N, K] (N output
+ * columns), so an expert's weight is an MX tensor of N rows.
+ * ---------------------------------------------------------------------- */
+
+/* ------------------------------------------------------------------------
+ * mx_quantize -- Q_MX of each row of a bf16 matrix:
+ *   x [rows, K] bf16; q [rows, K] codes OUT, s [rows, ld_s] scales OUT.
+ * Exact: the decisions depend only on the bf16 inputs.  Used for
+ * activations and to prepare MXFP8 weights ([E*N, K] rows).
+ * ---------------------------------------------------------------------- */
+moe_status mx_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ld_s, uint8_t* q,
+                       uint8_t* s, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_mx -- moe_permute whose gather writes Q_MX of each token row:
+ * the same row_id_map / sorted_slot / tokens_per_expert, and
+ *   xq [T*top_k, H] codes OUT, xs [T*top_k, ld_xs] scales OUT
+ * (row r of (xq, xs) = Q_MX(x[sorted_slot[r] / top_k, :])).  [MX] the
+ * tokens gathered per expert are quantised; quantising a row before or after
+ * the gather gives the same bytes, so each token is quantised once.
+ * H must be a multiple of 32.  Workspace as for moe_permute.
+ * ---------------------------------------------------------------------- */
+moe_status moe_permute_mx(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                          int64_t H, int64_t E, uint8_t* xq, uint8_t* xs, int64_t ld_xs,
+                          int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                          void* ws, size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_mx_fwd -- MX grouped matmul:
+ *   y[rows_e, :] = DQ(xq, xs)[rows_e, :] @ DQ(wq[e], ws[e])^T
+ * over the row ranges of group_list ([GMM] 算子语义 loop; [MX] GMM2, with
+ * dequantisation inside the matmul).  fp32 accumulation of the exactly
+ * scaled fp8 products; y rounded once to bf16 (RNE).
+ *
+ *   xq [M_cap, K] codes, xs [M_cap, ld_xs] scales;
+ *   wq [E, N, K] codes, ws [E, N, ld_ws] scales;
+ *   y [M_cap, N] bf16 OUT (rows >= R untouched).
+ * Limits as for gmm_fwd, plus K % 32 == 0.
+ * ---------------------------------------------------------------------- */
+moe_status gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
+                      const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
+                      int64_t M_cap, int64_t K, int64_t N, uint16_t* y, int32_t* dev_err,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_mx_fwd_swiglu -- GMM1 of the A8W8-FP block with the activation and the
+ * requantisation fused:
+ *   [G | U] = DQ(xq, xs)[rows_e, :] @ DQ(w1q[e], w1s[e])^T   (fp32)
+ *   A = SiLU(G) * U                                          (fp32)
+ *   (aq, as) = Q_MX(A)  over groups of 32 columns of A
+ * w1[e] holds the I gate rows first, then the I up rows.  The scale decision
+ * is taken on the fp32 A.  [MX]; [MegaMoE] activation formulas (swiglu).
+ *
+ *   xq [M_cap, K], xs [M_cap, ld_xs]; w1q [E, 2I, K], w1s [E, 2I, ld_w1s];
+ *   aq [M_cap, I] codes OUT, as [M_cap, ld_as] scales OUT (rows >= R and
+ *   scale padding untouched).
+ * Limits as for gmm_fwd_swiglu, plus K % 32 == 0 and I % 32 == 0.
+ * ---------------------------------------------------------------------- */
+moe_status gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                             const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                             const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                             int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                             int32_t* dev_err, void* stream);
 
 #ifdef __cplusplus
 }

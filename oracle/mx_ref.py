@@ -121,9 +121,20 @@ def mx_quantize(a):
     return codes, scales
 
 
+_E4M3_VALUES = None
+
+
+def _e4m3_table() -> np.ndarray:
+    """e4m3_decode of every code, for decoding large tensors by lookup."""
+    global _E4M3_VALUES
+    if _E4M3_VALUES is None:
+        _E4M3_VALUES = e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _E4M3_VALUES
+
+
 def mx_dequantize(codes, scales) -> np.ndarray:
     """(codes [..., K], scales [..., ceil(K/32)]) -> float64 [..., K]."""
-    v = e4m3_decode(codes)
+    v = _e4m3_table()[np.asarray(codes, dtype=np.uint8)]
     K = v.shape[-1]
     s = np.repeat(e8m0_decode(scales), GROUP, axis=-1)[..., :K]
     return v * s
@@ -137,13 +148,12 @@ def mx_dequantize(codes, scales) -> np.ndarray:
 def gmm_mx(xq, xs, wq, ws, group_list) -> np.ndarray:
     """y[rows_e] = DQ(x[rows_e]) @ DQ(w[e])^T with w stored [E, N, K]."""
     x = mx_dequantize(xq, xs)
-    w = mx_dequantize(wq, ws)  # [E, N, K]
     gl = np.asarray(group_list, dtype=np.int64)
     off = np.concatenate([[0], np.cumsum(gl)])
-    y = np.zeros((x.shape[0], w.shape[1]), dtype=np.float64)
+    y = np.zeros((x.shape[0], wq.shape[1]), dtype=np.float64)
     for e, n in enumerate(gl):
-        if n:
-            y[off[e]:off[e] + n] = x[off[e]:off[e] + n] @ w[e].T
+        if n:  # an empty expert's weights are never read
+            y[off[e]:off[e] + n] = x[off[e]:off[e] + n] @ mx_dequantize(wq[e], ws[e]).T
     return y
 
 

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input",
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
-              "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version"]:
+              "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
+              "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu"]:
         assert n in names, n
 
 
@@ -164,3 +165,56 @@ def test_fused_swiglu_rejects_bad_arguments(lib):
     assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 1 << 21, A16b, None, ws, 0, None, None) == MOE_ERR_INVALID
     assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 32, MIS, None, ws, 0, None, None) == MOE_ERR_INVALID
     assert lib.gmm_fwd_swiglu(A16, A16b, A16c, 4, 64, 64, 32, A16b, MIS, ws, 0, None, None) == MOE_ERR_INVALID
+
+
+def test_mx_calls_reject_bad_arguments(lib):
+    # mx_quantize(x, rows, K, ld_s, q, s, stream)
+    assert lib.mx_quantize(None, 4, 64, 16, A16b, A16c, None) == MOE_ERR_NULL
+    assert lib.mx_quantize(A16, 4, 48, 16, A16b, A16c, None) == MOE_ERR_INVALID   # K % 32
+    assert lib.mx_quantize(A16, 4, 64, 8, A16b, A16c, None) == MOE_ERR_INVALID    # ld % 16
+    assert lib.mx_quantize(A16, 4, 1024, 16, A16b, A16c, None) == MOE_ERR_INVALID  # ld < K/32
+    assert lib.mx_quantize(A16, -1, 64, 16, A16b, A16c, None) == MOE_ERR_INVALID
+    assert lib.mx_quantize(MIS, 4, 64, 16, A16b, A16c, None) == MOE_ERR_INVALID
+    assert lib.mx_quantize(None, 0, 64, 16, None, None, None) == MOE_OK
+    # gmm_mx_fwd(xq, xs, ld_xs, wq, ws, ld_ws, gl, E, M_cap, K, N, y, dev_err, stream)
+    good = dict(xq=A16, xs=A16b, lx=16, wq=A16c, wsc=A16, lw=16, gl=A16b, E=4, M=64, K=64, N=64,
+                y=A16c)
+
+    def g(**kw):
+        a = dict(good, **kw)
+        return lib.gmm_mx_fwd(a["xq"], a["xs"], a["lx"], a["wq"], a["wsc"], a["lw"], a["gl"], a["E"],
+                              a["M"], a["K"], a["N"], a["y"], None, None)
+
+    assert g(wsc=None) == MOE_ERR_NULL
+    assert g(y=None) == MOE_ERR_NULL
+    assert g(K=48) == MOE_ERR_INVALID
+    assert g(lx=8) == MOE_ERR_INVALID
+    assert g(lw=0) == MOE_ERR_INVALID
+    assert g(xs=MIS) == MOE_ERR_INVALID
+    assert g(E=0) == MOE_ERR_INVALID
+    assert g(N=1 << 22) == MOE_ERR_INVALID
+    # gmm_mx_fwd_swiglu(..., E, M_cap, K, I, aq, as, ld_as, dev_err, stream)
+    sw = dict(good, I=32, aq=A16c, asc=A16, la=16)
+
+    def s(**kw):
+        a = dict(sw, **kw)
+        return lib.gmm_mx_fwd_swiglu(a["xq"], a["xs"], a["lx"], a["wq"], a["wsc"], a["lw"], a["gl"],
+                                     a["E"], a["M"], a["K"], a["I"], a["aq"], a["asc"], a["la"],
+                                     None, None)
+
+    assert s(I=48) == MOE_ERR_INVALID   # I % 32
+    assert s(la=8) == MOE_ERR_INVALID
+    assert s(asc=None) == MOE_ERR_NULL
+    assert s(aq=MIS) == MOE_ERR_INVALID
+    # moe_permute_mx(x, ids, T, k, H, E, xq, xs, ld_xs, rmap, ss, tpe, ws, ws_bytes, dev_err, stream)
+    need = lib.moe_permute_workspace_size(64, 8, 256)
+    ws = ctypes.c_void_p(0x50000)
+
+    def p(H=2048, ld=64, xs=A16c, wsb=need):
+        return lib.moe_permute_mx(A16, A16b, 64, 8, H, 256, A16c, xs, ld, A16, A16b, A16c, ws, wsb,
+                                  None, None)
+
+    assert p(xs=None) == MOE_ERR_NULL
+    assert p(H=2056) == MOE_ERR_INVALID  # H % 32
+    assert p(ld=48) == MOE_ERR_INVALID   # ld < H/32
+    assert p(wsb=need - 1) == MOE_ERR_WORKSPACE

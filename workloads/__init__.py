@@ -188,3 +188,52 @@ def random_group_list(rng: np.random.Generator, M: int, E: int, empty_frac: floa
     gl = np.zeros(E, dtype=np.int64)
     gl[live] = rng.multinomial(total, p)
     return gl
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (A8W8-FP) layouts: the same bf16 weights, stored reduction-contiguous
+# ---------------------------------------------------------------------------
+def reduction_major_weights(wl: Workload):
+    """(w1t [E, 2I, H], w2t [E, H, I]) bf16 bit patterns: w1 and w2 of a layer
+    workload transposed so each output column's weights are contiguous (the
+    layout the MX weights are quantised in).  Only a copy of bits."""
+    w1t = np.ascontiguousarray(np.transpose(wl["w1"], (0, 2, 1)))
+    w2t = np.ascontiguousarray(np.transpose(wl["w2"], (0, 2, 1)))
+    return w1t, w2t
+
+
+def wide_range_bf16(rng: np.random.Generator, shape, lo: int = -40, hi: int = 40,
+                    zero_frac: float = 0.02) -> np.ndarray:
+    """N(0,1) rows times 2^u with u uniform in [lo, hi) per 32-element group,
+    with some groups zeroed: exercises every E8M0 scale path of Q_MX."""
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    K = shape[-1]
+    G = (K + 31) // 32
+    e = rng.integers(lo, hi, size=shape[:-1] + (G,)).astype(np.float32)
+    z = rng.random(shape[:-1] + (G,)) < zero_frac
+    f = np.where(z, np.float32(0), np.exp2(e)).astype(np.float32)
+    a = a * np.repeat(f, 32, axis=-1)[..., :K]
+    return _to_bf16_bits(a)
+
+
+def mx_random(rng: np.random.Generator, shape, std: float = 0.02):
+    """A synthetic MX tensor (E4M3 code bytes [..., K], E8M0 scale bytes
+    [..., K/32]) whose values spread like N(0, std^2) weights: elements
+    N(0, 64^2) packed into float8_e4m3fn by PyTorch's CPU cast (a library
+    routine, as for the bf16 draws), one scale per group of 32 near std/64
+    with a random +-1 in its exponent.  Drawn directly: neither side computes
+    these operands, and the stand-in for MX-quantised weights costs no
+    quantisation pass."""
+    import torch
+
+    K = shape[-1]
+    assert K % 32 == 0
+    # the normal draws come from a torch CPU generator seeded from rng (fast
+    # for weight-sized tensors, and just as reproducible)
+    g = torch.Generator().manual_seed(int(rng.integers(0, 2 ** 62)))
+    a = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    a.mul_(64.0).clamp_(-448.0, 448.0)
+    codes = a.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    base = 127 + int(np.rint(np.log2(std))) - 6
+    scales = (base + rng.integers(-1, 2, size=tuple(shape[:-1]) + (K // 32,))).astype(np.uint8)
+    return codes, scales

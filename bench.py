@@ -26,6 +26,9 @@ Also in the line:
                   attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak),
                   and the backward of the two ends (moe_unpermute_bwd,
                   moe_permute_bwd) on its buffers in HBM GB/s;
+  mxfp8        -- the A8W8-FP (MXFP8) forward on the decode and prefill layers
+                  and the ep rank: GB/s, TFLOP/s against the fp8 MFMA peak,
+                  fraction of the attainable roofline;
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -55,6 +58,7 @@ def parse_args():
     p.add_argument("--cpu-budget", type=float, default=12.0,
                    help="seconds of oracle work for the CPU baseline (0 = skip)")
     p.add_argument("--skip-decode", action="store_true", help="skip the decode and prefill layer legs")
+    p.add_argument("--skip-mx", action="store_true", help="skip the MXFP8 (A8W8-FP) legs")
     p.add_argument("--copy-calibration", action="store_true",
                    help="finish with three 512 MiB device copies (the reference kernel that scales "
                         "the FETCH_SIZE / WRITE_SIZE counters into bytes)")
@@ -396,6 +400,138 @@ def run_prefill(torch, dev, args):
 
 
 # ---------------------------------------------------------------------------
+# MXFP8 (A8W8-FP) forward: decode and prefill layers, the ep rank's GMMs
+# ---------------------------------------------------------------------------
+
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
+
+
+def mx_weights(torch, dev, wl):
+    """The workload's bf16 weights, stored reduction-contiguous and MX-quantised
+    on the device (offline preparation, not part of a timed step)."""
+    from grouped_gemm_moe_amd import mx_quantize
+
+    out = []
+    for name in ("w1", "w2"):
+        w = bf16_dev(torch, wl[name], dev).transpose(1, 2).contiguous()  # [E, N, K]
+        out.append(mx_quantize(w))
+        del w
+    return out
+
+
+def mx_layer_bytes(gl, T, K, H, I):
+    """Algorithmic bytes of one A8W8-FP layer forward: MX weights (codes and
+    one scale byte per 32) of experts with rows, once; x read; the MX
+    activations (xq/xs, aq/as) and Yp written once and read once; out
+    written; indices."""
+    n_active = int(np.sum(np.asarray(gl) > 0))
+    S = int(np.sum(gl))
+    mx = 1.0 + 1.0 / 32
+    w = n_active * (H * 2 * I + I * H) * mx
+    act = (T * H * 2 + S * H * mx * 2 + S * I * mx * 2 + S * H * 2 * 2 + T * H * 2)
+    idx = T * K * 4 * 3 + T * K * 4 + len(gl) * 8
+    return int(w + act + idx), n_active
+
+
+def mx_layer_forward(torch, dev, wl, steps, w=None):
+    """Time permute_mx -> gmm_mx_fwd_swiglu -> gmm_mx_fwd -> unpermute."""
+    from grouped_gemm_moe_amd import (gmm_mx_fwd, gmm_mx_fwd_swiglu, moe_permute_mx,
+                                      moe_unpermute, mx_scale_ld)
+
+    d = wl.dims
+    T, K, E, H, I = d["T"], d["K"], d["E"], d["H"], d["I"]
+    (w1q, w1s), (w2q, w2s) = w if w is not None else mx_weights(torch, dev, wl)
+    x = bf16_dev(torch, wl["x"], dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    S = T * K
+    u8 = dict(dtype=torch.uint8, device=dev)
+    xq, xs = torch.empty((S, H), **u8), torch.empty((S, mx_scale_ld(H)), **u8)
+    aq, asc = torch.empty((S, I), **u8), torch.empty((S, mx_scale_ld(I)), **u8)
+    rmap = torch.empty(S, dtype=torch.int32, device=dev)
+    sslot = torch.empty(S, dtype=torch.int32, device=dev)
+    tpe = torch.empty(E, dtype=torch.int64, device=dev)
+    yp = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    from grouped_gemm_moe_amd import moe_permute_workspace_size
+    ws = torch.empty(moe_permute_workspace_size(T, K, E), dtype=torch.uint8, device=dev)
+    timer = KernelTimer(torch)
+
+    def step(t):
+        t("moe_permute_mx", lambda: moe_permute_mx(x, ids, E, out=(xq, xs, rmap, sslot, tpe), ws=ws,
+                                                   dev_err=err))
+        t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu(xq, xs, w1q, w1s, tpe, out=(aq, asc),
+                                                         dev_err=err))
+        t("gmm_mx_fwd_down", lambda: gmm_mx_fwd(aq, asc, w2q, w2s, tpe, out=yp, dev_err=err))
+        t("moe_unpermute", lambda: moe_unpermute(yp, rmap, probs, out=out, dev_err=err))
+
+    plain = lambda name, fn: fn()  # noqa: E731
+    for _ in range(10):
+        step(plain)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(plain)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    for _ in range(min(50, steps)):
+        step(timer)
+    torch.cuda.synchronize()
+    per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
+    assert int(err.item()) == 0, "device error word set during the MX bench"
+    return ms, per, tpe.cpu().numpy()
+
+
+def run_mx(torch, dev, args):
+    """The A8W8-FP forward on the decode and prefill layers and the ep rank."""
+    import workloads
+
+    res = {}
+    for name, make, steps in (("decode", workloads.decode, args.decode_steps),
+                              ("prefill", workloads.prefill, args.prefill_steps),
+                              ("ep_forward", workloads.ep_slice, args.prefill_steps)):
+        wl = make()
+        d = wl.dims
+        T, K, H, I = d["T"], d["K"], d["H"], d["I"]
+        ms, per, gl = mx_layer_forward(torch, dev, wl, steps)
+        nbytes, n_active = mx_layer_bytes(gl, T, K, H, I)
+        S = int(np.sum(gl))
+        f1, f2 = 2.0 * S * H * 2 * I, 2.0 * S * I * H
+        t_mem = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = (f1 + f2) / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+        roof_ms = max(t_mem, t_mfma) * 1e3
+        g1 = per["gmm_mx_fwd_swiglu"] * 1e-3
+        g2 = per["gmm_mx_fwd_down"] * 1e-3
+        wbytes1 = n_active * H * 2 * I * (1 + 1 / 32)
+        wbytes2 = n_active * I * H * (1 + 1 / 32)
+        res[name] = dict(
+            ms_per_layer=round(ms, 4), gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
+            tflops=round((f1 + f2) / (ms * 1e-3) / 1e12, 2), bytes_per_layer=nbytes,
+            bound="hbm" if t_mem >= t_mfma else "mfma", roofline_ms=round(roof_ms, 4),
+            frac_of_attainable=round(roof_ms / ms, 4), active_experts=n_active,
+            gmm_tflops={"gmm_mx_fwd_swiglu": round(f1 / g1 / 1e12, 1),
+                        "gmm_mx_fwd_down": round(f2 / g2 / 1e12, 1)},
+            gmm_pct_fp8_peak={"gmm_mx_fwd_swiglu": round(100 * f1 / g1 / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2),
+                              "gmm_mx_fwd_down": round(100 * f2 / g2 / 1e12 / MFMA_FP8_PEAK_TFLOPS, 2)},
+            gmm_weight_stream_gbs={"gmm_mx_fwd_swiglu": round(wbytes1 / g1 / 1e9, 1),
+                                   "gmm_mx_fwd_down": round(wbytes2 / g2 / 1e9, 1)},
+            per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
+        )
+        log(f"mx {name}: {ms:.4f} ms/layer; {res[name]['gb_per_s']} GB/s; {res[name]['tflops']} TFLOP/s; "
+            f"per call {res[name]['per_call_us']}")
+        del wl
+        torch.cuda.empty_cache()
+    res["workload"] = ("A8W8-FP (MXFP8) forward: permute_mx (gather + MX quantisation) -> gate_up GMM "
+                       "with SwiGLU and MX requantisation -> down GMM -> unpermute; weights = the bf16 "
+                       "workload weights MX-quantised on the device; decode (T=64, top-8, E=256), "
+                       "prefill (T=4096, top-8, E=128), the ep rank (16384 rows, E=32, hidden 4096, "
+                       "intermediate 1536)")
+    res["dtype"] = "fp8 e4m3 x fp8 e4m3 (E8M0 scales), fp32 accumulation"
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample of the ep step
 # ---------------------------------------------------------------------------
 
@@ -464,6 +600,9 @@ def main():
         prefill = run_prefill(torch, dev, args)
         log(f"prefill: {prefill['ms_per_layer']:.4f} ms, {prefill['value']:.1f} % of attainable "
             f"({prefill['bound']}-bound); {prefill['per_call_us']}")
+    mx = None
+    if not args.skip_mx:
+        mx = run_mx(torch, dev, args)
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(wl, args.cpu_budget)
@@ -495,6 +634,7 @@ def main():
         "roofline": ep["roofline"],
         "decode": decode,
         "prefill": prefill,
+        "mxfp8": mx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

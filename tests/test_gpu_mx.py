@@ -132,7 +132,7 @@ def _gmm_case(name):
     bf16 and quantised by each side for the small cases, drawn directly as
     MX bytes for the large ones."""
     rng = np.random.default_rng({"tiny": 51, "ragged": 52, "sweep": 53, "decode": 54,
-                                 "ep": 55}[name])
+                                 "ep": 55, "stream_ragged": 56}[name])
     if name == "ep":
         wl = workloads.ep_slice(with_weights=False, with_acts=False)
         gl = wl["group_list"]
@@ -141,6 +141,8 @@ def _gmm_case(name):
         M, K, N, gl = {
             "tiny": (5, 64, 64, [1, 2, 0, 2]),
             "ragged": (700, 224, 520, [0, 300, 0, 250, 100, 50]),  # K % 64 == 32
+            # weight streaming (M_cap <= 8E): an expert past 32 rows, ragged K and N
+            "stream_ragged": (100, 224, 520, [3, 0, 40, 1, 0, 0, 2, 9, 0, 5, 0, 33, 0, 1, 6, 0]),
             "sweep": (1024, 512, 1024, None),
             "decode": (512, 2048, 1024, None),
         }[name]
@@ -150,7 +152,7 @@ def _gmm_case(name):
     gl = np.asarray(gl, dtype=np.int64)
     M_cap = int(gl.sum()) + 16
     x = workloads.normal_bf16(rng, (M_cap, K))
-    if name in ("tiny", "ragged", "sweep"):
+    if name in ("tiny", "ragged", "sweep", "stream_ragged"):
         w_bits = workloads.normal_bf16(rng, (len(gl), N, K), 0.02)
         return x, ("bf16", w_bits), gl
     return x, ("mx",) + workloads.mx_random(rng, (len(gl), N, K), 0.02), gl
@@ -188,7 +190,7 @@ def _expert_of_rows(gl, rows):
     return np.searchsorted(off, rows, side="right") - 1
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "sweep", "decode", "ep"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "stream_ragged", "sweep", "decode", "ep"])
 def test_gmm_mx_fwd(dev, name):
     x, wkind, gl = _gmm_case(name)
     E, N, K = wkind[1].shape
@@ -326,10 +328,12 @@ def _reference_h(xdq, ex, w_dq):
 
 
 def _swiglu_case(name):
-    rng = np.random.default_rng({"tiny": 61, "ragged": 62, "decode": 63, "prefill": 64}[name])
+    rng = np.random.default_rng({"tiny": 61, "ragged": 62, "decode": 63, "prefill": 64,
+                                 "stream_ragged": 65}[name])
     M, K, I, gl = {
         "tiny": (5, 64, 32, [1, 2, 0, 2]),
         "ragged": (700, 224, 160, [0, 300, 0, 250, 100, 50]),  # I not a multiple of 128
+        "stream_ragged": (100, 224, 160, [3, 0, 40, 1, 0, 0, 2, 9, 0, 5, 0, 33, 0, 1, 6, 0]),
         "decode": (512, 2048, 512, None),
         "prefill": (32768, 2048, 512, None),
     }[name]
@@ -343,7 +347,7 @@ def _swiglu_case(name):
     return x, w1q, w1s, gl
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "stream_ragged", "decode", "prefill"])
 def test_gmm_mx_swiglu_requant(dev, name):
     x, w1q, w1s, gl = _swiglu_case(name)
     E, N2, K = w1q.shape

@@ -95,7 +95,8 @@ class KernelTimer:
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gmm_dw_kernel_hbm_traffic_ep_rank.md")
-KERNEL_SOURCES = ["grouped_gemm_moe_amd/csrc/gmm.hip", "grouped_gemm_moe_amd/csrc/common.h"]
+KERNEL_SOURCES = ["grouped_gemm_moe_amd/csrc/gmm.hip", "grouped_gemm_moe_amd/csrc/gmm_engine.h",
+                  "grouped_gemm_moe_amd/csrc/common.h"]
 
 
 def kernel_source_hash():

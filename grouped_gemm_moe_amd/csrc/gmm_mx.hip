@@ -340,47 +340,34 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
 // ---------------------------------------------------------------------------
 // Decode-shaped MX GEMM: weight streaming.  When experts own a few rows
 // each, the work is reading every active expert's MX weights once; a 256-row
-// tile would idle and a LDS ring adds nothing.  A column group is 64 weight
-// rows (two 32-row MFMA operands: 64 output columns, or for SWIGLU the 32
-// gate and the matching 32 up rows of 32 output columns); KS waves share it,
-// each streaming one slice of the reduction straight from HBM into
-// registers in the MFMA operand layout (lane l: row l%32, bytes 16*(l/32)..
-// and 32+16*(l/32).. of each 64-byte step), kStreamSteps steps per batch of
-// loads, and their partial sums meet in LDS in a fixed order.  The expert's
-// rows ride as the other operand, 32 at a time (zeros past the last row),
-// read from L2.  Scale bytes come
-// 2 per step, one aligned load per batch and row.
+// tile would idle.  A wave owns a column group of 64 weight rows (two 32-row
+// MFMA operands: 64 output columns, or for SWIGLU the 32 gate and the
+// matching 32 up rows of 32 output columns) and streams its whole reduction
+// in batches of four 64-element steps.  Each batch lands in a private LDS
+// stage by coalesced LDS DMA (4 rows x 256 bytes per instruction), is read
+// back in the MFMA operand layout (lane l: row l%32, bytes 16*(l/32).. and
+// 32+16*(l/32).. of each 64-byte step), and the stage is refilled with the
+// next batch while the MFMAs run.  The expert's rows are the other operand,
+// 32 at a time (zeros past the last row), read from L2; scale bytes come 8
+// per batch and row.
+//
+// Direct register loads in the MFMA layout touch 32 rows x 32 bytes per
+// instruction; on 442 MB of weights that pattern reads at 4.6 TB/s against
+// 5.4 TB/s for the coalesced one.  Splitting the reduction across the waves
+// of a block (partial sums meeting in LDS) measured 10-20 % slower on the
+// decode shapes than whole-reduction waves, so there is no split.
 // ---------------------------------------------------------------------------
 constexpr int kStreamThreads = 256;
-#ifndef MOEGMM_MX_STREAM_STEPS
-#define MOEGMM_MX_STREAM_STEPS 4
-#endif
-constexpr int kStreamSteps = MOEGMM_MX_STREAM_STEPS;  // 64-element steps per batch of loads
+constexpr int kStreamSteps = 4;          // 64-element steps per batch
+constexpr int kSeg = kStreamSteps * 64;  // bytes of a row per batch
+constexpr int kDmaInst = 64 * kSeg / 1024;
 
-static_assert(kStreamSteps == 2 || kStreamSteps == 4 || kStreamSteps == 8, "scale bytes per batch");
-constexpr int kScaleWords = kStreamSteps / 2;  // 2 scale bytes per step, 4 per word
-
-// The 2*kStreamSteps scale bytes of a batch (one row), aligned: batches
-// start at multiples of 2*kStreamSteps bytes and rows at multiples of 16.
+// The 8 scale bytes of a batch (one row); batches start at multiples of 8
+// bytes and scale rows at multiples of 16, so the load is aligned.
 struct ScaleBatch {
-    uint32_t w[kScaleWords];
-    MOE_DEVICE void load(const uint8_t* p) {
-        if constexpr (kScaleWords == 1) {
-            w[0] = *reinterpret_cast<const uint32_t*>(p);
-        } else if constexpr (kScaleWords == 2) {
-            const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
-            w[0] = v[0];
-            w[1] = v[1];
-        } else {
-            const u32x4_t v = ld16(p);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = v[i];
-        }
-    }
-    MOE_DEVICE void unit() {
-#pragma unroll
-        for (int i = 0; i < kScaleWords; ++i) w[i] = 0x7F7F7F7Fu;
-    }
+    u32x2_t w;
+    MOE_DEVICE void load(const uint8_t* p) { w = *reinterpret_cast<const u32x2_t*>(p); }
+    MOE_DEVICE void unit() { w = u32x2_t{0x7F7F7F7Fu, 0x7F7F7F7Fu}; }
     // scale of group 2s + c of the batch
     MOE_DEVICE uint32_t pick(int s, int c) const {
         const int b = 2 * s + c;
@@ -388,64 +375,46 @@ struct ScaleBatch {
     }
 };
 
-#ifndef MOEGMM_MX_STREAM_OCC
-#define MOEGMM_MX_STREAM_OCC 3
-#endif
-template <bool SWIGLU, int KS>
-__global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_stream_kernel(
+template <bool SWIGLU>
+__global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, int64_t ld_xs,
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ WS, int64_t ld_ws,
     const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
     bf16_t* __restrict__ Y, uint8_t* __restrict__ AQ, uint8_t* __restrict__ AS, int64_t ld_as,
     int32_t* dev_err) {
     constexpr int kWaves = kStreamThreads / 64;
-    constexpr int kGroups = kWaves / KS;  // column groups per block; KS waves split K
     constexpr int kColsPerWave = SWIGLU ? 32 : 64;
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int64_t s_scan[kStreamThreads / 64];
-    // per wave: one batch of its 64 weight rows (kStreamSteps * 64 bytes
-    // each), filled by LDS DMA; reused for the partial sums at the end
-    __shared__ __attribute__((aligned(1024))) uint8_t stage[kWaves][64 * kStreamSteps * 64];
-    static_assert(KS == 1 || sizeof(stage) >= sizeof(float) * kWaves * 2 * 16 * 64, "red fits");
-    float(*red)[2][16][64] = reinterpret_cast<float(*)[2][16][64]>(&stage[0][0]);
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[kWaves][64 * kSeg];  // one batch per wave
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const int Nout = SWIGLU ? N / 2 : N;
-    const int NB = (Nout + kColsPerWave * kGroups - 1) / (kColsPerWave * kGroups);
+    const int NB = (Nout + kColsPerWave * kWaves - 1) / (kColsPerWave * kWaves);
     const int e = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int off = s_off[e], cnt = s_cnt[e];
-    if (cnt == 0) return;  // uniform across the block
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int grp = wid / KS, kq = wid % KS;
-    const int c0 = (nb * kGroups + grp) * kColsPerWave;  // first output column of the group
-    const bool live = c0 < Nout;                          // uniform per wave
+    const int c0 = (nb * kWaves + wid) * kColsPerWave;  // first output column of the wave
+    if (cnt == 0 || c0 >= Nout) return;                  // uniform per wave; no barrier follows
     const int c = lane >> 5, r32 = lane & 31;
-    // this lane's weight row in each of the two operands
+    // this lane's weight row in each of the two operands (for its scales)
     int wrow[2];
     bool wok[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         wrow[t] = SWIGLU ? (t == 0 ? c0 : Nout + c0) + r32 : c0 + 32 * t + r32;
-        wok[t] = live && (SWIGLU ? c0 + r32 < Nout : wrow[t] < N);
+        wok[t] = SWIGLU ? c0 + r32 < Nout : wrow[t] < N;
     }
     const uint8_t* We = W + (int64_t)e * N * K;
     const uint8_t* WSe = WS + (int64_t)e * N * ld_ws;
     const int nsteps = (K + 63) / 64;
     const int nblocks = K / kMxGroup;
-    // this wave's slice of the 64-element steps, whole batches
-    const int spw = ((nsteps + KS - 1) / KS + kStreamSteps - 1) / kStreamSteps * kStreamSteps;
-    const int s_beg = kq * spw;
-    const int s_end = s_beg + spw < nsteps ? s_beg + spw : nsteps;
-    const int k_end = 64 * s_end < K ? 64 * s_end : K;
 
     // LDS DMA of a batch: instruction i moves rows 4i .. 4i+3 of the wave's
     // 64 (operand t = i / 8), lane l 16 bytes of row 4i + l/16.  Lane l
     // fetches chunk (l%16) ^ (row%16) of the row's batch segment, so chunk q
     // of row r lands at position q ^ (r%16): the MFMA-layout reads below
     // (16 rows, one chunk) then hit 16 distinct bank groups.
-    constexpr int kSeg = kStreamSteps * 64;  // bytes of a row per batch
-    constexpr int kDmaInst = 64 * kSeg / 1024;
-    static_assert(kSeg == 256, "one DMA instruction = 4 rows x 256 bytes");
     const int dq = lane & 15;
     uint8_t* wst = &stage[wid][0];
     auto dma_batch = [&](int s0) {
@@ -454,10 +423,10 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
             const int t = i / 8;                       // operand
             const int r = 4 * (i % 8) + (lane >> 4);   // row within the operand
             const int row = SWIGLU ? (t == 0 ? c0 : Nout + c0) + r : c0 + 32 * t + r;
-            const bool rok = live && (SWIGLU ? c0 + r < Nout : row < N);
+            const bool rok = SWIGLU ? c0 + r < Nout : row < N;
             const int q = dq ^ (r & 15);
             const int k = 64 * s0 + 16 * q;
-            const uint32_t v = rok && k < k_end ? (uint32_t)((int64_t)row * K + k) : kOOB;
+            const uint32_t v = rok && k < K ? (uint32_t)((int64_t)row * K + k) : kOOB;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(We), (LDS_AS void*)(wst + i * 1024), 16, v,
                                                      0, 0, 0);
         }
@@ -469,7 +438,7 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
         return wst + (t * 8 + (r >> 2)) * 1024 + (r & 3) * 256 + ((q ^ (r & 15)) << 4);
     };
 
-    for (int rg = 0; rg < cnt; rg += 32) {  // uniform across the block
+    for (int rg = 0; rg < cnt; rg += 32) {  // uniform across the wave
         const int xr = rg + r32;           // this lane's expert row
         const bool xok = xr < cnt;
         const uint8_t* xrow = X + (int64_t)(off + xr) * K;
@@ -479,8 +448,8 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[t][q] = 0.f;
-        if (live && s_beg < s_end) dma_batch(s_beg);
-        for (int s0 = s_beg; live && s0 < s_end; s0 += kStreamSteps) {
+        dma_batch(0);
+        for (int s0 = 0; s0 < nsteps; s0 += kStreamSteps) {
             u32x4_t wa[2][kStreamSteps][2], xa[kStreamSteps][2];
             ScaleBatch wsc[2], xsc;
             const int sb = 2 * s0;  // first scale byte of the batch
@@ -494,7 +463,7 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int k = 64 * (s0 + s) + 32 * h + 16 * c;
-                    xa[s][h] = xok && k < k_end ? ld16(xrow + k) : u32x4_t{0u, 0u, 0u, 0u};
+                    xa[s][h] = xok && k < K ? ld16(xrow + k) : u32x4_t{0u, 0u, 0u, 0u};
                 }
             if (xok && sb < nblocks) xsc.load(xsrow + sb);
             else xsc.unit();
@@ -518,7 +487,7 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
                 for (int s = 0; s < kStreamSteps; ++s)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(wa[t][s][h]));
-            if (s0 + kStreamSteps < s_end) dma_batch(s0 + kStreamSteps);
+            if (s0 + kStreamSteps < nsteps) dma_batch(s0 + kStreamSteps);
 #pragma unroll
             for (int s = 0; s < kStreamSteps; ++s) {
                 const bool kb_ok = 2 * (s0 + s) + c < nblocks;  // padding bytes are no scales
@@ -533,29 +502,6 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
                 }
             }
         }
-        if constexpr (KS > 1) {
-            // partial sums meet in LDS (in the stages, now idle); the group's
-            // first wave adds them in slice order
-            __syncthreads();
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) red[wid][t][q][lane] = acc[t][q];
-            __syncthreads();
-            if (kq == 0) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        float v = red[wid][t][q][lane];
-#pragma unroll
-                        for (int j = 1; j < KS; ++j) v += red[wid + j][t][q][lane];
-                        acc[t][q] = v;
-                    }
-            }
-            __syncthreads();  // red and the stages are rewritten by the next row group
-        }
-        if (kq != 0 || !live) continue;
         // lane: expert row xr, output columns 8g + 4c + q of each operand
         if constexpr (SWIGLU) {
             float av[16];
@@ -596,54 +542,6 @@ __global__ __launch_bounds__(kStreamThreads, MOEGMM_MX_STREAM_OCC) void gmm_mx_s
     }
 }
 
-// K split over the waves of a block, only for grids too small to fill the
-// chip (as if every expert had rows): on the decode shapes a split measured
-// slower than whole-K waves (each keeps its next batch in flight while it
-// multiplies), so the target is low.
-#ifndef MOEGMM_MX_STREAM_WAVES
-#define MOEGMM_MX_STREAM_WAVES 4096
-#endif
-int stream_ksplit(int64_t E, int64_t Nout, int64_t K, int cols_per_wave) {
-    const int64_t nsteps = (K + 63) / 64;
-    int ks = 1;
-    while (ks < 4 && E * ((Nout + cols_per_wave - 1) / cols_per_wave) * ks < MOEGMM_MX_STREAM_WAVES &&
-           nsteps >= 2 * ks * kStreamSteps)
-        ks *= 2;
-    return ks;
-}
-
-template <bool SWIGLU, int KS>
-void launch_stream(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
-                   const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
-                   int64_t M_cap, int64_t K, int64_t N, uint16_t* y, uint8_t* aq, uint8_t* as,
-                   int64_t ld_as, int32_t* dev_err, hipStream_t stream) {
-    const int64_t Nout = SWIGLU ? N / 2 : N;
-    const int64_t cols = (SWIGLU ? 32 : 64) * (kStreamThreads / 64 / KS);
-    const int64_t NB = (Nout + cols - 1) / cols;
-    hipLaunchKernelGGL((gmm_mx_stream_kernel<SWIGLU, KS>), dim3((unsigned)(E * NB)),
-                       dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, wq, ws, ld_ws, group_list,
-                       (int)E, M_cap, (int)K, (int)N, y, aq, as, ld_as, dev_err);
-}
-
-template <bool SWIGLU>
-hipError_t launch_stream_any(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
-                             const uint8_t* wq, const uint8_t* ws, int64_t ld_ws,
-                             const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
-                             int64_t N, uint16_t* y, uint8_t* aq, uint8_t* as, int64_t ld_as,
-                             int32_t* dev_err, hipStream_t stream) {
-    const int ks = stream_ksplit(E, SWIGLU ? N / 2 : N, K, SWIGLU ? 32 : 64);
-    if (ks == 4)
-        launch_stream<SWIGLU, 4>(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap, K, N, y, aq, as,
-                                 ld_as, dev_err, stream);
-    else if (ks == 2)
-        launch_stream<SWIGLU, 2>(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap, K, N, y, aq, as,
-                                 ld_as, dev_err, stream);
-    else
-        launch_stream<SWIGLU, 1>(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap, K, N, y, aq, as,
-                                 ld_as, dev_err, stream);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 // Decode-shaped calls (a few rows per expert on average) stream the weights.
@@ -654,9 +552,13 @@ hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
                              int64_t M_cap, int64_t K, int64_t N, uint16_t* y, int32_t* dev_err,
                              hipStream_t stream) {
     if (M_cap == 0) return hipSuccess;
-    if (gmm_mx_stream_applies(E, M_cap))
-        return launch_stream_any<false>(xq, xs, ld_xs, wq, ws, ld_ws, group_list, E, M_cap, K, N, y,
-                                        nullptr, nullptr, 0, dev_err, stream);
+    if (gmm_mx_stream_applies(E, M_cap)) {
+        const int64_t NB = (N + 64 * 4 - 1) / (64 * 4);
+        hipLaunchKernelGGL(gmm_mx_stream_kernel<false>, dim3((unsigned)(E * NB)),
+                           dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, wq, ws, ld_ws, group_list,
+                           (int)E, M_cap, (int)K, (int)N, y, nullptr, nullptr, (int64_t)0, dev_err);
+        return hipGetLastError();
+    }
     const int64_t NT = (N + kBN - 1) / kBN;
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
     hipLaunchKernelGGL(gmm_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
@@ -671,9 +573,14 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
                                     int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
                                     int32_t* dev_err, hipStream_t stream) {
     if (M_cap == 0) return hipSuccess;
-    if (gmm_mx_stream_applies(E, M_cap))
-        return launch_stream_any<true>(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, E, M_cap, K,
-                                       2 * I, nullptr, aq, as, ld_as, dev_err, stream);
+    if (gmm_mx_stream_applies(E, M_cap)) {
+        const int64_t NB = (I + 32 * 4 - 1) / (32 * 4);
+        hipLaunchKernelGGL(gmm_mx_stream_kernel<true>, dim3((unsigned)(E * NB)),
+                           dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
+                           group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
+                           dev_err);
+        return hipGetLastError();
+    }
     const int64_t NT = (I + kBN / 2 - 1) / (kBN / 2);
     const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
     hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,

@@ -408,16 +408,12 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 
 
 def mx_weights(torch, dev, wl):
-    """The workload's bf16 weights, stored reduction-contiguous and MX-quantised
-    on the device (offline preparation, not part of a timed step)."""
-    from grouped_gemm_moe_amd import mx_quantize
+    """The workload's bf16 weights as MX pairs (MoeLayerMX.prepare_weights:
+    transposed once and MX-quantised on the device; not part of a timed
+    step)."""
+    from grouped_gemm_moe_amd.pipeline import MoeLayerMX
 
-    out = []
-    for name in ("w1", "w2"):
-        w = bf16_dev(torch, wl[name], dev).transpose(1, 2).contiguous()  # [E, N, K]
-        out.append(mx_quantize(w))
-        del w
-    return out
+    return MoeLayerMX.prepare_weights(bf16_dev(torch, wl["w1"], dev), bf16_dev(torch, wl["w2"], dev))
 
 
 def mx_layer_bytes(gl, T, K, H, I):
@@ -434,38 +430,30 @@ def mx_layer_bytes(gl, T, K, H, I):
     return int(w + act + idx), n_active
 
 
-def mx_layer_forward(torch, dev, wl, steps, w=None):
+def mx_layer_forward(torch, dev, wl, steps):
     """Time permute_mx -> gmm_mx_fwd_swiglu -> gmm_mx_fwd -> unpermute."""
     from grouped_gemm_moe_amd import (gmm_mx_fwd, gmm_mx_fwd_swiglu, moe_permute_mx,
-                                      moe_unpermute, mx_scale_ld)
+                                      moe_unpermute)
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
 
     d = wl.dims
     T, K, E, H, I = d["T"], d["K"], d["E"], d["H"], d["I"]
-    (w1q, w1s), (w2q, w2s) = w if w is not None else mx_weights(torch, dev, wl)
+    (w1q, w1s), (w2q, w2s) = mx_weights(torch, dev, wl)
     x = bf16_dev(torch, wl["x"], dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     probs = torch.from_numpy(wl["probs"]).to(dev)
-    S = T * K
-    u8 = dict(dtype=torch.uint8, device=dev)
-    xq, xs = torch.empty((S, H), **u8), torch.empty((S, mx_scale_ld(H)), **u8)
-    aq, asc = torch.empty((S, I), **u8), torch.empty((S, mx_scale_ld(I)), **u8)
-    rmap = torch.empty(S, dtype=torch.int32, device=dev)
-    sslot = torch.empty(S, dtype=torch.int32, device=dev)
-    tpe = torch.empty(E, dtype=torch.int64, device=dev)
-    yp = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    from grouped_gemm_moe_amd import moe_permute_workspace_size
-    ws = torch.empty(moe_permute_workspace_size(T, K, E), dtype=torch.uint8, device=dev)
+    L = MoeLayerMX(LayerShape(T, K, E, H, I), dev)
+    g, err = L.tokens_per_expert, L.dev_err
     timer = KernelTimer(torch)
 
     def step(t):
-        t("moe_permute_mx", lambda: moe_permute_mx(x, ids, E, out=(xq, xs, rmap, sslot, tpe), ws=ws,
-                                                   dev_err=err))
-        t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu(xq, xs, w1q, w1s, tpe, out=(aq, asc),
+        t("moe_permute_mx", lambda: moe_permute_mx(x, ids, E, out=(L.xq, L.xs, L.row_id_map,
+                                                                  L.sorted_slot, g),
+                                                   ws=L.ws_perm, dev_err=err))
+        t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu(L.xq, L.xs, w1q, w1s, g, out=(L.aq, L.as_),
                                                          dev_err=err))
-        t("gmm_mx_fwd_down", lambda: gmm_mx_fwd(aq, asc, w2q, w2s, tpe, out=yp, dev_err=err))
-        t("moe_unpermute", lambda: moe_unpermute(yp, rmap, probs, out=out, dev_err=err))
+        t("gmm_mx_fwd_down", lambda: gmm_mx_fwd(L.aq, L.as_, w2q, w2s, g, out=L.yp, dev_err=err))
+        t("moe_unpermute", lambda: moe_unpermute(L.yp, L.row_id_map, probs, out=L.out, dev_err=err))
 
     plain = lambda name, fn: fn()  # noqa: E731
     for _ in range(10):
@@ -481,7 +469,7 @@ def mx_layer_forward(torch, dev, wl, steps, w=None):
     torch.cuda.synchronize()
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     assert int(err.item()) == 0, "device error word set during the MX bench"
-    return ms, per, tpe.cpu().numpy()
+    return ms, per, g.cpu().numpy()
 
 
 def run_mx(torch, dev, args):

@@ -14,6 +14,10 @@ Backward of the whole layer from dout (the gradient at the layer output):
     dYp, dprobs = moe_unpermute_bwd(dout, Yp, probs); the expert block as
     above; dx = moe_permute_bwd(dX_perm)
 
+The A8W8-FP (MXFP8) forward ("MegaMoE", A8W8-FP scenario), MoeLayerMX:
+    moe_permute_mx (gather + Q_MX) -> gmm_mx_fwd_swiglu(W1; GMM1, SwiGLU and
+    Q_MX of A in one call) -> gmm_mx_fwd(W2) -> moe_unpermute
+
 Every step runs in the HIP kernels of libmoegmm; this module only owns the
 buffers and the call order.  group_list (tokens_per_expert) stays on the
 device between the calls.
@@ -24,8 +28,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_workspace_size, moe_permute,
-               moe_permute_bwd, moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd,
+from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
+               gmm_workspace_size, moe_permute, moe_permute_bwd, moe_permute_mx,
+               moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd, mx_quantize, mx_scale_ld,
                swiglu, swiglu_bwd)
 
 
@@ -134,3 +139,48 @@ class MoeLayer:
         self.unpermute_backward(dout, probs)
         self.backward(self.dyp, w1, w2)
         self.permute_backward()
+
+
+class MoeLayerMX:
+    """Buffers for the A8W8-FP forward of one layer shape.  Weights are MX
+    pairs (codes, scales) stored reduction-contiguous: W1 as [E, 2I, H] (gate
+    rows, then up rows), W2 as [E, H, I]; prepare_weights builds them from
+    the bf16 [E, H, 2I] / [E, I, H] weights."""
+
+    def __init__(self, shape: LayerShape, device):
+        s = shape
+        self.shape = s
+        d = device
+        u8 = dict(dtype=torch.uint8, device=d)
+        S = s.S
+        self.xq = torch.empty((S, s.H), **u8)
+        self.xs = torch.empty((S, mx_scale_ld(s.H)), **u8)
+        self.aq = torch.empty((S, s.I), **u8)
+        self.as_ = torch.empty((S, mx_scale_ld(s.I)), **u8)
+        self.row_id_map = torch.empty(S, dtype=torch.int32, device=d)
+        self.sorted_slot = torch.empty(S, dtype=torch.int32, device=d)
+        self.tokens_per_expert = torch.empty(s.E, dtype=torch.int64, device=d)
+        self.yp = torch.empty((S, s.H), dtype=torch.bfloat16, device=d)
+        self.out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=d)
+        self.dev_err = torch.zeros(1, dtype=torch.int32, device=d)
+        self.ws_perm = torch.empty(max(1, moe_permute_workspace_size(s.T, s.top_k, s.E)),
+                                   dtype=torch.uint8, device=d)
+
+    @staticmethod
+    def prepare_weights(w1, w2):
+        """bf16 W1 [E, H, 2I] and W2 [E, I, H] -> MX pairs of W1^T [E, 2I, H]
+        and W2^T [E, H, I] (the transposes are copies made once, off the
+        path; Q_MX runs in the library)."""
+        return (mx_quantize(w1.transpose(1, 2).contiguous()),
+                mx_quantize(w2.transpose(1, 2).contiguous()))
+
+    def forward(self, x, topk_ids, probs, w1mx, w2mx):
+        (w1q, w1s), (w2q, w2s) = w1mx, w2mx
+        g = self.tokens_per_expert
+        moe_permute_mx(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
+                       out=(self.xq, self.xs, self.row_id_map, self.sorted_slot, g))
+        gmm_mx_fwd_swiglu(self.xq, self.xs, w1q, w1s, g, out=(self.aq, self.as_),
+                          dev_err=self.dev_err)
+        gmm_mx_fwd(self.aq, self.as_, w2q, w2s, g, out=self.yp, dev_err=self.dev_err)
+        moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
+        return self.out

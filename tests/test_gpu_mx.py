@@ -451,3 +451,35 @@ def test_layer_mx(dev, name):
         v = rmap_ref[:, k] >= 0
         slack_o[v] += pr[v, k:k + 1] * slack_y[rmap_ref[v, k]]
     assert_close(dev_f64(out)[toks], ref["out"], f"layer {name} out", extra=slack_o)
+
+
+def test_layer_mx_pipeline_and_weight_preparation(dev):
+    """MoeLayerMX runs the same four calls (bit-identical outputs to the
+    explicit chain), and prepare_weights is Q_MX of the transposed bf16
+    weights, bit-exact against the oracle."""
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
+
+    wl = workloads.tiny()
+    d = wl.dims
+    w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
+    print("MoeLayerMX tiny: prepare_weights + forward", flush=True)
+    (w1q, w1s), (w2q, w2s) = MoeLayerMX.prepare_weights(w1, w2)
+    torch.cuda.synchronize()
+    w1t, w2t = workloads.reduction_major_weights(wl)
+    for (q, s), bits in (((w1q, w1s), w1t), ((w2q, w2s), w2t)):
+        rq, rs = mx_ref.mx_quantize(f64(bits))
+        assert np.array_equal(_u8(q), rq)
+        assert np.array_equal(_u8(s)[..., :rs.shape[-1]], rs)
+    L = MoeLayerMX(LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"]), dev)
+    x = bf16_dev(wl["x"], dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    out = L.forward(x, ids, probs, (w1q, w1s), (w2q, w2s)).clone()
+    xq, xs, rmap, _, tpe = moe.moe_permute_mx(x, ids, d["E"])
+    aq, asc = moe.gmm_mx_fwd_swiglu(xq, xs, w1q, w1s, tpe)
+    yp = moe.gmm_mx_fwd(aq, asc, w2q, w2s, tpe)
+    out2 = moe.moe_unpermute(yp, rmap, probs)
+    torch.cuda.synchronize()
+    assert int(L.dev_err.item()) == 0
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert L.tokens_per_expert.cpu().tolist() == [1, 2, 0, 2]

@@ -29,6 +29,12 @@ Also in the line:
   mxfp8        -- the A8W8-FP (MXFP8) forward on the decode and prefill layers
                   and the ep rank: GB/s, TFLOP/s against the fp8 MFMA peak,
                   fraction of the attainable roofline;
+  *_ms_events  -- p10 / p50 / p90 of per-step (per-layer) spans from HIP events,
+                  first call's start to last call's end; they come from the pass
+                  that records an event pair around every call, so they sit a
+                  few percent above ms_per_step / ms_per_layer (wall time);
+  ceilings     -- hipBLASLt on a dense bf16 product of the ep gate_up shape and
+                  a 512 MiB device copy, measured here for context;
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -91,6 +97,19 @@ class KernelTimer:
             out.setdefault(name, []).append(a.elapsed_time(b))
         self.pending = []
         return out
+
+    def spans(self, calls_per_step):
+        """ms from the first call's start to the last call's end of every
+        step (call before collect())."""
+        n = len(self.pending) // calls_per_step
+        return [self.pending[i * calls_per_step][1].elapsed_time(
+                    self.pending[(i + 1) * calls_per_step - 1][2]) for i in range(n)]
+
+
+def percentiles(ms):
+    """p10 / p50 / p90 of per-step times in ms."""
+    q = np.percentile(np.asarray(ms), [10, 50, 90])
+    return dict(p10=round(float(q[0]), 4), p50=round(float(q[1]), 4), p90=round(float(q[2]), 4))
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -196,6 +215,7 @@ def run_ep(torch, dev, args):
         step(timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    step_ms = timer.spans(9)
     per = timer.collect()
     assert int(layer.dev_err.item()) == 0, "device error word set during the bench"
     ms_per_step = wall * 1e3 / args.steps
@@ -211,8 +231,11 @@ def run_ep(torch, dev, args):
     dom_ms_per_launch = kern_ms[dom] / len(dom_calls)
     achieved = dom_flops_per_launch / (dom_ms_per_launch * 1e-3) / 1e12
     traffic = measured_traffic(dom)
+    t_mfma_ms = total_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3  # the step is MFMA-bound
     res = dict(
         ms_per_step=ms_per_step,
+        step_ms_events=percentiles(step_ms),
+        frac_of_attainable=round(t_mfma_ms / ms_per_step, 4),
         value=total_flops / (ms_per_step * 1e-3) / 1e12,
         gmm_only_tflops=total_flops / (gmm_ms * 1e-3) / 1e12,
         gemm_gflop_per_step=total_flops / 1e9,
@@ -292,9 +315,10 @@ def layer_forward(torch, dev, wl, steps):
     for _ in range(min(50, steps)):
         step(timer)
     torch.cuda.synchronize()
+    spans = percentiles(timer.spans(5 if not fused else 4))
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     gl = layer.tokens_per_expert.cpu().numpy()
-    return ms, per, gl, (layer, probs, fused)
+    return ms, per, gl, (layer, probs, fused, spans)
 
 
 def end_backward(torch, dev, layer, probs, steps=20):
@@ -358,7 +382,7 @@ def run_decode(torch, dev, args):
     wl = workloads.decode()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl, (_, _, fused) = layer_forward(torch, dev, wl, args.decode_steps)
+    ms, per, gl, (_, _, fused, spans) = layer_forward(torch, dev, wl, args.decode_steps)
     roof = layer_roofline(gl, T, K, H, I, ms, fused)
     nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -368,7 +392,7 @@ def run_decode(torch, dev, args):
         metric="decode MoE layer HBM GB/s",
         workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
                  "intermediate 512; permute -> gate_up (weight streaming) -> SwiGLU -> down -> unpermute",
-        value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4),
+        value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4), layer_ms_events=spans,
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=nbytes,
         active_experts=n_active, frac_of_attainable=roof["frac_of_attainable"],
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
@@ -382,7 +406,7 @@ def run_prefill(torch, dev, args):
     wl = workloads.prefill()
     d = wl.dims
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-    ms, per, gl, (layer, probs, fused) = layer_forward(torch, dev, wl, args.prefill_steps)
+    ms, per, gl, (layer, probs, fused, spans) = layer_forward(torch, dev, wl, args.prefill_steps)
     roof = layer_roofline(gl, T, K, H, I, ms, fused)
     ends = end_backward(torch, dev, layer, probs)
     gbs = roof["bytes_per_layer"] / (ms * 1e-3) / 1e9
@@ -392,7 +416,7 @@ def run_prefill(torch, dev, args):
         workload="prefill layer forward: T=4096 tokens, top-8 of E=128, hidden 2048, "
                  "intermediate 512; permute -> gate_up GMM fused with SwiGLU -> down -> unpermute",
         value=round(100.0 * roof["frac_of_attainable"], 2), unit="% of attainable roofline",
-        ms_per_layer=round(ms, 4), gb_per_s=round(gbs, 1), tflops=round(tflops, 2),
+        ms_per_layer=round(ms, 4), layer_ms_events=spans, gb_per_s=round(gbs, 1), tflops=round(tflops, 2),
         pct_bf16_mfma_peak=round(100.0 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **roof,
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
@@ -467,9 +491,10 @@ def mx_layer_forward(torch, dev, wl, steps):
     for _ in range(min(50, steps)):
         step(timer)
     torch.cuda.synchronize()
+    spans = percentiles(timer.spans(4))
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
     assert int(err.item()) == 0, "device error word set during the MX bench"
-    return ms, per, g.cpu().numpy()
+    return ms, per, g.cpu().numpy(), spans
 
 
 def run_mx(torch, dev, args):
@@ -483,7 +508,7 @@ def run_mx(torch, dev, args):
         wl = make()
         d = wl.dims
         T, K, H, I = d["T"], d["K"], d["H"], d["I"]
-        ms, per, gl = mx_layer_forward(torch, dev, wl, steps)
+        ms, per, gl, spans = mx_layer_forward(torch, dev, wl, steps)
         nbytes, n_active = mx_layer_bytes(gl, T, K, H, I)
         S = int(np.sum(gl))
         f1, f2 = 2.0 * S * H * 2 * I, 2.0 * S * I * H
@@ -495,7 +520,8 @@ def run_mx(torch, dev, args):
         wbytes1 = n_active * H * 2 * I * (1 + 1 / 32)
         wbytes2 = n_active * I * H * (1 + 1 / 32)
         res[name] = dict(
-            ms_per_layer=round(ms, 4), gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
+            ms_per_layer=round(ms, 4), layer_ms_events=spans,
+            gb_per_s=round(nbytes / (ms * 1e-3) / 1e9, 1),
             tflops=round((f1 + f2) / (ms * 1e-3) / 1e12, 2), bytes_per_layer=nbytes,
             bound="hbm" if t_mem >= t_mfma else "mfma", roofline_ms=round(roof_ms, 4),
             frac_of_attainable=round(roof_ms / ms, 4), active_experts=n_active,
@@ -518,6 +544,46 @@ def run_mx(torch, dev, args):
                        "intermediate 1536)")
     res["dtype"] = "fp8 e4m3 x fp8 e4m3 (E8M0 scales), fp32 accumulation"
     return res
+
+
+# ---------------------------------------------------------------------------
+# Achievable ceilings on this GPU, for context (outside every timed step)
+# ---------------------------------------------------------------------------
+
+def ceilings(torch, dev):
+    """hipBLASLt (torch.matmul) on a dense bf16 product of the ep gate_up
+    shape, and a 512 MiB device-to-device copy: what a vendor GEMM and a
+    plain copy reach here, next to the published peaks."""
+    def best_ms(fn, iters=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        best = 1e9
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / iters)
+        return best
+
+    M, K, N = 16384, 4096, 3072
+    a = torch.randn((M, K), device=dev).to(torch.bfloat16)
+    b = torch.randn((K, N), device=dev).to(torch.bfloat16)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    mm = best_ms(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    cp = best_ms(lambda: dst.copy_(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(hipblaslt_bf16_tflops=round(2.0 * M * K * N / (mm * 1e-3) / 1e12, 1),
+                hipblaslt_shape=[M, K, N],
+                d2d_copy_gbs=round(2 * 512 * 2 ** 20 / (cp * 1e-3) / 1e9, 1),
+                note="copy GB/s counts bytes read + written")
 
 
 # ---------------------------------------------------------------------------
@@ -558,7 +624,16 @@ def cpu_baseline(wl, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                cpu_model=model,
                 sample=f"oracle (NumPy float64) expert-block fwd+bwd GEMM chain of experts {done} "
                        f"({rows} of {int(gl.sum())} rows), {flops / 1e9:.1f} GFLOP in {el:.1f} s",
                 seconds=round(el, 2))
@@ -592,9 +667,14 @@ def main():
     mx = None
     if not args.skip_mx:
         mx = run_mx(torch, dev, args)
+    ceil = None
+    if not args.skip_mx and not args.skip_decode:
+        ceil = ceilings(torch, dev)
+        log(f"ceilings: {ceil}")
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu["gpu_speedup"] = round(ep["value"] / cpu["value"], 1)
         log(f"cpu baseline: {cpu}")
     line = {
         "metric": "GMM fwd+bwd TFLOP/s & % bf16 MFMA peak; decode MoE layer HBM GB/s",
@@ -604,6 +684,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ep["ms_per_step"], 4),
+        "step_ms_events": ep["step_ms_events"],
+        "frac_of_attainable": ep["frac_of_attainable"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -624,6 +706,7 @@ def main():
         "decode": decode,
         "prefill": prefill,
         "mxfp8": mx,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -88,6 +88,31 @@ def test_ragged_shapes(dev, M, K, N, gl):
     check_all(dev, x, w, dy, np.array(gl, dtype=np.int64), f"ragged{M}x{K}x{N}")
 
 
+def test_max_experts(dev):
+    """E = 1024 (the API limit): the schedules scan 1024 counts, and the
+    weight gradient takes experts in index order past 256 (no ranking)."""
+    rng = np.random.default_rng(1024)
+    E, M, K, N = 1024, 3000, 64, 136
+    gl = workloads.random_group_list(rng, M, E, empty_frac=0.7, fill=0.95)
+    x = workloads.normal_bf16(rng, (M, K))
+    w = workloads.normal_bf16(rng, (E, K, N), 0.05)
+    dy = workloads.normal_bf16(rng, (M, N))
+    check_all(dev, x, w, dy, gl, "E1024")
+
+
+def test_max_reduction_length(dev):
+    """K = 2^21 (the API limit: 256 rows of 2^21 bf16 still fit the 32-bit
+    buffer offsets): one forward tile runs 65536 reduction steps, the weight
+    gradient has 8192 k-tiles, the input gradient 8192 column tiles."""
+    rng = np.random.default_rng(21)
+    E, M, K, N = 2, 64, 1 << 21, 8
+    gl = np.array([40, 24], dtype=np.int64)
+    x = workloads.normal_bf16(rng, (M, K))
+    w = workloads.normal_bf16(rng, (E, K, N), 0.01)
+    dy = workloads.normal_bf16(rng, (M, N))
+    check_all(dev, x, w, dy, gl, "K=2^21")
+
+
 def test_rows_beyond_R_hold_nan(dev):
     """Capacity rows past R are undefined memory: NaN there must not leak."""
     rng = np.random.default_rng(3)

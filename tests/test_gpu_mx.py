@@ -132,7 +132,15 @@ def _gmm_case(name):
     bf16 and quantised by each side for the small cases, drawn directly as
     MX bytes for the large ones."""
     rng = np.random.default_rng({"tiny": 51, "ragged": 52, "sweep": 53, "decode": 54,
-                                 "ep": 55, "stream_ragged": 56}[name])
+                                 "ep": 55, "stream_ragged": 56, "e1024_stream": 57,
+                                 "e1024_tile": 58}[name])
+    if name.startswith("e1024"):
+        # E = 1024 (the API limit), most experts empty; M_cap <= 8E streams
+        M = 3000 if name == "e1024_stream" else 9000
+        gl = workloads.random_group_list(rng, M, 1024, empty_frac=0.7, fill=0.95)
+        M_cap = int(gl.sum()) + 16
+        x = workloads.normal_bf16(rng, (M_cap, 128))
+        return x, ("bf16", workloads.normal_bf16(rng, (1024, 136, 128), 0.02)), gl
     if name == "ep":
         wl = workloads.ep_slice(with_weights=False, with_acts=False)
         gl = wl["group_list"]
@@ -190,7 +198,8 @@ def _expert_of_rows(gl, rows):
     return np.searchsorted(off, rows, side="right") - 1
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged", "stream_ragged", "sweep", "decode", "ep"])
+@pytest.mark.parametrize("name", ["tiny", "ragged", "stream_ragged", "sweep", "decode", "ep",
+                                  "e1024_stream", "e1024_tile"])
 def test_gmm_mx_fwd(dev, name):
     x, wkind, gl = _gmm_case(name)
     E, N, K = wkind[1].shape

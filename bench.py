@@ -30,9 +30,11 @@ Also in the line:
                   and the ep rank: GB/s, TFLOP/s against the fp8 MFMA peak,
                   fraction of the attainable roofline;
   *_ms_events  -- p10 / p50 / p90 of per-step (per-layer) spans from HIP events,
-                  first call's start to last call's end; they come from the pass
-                  that records an event pair around every call, so they sit a
-                  few percent above ms_per_step / ms_per_layer (wall time);
+                  first call's start to last call's end; they come from a pass
+                  that records an event pair around every call (also the source
+                  of per_call_us), so they sit a few percent above ms_per_step /
+                  ms_per_layer, which are timed with events around the dominant
+                  kernel's launches only (its roofline) or none;
   ceilings     -- hipBLASLt on a dense bf16 product of the ep gate_up shape and
                   a 512 MiB device copy, measured here for context;
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
@@ -209,28 +211,56 @@ def run_ep(torch, dev, args):
     for _ in range(args.warmup):
         step(plain)
     torch.cuda.synchronize()
+    # 1. an instrumented pass (an event pair around every call): the per-call
+    #    breakdown, the per-step spans and which kernel dominates
     timer.collect()
-    t_start = time.perf_counter()
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
     step_ms = timer.spans(9)
     per = timer.collect()
-    assert int(layer.dev_err.item()) == 0, "device error word set during the bench"
-    ms_per_step = wall * 1e3 / args.steps
     flops = ep_gemm_flops(wl["group_list"], H, I)
     total_flops = sum(flops.values())
     mean_ms = {k: float(np.mean(v)) for k, v in per.items()}
     gmm_ms = sum(mean_ms[k] for k in flops)
-    # dominant kernel: the kernel symbol with the largest time per step
     kern_ms = {k: sum(mean_ms[c] for c in calls) for k, calls in EP_KERNELS.items()}
     dom = max(kern_ms, key=kern_ms.get)
     dom_calls = EP_KERNELS[dom]
+    # 2. the timed region: K steps, events only around the dominant kernel's
+    #    launches (its roofline), wall time for the whole step
+    only_dom = lambda name, fn: timer(name, fn) if name in dom_calls else fn()  # noqa: E731
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(only_dom)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    dom_per = timer.collect()
+    assert int(layer.dev_err.item()) == 0, "device error word set during the bench"
+    ms_per_step = wall * 1e3 / args.steps
     dom_flops_per_launch = sum(flops[c] for c in dom_calls) / len(dom_calls)
-    dom_ms_per_launch = kern_ms[dom] / len(dom_calls)
+    dom_ms_per_launch = float(np.mean([v for c in dom_calls for v in dom_per[c]]))
     achieved = dom_flops_per_launch / (dom_ms_per_launch * 1e-3) / 1e12
     traffic = measured_traffic(dom)
+    # the same step with the memory-optimised backward (A recomputed from H,
+    # gradients written over the forward's dead buffers)
+    lm = MoeLayer(LayerShape(R, 1, E, H, I), dev, with_backward=True, low_memory=True)
+
+    def step_lm():
+        lm.forward(x, ids, probs, w1, w2, fused=True, keep_h=True)
+        lm.backward(dyp, w1, w2)
+
+    for _ in range(3):
+        step_lm()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_lm()
+    torch.cuda.synchronize()
+    lm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert int(lm.dev_err.item()) == 0
+    saved = R * (I + 2 * I + H) * 2  # the dA, dH and dX buffers it does without
+    del lm
     t_mfma_ms = total_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3  # the step is MFMA-bound
     res = dict(
         ms_per_step=ms_per_step,
@@ -240,6 +270,11 @@ def run_ep(torch, dev, args):
         gmm_only_tflops=total_flops / (gmm_ms * 1e-3) / 1e12,
         gemm_gflop_per_step=total_flops / 1e9,
         per_call_us={k: round(v * 1e3, 2) for k, v in mean_ms.items()},
+        low_memory_backward=dict(ms_per_step=round(lm_ms, 4),
+                                 tflops=round(total_flops / (lm_ms * 1e-3) / 1e12, 2),
+                                 bytes_saved=saved,
+                                 note="A recomputed from H in the backward; dA, dH, dX written over "
+                                      "the dead A, H, X_perm buffers; wall time, no events"),
         roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 2),
                       peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
@@ -657,6 +692,7 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     ep, wl = run_ep(torch, dev, args)
     log(f"ep: {ep['ms_per_step']:.3f} ms/step, {ep['value']:.1f} TFLOP/s; per call {ep['per_call_us']}")
+    log(f"ep, memory-optimised backward: {ep['low_memory_backward']}")
     decode = prefill = None
     if not args.skip_decode:
         decode = run_decode(torch, dev, args)
@@ -702,6 +738,7 @@ def main():
         "pct_bf16_mfma_peak": round(100.0 * ep["value"] / MFMA_BF16_PEAK_TFLOPS, 2),
         "gmm_only_tflops": round(ep["gmm_only_tflops"], 2),
         "per_call_us": ep["per_call_us"],
+        "low_memory_backward": ep["low_memory_backward"],
         "roofline": ep["roofline"],
         "decode": decode,
         "prefill": prefill,

@@ -61,9 +61,12 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const bf16_t* __restri
     }
 }
 
+// dh may be h itself (in place): a thread reads G, U and dA of its 8
+// columns before it writes dG and dU to the same places, and no other thread
+// touches them -- so h and dh carry no restrict.
 __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(
-    const bf16_t* __restrict__ da, const bf16_t* __restrict__ h, const int64_t* __restrict__ group_list,
-    int E, int64_t M_cap, int64_t I, bf16_t* __restrict__ dh) {
+    const bf16_t* __restrict__ da, const bf16_t* h, const int64_t* __restrict__ group_list,
+    int E, int64_t M_cap, int64_t I, bf16_t* dh) {
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int64_t s_scan[kThreads / 64];

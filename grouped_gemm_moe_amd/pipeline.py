@@ -14,6 +14,14 @@ Backward of the whole layer from dout (the gradient at the layer output):
     dYp, dprobs = moe_unpermute_bwd(dout, Yp, probs); the expert block as
     above; dx = moe_permute_bwd(dX_perm)
 
+Memory-optimised backward (low_memory=True; "03 · grouped GEMM 路径",
+section 4: recompute the activation in the backward instead of keeping it,
+write gradients into dead buffers): the forward's A is not kept; the
+backward recomputes A = swiglu(H) into the dead Yp buffer, writes dA into
+A's buffer, dH over H (swiglu_bwd in place) and dX over X_perm (after dW1
+has read it).  No dA, dH or dX buffer is allocated: S*(I + 2I + H) bf16
+elements fewer, for one extra swiglu pass.
+
 The A8W8-FP (MXFP8) forward ("MegaMoE", A8W8-FP scenario), MoeLayerMX:
     moe_permute_mx (gather + Q_MX) -> gmm_mx_fwd_swiglu(W1; GMM1, SwiGLU and
     Q_MX of A in one call) -> gmm_mx_fwd(W2) -> moe_unpermute
@@ -51,9 +59,11 @@ class MoeLayer:
     """Buffers for one layer shape; forward() and backward() enqueue on the
     current torch stream and never synchronise."""
 
-    def __init__(self, shape: LayerShape, device, with_backward: bool = False):
+    def __init__(self, shape: LayerShape, device, with_backward: bool = False,
+                 low_memory: bool = False):
         s = shape
         self.shape = s
+        self.low_memory = bool(low_memory and with_backward)
         d = device
         bf = torch.bfloat16
         S = s.S
@@ -71,10 +81,17 @@ class MoeLayer:
         ws = max(gmm_workspace_size(s.E, S, k, n, op)
                  for (k, n) in ((s.H, 2 * s.I), (s.I, s.H)) for op in (0, 1, 2))
         self.ws_gmm = torch.empty(ws, dtype=torch.uint8, device=d) if ws > 0 else None
-        if with_backward:
+        if with_backward and self.low_memory:
+            # gradients live in dead forward buffers (see the module docstring)
+            self.da = self.a
+            self.dh = self.h
+            self.dx = self.x_perm
+            self.a_recomputed = self.yp.view(-1)[: S * s.I].view(S, s.I)
+        elif with_backward:
             self.da = torch.empty((S, s.I), dtype=bf, device=d)
             self.dh = torch.empty((S, 2 * s.I), dtype=bf, device=d)
             self.dx = torch.empty((S, s.H), dtype=bf, device=d)
+        if with_backward:
             self.dw1 = torch.empty((s.E, s.H, 2 * s.I), dtype=bf, device=d)
             self.dw2 = torch.empty((s.E, s.I, s.H), dtype=bf, device=d)
             self.dyp = torch.empty((S, s.H), dtype=bf, device=d)
@@ -118,7 +135,19 @@ class MoeLayer:
 
     # -- backward of the expert block --------------------------------------
     def backward(self, dyp, w1, w2):
+        """dYp -> dA, dW2, dH, dX_perm, dW1.  With low_memory, A is
+        recomputed from H first, Yp, A, H and X_perm are overwritten, and
+        dyp must not be the Yp buffer."""
         g = self.tokens_per_expert
+        if self.low_memory:
+            a = self.a_recomputed
+            swiglu(self.h, g, out=a)
+            gmm_bwd_weight(a, dyp, g, out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
+            gmm_bwd_input(dyp, w2, g, out=self.da, ws=self.ws_gmm, dev_err=self.dev_err)
+            swiglu_bwd(self.da, self.h, g, out=self.dh)  # in place over H
+            gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)
+            gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
+            return
         gmm_bwd_input(dyp, w2, g, out=self.da, ws=self.ws_gmm, dev_err=self.dev_err)
         gmm_bwd_weight(self.a, dyp, g, out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
         swiglu_bwd(self.da, self.h, g, out=self.dh)

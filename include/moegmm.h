@@ -204,6 +204,9 @@ moe_status swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64
  *   dh = [dG | dU]  for rows r < R.
  *
  *   da [M_cap, I] bf16, h [M_cap, 2I] bf16, dh [M_cap, 2I] bf16 OUT.
+ * dh may be h (in place, the exception to "outputs must not alias inputs"):
+ * the memory-optimised backward writes dH over the dead H ([MegaBlocks]
+ * section 4, memory-optimised backward: reuse buffers that are dead).
  * ---------------------------------------------------------------------- */
 moe_status swiglu_bwd(const uint16_t* da, const uint16_t* h, const int64_t* group_list, int64_t E,
                       int64_t M_cap, int64_t I, uint16_t* dh, void* stream);

@@ -111,15 +111,20 @@ def test_end_backward_bad_row_map_reported(dev):
     assert_close(dev_f64(dx), oracle.permute_bwd(f64(y), ok, T), "dx with bad rows masked")
 
 
-def test_tiny_full_layer_backward(dev):
+@pytest.mark.parametrize("low_memory", [False, True])
+def test_tiny_full_layer_backward(dev, low_memory):
     """Worked example: forward, then the whole backward from dout; every
     gradient (dYp, dprobs, dA, dH, dX_perm, dW1, dW2, dx) against the oracle
-    chain, which rounds at the same boundary points."""
+    chain, which rounds at the same boundary points.  low_memory: the same
+    gradients from the memory-optimised backward (A recomputed from H,
+    gradients over dead forward buffers)."""
     wl = workloads.tiny()
     d = wl.dims
     T, K, H = d["T"], d["K"], d["H"]
     R = 5
-    layer = MoeLayer(LayerShape(T, K, d["E"], H, d["I"]), dev, with_backward=True)
+    print(f"tiny full-layer backward, low_memory={low_memory}", flush=True)
+    layer = MoeLayer(LayerShape(T, K, d["E"], H, d["I"]), dev, with_backward=True,
+                     low_memory=low_memory)
     w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
     probs_d = torch.from_numpy(wl["probs"]).to(dev)
     layer.forward(bf16_dev(wl["x"], dev), torch.from_numpy(wl["topk_ids"]).to(dev), probs_d, w1, w2)

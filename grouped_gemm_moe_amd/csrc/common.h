@@ -21,16 +21,12 @@ MOE_DEVICE float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16)
 MOE_DEVICE float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 MOE_DEVICE float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-MOE_DEVICE uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
+// Two fp32 values -> packed bf16 (lo in bits 0..15), round to nearest even,
+// NaN stays a (quiet) NaN: one v_cvt_pk_bf16_f32 on gfx950.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 MOE_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // sigma(g) = 1 / (1 + e^-g), the gate of SiLU(g) = g * sigma(g) ("MegaMoE",

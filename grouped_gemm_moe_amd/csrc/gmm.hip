@@ -61,14 +61,14 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
         gemm_tile<kBM, kBN, kWM, kWN, true, false>(
             A + (int64_t)row0 * lda, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid,
             tile_cols, smem, [&](const auto& eng) {
-                eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left);
+                eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem);
             });
     } else {
         bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
         gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
             A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N,
             cols_left, 0, Kred, rows_valid, cols_left, smem,
-            [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left); });
+            [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); });
     }
 }
 
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
     }
     gemm_tile<kBM, kBN, kWM, kWN, false, false>(
         X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0, cnt,
-        rows_valid, cols_valid, smem, [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid); });
+        rows_valid, cols_valid, smem,
+        [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid, smem); });
 }
 
 }  // namespace

@@ -29,8 +29,9 @@
 //    NST-1 steps fly while a step runs its MFMAs.  One barrier per step;
 //    each wave waits only for its own loads of the step about to be read.
 //  * The MFMA is issued with operands swapped (B fragment as the hardware A
-//    operand) so each lane holds 4 consecutive output columns; the epilogue
-//    rounds to bf16 (RNE) and stores 8 bytes per lane, masked to the tile.
+//    operand) so each lane holds 4 consecutive output columns.  The epilogue
+//    rounds to bf16 (RNE) into an LDS image of the tile and writes it out as
+//    whole 128-byte lines with non-temporal stores.
 #pragma once
 
 #include <type_traits>
@@ -322,28 +323,48 @@ struct Engine {
         }
     }
 
-    // lane holds rows (l%32) and 4 consecutive columns per (i, j, g)
-    MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid) const {
+    // Epilogues.  A lane holds rows (l%32) and 4 consecutive columns per
+    // (i, j, g) of its wave's sub-tile, so writing straight from the
+    // accumulators would scatter 8-byte pieces over 32 rows per instruction.
+    // Instead the tile is rounded to bf16 into LDS (the ring is free once
+    // every wave has left the main loop), read back as whole rows and written
+    // 16 bytes per lane, a full 128-byte line per 8 lanes, with non-temporal
+    // stores: the output is not read again by this kernel and should not
+    // displace operand lines in L2.
+    //
+    // Wave image: [WTM rows][64 columns] bf16, 16-byte chunk c of row r at
+    // chunk c ^ ((r >> 1) & 7), so the 32 rows written by one instruction
+    // spread over the banks.
+    MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid,
+                          bf16_t* smem) const {
+        static_assert(WTN == 64, "one 128-byte row segment per wave row");
         const int lane = threadIdx.x & 63;
         const int wid = threadIdx.x >> 6;
         const int wm = wid / WN, wn = wid % WN;
+        __syncthreads();  // every wave is done reading the ring
+        bf16_t* img = smem + wid * (WTM * WTN);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 32 + (lane & 31);
-            if (row >= rows_valid) continue;
-            bf16_t* orow = out + (int64_t)row * ld;
+            const int r = i * 32 + (lane & 31);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int col = wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
-                    if (col < cols_valid) {
-                        u32x2_t pk;
-                        pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                        pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                        *reinterpret_cast<u32x2_t*>(orow + col) = pk;
-                    }
+                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
+                    u32x2_t pk;
+                    pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+                    pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
                 }
+        }
+        // each wave reads back only its own image: no barrier needed
+#pragma unroll
+        for (int it = 0; it < WTM / 8; ++it) {
+            const int r = it * 8 + (lane >> 3), c = lane & 7;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+            const int row = wm * WTM + r, col = wn * WTN + c * 8;
+            if (row < rows_valid && col < cols_valid)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (int64_t)row * ld + col));
         }
     }
 
@@ -351,43 +372,72 @@ struct Engine {
     // holds the gate values G and fragment 1 the up values U of the same 32
     // output columns.  Writes A = SiLU(G) * U (rounded once, from the fp32
     // accumulators) and, when h is given, G and U themselves to h[:, c] and
-    // h[:, pair + c].
+    // h[:, pair + c].  An output row of the tile (BN/2 columns) spans the
+    // WN waves of a wave row, so the images here cover the whole tile:
+    // [BM][BN/2] bf16 each (A and G together fill the ring; U follows in a
+    // second pass), 16-byte chunk c of row r at chunk c ^ (r % 16).
     MOE_DEVICE void store_swiglu(bf16_t* __restrict__ a, int64_t lda, bf16_t* __restrict__ h,
-                                 int64_t ldh, int pair, int rows_valid, int cols_valid) const {
+                                 int64_t ldh, int pair, int rows_valid, int cols_valid,
+                                 bf16_t* smem) const {
         static_assert(TN == 2, "one gate and one up fragment per wave");
+        constexpr int kCols = BN / 2, kChunks = kCols / 8;  // one output row: kChunks 16-byte chunks
+        static_assert(kChunks == 16 && 2 * BM * kCols <= (BM + BN) * BK * kNST, "images fit the ring");
         const int lane = threadIdx.x & 63;
         const int wid = threadIdx.x >> 6;
         const int wm = wid / WN, wn = wid % WN;
+        bf16_t* img_a = smem;
+        bf16_t* img_g = smem + BM * kCols;
+        auto put = [&](bf16_t* img, int r, int c, uint32_t lo, uint32_t hi) {
+            u32x2_t pk;
+            pk[0] = lo;
+            pk[1] = hi;
+            *reinterpret_cast<u32x2_t*>(img + r * kCols + ((c ^ (r & 15)) << 3) + (lane >> 5) * 4) = pk;
+        };
+        // whole rows out: 16 lanes per row, 16 bytes each
+        auto copy_out = [&](const bf16_t* img, bf16_t* dst, int64_t ld) {
+            constexpr int kRowsPerPass = kThreads / kChunks;
+#pragma unroll
+            for (int it = 0; it < BM / kRowsPerPass; ++it) {
+                const int r = it * kRowsPerPass + threadIdx.x / kChunks, c = threadIdx.x % kChunks;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(img + r * kCols + ((c ^ (r & 15)) << 3));
+                if (r < rows_valid && c * 8 < cols_valid)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + (int64_t)r * ld + c * 8));
+            }
+        };
+        __syncthreads();  // every wave is done reading the ring
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 32 + (lane & 31);
-            if (row >= rows_valid) continue;
+            const int r = wm * WTM + i * 32 + (lane & 31);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = wn * 32 + g * 8 + (lane >> 5) * 4;
-                if (col >= cols_valid) continue;
+                const int c = wn * 4 + g;
                 float av[4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float gv = acc[i][0][4 * g + c], uv = acc[i][1][4 * g + c];
-                    av[c] = gv * silu_sigmoid(gv) * uv;
+                for (int q = 0; q < 4; ++q) {
+                    const float gv = acc[i][0][4 * g + q], uv = acc[i][1][4 * g + q];
+                    av[q] = gv * silu_sigmoid(gv) * uv;
                 }
-                u32x2_t pk;
-                pk[0] = pack_bf16x2(av[0], av[1]);
-                pk[1] = pack_bf16x2(av[2], av[3]);
-                *reinterpret_cast<u32x2_t*>(a + (int64_t)row * lda + col) = pk;
-                if (h) {
-                    u32x2_t pg, pu;
-                    pg[0] = pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]);
-                    pg[1] = pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]);
-                    pu[0] = pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]);
-                    pu[1] = pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]);
-                    bf16_t* hr = h + (int64_t)row * ldh + col;
-                    *reinterpret_cast<u32x2_t*>(hr) = pg;
-                    *reinterpret_cast<u32x2_t*>(hr + pair) = pu;
-                }
+                put(img_a, r, c, pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+                if (h)
+                    put(img_g, r, c, pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]),
+                        pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]));
             }
         }
+        __syncthreads();
+        copy_out(img_a, a, lda);
+        if (!h) return;
+        copy_out(img_g, h, ldh);
+        __syncthreads();  // image A is read out; U takes its place
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                put(img_a, r, wn * 4 + g, pack_bf16x2(acc[i][1][4 * g], acc[i][1][4 * g + 1]),
+                    pack_bf16x2(acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]));
+        }
+        __syncthreads();
+        copy_out(img_a, h + pair, ldh);
     }
 };
 

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
         bf16_t* y = Y + (int64_t)row0 * N + n0;
         gemm_tile_mx<kBM, kBN, kWM, kWN>(
             Xt, rows_valid, XSt, ld_xs, We, cols_left, 0, Se, ld_ws, K, rows_valid, cols_left, smem,
-            ssc, [&](const auto& eng) { eng.store(y, N, rows_valid, cols_left); });
+            ssc, [&](const auto& eng) { eng.store(y, N, rows_valid, cols_left, smem); });
     }
 }
 

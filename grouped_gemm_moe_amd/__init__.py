@@ -77,11 +77,24 @@ def _out(out, shape, dtype, device, name):
     return out
 
 
-def _workspace(nbytes: int, device, ws):
+_ZEROED_WS = {}
+
+
+def _workspace(nbytes: int, device, ws, zeroed: bool = False):
+    """The caller's workspace, else a new one.  A `zeroed` workspace (GMM tile
+    queues) must be zero-filled before its first use and is left zero-filled
+    by every call, so one per (device, stream) is kept and reused."""
     if nbytes == 0:
         return None, 0
     if ws is not None:
         return ws, ws.numel() * ws.element_size()
+    if zeroed:
+        key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+        buf = _ZEROED_WS.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            _ZEROED_WS[key] = buf
+        return buf, buf.numel()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
@@ -128,7 +141,7 @@ def gmm_fwd(x, w, group_list, *, out=None, ws=None, dev_err=None):
     if K2 != K or group_list.shape[0] != E:
         raise MoeError("shape mismatch: x [M, K], w [E, K, N], group_list [E]")
     y = _out(out, (M, N), torch.bfloat16, x.device, "y")
-    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_FWD), x.device, ws)
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_FWD), x.device, ws, zeroed=True)
     _check(library().gmm_fwd(_ptr(x), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(y), _ptr(ws),
                              ws_bytes, _ptr(dev_err), _stream(x.device)), "gmm_fwd")
     return y
@@ -148,7 +161,7 @@ def gmm_fwd_swiglu(x, w1, group_list, *, out=None, h_out=None, ws=None, dev_err=
     a = _out(out, (M, I), torch.bfloat16, x.device, "a")
     if h_out is not None:
         _out(h_out, (M, N2), torch.bfloat16, x.device, "h_out")
-    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N2, OP_FWD), x.device, ws)
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N2, OP_FWD), x.device, ws, zeroed=True)
     _check(library().gmm_fwd_swiglu(_ptr(x), _ptr(w1), _ptr(group_list), E, M, K, I, _ptr(a),
                                     _ptr(h_out), _ptr(ws), ws_bytes, _ptr(dev_err),
                                     _stream(x.device)), "gmm_fwd_swiglu")
@@ -165,7 +178,7 @@ def gmm_bwd_input(dy, w, group_list, *, out=None, ws=None, dev_err=None):
     if N2 != N or group_list.shape[0] != E:
         raise MoeError("shape mismatch: dy [M, N], w [E, K, N], group_list [E]")
     dx = _out(out, (M, K), torch.bfloat16, dy.device, "dx")
-    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_INPUT), dy.device, ws)
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_INPUT), dy.device, ws, zeroed=True)
     _check(library().gmm_bwd_input(_ptr(dy), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(dx),
                                    _ptr(ws), ws_bytes, _ptr(dev_err), _stream(dy.device)),
            "gmm_bwd_input")
@@ -183,7 +196,7 @@ def gmm_bwd_weight(x, dy, group_list, *, out=None, ws=None, dev_err=None):
     if M2 != M:
         raise MoeError("shape mismatch: x [M, K], dy [M, N]")
     dw = _out(out, (E, K, N), torch.bfloat16, x.device, "dw")
-    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_WEIGHT), x.device, ws)
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD_WEIGHT), x.device, ws, zeroed=True)
     _check(library().gmm_bwd_weight(_ptr(x), _ptr(dy), _ptr(group_list), E, M, K, N, _ptr(dw),
                                     _ptr(ws), ws_bytes, _ptr(dev_err), _stream(x.device)),
            "gmm_bwd_weight")

@@ -58,6 +58,7 @@ moe_status check_gmm_common(const void* a, const void* b, const void* gl, const 
         E * K * N > (int64_t(1) << 40))
         return MOE_ERR_INVALID;
     if (ws_need > 0 && (ws == nullptr || ws_bytes < ws_need)) return MOE_ERR_WORKSPACE;
+    if (ws_need > 0 && !aligned(ws, 16)) return MOE_ERR_INVALID;
     return MOE_OK;
 }
 

@@ -29,6 +29,13 @@ namespace {
 // ---------------------------------------------------------------------------
 enum RowsMode { kFwd = 0, kDx = 1, kSwiGLU = 2 };
 
+// Tile queue of the weight gradient, in the caller's workspace: one counter
+// per XCD and a count of finished workgroups, 128 bytes apart.  The last
+// workgroup to finish puts them back to zero, so the workspace is
+// zero-filled again when the kernel ends.
+constexpr int kQueueStride = 32;  // uint32 per slot
+constexpr int kQueueWords = 9 * kQueueStride;
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
@@ -75,51 +82,42 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
 // ---------------------------------------------------------------------------
 // Weight gradient: dw[e] = x[rows_e]^T @ dy[rows_e].  Tiles (expert, k-tile,
 // n-tile), experts in descending row count (ties by index) so the longest
-// reductions start first.  Inside an expert, each of the 8 XCDs takes one
-// rectangle of the (k-tile, n-tile) grid, so its L2 streams a few x and dy
-// panels rather than nearly all of them.  Both operands are outer-contiguous;
-// the reduction runs over the expert's rows, zero-filled past its last row.
-// Empty experts write zeros.
+// reductions start first.  Both operands are outer-contiguous; the reduction
+// runs over the expert's rows, zero-filled past its last row.  Empty experts
+// write zeros.
+//
+// Persistent workgroups (a multiple of 8, at most one per CU) take tiles from
+// a queue.  Tile t belongs to XCD t % 8 (workgroup b runs on XCD b % 8), so
+// each XCD has its own counter and, with KT*NT % 8 == 0, takes one kx x (8/kx)
+// rectangle of every expert's (k-tile, n-tile) grid: its L2 then streams a
+// few x and dy panels rather than nearly all of them.  A workgroup computes
+// the schedule once and fetches its next tile while the current one runs;
+// the per-tile cost of a fresh workgroup (group_list read, ranking, launch)
+// matters here because most experts' tiles are short.
 // ---------------------------------------------------------------------------
-constexpr int kMaxRankedExperts = 256;  // beyond this, experts run in index order
-
-__global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
-    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int32_t* dev_err) {
+    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, uint32_t* __restrict__ queue,
+    int32_t* dev_err) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
-    __shared__ int s_pick;
-    // schedule arrays: in the last stage, which no load touches before the
-    // first barrier of the main loop
-    int* s_off = reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK);
-    int* s_cnt = s_off + kMaxExperts;
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_order[kMaxExperts];
+    __shared__ int s_next;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
-    const int rank = blockIdx.x / (KT * NT);
-    const int rem = blockIdx.x % (KT * NT);
-    if (E <= kMaxRankedExperts) {
-        // the expert whose (count desc, index asc) rank is `rank`
-        for (int e = threadIdx.x; e < E; e += kThreads) {
-            const int c = s_cnt[e];
-            int r = 0;
-            for (int f = 0; f < E; ++f) {
-                const int cf = s_cnt[f];
-                r += (cf > c) || (cf == c && f < e);
-            }
-            if (r == rank) s_pick = e;
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        const int c = s_cnt[e];
+        int r = 0;
+        for (int f = 0; f < E; ++f) {
+            const int cf = s_cnt[f];
+            r += (cf > c) || (cf == c && f < e);
         }
-    } else if (threadIdx.x == 0) {
-        s_pick = rank;
+        s_order[r] = e;
     }
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(s_pick);
-    // Workgroup ids go round-robin to the 8 XCDs and every expert's tile
-    // range starts at a multiple of 8 (KT*NT % 8 == 0): give XCD rem % 8 one
-    // rectangle of the expert's (k-tile, n-tile) grid, kx x (8/kx) rectangles
-    // chosen to minimise the x and dy panels each XCD reads.
-    int kx = 0;
-    {
+    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
+    const int per_e = KT * NT;
+    int kx = 0;  // rectangle shape: kx k-tile bands x (8/kx) n-tile bands
+    if (per_e % 8 == 0) {
         int best = 0x7fffffff;
         for (int c = 1; c <= 8; c *= 2) {
             const int ny = 8 / c;
@@ -129,43 +127,81 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_dw_kernel(
             }
         }
     }
-    int kt_out, nt;
-    if (kx) {
-        const int ny = 8 / kx, KTr = KT / kx, NTr = NT / ny;
-        const int x = rem & 7, p = rem >> 3;
-        kt_out = (x / ny) * KTr + p / NTr;
-        nt = (x % ny) * NTr + p % NTr;
-    } else {
-        kt_out = rem / NT;
-        nt = rem % NT;
-    }
-
-    const int k0 = kt_out * kBM, n0 = nt * kBN;
-    const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
-    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
-    __syncthreads();  // schedule arrays are dead from here on
-
-    const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
-    const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
-    bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
-    if (cnt == 0) {
-        constexpr int CPR = kBN / 8;
-        for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
-            const int row = u / CPR, c = u % CPR;
-            if (row < rows_valid && c * 8 < cols_valid)
-                st16(out + (int64_t)row * N + c * 8, u32x4_t{0u, 0u, 0u, 0u});
+    __syncthreads();
+    const int total = E * per_e;
+    const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
+    const int mine = (total - xcd + 7) / 8;  // tiles 8j + xcd, j < mine
+    uint32_t* ctr = queue + xcd * kQueueStride;
+    int j = blockIdx.x >> 3;  // first tile static, later ones from the counter
+    while (j < mine) {
+        int nj = 0;
+        if (threadIdx.x == 0) nj = wg_per_xcd + (int)atomicAdd(ctr, 1u);
+        const int t = 8 * j + xcd;
+        const int rank = t / per_e, rem = t % per_e;
+        int kt_out, nt;
+        if (kx) {
+            const int ny = 8 / kx, KTr = KT / kx, NTr = NT / ny;
+            const int x = rem & 7, p = rem >> 3;
+            kt_out = (x / ny) * KTr + p / NTr;
+            nt = (x % ny) * NTr + p % NTr;
+        } else {
+            kt_out = rem / NT;
+            nt = rem % NT;
         }
-        return;
+        const int e = __builtin_amdgcn_readfirstlane(s_order[rank]);
+        const int k0 = kt_out * kBM, n0 = nt * kBN;
+        const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
+        const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+        const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
+        const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
+        bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
+        if (cnt == 0) {
+            constexpr int CPR = kBN / 8;
+            for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
+                const int row = u / CPR, c = u % CPR;
+                if (row < rows_valid && c * 8 < cols_valid)
+                    st16(out + (int64_t)row * N + c * 8, u32x4_t{0u, 0u, 0u, 0u});
+            }
+        } else {
+            gemm_tile<kBM, kBN, kWM, kWN, false, false>(
+                X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0,
+                cnt, rows_valid, cols_valid, smem,
+                [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid, smem); });
+        }
+        if (threadIdx.x == 0) s_next = nj;
+        __syncthreads();  // the ring and the output image are free again
+        j = __builtin_amdgcn_readfirstlane(s_next);
     }
-    gemm_tile<kBM, kBN, kWM, kWN, false, false>(
-        X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0, cnt,
-        rows_valid, cols_valid, smem,
-        [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid, smem); });
+    // Every counter fetch of this workgroup has returned; the last workgroup
+    // to get here resets the queue for the next call.
+    if (threadIdx.x == 0) {
+        __threadfence();
+        if (atomicAdd(queue + 8 * kQueueStride, 1u) == gridDim.x - 1) {
+            for (int x = 0; x < 8; ++x) atomicExch(queue + x * kQueueStride, 0u);
+            atomicExch(queue + 8 * kQueueStride, 0u);
+        }
+    }
+}
+
+// Compute units of the current device (cached per device).
+int num_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
 }
 
 }  // namespace
 
-size_t gmm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) { return 0; }
+size_t gmm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int op) {
+    return op == MOE_GMM_OP_BWD_WEIGHT ? kQueueWords * sizeof(uint32_t) : 0;
+}
 
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void*,
@@ -193,10 +229,14 @@ hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int
 
 hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
                                  int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw,
-                                 void*, int32_t* dev_err, hipStream_t stream) {
-    const int64_t grid = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+                                 void* ws, int32_t* dev_err, hipStream_t stream) {
+    const int64_t tiles = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t need = (tiles + 7) / 8 * 8;
+    int64_t grid = num_cus() / 8 * 8;
+    if (grid > need) grid = need;
     hipLaunchKernelGGL(gmm_dw_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, dy,
-                       group_list, (int)E, M_cap, (int)K, (int)N, dw, dev_err);
+                       group_list, (int)E, M_cap, (int)K, (int)N, dw, static_cast<uint32_t*>(ws),
+                       dev_err);
     return hipGetLastError();
 }
 

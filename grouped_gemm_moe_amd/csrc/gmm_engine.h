@@ -75,6 +75,12 @@ MOE_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
                                              0x00020000);
 }
 
+// Non-temporal 16-byte store of lane data to base + byte offset `off`
+// (base wave-uniform); an offset of kOOB drops the lane's store.
+MOE_DEVICE void store_nt16(u32x4_t v, const void* base, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(base), off, 0, 2 /* nt */);
+}
+
 // Wave index as a scalar (the LDS-DMA destination must be wave-uniform).
 MOE_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -338,8 +344,10 @@ struct Engine {
     MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid,
                           bf16_t* smem) const {
         static_assert(WTN == 64, "one 128-byte row segment per wave row");
-        const int lane = threadIdx.x & 63;
-        const int wid = threadIdx.x >> 6;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
+        const int lane = tid & 63;
+        const int wid = wave_id();
         const int wm = wid / WN, wn = wid % WN;
         __syncthreads();  // every wave is done reading the ring
         bf16_t* img = smem + wid * (WTM * WTN);
@@ -357,14 +365,23 @@ struct Engine {
                     *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
                 }
         }
-        // each wave reads back only its own image: no barrier needed
+        // Each wave reads back only its own image (no barrier): all reads
+        // first, then one unconditional store per 8 rows, masked lanes
+        // getting an out-of-range offset, so the reads overlap each other.
+        constexpr int kIt = WTM / 8;
+        u32x4_t v[kIt];
 #pragma unroll
-        for (int it = 0; it < WTM / 8; ++it) {
+        for (int it = 0; it < kIt; ++it) {
             const int r = it * 8 + (lane >> 3), c = lane & 7;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
-            const int row = wm * WTM + r, col = wn * WTN + c * 8;
-            if (row < rows_valid && col < cols_valid)
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (int64_t)row * ld + col));
+            v[it] = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+        }
+        const int c = lane & 7;
+        const uint32_t lane_off = (uint32_t)(((int64_t)(lane >> 3) * ld + c * 8) * 2);
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int row = wm * WTM + it * 8 + (lane >> 3), col = wn * WTN + c * 8;
+            const bool ok = row < rows_valid && col < cols_valid;
+            store_nt16(v[it], out + (int64_t)(wm * WTM + it * 8) * ld + wn * WTN, ok ? lane_off : kOOB);
         }
     }
 
@@ -382,8 +399,10 @@ struct Engine {
         static_assert(TN == 2, "one gate and one up fragment per wave");
         constexpr int kCols = BN / 2, kChunks = kCols / 8;  // one output row: kChunks 16-byte chunks
         static_assert(kChunks == 16 && 2 * BM * kCols <= (BM + BN) * BK * kNST, "images fit the ring");
-        const int lane = threadIdx.x & 63;
-        const int wid = threadIdx.x >> 6;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
+        const int lane = tid & 63;
+        const int wid = wave_id();
         const int wm = wid / WN, wn = wid % WN;
         bf16_t* img_a = smem;
         bf16_t* img_g = smem + BM * kCols;
@@ -393,15 +412,25 @@ struct Engine {
             pk[1] = hi;
             *reinterpret_cast<u32x2_t*>(img + r * kCols + ((c ^ (r & 15)) << 3) + (lane >> 5) * 4) = pk;
         };
-        // whole rows out: 16 lanes per row, 16 bytes each
+        // whole rows out: 16 lanes per row, 16 bytes each; a wave covers 4
+        // rows per pass.  All reads first, then unconditional stores (masked
+        // lanes get an out-of-range offset).
         auto copy_out = [&](const bf16_t* img, bf16_t* dst, int64_t ld) {
             constexpr int kRowsPerPass = kThreads / kChunks;
+            constexpr int kIt = BM / kRowsPerPass;
+            const int c = lane % kChunks;
+            u32x4_t v[kIt];
 #pragma unroll
-            for (int it = 0; it < BM / kRowsPerPass; ++it) {
-                const int r = it * kRowsPerPass + threadIdx.x / kChunks, c = threadIdx.x % kChunks;
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(img + r * kCols + ((c ^ (r & 15)) << 3));
-                if (r < rows_valid && c * 8 < cols_valid)
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + (int64_t)r * ld + c * 8));
+            for (int it = 0; it < kIt; ++it) {
+                const int r = it * kRowsPerPass + wid * 4 + lane / kChunks;
+                v[it] = *reinterpret_cast<const u32x4_t*>(img + r * kCols + ((c ^ (r & 15)) << 3));
+            }
+            const uint32_t lane_off = (uint32_t)(((int64_t)(lane / kChunks) * ld + c * 8) * 2);
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int r0 = it * kRowsPerPass + wid * 4;
+                const bool ok = r0 + lane / kChunks < rows_valid && c * 8 < cols_valid;
+                store_nt16(v[it], dst + (int64_t)r0 * ld, ok ? lane_off : kOOB);
             }
         };
         __syncthreads();  // every wave is done reading the ring

@@ -80,7 +80,8 @@ class MoeLayer:
                                    dtype=torch.uint8, device=d)
         ws = max(gmm_workspace_size(s.E, S, k, n, op)
                  for (k, n) in ((s.H, 2 * s.I), (s.I, s.H)) for op in (0, 1, 2))
-        self.ws_gmm = torch.empty(ws, dtype=torch.uint8, device=d) if ws > 0 else None
+        # tile queues: zero-filled once, left zero-filled by every call
+        self.ws_gmm = torch.zeros(ws, dtype=torch.uint8, device=d) if ws > 0 else None
         if with_backward and self.low_memory:
             # gradients live in dead forward buffers (see the module docstring)
             self.da = self.a

@@ -127,10 +127,14 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
  * bf16 products accumulate in fp32; each output is rounded once (RNE).
  * w[e] of an empty expert is never read.
  * ---------------------------------------------------------------------- */
-/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  Every op currently needs
- * none (0): each workgroup derives its tile from group_list in LDS.  Callers
- * pass a workspace of the queried size (NULL for 0) so that a future kernel
- * needing one does not change the calls. */
+/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd_weight needs 1152
+ * bytes (its tile queue: counters the kernel increments with atomics); the
+ * other ops need none (0) and take NULL.  A workspace that is needed must be
+ * 16-byte aligned (else MOE_ERR_INVALID) and zero-filled before its first
+ * use; every call leaves it zero-filled again, so one workspace serves any
+ * number of calls issued one after another.  Calls that may run at the same
+ * time (on different streams) need distinct workspaces.  Too small or NULL:
+ * MOE_ERR_WORKSPACE. */
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
 #define MOE_GMM_OP_FWD 0
 #define MOE_GMM_OP_BWD_INPUT 1
@@ -180,6 +184,8 @@ moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* g
  *   dw [E, K, N] bf16 OUT -- every expert written; exact zeros for n_e == 0.
  * The reduction order of every output is fixed, so the result is
  * bit-reproducible whatever order the tiles run in.
+ * Workspace: gmm_workspace_size(E, M_cap, K, N, MOE_GMM_OP_BWD_WEIGHT) bytes,
+ * zero-filled before the first call (left zero-filled by every call).
  * ---------------------------------------------------------------------- */
 moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,

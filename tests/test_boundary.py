@@ -64,8 +64,10 @@ def test_workspace_queries(lib):
     assert lib.moe_permute_workspace_size(4096, 8, 128) >= 32 * 128 * 4
     assert lib.moe_permute_workspace_size(0, 8, 128) >= 0
     assert lib.moe_permute_workspace_size(-1, 8, 128) == 0
-    for op in range(3):
+    # forward and input gradient need none; the weight gradient its tile queue
+    for op in range(2):
         assert lib.gmm_workspace_size(32, 16384, 4096, 3072, op) == 0
+    assert lib.gmm_workspace_size(32, 16384, 4096, 3072, 2) == 1152
 
 
 # fake but aligned non-null device addresses: validation must reject the call
@@ -91,6 +93,11 @@ def test_gmm_rejects_bad_arguments(lib):
     assert lib.gmm_bwd_input(A16, MIS, A16c, 4, 64, 64, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID
     assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, None, ws, 0, None, None) == MOE_ERR_NULL
     assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, MIS, ws, 0, None, None) == MOE_ERR_INVALID
+    # the weight gradient's tile queue: missing, short or misaligned workspace
+    need = lib.gmm_workspace_size(4, 64, 64, 64, 2)
+    assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, None, need, None, None) == MOE_ERR_WORKSPACE
+    assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, ws, need - 1, None, None) == MOE_ERR_WORKSPACE
+    assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, MIS, need, None, None) == MOE_ERR_INVALID
     # rows longer than 32-bit tile offsets can address, and oversized products
     big = 1 << 22
     assert lib.gmm_fwd(A16, A16b, A16c, 4, 64, big, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID

@@ -276,3 +276,27 @@ def test_ep_full_size_sampled(dev):
         assert_close(got, xe.T @ dhe, f"ep dW1 expert {e} rows {ks.tolist()}")
         dw_host[e] = True
     assert len(dw_host) == int((gl > 0).sum())
+
+
+def test_dw_tile_queue_workspace(dev):
+    """gmm_bwd_weight's tile queue lives in the caller's workspace: the call
+    leaves it zero-filled, so back-to-back calls of different shapes through
+    one workspace give the same bits as calls with fresh workspaces."""
+    rng = np.random.default_rng(11)
+    ws = torch.zeros(moe.gmm_workspace_size(8, 1000, 520, 264, moe.OP_BWD_WEIGHT), dtype=torch.uint8,
+                     device=dev)
+    cases = [(1000, 520, 264, [300, 0, 200, 100, 0, 150, 250, 0]), (300, 64, 64, [100, 100, 100]),
+             (1000, 520, 264, [0, 0, 1000, 0, 0, 0, 0, 0])]
+    for M, K, N, gl in cases:
+        print(f"dw queue: M={M} K={K} N={N} E={len(gl)}", flush=True)
+        x = bf16_dev(workloads.normal_bf16(rng, (M, K)), dev)
+        dy = bf16_dev(workloads.normal_bf16(rng, (M, N)), dev)
+        g = _gl(dev, gl)
+        shared = moe.gmm_bwd_weight(x, dy, g, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0, "workspace not left zero-filled"
+        fresh = moe.gmm_bwd_weight(x, dy, g, ws=torch.zeros_like(ws))
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_bits(shared), dev_bits(fresh))
+        assert_close(f64(dev_bits(shared)), oracle.gmm_bwd_weight(f64(dev_bits(x)), f64(dev_bits(dy)), gl),
+                     "dw queue")

@@ -9,8 +9,8 @@ one pass of the whole hot path:
     moe_permute (top_k=1 local re-routing, histogram)
     -> gmm_fwd_swiglu(W1; writes A and, for the backward, H) -> gmm_fwd(W2)
     -> moe_unpermute
-    -> gmm_bwd_input(W2) -> gmm_bwd_weight(dW2) -> swiglu_bwd
-    -> gmm_bwd_input(W1) -> gmm_bwd_weight(dW1)
+    -> gmm_bwd(W2: dA and dW2 in one launch) -> swiglu_bwd
+    -> gmm_bwd(W1: dX and dW1 in one launch)
 
 ``value`` = algorithmic GEMM FLOPs of the step (real rows only, 6 GEMMs)
 divided by the wall time of the whole step, inputs resident in HBM.
@@ -115,7 +115,12 @@ def percentiles(ms):
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gmm_dw_kernel_hbm_traffic_ep_rank.md")
+def traffic_profile(kernel):
+    """The committed HBM-counter summary of `kernel` on the ep step."""
+    stem = re.sub(r"[^A-Za-z0-9_]+", "_", kernel).strip("_")
+    return os.path.join(ROOT, "profiles", f"{stem}_hbm_traffic_ep_rank.md")
+
+
 KERNEL_SOURCES = ["grouped_gemm_moe_amd/csrc/gmm.hip", "grouped_gemm_moe_amd/csrc/gmm_engine.h",
                   "grouped_gemm_moe_amd/csrc/common.h"]
 
@@ -133,7 +138,7 @@ def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None if it is missing or was taken on different kernel source."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(traffic_profile(kernel)).read()
     except OSError:
         return None
     vals = dict(re.findall(r"^- (\w+): `([^`]+)`", text, flags=re.M))
@@ -154,17 +159,16 @@ def ep_gemm_flops(gl, H, I):
     R = int(np.sum(gl))
     fwd1 = 2.0 * R * H * 2 * I
     fwd2 = 2.0 * R * I * H
+    # each backward call computes the input and the weight gradient
     return {"gmm_fwd_swiglu": fwd1, "gmm_fwd_down": fwd2,
-            "gmm_bwd_input_down": fwd2, "gmm_bwd_weight_down": fwd2,
-            "gmm_bwd_input_gate_up": fwd1, "gmm_bwd_weight_gate_up": fwd1}
+            "gmm_bwd_down": 2 * fwd2, "gmm_bwd_gate_up": 2 * fwd1}
 
 
 # libmoegmm kernel behind each call of the step (kernel symbol -> calls)
 EP_KERNELS = {
     "gmm_rows_kernel<fwd+swiglu>": ["gmm_fwd_swiglu"],
     "gmm_rows_kernel<fwd>": ["gmm_fwd_down"],
-    "gmm_rows_kernel<dX>": ["gmm_bwd_input_down", "gmm_bwd_input_gate_up"],
-    "gmm_dw_kernel": ["gmm_bwd_weight_down", "gmm_bwd_weight_gate_up"],
+    "gmm_bwd_kernel": ["gmm_bwd_down", "gmm_bwd_gate_up"],
 }
 
 
@@ -187,8 +191,7 @@ def run_ep(torch, dev, args):
     timer = KernelTimer(torch)
     g = layer.tokens_per_expert
 
-    from grouped_gemm_moe_amd import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu,
-                                      moe_unpermute, swiglu_bwd)
+    from grouped_gemm_moe_amd import gmm_bwd, gmm_fwd, gmm_fwd_swiglu, moe_unpermute, swiglu_bwd
 
     def step(t):
         t("moe_permute", lambda: layer.permute(x, ids))
@@ -198,14 +201,11 @@ def run_ep(torch, dev, args):
         t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp, dev_err=layer.dev_err))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out,
                                                  dev_err=layer.dev_err))
-        t("gmm_bwd_input_down", lambda: gmm_bwd_input(dyp, w2, g, out=layer.da, dev_err=layer.dev_err))
-        t("gmm_bwd_weight_down", lambda: gmm_bwd_weight(layer.a, dyp, g, out=layer.dw2,
-                                                        dev_err=layer.dev_err))
+        t("gmm_bwd_down", lambda: gmm_bwd(layer.a, dyp, w2, g, dx_out=layer.da, dw_out=layer.dw2,
+                                          ws=layer.ws_gmm, dev_err=layer.dev_err))
         t("swiglu_bwd", lambda: swiglu_bwd(layer.da, layer.h, g, out=layer.dh))
-        t("gmm_bwd_input_gate_up", lambda: gmm_bwd_input(layer.dh, w1, g, out=layer.dx,
-                                                         dev_err=layer.dev_err))
-        t("gmm_bwd_weight_gate_up", lambda: gmm_bwd_weight(layer.x_perm, layer.dh, g, out=layer.dw1,
-                                                           dev_err=layer.dev_err))
+        t("gmm_bwd_gate_up", lambda: gmm_bwd(layer.x_perm, layer.dh, w1, g, dx_out=layer.dx,
+                                             dw_out=layer.dw1, ws=layer.ws_gmm, dev_err=layer.dev_err))
 
     plain = lambda name, fn: fn()  # noqa: E731
     for _ in range(args.warmup):
@@ -217,7 +217,7 @@ def run_ep(torch, dev, args):
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
-    step_ms = timer.spans(9)
+    step_ms = timer.spans(7)
     per = timer.collect()
     flops = ep_gemm_flops(wl["group_list"], H, I)
     total_flops = sum(flops.values())

@@ -23,7 +23,8 @@ import torch
 from . import _lib as _L
 
 __all__ = [
-    "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "swiglu",
+    "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
+    "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
     "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu",
@@ -33,7 +34,7 @@ __all__ = [
 DEVERR_EXPERT_ID = 1
 DEVERR_GROUP_LIST = 2
 DEVERR_ROW_MAP = 4
-OP_FWD, OP_BWD_INPUT, OP_BWD_WEIGHT = 0, 1, 2
+OP_FWD, OP_BWD_INPUT, OP_BWD_WEIGHT, OP_BWD = 0, 1, 2, 3
 
 
 class MoeError(RuntimeError):
@@ -201,6 +202,27 @@ def gmm_bwd_weight(x, dy, group_list, *, out=None, ws=None, dev_err=None):
                                     _ptr(ws), ws_bytes, _ptr(dev_err), _stream(x.device)),
            "gmm_bwd_weight")
     return dw
+
+
+def gmm_bwd(x, dy, w, group_list, *, dx_out=None, dw_out=None, ws=None, dev_err=None):
+    """(dx, dw): dx[rows_e] = dy[rows_e] @ w[e]^T and dw[e] = x[rows_e]^T @ dy[rows_e]
+    in one launch; bit-identical to gmm_bwd_input and gmm_bwd_weight."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(dy, "dy", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, K = x.shape
+    M2, N = dy.shape
+    E = group_list.shape[0]
+    if M2 != M or tuple(w.shape) != (E, K, N):
+        raise MoeError("shape mismatch: x [M, K], dy [M, N], w [E, K, N]")
+    dx = _out(dx_out, (M, K), torch.bfloat16, x.device, "dx")
+    dw = _out(dw_out, (E, K, N), torch.bfloat16, x.device, "dw")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD), x.device, ws, zeroed=True)
+    _check(library().gmm_bwd(_ptr(x), _ptr(dy), _ptr(w), _ptr(group_list), E, M, K, N, _ptr(dx),
+                             _ptr(dw), _ptr(ws), ws_bytes, _ptr(dev_err), _stream(x.device)),
+           "gmm_bwd")
+    return dx, dw
 
 
 def swiglu(h, group_list, *, out=None):

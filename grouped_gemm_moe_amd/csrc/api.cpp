@@ -45,6 +45,13 @@ moe_status check_gmm_mx(const void* xq, const void* xs, int64_t ld_xs, const voi
     return MOE_OK;
 }
 
+// Byte ranges [a, a + na) and [b, b + nb) share an address (empty ranges never do).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
 moe_status check_gmm_common(const void* a, const void* b, const void* gl, const void* out,
                             int64_t E, int64_t M_cap, int64_t K, int64_t N, size_t ws_need,
                             size_t ws_bytes, const void* ws) {
@@ -77,7 +84,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 4; }
+int moegmm_abi_version(void) { return 5; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -155,6 +162,25 @@ moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* 
     if (!aligned(dw, 16)) return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_gmm_bwd_weight(x, dy, group_list, E, M_cap, K, N, dw, ws,
                                                   dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
+                   int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx, uint16_t* dw,
+                   void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!dw || !dx) return MOE_ERR_NULL;
+    if (M_cap > 0 && (!x || !dy)) return MOE_ERR_NULL;
+    moe_status st = check_gmm_common(dy ? dy : w, w, group_list, dx, E, M_cap, K, N,
+                                     moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_BWD),
+                                     ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(dw, 16)) return MOE_ERR_INVALID;
+    const size_t bx = (size_t)(M_cap * K) * 2, bdy = (size_t)(M_cap * N) * 2, bw = (size_t)(E * K * N) * 2;
+    if (overlaps(dx, bx, x, bx) || overlaps(dx, bx, dy, bdy) || overlaps(dx, bx, w, bw) ||
+        overlaps(dx, bx, dw, bw) || overlaps(dw, bw, x, bx) || overlaps(dw, bw, dy, bdy) ||
+        overlaps(dw, bw, w, bw))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_bwd(x, dy, w, group_list, E, M_cap, K, N, dx, dw, ws, dev_err,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 moe_status swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,

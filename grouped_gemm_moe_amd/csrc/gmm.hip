@@ -95,6 +95,88 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
 // the per-tile cost of a fresh workgroup (group_list read, ranking, launch)
 // matters here because most experts' tiles are short.
 // ---------------------------------------------------------------------------
+// Weight-gradient schedule, computed once per workgroup: s_order[r] = the
+// expert of rank r (descending row count, ties by index) and the tile grid.
+struct DwSched {
+    int KT, NT, per_e, kx;  // kx: rectangle of kx k-tile bands x (8/kx) n-tile bands, or 0
+};
+
+MOE_DEVICE DwSched dw_schedule(const int* s_cnt, int E, int K, int N, int* s_order) {
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        const int c = s_cnt[e];
+        int r = 0;
+        for (int f = 0; f < E; ++f) {
+            const int cf = s_cnt[f];
+            r += (cf > c) || (cf == c && f < e);
+        }
+        s_order[r] = e;
+    }
+    DwSched ds;
+    ds.KT = (K + kBM - 1) / kBM;
+    ds.NT = (N + kBN - 1) / kBN;
+    ds.per_e = ds.KT * ds.NT;
+    ds.kx = 0;
+    if (ds.per_e % 8 == 0) {
+        int best = 0x7fffffff;
+        for (int c = 1; c <= 8; c *= 2) {
+            const int ny = 8 / c;
+            if (ds.KT % c == 0 && ds.NT % ny == 0 && ds.KT / c + ds.NT / ny < best) {
+                best = ds.KT / c + ds.NT / ny;
+                ds.kx = c;
+            }
+        }
+    }
+    __syncthreads();
+    return ds;
+}
+
+// Weight-gradient tile t (XCD t % 8): dw[e][k0.., n0..] over the expert's rows.
+MOE_DEVICE void dw_tile(int t, const DwSched& ds, const int* s_off, const int* s_cnt, const int* s_order,
+                        const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, int K, int N,
+                        bf16_t* __restrict__ DW, bf16_t* smem) {
+    const int rank = t / ds.per_e, rem = t % ds.per_e;
+    int kt_out, nt;
+    if (ds.kx) {
+        const int ny = 8 / ds.kx, KTr = ds.KT / ds.kx, NTr = ds.NT / ny;
+        const int x = rem & 7, p = rem >> 3;
+        kt_out = (x / ny) * KTr + p / NTr;
+        nt = (x % ny) * NTr + p % NTr;
+    } else {
+        kt_out = rem / ds.NT;
+        nt = rem % ds.NT;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(s_order[rank]);
+    const int k0 = kt_out * kBM, n0 = nt * kBN;
+    const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
+    const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
+    const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
+    bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
+    if (cnt == 0) {
+        constexpr int CPR = kBN / 8;
+        for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
+            const int row = u / CPR, c = u % CPR;
+            if (row < rows_valid && c * 8 < cols_valid)
+                st16(out + (int64_t)row * N + c * 8, u32x4_t{0u, 0u, 0u, 0u});
+        }
+        return;
+    }
+    gemm_tile<kBM, kBN, kWM, kWN, false, false>(
+        X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0, cnt,
+        rows_valid, cols_valid, smem,
+        [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid, smem); });
+}
+
+// Every counter fetch of the calling workgroup has returned; the last
+// workgroup to get here resets the queue for the next call.  Thread 0 only.
+MOE_DEVICE void queue_release(uint32_t* queue) {
+    __threadfence();
+    if (atomicAdd(queue + 8 * kQueueStride, 1u) == gridDim.x - 1) {
+        for (int x = 0; x < 8; ++x) atomicExch(queue + x * kQueueStride, 0u);
+        atomicExch(queue + 8 * kQueueStride, 0u);
+    }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, uint32_t* __restrict__ queue,
@@ -105,30 +187,8 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
     __shared__ int s_next;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    for (int e = threadIdx.x; e < E; e += kThreads) {
-        const int c = s_cnt[e];
-        int r = 0;
-        for (int f = 0; f < E; ++f) {
-            const int cf = s_cnt[f];
-            r += (cf > c) || (cf == c && f < e);
-        }
-        s_order[r] = e;
-    }
-    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
-    const int per_e = KT * NT;
-    int kx = 0;  // rectangle shape: kx k-tile bands x (8/kx) n-tile bands
-    if (per_e % 8 == 0) {
-        int best = 0x7fffffff;
-        for (int c = 1; c <= 8; c *= 2) {
-            const int ny = 8 / c;
-            if (KT % c == 0 && NT % ny == 0 && KT / c + NT / ny < best) {
-                best = KT / c + NT / ny;
-                kx = c;
-            }
-        }
-    }
-    __syncthreads();
-    const int total = E * per_e;
+    const DwSched ds = dw_schedule(s_cnt, E, K, N, s_order);
+    const int total = E * ds.per_e;
     const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
     const int mine = (total - xcd + 7) / 8;  // tiles 8j + xcd, j < mine
     uint32_t* ctr = queue + xcd * kQueueStride;
@@ -136,51 +196,67 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
     while (j < mine) {
         int nj = 0;
         if (threadIdx.x == 0) nj = wg_per_xcd + (int)atomicAdd(ctr, 1u);
-        const int t = 8 * j + xcd;
-        const int rank = t / per_e, rem = t % per_e;
-        int kt_out, nt;
-        if (kx) {
-            const int ny = 8 / kx, KTr = KT / kx, NTr = NT / ny;
-            const int x = rem & 7, p = rem >> 3;
-            kt_out = (x / ny) * KTr + p / NTr;
-            nt = (x % ny) * NTr + p % NTr;
+        dw_tile(8 * j + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
+        if (threadIdx.x == 0) s_next = nj;
+        __syncthreads();  // the ring and the output image are free again
+        j = __builtin_amdgcn_readfirstlane(s_next);
+    }
+    if (threadIdx.x == 0) queue_release(queue);
+}
+
+// ---------------------------------------------------------------------------
+// Both gradients of one grouped matmul in one launch: dx = dy @ w[e]^T (row
+// tiles, as gmm_rows_kernel<kDx>) and dw[e] = x^T @ dy (as gmm_dw_kernel).
+// Each XCD's queue hands out its share of the input-gradient tiles first (a
+// contiguous eighth of the row-tile order, so neighbouring tiles share an
+// L2) and then its weight-gradient tiles.  The many short weight-gradient
+// tiles fill the CUs that the input gradient's last, partial round of long
+// tiles leaves idle, which two separate launches cannot do.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const bf16_t* __restrict__ W,
+    const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
+    bf16_t* __restrict__ DX, bf16_t* __restrict__ DW, uint32_t* __restrict__ queue, int32_t* dev_err) {
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
+    __shared__ int64_t s_scan[kThreads / 64];
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_order[kMaxExperts], s_tst[kMaxExperts];
+    __shared__ int s_next;
+
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const DwSched ds = dw_schedule(s_cnt, E, K, N, s_order);
+    const int total_mt = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan);
+    const int NTx = (K + kBN - 1) / kBN;  // dx has K columns
+    const int nx = total_mt * NTx;
+    const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
+    // this XCD's input-gradient tiles: [x0, x0 + nxx) of the row-tile order
+    const int q = nx >> 3, r = nx & 7;
+    const int x0 = xcd * q + (xcd < r ? xcd : r), nxx = q + (xcd < r ? 1 : 0);
+    const int mine_w = (E * ds.per_e - xcd + 7) / 8;
+    const int items = nxx + mine_w;
+    uint32_t* ctr = queue + xcd * kQueueStride;
+    int j = blockIdx.x >> 3;
+    while (j < items) {
+        int nj = 0;
+        if (threadIdx.x == 0) nj = wg_per_xcd + (int)atomicAdd(ctr, 1u);
+        if (j < nxx) {
+            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NTx, x0 + j);
+            const int row0 = rt.row0, rows_valid = rt.rows_valid;
+            const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kBN);
+            const int cols_left = K - n0;
+            const bf16_t* We = W + (int64_t)rt.e * K * N;
+            bf16_t* y = DX + (int64_t)row0 * K + n0;
+            gemm_tile<kBM, kBN, kWM, kWN, true, true>(
+                DY + (int64_t)row0 * N, N, rows_valid, We + (int64_t)n0 * N, N, cols_left, 0, N,
+                rows_valid, cols_left, smem,
+                [&](const auto& eng) { eng.store(y, K, rows_valid, cols_left, smem); });
         } else {
-            kt_out = rem / NT;
-            nt = rem % NT;
-        }
-        const int e = __builtin_amdgcn_readfirstlane(s_order[rank]);
-        const int k0 = kt_out * kBM, n0 = nt * kBN;
-        const int off = __builtin_amdgcn_readfirstlane(s_off[e]);
-        const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[e]);
-        const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
-        const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
-        bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
-        if (cnt == 0) {
-            constexpr int CPR = kBN / 8;
-            for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
-                const int row = u / CPR, c = u % CPR;
-                if (row < rows_valid && c * 8 < cols_valid)
-                    st16(out + (int64_t)row * N + c * 8, u32x4_t{0u, 0u, 0u, 0u});
-            }
-        } else {
-            gemm_tile<kBM, kBN, kWM, kWN, false, false>(
-                X + (int64_t)off * K + k0, K, rows_valid, DY + (int64_t)off * N + n0, N, cols_valid, 0,
-                cnt, rows_valid, cols_valid, smem,
-                [&](const auto& eng) { eng.store(out, N, rows_valid, cols_valid, smem); });
+            dw_tile(8 * (j - nxx) + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
         }
         if (threadIdx.x == 0) s_next = nj;
         __syncthreads();  // the ring and the output image are free again
         j = __builtin_amdgcn_readfirstlane(s_next);
     }
-    // Every counter fetch of this workgroup has returned; the last workgroup
-    // to get here resets the queue for the next call.
-    if (threadIdx.x == 0) {
-        __threadfence();
-        if (atomicAdd(queue + 8 * kQueueStride, 1u) == gridDim.x - 1) {
-            for (int x = 0; x < 8; ++x) atomicExch(queue + x * kQueueStride, 0u);
-            atomicExch(queue + 8 * kQueueStride, 0u);
-        }
-    }
+    if (threadIdx.x == 0) queue_release(queue);
 }
 
 // Compute units of the current device (cached per device).
@@ -200,7 +276,7 @@ int num_cus() {
 }  // namespace
 
 size_t gmm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int op) {
-    return op == MOE_GMM_OP_BWD_WEIGHT ? kQueueWords * sizeof(uint32_t) : 0;
+    return op == MOE_GMM_OP_BWD_WEIGHT || op == MOE_GMM_OP_BWD ? kQueueWords * sizeof(uint32_t) : 0;
 }
 
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
@@ -237,6 +313,15 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
     hipLaunchKernelGGL(gmm_dw_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, dy,
                        group_list, (int)E, M_cap, (int)K, (int)N, dw, static_cast<uint32_t*>(ws),
                        dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w,
+                          const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
+                          uint16_t* dx, uint16_t* dw, void* ws, int32_t* dev_err, hipStream_t stream) {
+    hipLaunchKernelGGL(gmm_bwd_kernel, dim3((unsigned)(num_cus() / 8 * 8)), dim3(kThreads), 0, stream,
+                       x, dy, w, group_list, (int)E, M_cap, (int)K, (int)N, dx, dw,
+                       static_cast<uint32_t*>(ws), dev_err);
     return hipGetLastError();
 }
 

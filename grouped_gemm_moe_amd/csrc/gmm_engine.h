@@ -587,13 +587,10 @@ struct RowTile {
     int e, row0, rows_valid, nt;
 };
 
+// s_tst[e] = number of BM-row tiles of the experts before e; returns the
+// total.  All threads of the block; ends with a barrier.
 template <int BM>
-MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int64_t M_cap, int NT,
-                              int* sched, int64_t* s_scan, int32_t* dev_err, RowTile& rt) {
-    int* s_off = sched;
-    int* s_cnt = s_off + kMaxExperts;
-    int* s_tst = s_cnt + kMaxExperts;
-    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+MOE_DEVICE int row_tile_starts(const int* s_cnt, int E, int* s_tst, int64_t* s_scan) {
     const int per = (E + kThreads - 1) / kThreads;
     const int e0 = threadIdx.x * per;
     int64_t my_tiles = 0;
@@ -607,26 +604,45 @@ MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int
             run += (s_cnt[e0 + i] + BM - 1) / BM;
         }
     __syncthreads();
+    return (int)total_mt;
+}
 
-    const int ntiles = (int)total_mt * NT;
-    if ((int)blockIdx.x >= ntiles) return false;  // uniform across the block
-#if defined(MOEGMM_NO_XCD_REMAP)
-    const int t = blockIdx.x;
-#else
-    const int t = xcd_remap(blockIdx.x, ntiles);
-#endif
-    const int mt = t / NT;
+// Logical tile lt (M-tile lt / NT, N-tile lt % NT) of a row-grouped GEMM.
+template <int BM>
+MOE_DEVICE RowTile row_tile_at(const int* s_off, const int* s_cnt, const int* s_tst, int E, int NT,
+                               int lt) {
+    const int mt = lt / NT;
     int lo = 0, hi = E - 1;  // last expert whose first tile is <= mt
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_tst[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     // block-uniform values read from LDS: keep them in scalar registers
+    RowTile rt;
     rt.e = __builtin_amdgcn_readfirstlane(lo);
     rt.row0 = __builtin_amdgcn_readfirstlane(s_off[rt.e] + (mt - s_tst[rt.e]) * BM);
     const int row_end = __builtin_amdgcn_readfirstlane(s_off[rt.e] + s_cnt[rt.e]);
     rt.rows_valid = row_end - rt.row0 < BM ? row_end - rt.row0 : BM;
-    rt.nt = t % NT;
+    rt.nt = lt % NT;
+    return rt;
+}
+
+template <int BM>
+MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int64_t M_cap, int NT,
+                              int* sched, int64_t* s_scan, int32_t* dev_err, RowTile& rt) {
+    int* s_off = sched;
+    int* s_cnt = s_off + kMaxExperts;
+    int* s_tst = s_cnt + kMaxExperts;
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const int total_mt = row_tile_starts<BM>(s_cnt, E, s_tst, s_scan);
+    const int ntiles = total_mt * NT;
+    if ((int)blockIdx.x >= ntiles) return false;  // uniform across the block
+#if defined(MOEGMM_NO_XCD_REMAP)
+    const int t = blockIdx.x;
+#else
+    const int t = xcd_remap(blockIdx.x, ntiles);
+#endif
+    rt = row_tile_at<BM>(s_off, s_cnt, s_tst, E, NT, t);
     __syncthreads();  // schedule arrays are dead from here on
     return true;
 }

@@ -30,6 +30,11 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
                                  int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw,
                                  void* ws, int32_t* dev_err, hipStream_t stream);
 
+// dx and dw of one grouped matmul in one persistent launch (queue in ws)
+hipError_t launch_gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w,
+                          const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
+                          uint16_t* dx, uint16_t* dw, void* ws, int32_t* dev_err, hipStream_t stream);
+
 hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
                                  int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
                                  uint16_t* h, void* ws, int32_t* dev_err, hipStream_t stream);

@@ -9,6 +9,7 @@ Backward of the expert block, from the gradient dYp at the down-GMM output
     dA = gmm_bwd_input(dYp, W2); dW2 = gmm_bwd_weight(A, dYp);
     dH = swiglu_bwd(dA, H);      dX  = gmm_bwd_input(dH, W1);
     dW1 = gmm_bwd_weight(X_perm, dH)
+each input/weight gradient pair as one gmm_bwd launch (same bits).
 
 Backward of the whole layer from dout (the gradient at the layer output):
     dYp, dprobs = moe_unpermute_bwd(dout, Yp, probs); the expert block as
@@ -19,7 +20,7 @@ section 4: recompute the activation in the backward instead of keeping it,
 write gradients into dead buffers): the forward's A is not kept; the
 backward recomputes A = swiglu(H) into the dead Yp buffer, writes dA into
 A's buffer, dH over H (swiglu_bwd in place) and dX over X_perm (after dW1
-has read it).  No dA, dH or dX buffer is allocated: S*(I + 2I + H) bf16
+has read it, so that pair runs as two launches).  No dA, dH or dX buffer is allocated: S*(I + 2I + H) bf16
 elements fewer, for one extra swiglu pass.
 
 The A8W8-FP (MXFP8) forward ("MegaMoE", A8W8-FP scenario), MoeLayerMX:
@@ -36,7 +37,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
+from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
                gmm_workspace_size, moe_permute, moe_permute_bwd, moe_permute_mx,
                moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd, mx_quantize, mx_scale_ld,
                swiglu, swiglu_bwd)
@@ -79,7 +80,7 @@ class MoeLayer:
         self.ws_perm = torch.empty(max(1, moe_permute_workspace_size(s.T, s.top_k, s.E)),
                                    dtype=torch.uint8, device=d)
         ws = max(gmm_workspace_size(s.E, S, k, n, op)
-                 for (k, n) in ((s.H, 2 * s.I), (s.I, s.H)) for op in (0, 1, 2))
+                 for (k, n) in ((s.H, 2 * s.I), (s.I, s.H)) for op in (0, 1, 2, 3))
         # tile queues: zero-filled once, left zero-filled by every call
         self.ws_gmm = torch.zeros(ws, dtype=torch.uint8, device=d) if ws > 0 else None
         if with_backward and self.low_memory:
@@ -143,17 +144,16 @@ class MoeLayer:
         if self.low_memory:
             a = self.a_recomputed
             swiglu(self.h, g, out=a)
-            gmm_bwd_weight(a, dyp, g, out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
-            gmm_bwd_input(dyp, w2, g, out=self.da, ws=self.ws_gmm, dev_err=self.dev_err)
+            # dA goes to A's buffer, which this pair does not read (A is in Yp's)
+            gmm_bwd(a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
             swiglu_bwd(self.da, self.h, g, out=self.dh)  # in place over H
             gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)
             gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
             return
-        gmm_bwd_input(dyp, w2, g, out=self.da, ws=self.ws_gmm, dev_err=self.dev_err)
-        gmm_bwd_weight(self.a, dyp, g, out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
+        gmm_bwd(self.a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
         swiglu_bwd(self.da, self.h, g, out=self.dh)
-        gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
-        gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)
+        gmm_bwd(self.x_perm, self.dh, w1, g, dx_out=self.dx, dw_out=self.dw1, ws=self.ws_gmm,
+                dev_err=self.dev_err)
 
     # -- backward of the two ends and of the whole layer --------------------
     def unpermute_backward(self, dout, probs):

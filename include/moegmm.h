@@ -127,9 +127,9 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
  * bf16 products accumulate in fp32; each output is rounded once (RNE).
  * w[e] of an empty expert is never read.
  * ---------------------------------------------------------------------- */
-/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd_weight needs 1152
- * bytes (its tile queue: counters the kernel increments with atomics); the
- * other ops need none (0) and take NULL.  A workspace that is needed must be
+/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd_weight and gmm_bwd
+ * need 1152 bytes (their tile queue: counters the kernel increments with
+ * atomics); the other ops need none (0) and take NULL.  A workspace that is needed must be
  * 16-byte aligned (else MOE_ERR_INVALID) and zero-filled before its first
  * use; every call leaves it zero-filled again, so one workspace serves any
  * number of calls issued one after another.  Calls that may run at the same
@@ -139,6 +139,7 @@ size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op
 #define MOE_GMM_OP_FWD 0
 #define MOE_GMM_OP_BWD_INPUT 1
 #define MOE_GMM_OP_BWD_WEIGHT 2
+#define MOE_GMM_OP_BWD 3 /* gmm_bwd: both gradients in one launch */
 moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list, int64_t E,
                    int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
                    int32_t* dev_err, void* stream);
@@ -190,6 +191,27 @@ moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* g
 moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,
                           size_t ws_bytes, int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_bwd -- gmm_bwd_input and gmm_bwd_weight of one grouped matmul in one
+ * launch:  dx[off_e + i, :] = dy[off_e + i, :] @ w[e]^T  and
+ *          dw[e] = x[rows_e]^T @ dy[rows_e].
+ * [GMM] 算子语义, backward (both gradients over the same group boundaries).
+ * Every output is bit-identical to what the two separate calls write; one
+ * launch lets the short weight-gradient tiles fill the CUs the input
+ * gradient's last round of tiles leaves idle.
+ *
+ *   x [M_cap, K] bf16, dy [M_cap, N] bf16, w [E, K, N] bf16, group_list [E],
+ *   dx [M_cap, K] bf16 OUT (rows < R written; rows >= R untouched),
+ *   dw [E, K, N] bf16 OUT (every expert; exact zeros for n_e == 0).
+ * dx and dw must not overlap each other or any input (MOE_ERR_INVALID):
+ * both are written while the inputs are still being read.
+ * Workspace: gmm_workspace_size(E, M_cap, K, N, MOE_GMM_OP_BWD) bytes,
+ * zero-filled before the first call (left zero-filled by every call).
+ * ---------------------------------------------------------------------- */
+moe_status gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
+                   int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx, uint16_t* dw,
+                   void* ws, size_t ws_bytes, int32_t* dev_err, void* stream);
 
 /* ------------------------------------------------------------------------
  * swiglu -- a[r, j] = SiLU(h[r, j]) * h[r, I + j],  SiLU(z) = z / (1 + e^-z),

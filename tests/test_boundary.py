@@ -98,6 +98,20 @@ def test_gmm_rejects_bad_arguments(lib):
     assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, None, need, None, None) == MOE_ERR_WORKSPACE
     assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, ws, need - 1, None, None) == MOE_ERR_WORKSPACE
     assert lib.gmm_bwd_weight(A16, A16b, A16c, 4, 64, 64, 64, A16c, MIS, need, None, None) == MOE_ERR_INVALID
+    # gmm_bwd(x, dy, w, group_list, E, M_cap, K, N, dx, dw, ws, ws_bytes, dev_err, stream)
+    need_b = lib.gmm_workspace_size(4, 64, 64, 64, 3)
+    assert need_b == need
+    D1, D2 = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, None, D2, ws, need, None, None) == MOE_ERR_NULL
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1, None, ws, need, None, None) == MOE_ERR_NULL
+    assert lib.gmm_bwd(None, A16b, A16c, A16, 4, 64, 64, 64, D1, D2, ws, need, None, None) == MOE_ERR_NULL
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1, D2, None, need, None, None) == MOE_ERR_WORKSPACE
+    assert lib.gmm_bwd(MIS, A16b, A16c, A16, 4, 64, 64, 64, D1, D2, ws, need, None, None) == MOE_ERR_INVALID
+    # outputs overlapping an input or each other
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, A16, D2, ws, need, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1, A16c, ws, need, None, None) == MOE_ERR_INVALID
+    assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1,
+                       ctypes.c_void_p(0x100000 + 64 * 64 * 2 - 16), ws, need, None, None) == MOE_ERR_INVALID
     # rows longer than 32-bit tile offsets can address, and oversized products
     big = 1 << 22
     assert lib.gmm_fwd(A16, A16b, A16c, 4, 64, big, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID

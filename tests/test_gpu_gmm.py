@@ -41,7 +41,12 @@ def run_all(dev, x_bits, w_bits, dy_bits, gl, tag):
     y = moe.gmm_fwd(x, w, g, out=_sentinel(dev, (M, N)), dev_err=err)
     dx = moe.gmm_bwd_input(dy, w, g, out=_sentinel(dev, (M, K)), dev_err=err)
     dw = moe.gmm_bwd_weight(x, dy, g, out=_sentinel(dev, (E, K, N)), dev_err=err)
+    # both gradients in one launch: the same bits, rows >= R untouched
+    dx2, dw2 = moe.gmm_bwd(x, dy, w, g, dx_out=_sentinel(dev, (M, K)), dw_out=_sentinel(dev, (E, K, N)),
+                           dev_err=err)
     torch.cuda.synchronize()
+    assert np.array_equal(dev_bits(dx2), dev_bits(dx)), f"{tag}: gmm_bwd dx differs from gmm_bwd_input"
+    assert np.array_equal(dev_bits(dw2), dev_bits(dw)), f"{tag}: gmm_bwd dw differs from gmm_bwd_weight"
     return dev_bits(y), dev_bits(dx), dev_bits(dw), int(err.item())
 
 

@@ -9,7 +9,7 @@ one pass of the whole hot path:
     moe_permute (top_k=1 local re-routing, histogram)
     -> gmm_fwd_swiglu(W1; writes A and, for the backward, H) -> gmm_fwd(W2)
     -> moe_unpermute
-    -> gmm_bwd(W2: dA and dW2 in one launch) -> swiglu_bwd
+    -> gmm_bwd_swiglu(W2: dW2, and dH = SwiGLU backward of dA, in one launch)
     -> gmm_bwd(W1: dX and dW1 in one launch)
 
 ``value`` = algorithmic GEMM FLOPs of the step (real rows only, 6 GEMMs)
@@ -161,14 +161,15 @@ def ep_gemm_flops(gl, H, I):
     fwd2 = 2.0 * R * I * H
     # each backward call computes the input and the weight gradient
     return {"gmm_fwd_swiglu": fwd1, "gmm_fwd_down": fwd2,
-            "gmm_bwd_down": 2 * fwd2, "gmm_bwd_gate_up": 2 * fwd1}
+            "gmm_bwd_swiglu_down": 2 * fwd2, "gmm_bwd_gate_up": 2 * fwd1}
 
 
 # libmoegmm kernel behind each call of the step (kernel symbol -> calls)
 EP_KERNELS = {
-    "gmm_rows_kernel<fwd+swiglu>": ["gmm_fwd_swiglu"],
-    "gmm_rows_kernel<fwd>": ["gmm_fwd_down"],
-    "gmm_bwd_kernel": ["gmm_bwd_down", "gmm_bwd_gate_up"],
+    "gmm_rows_kernel<2>": ["gmm_fwd_swiglu"],
+    "gmm_rows_kernel<0>": ["gmm_fwd_down"],
+    "gmm_bwd_kernel<true>": ["gmm_bwd_swiglu_down"],
+    "gmm_bwd_kernel<false>": ["gmm_bwd_gate_up"],
 }
 
 
@@ -191,7 +192,7 @@ def run_ep(torch, dev, args):
     timer = KernelTimer(torch)
     g = layer.tokens_per_expert
 
-    from grouped_gemm_moe_amd import gmm_bwd, gmm_fwd, gmm_fwd_swiglu, moe_unpermute, swiglu_bwd
+    from grouped_gemm_moe_amd import gmm_bwd, gmm_bwd_swiglu, gmm_fwd, gmm_fwd_swiglu, moe_unpermute
 
     def step(t):
         t("moe_permute", lambda: layer.permute(x, ids))
@@ -201,9 +202,9 @@ def run_ep(torch, dev, args):
         t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp, dev_err=layer.dev_err))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out,
                                                  dev_err=layer.dev_err))
-        t("gmm_bwd_down", lambda: gmm_bwd(layer.a, dyp, w2, g, dx_out=layer.da, dw_out=layer.dw2,
-                                          ws=layer.ws_gmm, dev_err=layer.dev_err))
-        t("swiglu_bwd", lambda: swiglu_bwd(layer.da, layer.h, g, out=layer.dh))
+        t("gmm_bwd_swiglu_down", lambda: gmm_bwd_swiglu(layer.a, dyp, w2, layer.h, g, dh_out=layer.dh,
+                                                        dw_out=layer.dw2, ws=layer.ws_gmm,
+                                                        dev_err=layer.dev_err))
         t("gmm_bwd_gate_up", lambda: gmm_bwd(layer.x_perm, layer.dh, w1, g, dx_out=layer.dx,
                                              dw_out=layer.dw1, ws=layer.ws_gmm, dev_err=layer.dev_err))
 
@@ -217,7 +218,7 @@ def run_ep(torch, dev, args):
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
-    step_ms = timer.spans(7)
+    step_ms = timer.spans(6)
     per = timer.collect()
     flops = ep_gemm_flops(wl["group_list"], H, I)
     total_flops = sum(flops.values())

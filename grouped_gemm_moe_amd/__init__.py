@@ -24,6 +24,7 @@ from . import _lib as _L
 
 __all__ = [
     "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
+    "gmm_bwd_swiglu",
     "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
@@ -223,6 +224,29 @@ def gmm_bwd(x, dy, w, group_list, *, dx_out=None, dw_out=None, ws=None, dev_err=
                              _ptr(dw), _ptr(ws), ws_bytes, _ptr(dev_err), _stream(x.device)),
            "gmm_bwd")
     return dx, dw
+
+
+def gmm_bwd_swiglu(x, dy, w, h, group_list, *, dh_out=None, dw_out=None, ws=None, dev_err=None):
+    """(dh, dw) of the down GMM with the SwiGLU backward fused: dh =
+    swiglu_bwd(dy[rows_e] @ w[e]^T, h) (the product not rounded in between),
+    dw[e] = x[rows_e]^T @ dy[rows_e].  dh_out may be h (in place)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(dy, "dy", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(h, "h", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, K = x.shape
+    M2, N = dy.shape
+    E = group_list.shape[0]
+    if M2 != M or tuple(w.shape) != (E, K, N) or tuple(h.shape) != (M, 2 * K):
+        raise MoeError("shape mismatch: x [M, K], dy [M, N], w [E, K, N], h [M, 2K]")
+    dh = _out(dh_out, (M, 2 * K), torch.bfloat16, x.device, "dh")
+    dw = _out(dw_out, (E, K, N), torch.bfloat16, x.device, "dw")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_BWD), x.device, ws, zeroed=True)
+    _check(library().gmm_bwd_swiglu(_ptr(x), _ptr(dy), _ptr(w), _ptr(h), _ptr(group_list), E, M, K, N,
+                                    _ptr(dh), _ptr(dw), _ptr(ws), ws_bytes, _ptr(dev_err),
+                                    _stream(x.device)), "gmm_bwd_swiglu")
+    return dh, dw
 
 
 def swiglu(h, group_list, *, out=None):

@@ -28,6 +28,7 @@ SIGNATURES = {
     "gmm_bwd_input": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd_weight": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
+    "gmm_bwd_swiglu": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
     "swiglu": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
     "swiglu_bwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "moe_unpermute": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]),
@@ -41,7 +42,7 @@ SIGNATURES = {
                                  _i64, _p, _p]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 

@@ -84,7 +84,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 5; }
+int moegmm_abi_version(void) { return 6; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -181,6 +181,28 @@ moe_status gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w, con
         return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_gmm_bwd(x, dy, w, group_list, E, M_cap, K, N, dx, dw, ws, dev_err,
                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const uint16_t* w, const uint16_t* h,
+                          const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
+                          uint16_t* dh, uint16_t* dw, void* ws, size_t ws_bytes, int32_t* dev_err,
+                          void* stream) {
+    if (!dw || !dh) return MOE_ERR_NULL;
+    if (M_cap > 0 && (!x || !dy || !h)) return MOE_ERR_NULL;
+    moe_status st = check_gmm_common(dy ? dy : w, w, group_list, dh, E, M_cap, K, N,
+                                     moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_BWD),
+                                     ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(dw, 16)) return MOE_ERR_INVALID;
+    if (M_cap * 2 * K > (int64_t(1) << 40)) return MOE_ERR_INVALID;
+    const size_t bx = (size_t)(M_cap * K) * 2, bdy = (size_t)(M_cap * N) * 2, bw = (size_t)(E * K * N) * 2;
+    const size_t bh = 2 * bx;
+    if ((dh != h && overlaps(dh, bh, h, bh)) || overlaps(dh, bh, x, bx) || overlaps(dh, bh, dy, bdy) ||
+        overlaps(dh, bh, w, bw) || overlaps(dh, bh, dw, bw) || overlaps(dw, bw, x, bx) ||
+        overlaps(dw, bw, dy, bdy) || overlaps(dw, bw, w, bw) || overlaps(dw, bw, h, bh))
+        return MOE_ERR_INVALID;
+    return from_hip(moegmm::launch_gmm_bwd_swiglu(x, dy, w, h, group_list, E, M_cap, K, N, dh, dw, ws,
+                                                  dev_err, static_cast<hipStream_t>(stream)));
 }
 
 moe_status swiglu(const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,

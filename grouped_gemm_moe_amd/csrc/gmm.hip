@@ -213,10 +213,16 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
 // tiles fill the CUs that the input gradient's last, partial round of long
 // tiles leaves idle, which two separate launches cannot do.
 // ---------------------------------------------------------------------------
+//
+// SWIGLU_BWD: the input gradient is dA of the down GMM and its tiles go out
+// through the SwiGLU backward (Engine::store_swiglu_bwd): dH = [dG | dU]
+// from dA and H = [G | U] ([M_cap, 2K]) is written instead of dA.
+template <bool SWIGLU_BWD>
 __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const bf16_t* __restrict__ W,
     const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
-    bf16_t* __restrict__ DX, bf16_t* __restrict__ DW, uint32_t* __restrict__ queue, int32_t* dev_err) {
+    bf16_t* __restrict__ DX, bf16_t* __restrict__ DW, const bf16_t* Hin, bf16_t* DH,
+    uint32_t* __restrict__ queue, int32_t* dev_err) {
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_order[kMaxExperts], s_tst[kMaxExperts];
@@ -244,11 +250,16 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
             const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kBN);
             const int cols_left = K - n0;
             const bf16_t* We = W + (int64_t)rt.e * K * N;
-            bf16_t* y = DX + (int64_t)row0 * K + n0;
             gemm_tile<kBM, kBN, kWM, kWN, true, true>(
                 DY + (int64_t)row0 * N, N, rows_valid, We + (int64_t)n0 * N, N, cols_left, 0, N,
-                rows_valid, cols_left, smem,
-                [&](const auto& eng) { eng.store(y, K, rows_valid, cols_left, smem); });
+                rows_valid, cols_left, smem, [&](const auto& eng) {
+                    if constexpr (SWIGLU_BWD) {
+                        const int64_t o = (int64_t)row0 * 2 * K + n0;
+                        eng.store_swiglu_bwd(DH + o, Hin + o, 2 * K, K, rows_valid, cols_left, smem);
+                    } else {
+                        eng.store(DX + (int64_t)row0 * K + n0, K, rows_valid, cols_left, smem);
+                    }
+                });
         } else {
             dw_tile(8 * (j - nxx) + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
         }
@@ -319,8 +330,18 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
 hipError_t launch_gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w,
                           const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
                           uint16_t* dx, uint16_t* dw, void* ws, int32_t* dev_err, hipStream_t stream) {
-    hipLaunchKernelGGL(gmm_bwd_kernel, dim3((unsigned)(num_cus() / 8 * 8)), dim3(kThreads), 0, stream,
-                       x, dy, w, group_list, (int)E, M_cap, (int)K, (int)N, dx, dw,
+    hipLaunchKernelGGL(gmm_bwd_kernel<false>, dim3((unsigned)(num_cus() / 8 * 8)), dim3(kThreads), 0,
+                       stream, x, dy, w, group_list, (int)E, M_cap, (int)K, (int)N, dx, dw, nullptr,
+                       nullptr, static_cast<uint32_t*>(ws), dev_err);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const uint16_t* w,
+                                 const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                                 int64_t K, int64_t N, uint16_t* dh, uint16_t* dw, void* ws,
+                                 int32_t* dev_err, hipStream_t stream) {
+    hipLaunchKernelGGL(gmm_bwd_kernel<true>, dim3((unsigned)(num_cus() / 8 * 8)), dim3(kThreads), 0,
+                       stream, x, dy, w, group_list, (int)E, M_cap, (int)K, (int)N, nullptr, dw, h, dh,
                        static_cast<uint32_t*>(ws), dev_err);
     return hipGetLastError();
 }

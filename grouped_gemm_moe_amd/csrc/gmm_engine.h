@@ -385,6 +385,99 @@ struct Engine {
         }
     }
 
+    // Input-gradient tile of the down GMM fused with the SwiGLU backward.
+    // The accumulators hold dA (fp32, not rounded).  With G = h[:, c] and
+    // U = h[:, pair + c] at the same rows and columns and s = sigmoid(G),
+    // writes dG = dA*U*s*(1 + G*(1 - s)) to dh[:, c] and dU = dA*G*s to
+    // dh[:, pair + c], each rounded once (RNE), through the wave's LDS image
+    // as in store().  dh may be h: a lane has read G and U of its outputs
+    // before anything is written, and no other lane writes them.
+    MOE_DEVICE void store_swiglu_bwd(bf16_t* dh, const bf16_t* h, int64_t ld, int pair, int rows_valid,
+                                     int cols_valid, bf16_t* smem) const {
+        static_assert(WTN == 64, "one 128-byte row segment per wave row");
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
+        const int lane = tid & 63;
+        const int wid = wave_id();
+        const int wm = wid / WN, wn = wid % WN;
+        __syncthreads();  // every wave is done reading the ring
+        bf16_t* img = smem + wid * (WTM * WTN);
+        const uint32_t ld_off = (uint32_t)(((int64_t)(lane & 31) * ld + (lane >> 5) * 4) * 2);
+        const int rl = rows_valid - wm * WTM - (lane & 31), cl = cols_valid - wn * WTN - (lane >> 5) * 4;
+        u32x2_t du[TM][TN][4];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const __amdgpu_buffer_rsrc_t rg = make_rsrc(h + (int64_t)(wm * WTM + i * 32) * ld + wn * WTN);
+            const __amdgpu_buffer_rsrc_t ru =
+                make_rsrc(h + (int64_t)(wm * WTM + i * 32) * ld + pair + wn * WTN);
+            u32x2_t gq[TN][4], uq[TN][4];
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const bool ok = i * 32 < rl && j * 32 + g * 8 < cl;
+                    const uint32_t off = ok ? ld_off + (uint32_t)((j * 32 + g * 8) * 2) : kOOB;
+                    gq[j][g] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
+                    uq[j][g] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ru, off, 0, 0));
+                }
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float dgv[4], duv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t gw = gq[j][g][q >> 1], uw = uq[j][g][q >> 1];
+                        const float gv = (q & 1) ? bf16_hi(gw) : bf16_lo(gw);
+                        const float uv = (q & 1) ? bf16_hi(uw) : bf16_lo(uw);
+                        const float dv = acc[i][j][4 * g + q];
+                        const float sg = silu_sigmoid(gv);
+                        dgv[q] = dv * uv * sg * (1.0f + gv * (1.0f - sg));
+                        duv[q] = dv * gv * sg;
+                    }
+                    u32x2_t pk;
+                    pk[0] = pack_bf16x2(dgv[0], dgv[1]);
+                    pk[1] = pack_bf16x2(dgv[2], dgv[3]);
+                    du[i][j][g][0] = pack_bf16x2(duv[0], duv[1]);
+                    du[i][j][g][1] = pack_bf16x2(duv[2], duv[3]);
+                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
+                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
+                }
+        }
+        const int c = lane & 7;
+        const uint32_t lane_off = (uint32_t)(((int64_t)(lane >> 3) * ld + c * 8) * 2);
+        constexpr int kIt = WTM / 8;
+        auto copy_out = [&](bf16_t* dst) {
+            u32x4_t v[kIt];
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int r = it * 8 + (lane >> 3);
+                v[it] = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+            }
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int row = wm * WTM + it * 8 + (lane >> 3), col = wn * WTN + c * 8;
+                const bool ok = row < rows_valid && col < cols_valid;
+                store_nt16(v[it], dst + (int64_t)(wm * WTM + it * 8) * ld + wn * WTN, ok ? lane_off : kOOB);
+            }
+        };
+        copy_out(dh);  // dG
+        // the wave's image again (its reads above are done before these writes)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
+                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = du[i][j][g];
+                }
+        }
+        copy_out(dh + pair);  // dU
+    }
+
     // Gate_up tile with paired columns (see Dma::init): fragment 0 of a wave
     // holds the gate values G and fragment 1 the up values U of the same 32
     // output columns.  Writes A = SiLU(G) * U (rounded once, from the fp32

@@ -35,6 +35,12 @@ hipError_t launch_gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t*
                           const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
                           uint16_t* dx, uint16_t* dw, void* ws, int32_t* dev_err, hipStream_t stream);
 
+// the same for the down GMM, its dA tiles turned into dH = swiglu_bwd(dA, h)
+hipError_t launch_gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const uint16_t* w,
+                                 const uint16_t* h, const int64_t* group_list, int64_t E, int64_t M_cap,
+                                 int64_t K, int64_t N, uint16_t* dh, uint16_t* dw, void* ws,
+                                 int32_t* dev_err, hipStream_t stream);
+
 hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
                                  int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
                                  uint16_t* h, void* ws, int32_t* dev_err, hipStream_t stream);

@@ -9,7 +9,9 @@ Backward of the expert block, from the gradient dYp at the down-GMM output
     dA = gmm_bwd_input(dYp, W2); dW2 = gmm_bwd_weight(A, dYp);
     dH = swiglu_bwd(dA, H);      dX  = gmm_bwd_input(dH, W1);
     dW1 = gmm_bwd_weight(X_perm, dH)
-each input/weight gradient pair as one gmm_bwd launch (same bits).
+each input/weight gradient pair as one gmm_bwd launch (same bits), and by
+default the first pair with the SwiGLU backward in the same launch
+(gmm_bwd_swiglu: dH from dA before rounding; dA is not stored).
 
 Backward of the whole layer from dout (the gradient at the layer output):
     dYp, dprobs = moe_unpermute_bwd(dout, Yp, probs); the expert block as
@@ -37,7 +39,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
+from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
                gmm_workspace_size, moe_permute, moe_permute_bwd, moe_permute_mx,
                moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd, mx_quantize, mx_scale_ld,
                swiglu, swiglu_bwd)
@@ -61,10 +63,13 @@ class MoeLayer:
     current torch stream and never synchronise."""
 
     def __init__(self, shape: LayerShape, device, with_backward: bool = False,
-                 low_memory: bool = False):
+                 low_memory: bool = False, fuse_swiglu_bwd: bool = True):
         s = shape
         self.shape = s
         self.low_memory = bool(low_memory and with_backward)
+        # dH straight from the down GMM's backward (gmm_bwd_swiglu): dA is
+        # neither rounded nor stored, and no separate swiglu_bwd runs
+        self.fuse_swiglu_bwd = bool(fuse_swiglu_bwd)
         d = device
         bf = torch.bfloat16
         S = s.S
@@ -90,7 +95,7 @@ class MoeLayer:
             self.dx = self.x_perm
             self.a_recomputed = self.yp.view(-1)[: S * s.I].view(S, s.I)
         elif with_backward:
-            self.da = torch.empty((S, s.I), dtype=bf, device=d)
+            self.da = None if self.fuse_swiglu_bwd else torch.empty((S, s.I), dtype=bf, device=d)
             self.dh = torch.empty((S, 2 * s.I), dtype=bf, device=d)
             self.dx = torch.empty((S, s.H), dtype=bf, device=d)
         if with_backward:
@@ -141,19 +146,26 @@ class MoeLayer:
         recomputed from H first, Yp, A, H and X_perm are overwritten, and
         dyp must not be the Yp buffer."""
         g = self.tokens_per_expert
+        ws, err = self.ws_gmm, self.dev_err
         if self.low_memory:
             a = self.a_recomputed
             swiglu(self.h, g, out=a)
-            # dA goes to A's buffer, which this pair does not read (A is in Yp's)
-            gmm_bwd(a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
-            swiglu_bwd(self.da, self.h, g, out=self.dh)  # in place over H
-            gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=self.ws_gmm, dev_err=self.dev_err)
-            gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=self.ws_gmm, dev_err=self.dev_err)
+            if self.fuse_swiglu_bwd:
+                # dH written over H in the same launch (each tile reads G, U first)
+                gmm_bwd_swiglu(a, dyp, w2, self.h, g, dh_out=self.dh, dw_out=self.dw2, ws=ws, dev_err=err)
+            else:
+                # dA goes to A's buffer, which this pair does not read (A is in Yp's)
+                gmm_bwd(a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=ws, dev_err=err)
+                swiglu_bwd(self.da, self.h, g, out=self.dh)  # in place over H
+            gmm_bwd_weight(self.x_perm, self.dh, g, out=self.dw1, ws=ws, dev_err=err)
+            gmm_bwd_input(self.dh, w1, g, out=self.dx, ws=ws, dev_err=err)
             return
-        gmm_bwd(self.a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=self.ws_gmm, dev_err=self.dev_err)
-        swiglu_bwd(self.da, self.h, g, out=self.dh)
-        gmm_bwd(self.x_perm, self.dh, w1, g, dx_out=self.dx, dw_out=self.dw1, ws=self.ws_gmm,
-                dev_err=self.dev_err)
+        if self.fuse_swiglu_bwd:
+            gmm_bwd_swiglu(self.a, dyp, w2, self.h, g, dh_out=self.dh, dw_out=self.dw2, ws=ws, dev_err=err)
+        else:
+            gmm_bwd(self.a, dyp, w2, g, dx_out=self.da, dw_out=self.dw2, ws=ws, dev_err=err)
+            swiglu_bwd(self.da, self.h, g, out=self.dh)
+        gmm_bwd(self.x_perm, self.dh, w1, g, dx_out=self.dx, dw_out=self.dw1, ws=ws, dev_err=err)
 
     # -- backward of the two ends and of the whole layer --------------------
     def unpermute_backward(self, dout, probs):

@@ -214,6 +214,31 @@ moe_status gmm_bwd(const uint16_t* x, const uint16_t* dy, const uint16_t* w, con
                    void* ws, size_t ws_bytes, int32_t* dev_err, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gmm_bwd_swiglu -- gmm_bwd of the down GMM with the SwiGLU backward applied
+ * to its input gradient in the same launch:
+ *   dA = dy[rows_e] @ w[e]^T (fp32, never rounded),
+ *   dh[:, j] = dA * U * s * (1 + G * (1 - s)),  dh[:, K + j] = dA * G * s,
+ *   with G = h[:, j], U = h[:, K + j], s = 1 / (1 + e^-G),
+ *   dw[e] = x[rows_e]^T @ dy[rows_e].
+ * [GMM] 算子语义, backward of the down GMM; the SwiGLU derivative is derived
+ * (not on the pages): d SiLU(z)/dz = s + z s (1 - s).  dh is what
+ * swiglu_bwd(gmm_bwd_input(dy, w), h) writes, except that dA is not rounded
+ * to bf16 in between; dw is bit-identical to gmm_bwd_weight.
+ *
+ *   x [M_cap, K] bf16 (the activation A), dy [M_cap, N] bf16, w [E, K, N]
+ *   bf16 (W2), h [M_cap, 2K] bf16 (H = [G | U]), group_list [E] int64,
+ *   dh [M_cap, 2K] bf16 OUT (rows < R written; rows >= R untouched), may be
+ *   h itself (in place: each output is written after its G and U are read),
+ *   dw [E, K, N] bf16 OUT.
+ * Otherwise dh and dw must not overlap each other or any input
+ * (MOE_ERR_INVALID).  Workspace as gmm_bwd (MOE_GMM_OP_BWD).
+ * ---------------------------------------------------------------------- */
+moe_status gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const uint16_t* w, const uint16_t* h,
+                          const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K, int64_t N,
+                          uint16_t* dh, uint16_t* dw, void* ws, size_t ws_bytes, int32_t* dev_err,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
  * swiglu -- a[r, j] = SiLU(h[r, j]) * h[r, I + j],  SiLU(z) = z / (1 + e^-z),
  * for rows r < R = sum(group_list) (clamped to M_cap).  gate = first I
  * columns, up = last I columns; no clamp.  [MegaMoE] activation formulas,

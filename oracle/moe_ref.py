@@ -316,23 +316,26 @@ def moe_layer_forward(x, topk_ids, probs, w1, w2, num_experts: int,
 
 
 def expert_block_backward(x_perm, h, a, dyp, w1, w2, group_list,
-                          rounding=round_bf16) -> dict:
+                          rounding=round_bf16, fused_swiglu_bwd=False) -> dict:
     """Backward of gate_up GMM -> SwiGLU -> down GMM from dYp (permuted rows).
 
     dA = dYp W2^T, dW2 = A^T dYp, dH = swiglu_bwd(dA, H), dX = dH W1^T,
     dW1 = X^T dH; dA and dH rounded to bf16 at the boundary (``rounding``;
-    ``None`` for the exact chain).
+    ``None`` for the exact chain).  ``fused_swiglu_bwd``: the SwiGLU backward
+    runs on the unrounded dA (dA never crosses a boundary); the returned dA
+    is still its rounded value, for reference.
     """
     rnd = rounding if rounding is not None else (lambda v: v)
-    da = rnd(gmm_bwd_input(dyp, w2, group_list))
+    da_exact = gmm_bwd_input(dyp, w2, group_list)
+    da = rnd(da_exact)
     dw2 = gmm_bwd_weight(a, dyp, group_list)
-    dh = rnd(swiglu_bwd(da, h))
+    dh = rnd(swiglu_bwd(da_exact if fused_swiglu_bwd else da, h))
     dx = gmm_bwd_input(dh, w1, group_list)
     dw1 = gmm_bwd_weight(x_perm, dh, group_list)
     return dict(da=da, dw2=dw2, dh=dh, dx=dx, dw1=dw1)
 
 
-def moe_layer_backward(fwd, dout, probs, w1, w2, rounding=round_bf16) -> dict:
+def moe_layer_backward(fwd, dout, probs, w1, w2, rounding=round_bf16, fused_swiglu_bwd=False) -> dict:
     """Full layer backward from dout, given the forward dict ``fwd``.
 
     unpermute_bwd -> expert block backward -> permute_bwd.  dYp and dX_perm
@@ -345,7 +348,8 @@ def moe_layer_backward(fwd, dout, probs, w1, w2, rounding=round_bf16) -> dict:
     dyp, dprobs = unpermute_bwd(dout, fwd["yp"], fwd["row_id_map"], probs)
     dyp = rnd(dyp)
     blk = expert_block_backward(fwd["x_perm"], fwd["h"], fwd["a"], dyp, w1, w2,
-                                fwd["tokens_per_expert"], rounding=rounding)
+                                fwd["tokens_per_expert"], rounding=rounding,
+                                fused_swiglu_bwd=fused_swiglu_bwd)
     dx_perm = rnd(blk["dx"])
     dx = permute_bwd(dx_perm, fwd["row_id_map"], T)
     return dict(dyp=dyp, dprobs=dprobs, da=blk["da"], dw2=blk["dw2"], dh=blk["dh"],

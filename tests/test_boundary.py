@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input",
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
-              "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu"]:
+              "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu"]:
         assert n in names, n
 
 
@@ -112,6 +112,19 @@ def test_gmm_rejects_bad_arguments(lib):
     assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1, A16c, ws, need, None, None) == MOE_ERR_INVALID
     assert lib.gmm_bwd(A16, A16b, A16c, A16, 4, 64, 64, 64, D1,
                        ctypes.c_void_p(0x100000 + 64 * 64 * 2 - 16), ws, need, None, None) == MOE_ERR_INVALID
+    # gmm_bwd_swiglu(x, dy, w, h, group_list, E, M_cap, K, N, dh, dw, ws, ws_bytes, dev_err, stream)
+    Hh = ctypes.c_void_p(0x300000)
+    sw = lambda x_, h_, dh_, dw_, ws_=ws, n_=need: lib.gmm_bwd_swiglu(  # noqa: E731
+        x_, A16b, A16c, h_, A16, 4, 64, 64, 64, dh_, dw_, ws_, n_, None, None)
+    assert sw(A16, Hh, None, D2) == MOE_ERR_NULL
+    assert sw(A16, None, D1, D2) == MOE_ERR_NULL
+    assert sw(A16, Hh, D1, D2, ws_=None) == MOE_ERR_WORKSPACE
+    assert sw(A16, ctypes.c_void_p(0x300008), D1, D2) == MOE_ERR_INVALID   # misaligned h
+    # dh may be h exactly, but not a shifted view of it, nor an input or dw
+    assert sw(A16, Hh, ctypes.c_void_p(0x300000 + 256), D2) == MOE_ERR_INVALID
+    assert sw(A16, Hh, A16b, D2) == MOE_ERR_INVALID
+    assert sw(A16, Hh, D1, ctypes.c_void_p(0x100000 + 1024)) == MOE_ERR_INVALID
+    assert sw(A16, Hh, D1, Hh) == MOE_ERR_INVALID
     # rows longer than 32-bit tile offsets can address, and oversized products
     big = 1 << 22
     assert lib.gmm_fwd(A16, A16b, A16c, 4, 64, big, 64, A16c, ws, 0, None, None) == MOE_ERR_INVALID

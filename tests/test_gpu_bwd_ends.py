@@ -111,8 +111,9 @@ def test_end_backward_bad_row_map_reported(dev):
     assert_close(dev_f64(dx), oracle.permute_bwd(f64(y), ok, T), "dx with bad rows masked")
 
 
-@pytest.mark.parametrize("low_memory", [False, True])
-def test_tiny_full_layer_backward(dev, low_memory):
+@pytest.mark.parametrize("low_memory,fuse_swiglu_bwd", [(False, True), (True, True), (False, False),
+                                                       (True, False)])
+def test_tiny_full_layer_backward(dev, low_memory, fuse_swiglu_bwd):
     """Worked example: forward, then the whole backward from dout; every
     gradient (dYp, dprobs, dA, dH, dX_perm, dW1, dW2, dx) against the oracle
     chain, which rounds at the same boundary points.  low_memory: the same
@@ -122,9 +123,9 @@ def test_tiny_full_layer_backward(dev, low_memory):
     d = wl.dims
     T, K, H = d["T"], d["K"], d["H"]
     R = 5
-    print(f"tiny full-layer backward, low_memory={low_memory}", flush=True)
+    print(f"tiny full-layer backward, low_memory={low_memory} fuse_swiglu_bwd={fuse_swiglu_bwd}", flush=True)
     layer = MoeLayer(LayerShape(T, K, d["E"], H, d["I"]), dev, with_backward=True,
-                     low_memory=low_memory)
+                     low_memory=low_memory, fuse_swiglu_bwd=fuse_swiglu_bwd)
     w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
     probs_d = torch.from_numpy(wl["probs"]).to(dev)
     layer.forward(bf16_dev(wl["x"], dev), torch.from_numpy(wl["topk_ids"]).to(dev), probs_d, w1, w2)
@@ -133,7 +134,8 @@ def test_tiny_full_layer_backward(dev, low_memory):
     assert int(layer.dev_err.item()) == 0
     probs = wl["probs"].astype(np.float64)
     fwd = oracle.moe_layer_forward(f64(wl["x"]), wl["topk_ids"], probs, f64(wl["w1"]), f64(wl["w2"]), d["E"])
-    g = oracle.moe_layer_backward(fwd, f64(wl["dout"]), probs, f64(wl["w1"]), f64(wl["w2"]))
+    g = oracle.moe_layer_backward(fwd, f64(wl["dout"]), probs, f64(wl["w1"]), f64(wl["w2"]),
+                                  fused_swiglu_bwd=fuse_swiglu_bwd)
     gl = [1, 2, 0, 2]
     off = oracle.expert_offsets(gl)
     rmap = fwd["row_id_map"].reshape(T, K)
@@ -146,7 +148,8 @@ def test_tiny_full_layer_backward(dev, low_memory):
             if rmap[t, k] >= 0:
                 slack[t, k] = chained_reduction_slack(dout[t][:, None], fwd["yp"][rmap[t, k]][:, None])[0, 0]
     assert_close(layer.dprobs.cpu().numpy().astype(np.float64), g["dprobs"], "dprobs", extra=slack)
-    assert_close(dev_f64(layer.da)[:R], g["da"], "dA")
+    if not fuse_swiglu_bwd:  # the fused backward never stores dA
+        assert_close(dev_f64(layer.da)[:R], g["da"], "dA")
     assert_close(dev_f64(layer.dh)[:R], g["dh"], "dH")
     assert_close(dev_f64(layer.dx)[:R], g["dx_perm"], "dX_perm")
     for name, u, v in (("dw1", fwd["x_perm"], g["dh"]), ("dw2", fwd["a"], g["dyp"])):

@@ -305,3 +305,37 @@ def test_dw_tile_queue_workspace(dev):
         assert np.array_equal(dev_bits(shared), dev_bits(fresh))
         assert_close(f64(dev_bits(shared)), oracle.gmm_bwd_weight(f64(dev_bits(x)), f64(dev_bits(dy)), gl),
                      "dw queue")
+
+
+@pytest.mark.parametrize("M,K,N,gl,in_place", [
+    (1000, 264, 520, [300, 0, 200, 100, 0, 150, 250, 0], False),  # ragged tiles, empty experts
+    (777, 72, 264, [0, 777, 0], True),                            # dH written over H
+    (129, 8, 8, [64, 1, 64], False),                              # tiny K and N
+    (600, 512, 2048, [256, 128, 216], True),                      # several full tiles
+])
+def test_bwd_swiglu(dev, M, K, N, gl, in_place):
+    """gmm_bwd_swiglu: dH = swiglu_bwd(dy @ w[e]^T, h) with the product kept
+    in fp32, and dW bit-identical to gmm_bwd_weight; rows >= R untouched."""
+    rng = np.random.default_rng(M + K + N)
+    E, R = len(gl), int(sum(gl))
+    print(f"gmm_bwd_swiglu: E={E} M={M} K={K} N={N} in_place={in_place}", flush=True)
+    x_b = workloads.normal_bf16(rng, (M, K))
+    dy_b = workloads.normal_bf16(rng, (M, N))
+    w_b = workloads.normal_bf16(rng, (E, K, N), std=0.05)
+    h_b = workloads.normal_bf16(rng, (M, 2 * K), std=1.5)
+    x, dy, w, h = (bf16_dev(b, dev) for b in (x_b, dy_b, w_b, h_b))
+    g = _gl(dev, gl)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    if in_place:
+        dh_out = bf16_dev(h_b, dev)
+        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, dh_out, g, dh_out=dh_out, dev_err=err)
+    else:
+        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, h, g, dh_out=_sentinel(dev, (M, 2 * K)), dev_err=err)
+    dw_ref_bits = dev_bits(moe.gmm_bwd_weight(x, dy, g, dev_err=err))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.swiglu_bwd(oracle.gmm_bwd_input(f64(dy_b), f64(w_b), gl), f64(h_b))
+    assert_close(f64(dev_bits(dh))[:R], ref[:R], "gmm_bwd_swiglu dH")
+    tail = dev_bits(dh)[R:]
+    assert (tail == (h_b[R:] if in_place else SENT)).all(), "rows >= R were written"
+    assert np.array_equal(dev_bits(dw), dw_ref_bits), "dW differs from gmm_bwd_weight"

@@ -28,11 +28,12 @@ def dev():
     return require_gpu()
 
 
-def _run_forward(dev, wl, with_backward=False, dyp_bits=None, low_memory=False):
+def _run_forward(dev, wl, with_backward=False, dyp_bits=None, low_memory=False, fuse_swiglu_bwd=True):
     d = wl.dims
     shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
-    print(f"layer {wl.name}: {shape} low_memory={low_memory}", flush=True)
-    layer = MoeLayer(shape, dev, with_backward=with_backward, low_memory=low_memory)
+    print(f"layer {wl.name}: {shape} low_memory={low_memory} fuse_swiglu_bwd={fuse_swiglu_bwd}", flush=True)
+    layer = MoeLayer(shape, dev, with_backward=with_backward, low_memory=low_memory,
+                     fuse_swiglu_bwd=fuse_swiglu_bwd)
     w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
     layer.forward(bf16_dev(wl["x"], dev), torch.from_numpy(wl["topk_ids"]).to(dev),
                   torch.from_numpy(wl["probs"]).to(dev), w1, w2)
@@ -65,19 +66,22 @@ def _oracle_forward(wl):
                                     f64(wl["w1"]), f64(wl["w2"]), wl.dims["E"])
 
 
-def test_tiny_forward_backward(dev):
+@pytest.mark.parametrize("fuse_swiglu_bwd", [True, False])
+def test_tiny_forward_backward(dev, fuse_swiglu_bwd):
     wl = workloads.tiny()
     R = 5
     S = wl.dims["T"] * wl.dims["K"]
     dyp = np.full((S, wl.dims["H"]), SENT, dtype=np.uint16)   # rows >= R undefined (NaN)
     dyp[:R] = wl["dyp"]
-    layer = _run_forward(dev, wl, with_backward=True, dyp_bits=dyp)
+    layer = _run_forward(dev, wl, with_backward=True, dyp_bits=dyp, fuse_swiglu_bwd=fuse_swiglu_bwd)
     ref = _oracle_forward(wl)
     assert ref["tokens_per_expert"].tolist() == [1, 2, 0, 2]
     _check_forward(layer, ref, R)
     g = oracle.expert_block_backward(ref["x_perm"], ref["h"], ref["a"], f64(wl["dyp"]),
-                                     f64(wl["w1"]), f64(wl["w2"]), ref["tokens_per_expert"])
-    assert_close(dev_f64(layer.da)[:R], g["da"][:R], "dA")
+                                     f64(wl["w1"]), f64(wl["w2"]), ref["tokens_per_expert"],
+                                     fused_swiglu_bwd=fuse_swiglu_bwd)
+    if not fuse_swiglu_bwd:  # the fused backward never stores dA
+        assert_close(dev_f64(layer.da)[:R], g["da"][:R], "dA")
     assert_close(dev_f64(layer.dh)[:R], g["dh"][:R], "dH")
     assert_close(dev_f64(layer.dx)[:R], g["dx"][:R], "dX")
     assert_close(dev_f64(layer.dw2), g["dw2"], "dW2", extra=_slack_per_expert(ref["a"], f64(wl["dyp"]), [1, 2, 0, 2]))
@@ -117,7 +121,8 @@ def test_ep_rank_forward_backward_sampled(dev, low_memory):
     rows = np.unique(np.concatenate([off[:-1][gl > 0], off[1:][gl > 0] - 1,
                                      rng.integers(0, 16384, 48)]))
     idx = torch.from_numpy(rows).to(dev)
-    kept = ("da", "dh", "dx") if low_memory else ("h", "a", "yp", "da", "dh", "dx")
+    # dA is not stored (the SwiGLU backward runs in the down GMM's backward)
+    kept = ("dh", "dx") if low_memory else ("h", "a", "yp", "dh", "dx")
     got = {k: dev_f64(getattr(layer, k)[idx]) for k in kept}
     out_tok = dev_f64(layer.out[torch.from_numpy(ss[rows]).to(dev)])
     probs = wl["probs"].astype(np.float64)
@@ -128,7 +133,7 @@ def test_ep_rank_forward_backward_sampled(dev, low_memory):
         h = oracle.round_bf16(oracle.gmm(xr, f64(w1[e:e + 1]), one))
         a = oracle.round_bf16(oracle.swiglu(h))
         yp = oracle.round_bf16(oracle.gmm(a, f64(w2[e:e + 1]), one))
-        da = oracle.round_bf16(oracle.gmm_bwd_input(f64(wl["dyp"][r:r + 1]), f64(w2[e:e + 1]), one))
+        da = oracle.gmm_bwd_input(f64(wl["dyp"][r:r + 1]), f64(w2[e:e + 1]), one)  # not rounded: fused
         dh = oracle.round_bf16(oracle.swiglu_bwd(da, h))
         dx = oracle.gmm_bwd_input(dh, f64(w1[e:e + 1]), one)
         for k, ref in (("h", h), ("a", a), ("yp", yp), ("da", da), ("dh", dh), ("dx", dx)):
@@ -144,7 +149,7 @@ def test_ep_rank_forward_backward_sampled(dev, low_memory):
         h = oracle.round_bf16(oracle.gmm(xe, f64(w1[e:e + 1]), [n]))
         a = oracle.round_bf16(oracle.swiglu(h))
         dye = f64(wl["dyp"][off[e]:off[e + 1]])
-        da = oracle.round_bf16(oracle.gmm_bwd_input(dye, f64(w2[e:e + 1]), [n]))
+        da = oracle.gmm_bwd_input(dye, f64(w2[e:e + 1]), [n])  # not rounded: fused
         dh = oracle.round_bf16(oracle.swiglu_bwd(da, h))
         ks1 = rng.integers(0, 4096, 4)
         ks2 = rng.integers(0, 1536, 4)

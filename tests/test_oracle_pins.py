@@ -641,6 +641,31 @@ def test_gmm_swiglu_bruteforce():
     check_gmm_swiglu_brute(oracle.gmm_swiglu)
 
 
+def test_fused_swiglu_bwd_moves_only_a_rounding_point():
+    """The fused chain differs from the plain one only in where dA is rounded:
+    with no rounding both are the same chain; with bf16 rounding dA itself is
+    unchanged, and dH = round(swiglu_bwd(dA, H)) follows the unrounded dA."""
+    rng = np.random.default_rng(5)
+    gl = [3, 0, 2]
+    R, H, I = 5, 16, 8
+    x = oracle.round_bf16(rng.standard_normal((R, H)))
+    w1 = oracle.round_bf16(rng.standard_normal((3, H, 2 * I)) * 0.3)
+    w2 = oracle.round_bf16(rng.standard_normal((3, I, H)) * 0.3)
+    dyp = oracle.round_bf16(rng.standard_normal((R, H)))
+    h = oracle.round_bf16(oracle.gmm(x, w1, gl))
+    a = oracle.round_bf16(oracle.swiglu(h))
+    exact = [oracle.expert_block_backward(x, h, a, dyp, w1, w2, gl, rounding=None, fused_swiglu_bwd=f)
+             for f in (False, True)]
+    for k in exact[0]:
+        np.testing.assert_array_equal(exact[0][k], exact[1][k])
+    plain = oracle.expert_block_backward(x, h, a, dyp, w1, w2, gl)
+    fused = oracle.expert_block_backward(x, h, a, dyp, w1, w2, gl, fused_swiglu_bwd=True)
+    np.testing.assert_array_equal(plain["da"], fused["da"])
+    da_exact = oracle.gmm_bwd_input(dyp, w2, gl)
+    np.testing.assert_array_equal(fused["dh"], oracle.round_bf16(oracle.swiglu_bwd(da_exact, h)))
+    assert not np.array_equal(plain["dh"], fused["dh"])  # the rounding point does move
+
+
 # ---------------------------------------------------------------------------
 # mutation tests: a planted mistake in a copy of an oracle function must trip
 # at least one pin (run on the CPU only)

@@ -263,6 +263,12 @@ MOE_DEVICE void lds_wait(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN]) {
     for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(b[t]));
 }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+MOE_DEVICE void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // The tile engine: C[BM][BN] = A[BM][red] * B[red][BN], fp32 accumulation.
 // ---------------------------------------------------------------------------
@@ -389,93 +395,108 @@ struct Engine {
     // The accumulators hold dA (fp32, not rounded).  With G = h[:, c] and
     // U = h[:, pair + c] at the same rows and columns and s = sigmoid(G),
     // writes dG = dA*U*s*(1 + G*(1 - s)) to dh[:, c] and dU = dA*G*s to
-    // dh[:, pair + c], each rounded once (RNE), through the wave's LDS image
-    // as in store().  dh may be h: a lane has read G and U of its outputs
-    // before anything is written, and no other lane writes them.
+    // dh[:, pair + c], each rounded once (RNE).
+    // A wave takes its rows 32 at a time (one accumulator fragment row),
+    // through two 8 KiB LDS regions used in turn: G and U of the next 32 rows
+    // arrive by LDS DMA as whole 128-byte lines while the current ones are
+    // read back in the accumulator layout, turned into dG and dU in place,
+    // and sent out as whole lines (16-byte chunk c of region row r at chunk
+    // c ^ ((r >> 1) & 7), as in store()).  Every wave issues the same loads
+    // and stores (lanes outside the tile get an out-of-range offset), so the
+    // in-order vector-memory counter tells when a region has landed.  dh may
+    // be h: a wave reads G and U of exactly the outputs it writes, before it
+    // writes them.
     MOE_DEVICE void store_swiglu_bwd(bf16_t* dh, const bf16_t* h, int64_t ld, int pair, int rows_valid,
                                      int cols_valid, bf16_t* smem) const {
-        static_assert(WTN == 64, "one 128-byte row segment per wave row");
+        static_assert(WTN == 64 && TM >= 2, "128-byte row segments, at least two passes");
+        constexpr int kRows = 32;       // rows per pass
+        constexpr int kIt = kRows / 8;  // 8 rows of 128 bytes per instruction
+        constexpr int kRegion = 2 * kRows * WTN;  // G and U of one pass, bf16 elements
+        static_assert(kWaves * 2 * kRegion <= (BM + BN) * BK * kNST, "regions fit the ring");
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
         const int lane = tid & 63;
         const int wid = wave_id();
         const int wm = wid / WN, wn = wid % WN;
+        const int lr = lane >> 3, pch = lane & 7;  // row, physical chunk of one 1 KiB transfer
+        const int wcol = wn * WTN;
+        const uint32_t row_off = (uint32_t)(((int64_t)lr * ld) * 2);
+        bf16_t* regions = smem + wid * (2 * kRegion);
         __syncthreads();  // every wave is done reading the ring
-        bf16_t* img = smem + wid * (WTM * WTN);
-        const uint32_t ld_off = (uint32_t)(((int64_t)(lane & 31) * ld + (lane >> 5) * 4) * 2);
-        const int rl = rows_valid - wm * WTM - (lane & 31), cl = cols_valid - wn * WTN - (lane >> 5) * 4;
-        u32x2_t du[TM][TN][4];
+        auto fetch = [&](int i) {  // G and U of pass i into region i & 1 (zeros outside the tile)
+            bf16_t* img_g = regions + (i & 1) * kRegion;
+            const int row_base = wm * WTM + i * kRows;
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int r = it * 8 + lr;
+                const int lc = pch ^ ((r >> 1) & 7);  // logical chunk that lands at pch
+                const bool ok = row_base + r < rows_valid && wcol + lc * 8 < cols_valid;
+                const uint32_t off = ok ? row_off + (uint32_t)(lc * 16) : kOOB;
+                const bf16_t* src = h + (int64_t)(row_base + it * 8) * ld + wcol;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src), (LDS_AS void*)(img_g + it * 512),
+                                                         16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(src + pair),
+                                                         (LDS_AS void*)(img_g + kRows * WTN + it * 512), 16,
+                                                         off, 0, 0, 0);
+            }
+        };
+        const uint32_t out_off = (uint32_t)(((int64_t)lr * ld + pch * 8) * 2);
+        fetch(0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const __amdgpu_buffer_rsrc_t rg = make_rsrc(h + (int64_t)(wm * WTM + i * 32) * ld + wn * WTN);
-            const __amdgpu_buffer_rsrc_t ru =
-                make_rsrc(h + (int64_t)(wm * WTM + i * 32) * ld + pair + wn * WTN);
-            u32x2_t gq[TN][4], uq[TN][4];
+            if (i + 1 < TM) fetch(i + 1);
+            // pass i's transfers have landed once at most the later ones are
+            // outstanding: pass i+1's (2 kIt) and pass i-1's stores (2 kIt)
+            if (i == 0) wait_vmcnt<2 * kIt>();
+            else if (i + 1 < TM) wait_vmcnt<4 * kIt>();
+            else wait_vmcnt<2 * kIt>();
+            bf16_t* img_g = regions + (i & 1) * kRegion;
+            bf16_t* img_u = img_g + kRows * WTN;
+            const int r = lane & 31;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const bool ok = i * 32 < rl && j * 32 + g * 8 < cl;
-                    const uint32_t off = ok ? ld_off + (uint32_t)((j * 32 + g * 8) * 2) : kOOB;
-                    gq[j][g] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
-                    uq[j][g] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(ru, off, 0, 0));
-                }
-            const int r = i * 32 + (lane & 31);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                    const int o = r * 64 + (((j * 4 + g) ^ ((r >> 1) & 7)) << 3) + (lane >> 5) * 4;
+                    const u32x2_t gq = *reinterpret_cast<const u32x2_t*>(img_g + o);
+                    const u32x2_t uq = *reinterpret_cast<const u32x2_t*>(img_u + o);
                     float dgv[4], duv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint32_t gw = gq[j][g][q >> 1], uw = uq[j][g][q >> 1];
-                        const float gv = (q & 1) ? bf16_hi(gw) : bf16_lo(gw);
-                        const float uv = (q & 1) ? bf16_hi(uw) : bf16_lo(uw);
+                        const float gv = (q & 1) ? bf16_hi(gq[q >> 1]) : bf16_lo(gq[q >> 1]);
+                        const float uv = (q & 1) ? bf16_hi(uq[q >> 1]) : bf16_lo(uq[q >> 1]);
                         const float dv = acc[i][j][4 * g + q];
                         const float sg = silu_sigmoid(gv);
                         dgv[q] = dv * uv * sg * (1.0f + gv * (1.0f - sg));
                         duv[q] = dv * gv * sg;
                     }
-                    u32x2_t pk;
-                    pk[0] = pack_bf16x2(dgv[0], dgv[1]);
-                    pk[1] = pack_bf16x2(dgv[2], dgv[3]);
-                    du[i][j][g][0] = pack_bf16x2(duv[0], duv[1]);
-                    du[i][j][g][1] = pack_bf16x2(duv[2], duv[3]);
-                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
-                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
+                    u32x2_t pg, pu;
+                    pg[0] = pack_bf16x2(dgv[0], dgv[1]);
+                    pg[1] = pack_bf16x2(dgv[2], dgv[3]);
+                    pu[0] = pack_bf16x2(duv[0], duv[1]);
+                    pu[1] = pack_bf16x2(duv[2], duv[3]);
+                    // the same 8 bytes this lane read: no other lane touches them
+                    *reinterpret_cast<u32x2_t*>(img_g + o) = pg;
+                    *reinterpret_cast<u32x2_t*>(img_u + o) = pu;
                 }
-        }
-        const int c = lane & 7;
-        const uint32_t lane_off = (uint32_t)(((int64_t)(lane >> 3) * ld + c * 8) * 2);
-        constexpr int kIt = WTM / 8;
-        auto copy_out = [&](bf16_t* dst) {
-            u32x4_t v[kIt];
+            u32x4_t vg[kIt], vu[kIt];
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
-                const int r = it * 8 + (lane >> 3);
-                v[it] = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+                const int rr = it * 8 + lr;
+                const int o = rr * 64 + ((pch ^ ((rr >> 1) & 7)) << 3);
+                vg[it] = *reinterpret_cast<const u32x4_t*>(img_g + o);
+                vu[it] = *reinterpret_cast<const u32x4_t*>(img_u + o);
             }
+            const int row_base = wm * WTM + i * kRows;
 #pragma unroll
             for (int it = 0; it < kIt; ++it) {
-                const int row = wm * WTM + it * 8 + (lane >> 3), col = wn * WTN + c * 8;
-                const bool ok = row < rows_valid && col < cols_valid;
-                store_nt16(v[it], dst + (int64_t)(wm * WTM + it * 8) * ld + wn * WTN, ok ? lane_off : kOOB);
+                const int r0 = row_base + it * 8;
+                const bool ok = r0 + lr < rows_valid && wcol + pch * 8 < cols_valid;
+                bf16_t* dst = dh + (int64_t)r0 * ld + wcol;
+                store_nt16(vg[it], dst, ok ? out_off : kOOB);
+                store_nt16(vu[it], dst + pair, ok ? out_off : kOOB);
             }
-        };
-        copy_out(dh);  // dG
-        // the wave's image again (its reads above are done before these writes)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = i * 32 + (lane & 31);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
-                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = du[i][j][g];
-                }
         }
-        copy_out(dh + pair);  // dU
     }
 
     // Gate_up tile with paired columns (see Dma::init): fragment 0 of a wave
@@ -562,12 +583,6 @@ struct Engine {
         copy_out(img_a, h + pair, ldh);
     }
 };
-
-// Wait until at most N of this wave's vector-memory loads are outstanding.
-template <int N>
-MOE_DEVICE void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
-}
 
 // One output tile over a ring of kNST LDS stages.  Per step s: wait for this
 // wave's copies of step s (the kNST-2 later steps stay in flight), barrier

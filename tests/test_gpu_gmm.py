@@ -94,8 +94,8 @@ def test_ragged_shapes(dev, M, K, N, gl):
 
 
 def test_max_experts(dev):
-    """E = 1024 (the API limit): the schedules scan 1024 counts, and the
-    weight gradient takes experts in index order past 256 (no ranking)."""
+    """E = 1024 (the API limit): the schedules scan 1024 counts and the
+    weight gradient ranks all 1024 experts."""
     rng = np.random.default_rng(1024)
     E, M, K, N = 1024, 3000, 64, 136
     gl = workloads.random_group_list(rng, M, E, empty_frac=0.7, fill=0.95)
@@ -307,6 +307,43 @@ def test_dw_tile_queue_workspace(dev):
                      "dw queue")
 
 
+def _bwd_swiglu_case(dev, x_b, dy_b, w_b, h_b, gl, in_place, tag):
+    M, K = x_b.shape
+    R = int(np.sum(gl))
+    print(f"gmm_bwd_swiglu {tag}: E={len(gl)} M={M} K={K} N={dy_b.shape[1]} in_place={in_place}", flush=True)
+    x, dy, w, h = (bf16_dev(b, dev) for b in (x_b, dy_b, w_b, h_b))
+    g = _gl(dev, gl)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    if in_place:
+        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, h, g, dh_out=h, dev_err=err)
+    else:
+        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, h, g, dh_out=_sentinel(dev, (M, 2 * K)), dev_err=err)
+    dw_ref_bits = dev_bits(moe.gmm_bwd_weight(x, dy, g, dev_err=err))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.swiglu_bwd(oracle.gmm_bwd_input(f64(dy_b), f64(w_b), gl), f64(h_b))
+    assert_close(f64(dev_bits(dh))[:R], ref[:R], f"gmm_bwd_swiglu {tag} dH")
+    tail = dev_bits(dh)[R:]
+    assert (tail == (h_b[R:] if in_place else SENT)).all(), "rows >= R were written"
+    assert np.array_equal(dev_bits(dw), dw_ref_bits), "dW differs from gmm_bwd_weight"
+
+
+def test_bwd_swiglu_limits(dev):
+    """gmm_bwd_swiglu at the API limits: E = 1024 experts (mostly empty), and a
+    2^21-long reduction for the input gradient (N = 2^21)."""
+    rng = np.random.default_rng(2024)
+    E, M, K, N = 1024, 3000, 64, 136
+    gl = workloads.random_group_list(rng, M, E, empty_frac=0.7, fill=0.95)
+    _bwd_swiglu_case(dev, workloads.normal_bf16(rng, (M, K)), workloads.normal_bf16(rng, (M, N)),
+                     workloads.normal_bf16(rng, (E, K, N), 0.05), workloads.normal_bf16(rng, (M, 2 * K), 1.5),
+                     gl, False, "E1024")
+    E, M, K, N = 2, 64, 8, 1 << 21
+    gl = np.array([40, 24], dtype=np.int64)
+    _bwd_swiglu_case(dev, workloads.normal_bf16(rng, (M, K)), workloads.normal_bf16(rng, (M, N)),
+                     workloads.normal_bf16(rng, (E, K, N), 0.001), workloads.normal_bf16(rng, (M, 2 * K), 1.5),
+                     gl, True, "N=2^21")
+
+
 @pytest.mark.parametrize("M,K,N,gl,in_place", [
     (1000, 264, 520, [300, 0, 200, 100, 0, 150, 250, 0], False),  # ragged tiles, empty experts
     (777, 72, 264, [0, 777, 0], True),                            # dH written over H
@@ -317,25 +354,7 @@ def test_bwd_swiglu(dev, M, K, N, gl, in_place):
     """gmm_bwd_swiglu: dH = swiglu_bwd(dy @ w[e]^T, h) with the product kept
     in fp32, and dW bit-identical to gmm_bwd_weight; rows >= R untouched."""
     rng = np.random.default_rng(M + K + N)
-    E, R = len(gl), int(sum(gl))
-    print(f"gmm_bwd_swiglu: E={E} M={M} K={K} N={N} in_place={in_place}", flush=True)
-    x_b = workloads.normal_bf16(rng, (M, K))
-    dy_b = workloads.normal_bf16(rng, (M, N))
-    w_b = workloads.normal_bf16(rng, (E, K, N), std=0.05)
-    h_b = workloads.normal_bf16(rng, (M, 2 * K), std=1.5)
-    x, dy, w, h = (bf16_dev(b, dev) for b in (x_b, dy_b, w_b, h_b))
-    g = _gl(dev, gl)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    if in_place:
-        dh_out = bf16_dev(h_b, dev)
-        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, dh_out, g, dh_out=dh_out, dev_err=err)
-    else:
-        dh, dw = moe.gmm_bwd_swiglu(x, dy, w, h, g, dh_out=_sentinel(dev, (M, 2 * K)), dev_err=err)
-    dw_ref_bits = dev_bits(moe.gmm_bwd_weight(x, dy, g, dev_err=err))
-    torch.cuda.synchronize()
-    assert int(err.item()) == 0
-    ref = oracle.swiglu_bwd(oracle.gmm_bwd_input(f64(dy_b), f64(w_b), gl), f64(h_b))
-    assert_close(f64(dev_bits(dh))[:R], ref[:R], "gmm_bwd_swiglu dH")
-    tail = dev_bits(dh)[R:]
-    assert (tail == (h_b[R:] if in_place else SENT)).all(), "rows >= R were written"
-    assert np.array_equal(dev_bits(dw), dw_ref_bits), "dW differs from gmm_bwd_weight"
+    E = len(gl)
+    _bwd_swiglu_case(dev, workloads.normal_bf16(rng, (M, K)), workloads.normal_bf16(rng, (M, N)),
+                     workloads.normal_bf16(rng, (E, K, N), std=0.05),
+                     workloads.normal_bf16(rng, (M, 2 * K), std=1.5), gl, in_place, "sweep")

@@ -288,50 +288,55 @@ struct Engine {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     }
 
+    // NA: the wave's 32-row fragments that hold valid rows (the others are
+    // past an expert's last row: their LDS reads and MFMAs are skipped).
+    template <int NA = TM>
     MOE_DEVICE void load_frags(bf16x8_t (&a)[TM], bf16x8_t (&b)[TN], const bf16_t* la, const bf16_t* lb,
                                int ks) const {
         const int wid = threadIdx.x >> 6;
         const int wm = wid / WN, wn = wid % WN;
 #pragma unroll
-        for (int t = 0; t < TM; ++t) Frag<BM, A_KMAJOR>::load(a[t], la, wm * WTM + t * 32, ks * 16);
+        for (int t = 0; t < NA; ++t) Frag<BM, A_KMAJOR>::load(a[t], la, wm * WTM + t * 32, ks * 16);
 #pragma unroll
         for (int t = 0; t < TN; ++t) Frag<BN, B_KMAJOR>::load(b[t], lb, wn * WTN + t * 32, ks * 16);
     }
 
-    // MFMAs of one sub-step; hook(m) runs after the m-th MFMA of the step
-    // (m counts across sub-steps), so loads can be spread between MFMAs.
-    template <class Hook>
+    // MFMAs of one sub-step; hook(m) runs after the m-th MFMA slot of the
+    // step (m counts across sub-steps, skipped fragments included), so loads
+    // can be spread between MFMAs and every hook runs whatever NA is.
+    template <int NA = TM, class Hook>
     MOE_DEVICE void mfmas(const bf16x8_t (&a)[TM], const bf16x8_t (&b)[TN], int ks, Hook& hook) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+                if (i < NA) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
                 hook(ks * TM * TN + i * TN + j);
             }
     }
 
     // One reduction step from LDS: fragments of sub-step ks+1 are read while
     // the MFMAs of sub-step ks run.
-    template <class Hook>
+    template <int NA = TM, class Hook>
     MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb, Hook& hook) {
         static_assert(BK / 16 == 2 || BK / 16 == 4, "sub-steps");
+        static_assert(NA >= 1 && NA <= TM, "active fragments");
         bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-        load_frags(a0, b0, la, lb, 0);
+        load_frags<NA>(a0, b0, la, lb, 0);
         lds_wait(a0, b0);
-        load_frags(a1, b1, la, lb, 1);
-        mfmas(a0, b0, 0, hook);
+        load_frags<NA>(a1, b1, la, lb, 1);
+        mfmas<NA>(a0, b0, 0, hook);
         lds_wait(a1, b1);
         if constexpr (BK / 16 == 4) {
-            load_frags(a0, b0, la, lb, 2);
-            mfmas(a1, b1, 1, hook);
+            load_frags<NA>(a0, b0, la, lb, 2);
+            mfmas<NA>(a1, b1, 1, hook);
             lds_wait(a0, b0);
-            load_frags(a1, b1, la, lb, 3);
-            mfmas(a0, b0, 2, hook);
+            load_frags<NA>(a1, b1, la, lb, 3);
+            mfmas<NA>(a0, b0, 2, hook);
             lds_wait(a1, b1);
-            mfmas(a1, b1, 3, hook);
+            mfmas<NA>(a1, b1, 3, hook);
         } else {
-            mfmas(a1, b1, 1, hook);
+            mfmas<NA>(a1, b1, 1, hook);
         }
     }
 
@@ -641,17 +646,28 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
                 }
             }
         };
-        if constexpr (decltype(active_tag)::value) {
+        if constexpr (decltype(active_tag)::value > 0) {
             const bf16_t* st = smem + (s % kNST) * kStage;
-            eng.compute(st, st + BM * BK, hook);
+            eng.template compute<decltype(active_tag)::value>(st, st + BM * BK, hook);
         } else {
 #pragma unroll
             for (int m = 0; m < kMfmaPerStep; ++m) hook(m);
         }
     }
     };
-    if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
-    else run_steps(std::false_type{});
+    // 32-row fragments of this wave with valid rows: a copy of the step loop
+    // per count, so the full-tile loop carries no branch
+    constexpr int TM = BM / WM / 32;
+    const int na = wcol0 < cols_valid ? (rows_valid - wrow0 + 31) / 32 : 0;
+    if (na >= TM) run_steps(std::integral_constant<int, TM>{});
+    else if (na <= 0) run_steps(std::integral_constant<int, 0>{});
+    else if (na == 1) run_steps(std::integral_constant<int, 1>{});
+    else if constexpr (TM > 2) {
+        if (na == 2) run_steps(std::integral_constant<int, 2>{});
+        else run_steps(std::integral_constant<int, TM - 1>{});
+    } else {
+        run_steps(std::integral_constant<int, TM>{});
+    }
     wait_vmcnt<0>();  // no LDS write may outlive the workgroup
     store(eng);
 }

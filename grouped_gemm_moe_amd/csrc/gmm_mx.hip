@@ -116,10 +116,13 @@ struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
 
     // One 64-element step.  kb: this lane's group within the scale slot;
     // kb_ok false for a group past ceil(K/32) (its codes are zero; its scale
-    // byte, padding, is replaced by 2^0).
-    template <class Hook>
+    // byte, padding, is replaced by 2^0).  NA: the wave's 32-row fragments
+    // with valid rows; the others skip their reads and MFMAs (every hook
+    // still runs).
+    template <int NA = TM, class Hook>
     MOE_DEVICE void compute(const bf16_t* la, const bf16_t* lb, const uint8_t* sla, const uint8_t* slb,
                             int kb, bool kb_ok, Hook& hook) {
+        static_assert(NA >= 1 && NA <= TM, "active fragments");
         const int wid = threadIdx.x >> 6;
         const int wm = wid / WN, wn = wid % WN;
         i32x8_t a[TM], b[TN];
@@ -131,6 +134,7 @@ struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
         }
 #pragma unroll
         for (int i = 0; i < TM / 2; ++i) {
+            if (i >= NA) continue;
             frag(a[i], la, wm * WTM + i * 32);
             scale(sa[i], sla, wm * WTM + i * 32, kb);
         }
@@ -138,9 +142,11 @@ struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
 #pragma unroll
         for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(b[j]), "+v"(sb[j]));
 #pragma unroll
-        for (int i = 0; i < TM / 2; ++i) asm volatile("" : "+v"(a[i]), "+v"(sa[i]));
+        for (int i = 0; i < TM / 2; ++i)
+            if (i < NA) asm volatile("" : "+v"(a[i]), "+v"(sa[i]));
 #pragma unroll
         for (int i = TM / 2; i < TM; ++i) {
+            if (i >= NA) continue;
             frag(a[i], la, wm * WTM + i * 32);
             scale(sa[i], sla, wm * WTM + i * 32, kb);
         }
@@ -148,17 +154,18 @@ struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
         for (int j = 0; j < TN; ++j) sb[j] = kb_ok ? sb[j] : 127u;
 #pragma unroll
         for (int i = 0; i < TM / 2; ++i) sa[i] = kb_ok ? sa[i] : 127u;
-        mfmas(a, b, sa, sb, 0, TM / 2, hook);
+        mfmas<NA>(a, b, sa, sb, 0, TM / 2, hook);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int i = TM / 2; i < TM; ++i) {
+            if (i >= NA) continue;
             asm volatile("" : "+v"(a[i]), "+v"(sa[i]));
             sa[i] = kb_ok ? sa[i] : 127u;
         }
-        mfmas(a, b, sa, sb, TM / 2, TM, hook);
+        mfmas<NA>(a, b, sa, sb, TM / 2, TM, hook);
     }
 
-    template <class Hook>
+    template <int NA, class Hook>
     MOE_DEVICE void mfmas(const i32x8_t (&a)[TM], const i32x8_t (&b)[TN], const uint32_t (&sa)[TM],
                           const uint32_t (&sb)[TN], int i0, int i1, Hook& hook) {
 #pragma unroll
@@ -166,8 +173,9 @@ struct EngineMx : Engine<BM, BN, WM, WN, true, true> {
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 // operands swapped, as in the bf16 engine: B is the hardware A
-                this->acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[j], a[i], this->acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
+                if (i < NA)
+                    this->acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        b[j], a[i], this->acc[i][j], 0, 0, 0, (int)sb[j], 0, (int)sa[i]);
                 hook(i * TN + j);
             }
     }
@@ -272,19 +280,28 @@ MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a
                     }
                 }
             };
-            if constexpr (decltype(active_tag)::value) {
+            if constexpr (decltype(active_tag)::value > 0) {
                 const bf16_t* st = smem + (s % kNST) * kStage;
                 const uint8_t* sl = ssc + ((s / kStepsPerScaleLoad) & 1) * kScaleSlot;
                 const int kb = 2 * s + lane_grp;
-                eng.compute(st, st + BM * BK, sl, sl + BM * 16, kb & 15, kb < nblocks, hook);
+                eng.template compute<decltype(active_tag)::value>(st, st + BM * BK, sl, sl + BM * 16,
+                                                                  kb & 15, kb < nblocks, hook);
             } else {
 #pragma unroll
                 for (int m = 0; m < kMfmaPerStep; ++m) hook(m);
             }
         }
     };
-    if (wrow0 < rows_valid && wcol0 < cols_valid) run_steps(std::true_type{});
-    else run_steps(std::false_type{});
+    // 32-row fragments of this wave with valid rows: one copy of the step
+    // loop per count, so the full-tile loop carries no branch
+    constexpr int TM = EngineMx<BM, BN, WM, WN>::TM;
+    static_assert(TM == 4, "fragment-count dispatch below");
+    const int na = wcol0 < cols_valid ? (rows_valid - wrow0 + 31) / 32 : 0;
+    if (na >= TM) run_steps(std::integral_constant<int, TM>{});
+    else if (na <= 0) run_steps(std::integral_constant<int, 0>{});
+    else if (na == 1) run_steps(std::integral_constant<int, 1>{});
+    else if (na == 2) run_steps(std::integral_constant<int, 2>{});
+    else run_steps(std::integral_constant<int, 3>{});
     wait_vmcnt<0>();  // no LDS write may outlive the workgroup
     store(eng);
 }

@@ -44,12 +44,11 @@ namespace moegmm {
 
 namespace {
 
-#ifndef MOEGMM_THREADS
-#define MOEGMM_THREADS 512
-#endif
-constexpr int kThreads = MOEGMM_THREADS;  // 4 or 8 waves
+constexpr int kThreads = 512;  // 8 waves
 constexpr int kWaves = kThreads / 64;
 
+// The ring: (BK, NST) = (32, 4), or (64, 2) as a build option.  Both hold
+// 128 KiB, which the epilogue images need.
 #ifndef MOEGMM_BK
 #define MOEGMM_BK 32
 #endif
@@ -58,8 +57,7 @@ constexpr int kWaves = kThreads / 64;
 #endif
 constexpr int BK = MOEGMM_BK;     // reduction depth of one LDS stage
 constexpr int kNST = MOEGMM_NST;  // LDS stages in the ring
-static_assert(BK == 32 || BK == 64, "stage depth");
-static_assert(kNST >= 2 && kNST <= 6, "stage count");
+static_assert((BK == 32 && kNST == 4) || (BK == 64 && kNST == 2), "ring of 128 KiB");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -680,19 +678,9 @@ MOE_DEVICE int xcd_remap(int bid, int n) {
     return x * q + (x < r ? x : r) + j;
 }
 
-#ifndef MOEGMM_BM
-#define MOEGMM_BM 256
-#endif
-#ifndef MOEGMM_BN
-#define MOEGMM_BN 256
-#endif
-#ifndef MOEGMM_WM
-#define MOEGMM_WM 2
-#endif
-#ifndef MOEGMM_WN
-#define MOEGMM_WN 4
-#endif
-constexpr int kBM = MOEGMM_BM, kBN = MOEGMM_BN, kWM = MOEGMM_WM, kWN = MOEGMM_WN;
+// 256x256 output tiles, 8 waves of 128x64: the copy split, the epilogue
+// images and the SwiGLU passes assume this shape (see their static_asserts).
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
 // two workgroups per CU when the LDS ring and the accumulators allow it: one
 // workgroup's epilogue and first loads then overlap the other's MFMAs
@@ -761,11 +749,7 @@ MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int
     const int total_mt = row_tile_starts<BM>(s_cnt, E, s_tst, s_scan);
     const int ntiles = total_mt * NT;
     if ((int)blockIdx.x >= ntiles) return false;  // uniform across the block
-#if defined(MOEGMM_NO_XCD_REMAP)
-    const int t = blockIdx.x;
-#else
     const int t = xcd_remap(blockIdx.x, ntiles);
-#endif
     rt = row_tile_at<BM>(s_off, s_cnt, s_tst, E, NT, t);
     __syncthreads();  // schedule arrays are dead from here on
     return true;

@@ -26,6 +26,14 @@ namespace {
 //   kSwiGLU: the gate_up forward with N = 2I fused with SwiGLU: a tile covers
 //            kBN/2 output columns c of a [M_cap, I], reading gate columns c
 //            and up columns I + c of w[e]; optionally h [M_cap, 2I] too.
+//
+// Persistent workgroups, a multiple of 8 (workgroup b runs on XCD b % 8).
+// XCD x owns a contiguous eighth of the logical tile order (expert, row tile,
+// column tile), and its P workgroups take that range's tiles c, c + P,
+// c + 2P, ...  The tiles an XCD runs at one time are then consecutive in that
+// order and start together, so the row and weight panels they share come into
+// its L2 once; with one workgroup per tile they started wherever a CU freed
+// up.  Each workgroup reads group_list and builds the schedule once.
 // ---------------------------------------------------------------------------
 enum RowsMode { kFwd = 0, kDx = 1, kSwiGLU = 2 };
 
@@ -45,37 +53,40 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     constexpr int kCols = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_tst[kMaxExperts];
     const int Ncols = IS_DX ? K : (MODE == kSwiGLU ? N / 2 : N);  // output columns
     const int Kred = IS_DX ? N : K;                                 // reduction length
     const int NT = (Ncols + kCols - 1) / kCols;
-    // schedule arrays: in the last stage, which no load touches before the
-    // first barrier of the main loop
-    RowTile rt;
-    if (!find_row_tile<kBM>(group_list, E, M_cap, NT,
-                            reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK), s_scan,
-                            dev_err, rt))
-        return;
-    const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
-    const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
+    const int xcd = blockIdx.x & 7, P = gridDim.x >> 3;
+    const int q = ntiles >> 3, r = ntiles & 7;
+    const int first = xcd * q + (xcd < r ? xcd : r), count = q + (xcd < r ? 1 : 0);
+    for (int j = blockIdx.x >> 3; j < count; j += P) {
+        const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, first + j);
+        const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
+        const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
 
-    const int64_t lda = IS_DX ? N : K;
-    const bf16_t* We = W + (int64_t)e * K * N;
-    const int cols_left = Ncols - n0;
-    if constexpr (MODE == kSwiGLU) {
-        bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
-        bf16_t* h = Hout ? Hout + (int64_t)row0 * N + n0 : nullptr;
-        const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
-        gemm_tile<kBM, kBN, kWM, kWN, true, false>(
-            A + (int64_t)row0 * lda, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid,
-            tile_cols, smem, [&](const auto& eng) {
-                eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem);
-            });
-    } else {
-        bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
-        gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
-            A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N,
-            cols_left, 0, Kred, rows_valid, cols_left, smem,
-            [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); });
+        const int64_t lda = IS_DX ? N : K;
+        const bf16_t* We = W + (int64_t)e * K * N;
+        const int cols_left = Ncols - n0;
+        if constexpr (MODE == kSwiGLU) {
+            bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
+            bf16_t* h = Hout ? Hout + (int64_t)row0 * N + n0 : nullptr;
+            const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
+            gemm_tile<kBM, kBN, kWM, kWN, true, false>(
+                A + (int64_t)row0 * lda, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid,
+                tile_cols, smem, [&](const auto& eng) {
+                    eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem);
+                });
+        } else {
+            bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
+            gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
+                A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N,
+                cols_left, 0, Kred, rows_valid, cols_left, smem,
+                [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); });
+        }
+        __syncthreads();  // every wave is done with its epilogue image before the next tile's copies
     }
 }
 
@@ -296,8 +307,7 @@ hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* g
     if (M_cap == 0) return hipSuccess;
     if (gmm_stream_applies(E, M_cap, K))
         return launch_gmm_stream(x, w, group_list, E, M_cap, K, N, y, dev_err, stream);
-    const int64_t NT = (N + kBN - 1) / kBN;
-    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
     hipLaunchKernelGGL(gmm_rows_kernel<kFwd>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
                        group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err);
     return hipGetLastError();
@@ -307,8 +317,7 @@ hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int
                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx,
                                 void*, int32_t* dev_err, hipStream_t stream) {
     if (M_cap == 0) return hipSuccess;
-    const int64_t NT = (K + kBN - 1) / kBN;
-    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
     hipLaunchKernelGGL(gmm_rows_kernel<kDx>, dim3((unsigned)grid), dim3(kThreads), 0, stream, dy, w,
                        group_list, (int)E, M_cap, (int)K, (int)N, dx, nullptr, dev_err);
     return hipGetLastError();
@@ -352,8 +361,7 @@ hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const in
     if (M_cap == 0) return hipSuccess;
     if (gmm_stream_applies(E, M_cap, K))
         return launch_gmm_stream_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, dev_err, stream);
-    const int64_t NT = (I + kBN / 2 - 1) / (kBN / 2);
-    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
     hipLaunchKernelGGL(gmm_rows_kernel<kSwiGLU>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x,
                        w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h, dev_err);
     return hipGetLastError();

@@ -7,8 +7,9 @@
 //    in LDS and finds its own tile: a row-grouped tile list for fwd / dX (sum
 //    over experts of ceil(n_e/BM) M-tiles times the N-tiles, walked in an
 //    XCD-aware order so neighbouring tiles share an L2) and an (expert,
-//    k-tile, n-tile) list for dW, largest experts first.  The grid is sized
-//    from host-known bounds; surplus workgroups exit at once.
+//    k-tile, n-tile) list for dW, largest experts first.  The bf16 kernels
+//    run persistent workgroups, one per CU; the MXFP8 kernel sizes its grid
+//    from host-known bounds, and its surplus workgroups exit at once.
 //  * One MFMA engine: 256x256 output tile per workgroup, 8 waves (two per
 //    SIMD, so one hides the other's waits) of 128x64 each,
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave whose

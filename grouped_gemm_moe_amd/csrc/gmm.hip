@@ -59,11 +59,9 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const int NT = (Ncols + kCols - 1) / kCols;
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
-    const int xcd = blockIdx.x & 7, P = gridDim.x >> 3;
-    const int q = ntiles >> 3, r = ntiles & 7;
-    const int first = xcd * q + (xcd < r ? xcd : r), count = q + (xcd < r ? 1 : 0);
-    for (int j = blockIdx.x >> 3; j < count; j += P) {
-        const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, first + j);
+    const XcdRange xr = xcd_range(blockIdx.x & 7, ntiles);
+    for (int j = blockIdx.x >> 3; j < xr.count; j += gridDim.x >> 3) {
+        const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
         const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
         const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
 
@@ -246,8 +244,8 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
     const int nx = total_mt * NTx;
     const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
     // this XCD's input-gradient tiles: [x0, x0 + nxx) of the row-tile order
-    const int q = nx >> 3, r = nx & 7;
-    const int x0 = xcd * q + (xcd < r ? xcd : r), nxx = q + (xcd < r ? 1 : 0);
+    const XcdRange xr = xcd_range(xcd, nx);
+    const int x0 = xr.first, nxx = xr.count;
     const int mine_w = (E * ds.per_e - xcd + 7) / 8;
     const int items = nxx + mine_w;
     uint32_t* ctr = queue + xcd * kQueueStride;
@@ -281,7 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
     if (threadIdx.x == 0) queue_release(queue);
 }
 
-// Compute units of the current device (cached per device).
+}  // namespace
+
 int num_cus() {
     static int cache[64];
     int dev = 0;
@@ -294,8 +293,6 @@ int num_cus() {
     }
     return cache[dev];
 }
-
-}  // namespace
 
 size_t gmm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int op) {
     return op == MOE_GMM_OP_BWD_WEIGHT || op == MOE_GMM_OP_BWD ? kQueueWords * sizeof(uint32_t) : 0;

@@ -7,9 +7,8 @@
 //    in LDS and finds its own tile: a row-grouped tile list for fwd / dX (sum
 //    over experts of ceil(n_e/BM) M-tiles times the N-tiles, walked in an
 //    XCD-aware order so neighbouring tiles share an L2) and an (expert,
-//    k-tile, n-tile) list for dW, largest experts first.  The bf16 kernels
-//    run persistent workgroups, one per CU; the MXFP8 kernel sizes its grid
-//    from host-known bounds, and its surplus workgroups exit at once.
+//    k-tile, n-tile) list for dW, largest experts first.  The kernels run
+//    persistent workgroups, one per CU.
 //  * One MFMA engine: 256x256 output tile per workgroup, 8 waves (two per
 //    SIMD, so one hides the other's waits) of 128x64 each,
 //    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.  A wave whose
@@ -671,12 +670,15 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     store(eng);
 }
 
-// Workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
-// contiguous range of logical tiles so tiles that share operands share an L2.
-MOE_DEVICE int xcd_remap(int bid, int n) {
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+// b % 8).  XCD x owns the contiguous range [first, first + count) of n
+// logical tiles, so tiles that share operands share its L2.
+struct XcdRange {
+    int first, count;
+};
+MOE_DEVICE XcdRange xcd_range(int xcd, int n) {
     const int q = n >> 3, r = n & 7;
-    const int x = bid & 7, j = bid >> 3;
-    return x * q + (x < r ? x : r) + j;
+    return XcdRange{xcd * q + (xcd < r ? xcd : r), q + (xcd < r ? 1 : 0)};
 }
 
 // 256x256 output tiles, 8 waves of 128x64: the copy split, the epilogue
@@ -687,14 +689,11 @@ constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
 // workgroup's epilogue and first loads then overlap the other's MFMAs
 constexpr int kAccRegs = (kBM / kWM) * (kBN / kWN) / 64;
 constexpr int kOccupancy = (kSmemElems * 2 <= 80 * 1024 && kAccRegs <= 128) ? 2 : 1;
-static_assert((kBM + kBN) * BK * 2 >= 12 * 1024, "schedule arrays live in the last stage");
 
 // ---------------------------------------------------------------------------
-// The output tile of this workgroup in a row-grouped GEMM.  Tiles are
-// (expert M-tile, N-tile) pairs: sum over experts of ceil(n_e/BM) M-tiles
-// times NT N-tiles, in logical order expert-major, then walked XCD-aware.
-// `sched` is LDS for 3*kMaxExperts ints (dead once this returns).  Returns
-// false, uniformly across the block, for surplus workgroups.
+// Tiles of a row-grouped GEMM: (expert M-tile, N-tile) pairs, sum over
+// experts of ceil(n_e/BM) M-tiles times NT N-tiles, in logical order
+// expert-major, then M-tile, then N-tile.
 // ---------------------------------------------------------------------------
 struct RowTile {
     int e, row0, rows_valid, nt;
@@ -739,25 +738,6 @@ MOE_DEVICE RowTile row_tile_at(const int* s_off, const int* s_cnt, const int* s_
     rt.nt = lt % NT;
     return rt;
 }
-
-template <int BM>
-MOE_DEVICE bool find_row_tile(const int64_t* __restrict__ group_list, int E, int64_t M_cap, int NT,
-                              int* sched, int64_t* s_scan, int32_t* dev_err, RowTile& rt) {
-    int* s_off = sched;
-    int* s_cnt = s_off + kMaxExperts;
-    int* s_tst = s_cnt + kMaxExperts;
-    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int total_mt = row_tile_starts<BM>(s_cnt, E, s_tst, s_scan);
-    const int ntiles = total_mt * NT;
-    if ((int)blockIdx.x >= ntiles) return false;  // uniform across the block
-    const int t = xcd_remap(blockIdx.x, ntiles);
-    rt = row_tile_at<BM>(s_off, s_cnt, s_tst, E, NT, t);
-    __syncthreads();  // schedule arrays are dead from here on
-    return true;
-}
-
-// Grid bound for a row-grouped launch: every expert may end in a partial tile.
-inline int64_t row_tiles_bound(int64_t M_cap, int64_t E, int bm) { return (M_cap + bm - 1) / bm + E; }
 
 }  // namespace
 

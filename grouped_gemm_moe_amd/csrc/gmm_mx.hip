@@ -307,7 +307,8 @@ MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a
 }
 
 // ---------------------------------------------------------------------------
-// Row-grouped MX GEMM: tiles (expert M-tile, N-tile) as in gmm_rows_kernel.
+// Row-grouped MX GEMM: tiles (expert M-tile, N-tile) on persistent
+// workgroups, scheduled as in gmm_rows_kernel.
 //   SWIGLU false: y [M_cap, N] bf16 = DQ(x) @ DQ(w[e])^T, w[e] [N][K].
 //   SWIGLU true:  N = 2I weight rows; a tile covers kBN/2 output columns c,
 //                 reading gate rows c and up rows I + c; writes (aq, as).
@@ -323,34 +324,37 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ __attribute__((aligned(16))) uint8_t ssc[2 * kScaleSlot];
     __shared__ int64_t s_scan[kThreads / 64];
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_tst[kMaxExperts];
     const int Ncols = SWIGLU ? N / 2 : N;
     const int NT = (Ncols + kCols - 1) / kCols;
-    RowTile rt;
-    if (!find_row_tile<kBM>(group_list, E, M_cap, NT,
-                            reinterpret_cast<int*>(smem + (kNST - 1) * (kBM + kBN) * BK), s_scan,
-                            dev_err, rt))
-        return;
-    const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
-    const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
-    const int cols_left = Ncols - n0;
-    const uint8_t* We = W + ((int64_t)e * N + n0) * K;
-    const uint8_t* Se = WS + ((int64_t)e * N + n0) * ld_ws;
-    const uint8_t* Xt = X + (int64_t)row0 * K;
-    const uint8_t* XSt = XS + (int64_t)row0 * ld_xs;
-    if constexpr (SWIGLU) {
-        const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
-        gemm_tile_mx<kBM, kBN, kWM, kWN>(
-            Xt, rows_valid, XSt, ld_xs, We, cols_left, Ncols, Se, ld_ws, K, rows_valid, tile_cols,
-            smem, ssc, [&](const auto& eng) {
-                eng.store_swiglu_mx(AQ + (int64_t)row0 * Ncols + n0, Ncols,
-                                    AS + (int64_t)row0 * ld_as, ld_as, n0 / kMxGroup, rows_valid,
-                                    cols_left);
-            });
-    } else {
-        bf16_t* y = Y + (int64_t)row0 * N + n0;
-        gemm_tile_mx<kBM, kBN, kWM, kWN>(
-            Xt, rows_valid, XSt, ld_xs, We, cols_left, 0, Se, ld_ws, K, rows_valid, cols_left, smem,
-            ssc, [&](const auto& eng) { eng.store(y, N, rows_valid, cols_left, smem); });
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
+    const XcdRange xr = xcd_range(blockIdx.x & 7, ntiles);
+    for (int j = blockIdx.x >> 3; j < xr.count; j += gridDim.x >> 3) {
+        const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
+        const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
+        const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
+        const int cols_left = Ncols - n0;
+        const uint8_t* We = W + ((int64_t)e * N + n0) * K;
+        const uint8_t* Se = WS + ((int64_t)e * N + n0) * ld_ws;
+        const uint8_t* Xt = X + (int64_t)row0 * K;
+        const uint8_t* XSt = XS + (int64_t)row0 * ld_xs;
+        if constexpr (SWIGLU) {
+            const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
+            gemm_tile_mx<kBM, kBN, kWM, kWN>(
+                Xt, rows_valid, XSt, ld_xs, We, cols_left, Ncols, Se, ld_ws, K, rows_valid, tile_cols,
+                smem, ssc, [&](const auto& eng) {
+                    eng.store_swiglu_mx(AQ + (int64_t)row0 * Ncols + n0, Ncols,
+                                        AS + (int64_t)row0 * ld_as, ld_as, n0 / kMxGroup, rows_valid,
+                                        cols_left);
+                });
+        } else {
+            bf16_t* y = Y + (int64_t)row0 * N + n0;
+            gemm_tile_mx<kBM, kBN, kWM, kWN>(
+                Xt, rows_valid, XSt, ld_xs, We, cols_left, 0, Se, ld_ws, K, rows_valid, cols_left, smem,
+                ssc, [&](const auto& eng) { eng.store(y, N, rows_valid, cols_left, smem); });
+        }
+        __syncthreads();  // every wave is done with its epilogue image before the next tile's copies
     }
 }
 
@@ -576,8 +580,7 @@ hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
                            (int)E, M_cap, (int)K, (int)N, y, nullptr, nullptr, (int64_t)0, dev_err);
         return hipGetLastError();
     }
-    const int64_t NT = (N + kBN - 1) / kBN;
-    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
     hipLaunchKernelGGL(gmm_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        xq, xs, ld_xs, wq, ws, ld_ws, group_list, (int)E, M_cap, (int)K, (int)N, y,
                        nullptr, nullptr, (int64_t)0, dev_err);
@@ -598,8 +601,7 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
                            dev_err);
         return hipGetLastError();
     }
-    const int64_t NT = (I + kBN / 2 - 1) / (kBN / 2);
-    const int64_t grid = row_tiles_bound(M_cap, E, kBM) * NT;
+    const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
     hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
                        (int)(2 * I), nullptr, aq, as, ld_as, dev_err);

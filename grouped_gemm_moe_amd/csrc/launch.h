@@ -19,6 +19,9 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                           hipStream_t stream);
 
 // gmm.hip
+// Compute units of the current device (cached per device; 256 if the query fails).
+int num_cus();
+
 size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws,

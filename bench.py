@@ -164,6 +164,25 @@ def ep_gemm_flops(gl, H, I):
             "gmm_bwd_swiglu_down": 2 * fwd2, "gmm_bwd_gate_up": 2 * fwd1}
 
 
+def ep_gemm_bytes(gl, H, I):
+    """Algorithmic HBM bytes per call of the step's GEMMs: every operand read
+    once (weights only of experts with rows), every output written once (the
+    weight gradients of empty experts too: they are written as zeros)."""
+    R = int(np.sum(gl))
+    E = len(gl)
+    act = int(np.sum(np.asarray(gl) > 0))
+    w1, w2 = H * 2 * I * 2, I * H * 2
+    x, h, a, yp = R * H * 2, R * 2 * I * 2, R * I * 2, R * H * 2
+    return {
+        "gmm_fwd_swiglu": dict(read=x + act * w1, write=h + a),
+        "gmm_fwd_down": dict(read=a + act * w2, write=yp),
+        # dW2 = A^T dYp and dH = swiglu_bwd(dYp W2^T, H)
+        "gmm_bwd_swiglu_down": dict(read=a + yp + h + act * w2, write=E * w2 + h),
+        # dX = dH W1^T and dW1 = X^T dH
+        "gmm_bwd_gate_up": dict(read=x + h + act * w1, write=x + E * w1),
+    }
+
+
 # libmoegmm kernel behind each call of the step (kernel symbol -> calls)
 EP_KERNELS = {
     "gmm_rows_kernel<2>": ["gmm_fwd_swiglu"],
@@ -192,21 +211,12 @@ def run_ep(torch, dev, args):
     timer = KernelTimer(torch)
     g = layer.tokens_per_expert
 
-    from grouped_gemm_moe_amd import gmm_bwd, gmm_bwd_swiglu, gmm_fwd, gmm_fwd_swiglu, moe_unpermute
+    # the step's calls, shared with the GPU test of the same composition
+    calls = layer.training_step_calls(x, ids, probs, dyp, w1, w2)
 
     def step(t):
-        t("moe_permute", lambda: layer.permute(x, ids))
-        # gate_up GMM fused with SwiGLU; H is kept for the SwiGLU backward
-        t("gmm_fwd_swiglu", lambda: gmm_fwd_swiglu(layer.x_perm, w1, g, out=layer.a, h_out=layer.h,
-                                                   dev_err=layer.dev_err))
-        t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp, dev_err=layer.dev_err))
-        t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out,
-                                                 dev_err=layer.dev_err))
-        t("gmm_bwd_swiglu_down", lambda: gmm_bwd_swiglu(layer.a, dyp, w2, layer.h, g, dh_out=layer.dh,
-                                                        dw_out=layer.dw2, ws=layer.ws_gmm,
-                                                        dev_err=layer.dev_err))
-        t("gmm_bwd_gate_up", lambda: gmm_bwd(layer.x_perm, layer.dh, w1, g, dx_out=layer.dx,
-                                             dw_out=layer.dw1, ws=layer.ws_gmm, dev_err=layer.dev_err))
+        for name, fn in calls:
+            t(name, fn)
 
     plain = lambda name, fn: fn()  # noqa: E731
     for _ in range(args.warmup):
@@ -243,6 +253,9 @@ def run_ep(torch, dev, args):
     dom_ms_per_launch = float(np.mean([v for c in dom_calls for v in dom_per[c]]))
     achieved = dom_flops_per_launch / (dom_ms_per_launch * 1e-3) / 1e12
     traffic = measured_traffic(dom)
+    alg = ep_gemm_bytes(wl["group_list"], H, I)
+    dom_alg_read = sum(alg[c]["read"] for c in dom_calls) / len(dom_calls)
+    dom_alg = dom_alg_read + sum(alg[c]["write"] for c in dom_calls) / len(dom_calls)
     # the same step with the memory-optimised backward (A recomputed from H,
     # gradients written over the forward's dead buffers)
     lm = MoeLayer(LayerShape(R, 1, E, H, I), dev, with_backward=True, low_memory=True)
@@ -280,6 +293,8 @@ def run_ep(torch, dev, args):
                       peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=traffic,
                       traffic_unit="bytes per launch (HBM read + write)",
+                      algorithmic_bytes=dom_alg, algorithmic_read_bytes=dom_alg_read,
+                      traffic_over_algorithmic=round(traffic / dom_alg, 3) if traffic else None,
                       flops_per_launch=dom_flops_per_launch,
                       mean_launch_us=round(dom_ms_per_launch * 1e3, 2)),
     )
@@ -629,12 +644,19 @@ def ceilings(torch, dev):
 def cpu_baseline(wl, budget_s):
     import oracle
 
+    # The host cores this process may run on; the BLAS pool is pinned to
+    # them, or to the thread limit the environment sets if that is lower
+    # (a GPU machine shares its host: OMP_NUM_THREADS states this process's share).
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    env_limit = os.environ.get("OMP_NUM_THREADS", "")
+    if env_limit.isdigit() and 0 < int(env_limit) < threads:
+        threads = int(env_limit)
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        pin = threadpool_limits(limits=threads, user_api="blas")
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pin = None
     gl = wl["group_list"]
     H, I = wl.dims["H"], wl.dims["I"]
     ss, _, _ = oracle.permute_maps(wl["topk_ids"], len(gl))
@@ -667,6 +689,8 @@ def cpu_baseline(wl, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    if pin is not None:
+        pin.restore_original_limits()
     what = f"{passes} whole pass{'es' if passes != 1 else ''} over the {len(active)} active experts"
     if done:
         what += f" and experts {done} of one more"
@@ -679,7 +703,7 @@ def cpu_baseline(wl, budget_s):
     except OSError:
         pass
     return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s", cores=int(threads), kind="oracle",
-                cpu_model=model,
+                affinity_cpus=affinity, cpu_model=model,
                 sample=f"oracle (NumPy float64) expert-block fwd+bwd GEMM chain: {what} "
                        f"({rows} rows; {int(gl.sum())} per pass), {flops / 1e9:.1f} GFLOP in {el:.1f} s",
                 seconds=round(el, 2))

@@ -42,7 +42,7 @@ SIGNATURES = {
                                  _i64, _p, _p]),
 }
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 

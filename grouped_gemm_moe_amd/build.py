@@ -79,6 +79,59 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB_PATH
 
 
+# Host-side checking build: the C ABI layer (api.cpp: argument validation,
+# workspace sizing, dispatch) compiled by g++ with AddressSanitizer and
+# UndefinedBehaviorSanitizer, linked with the release objects of the kernels
+# (their host launchers and device code unchanged).  Only CPU tests load it,
+# through MOEGMM_LIB, with the sanitizer runtime preloaded; see
+# host_check_env().
+HOST_CHECK_DIR = os.path.join(BUILD_DIR, "hostcheck")
+HOST_CHECK_LIB = os.path.join(HOST_CHECK_DIR, "libmoegmm_hostcheck.so")
+HOST_CHECK_FLAGS = ["-std=c++17", "-O1", "-g", "-fPIC", "-fno-omit-frame-pointer",
+                    "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def _rocm() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """Build the sanitizer-instrumented host library (after build())."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found; the host-check build needs it")
+    os.makedirs(HOST_CHECK_DIR, exist_ok=True)
+    api_obj = os.path.join(HOST_CHECK_DIR, "api.o")
+    _run([gxx] + HOST_CHECK_FLAGS + ["-D__HIP_PLATFORM_AMD__", f"-I{_rocm()}/include", f"-I{INCLUDE}",
+                                     f"-I{CSRC}", "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj],
+         verbose)
+    kernels = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "api.cpp"]
+    missing = [k for k in kernels if not os.path.exists(k)]
+    if missing:
+        raise RuntimeError(f"build() first: {missing} missing")
+    tmp = HOST_CHECK_LIB + f".tmp{os.getpid()}"
+    _run([gxx, "-shared", "-fsanitize=address,undefined", "-o", tmp, api_obj] + kernels +
+         [f"-L{_rocm()}/lib", "-lamdhip64", f"-Wl,-rpath,{_rocm()}/lib"], verbose)
+    os.replace(tmp, HOST_CHECK_LIB)
+    return HOST_CHECK_LIB
+
+
+def host_check_env(base=None) -> dict:
+    """Environment for a child process that loads the host-check library:
+    MOEGMM_LIB points at it and g++'s AddressSanitizer runtime is preloaded
+    ahead of whatever the parent preloads (it must come first).  Leak
+    detection is off (the interpreter itself is not instrumented); any
+    sanitizer report aborts the child."""
+    env = dict(os.environ if base is None else base)
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], stdout=subprocess.PIPE,
+                          text=True).stdout.strip()
+    env["MOEGMM_LIB"] = HOST_CHECK_LIB
+    env["LD_PRELOAD"] = ":".join(p for p in (asan, env.get("LD_PRELOAD", "")) if p)
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    return env
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

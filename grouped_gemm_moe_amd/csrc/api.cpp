@@ -24,6 +24,12 @@ constexpr int64_t kMaxGmmDim = int64_t(1) << 21;
 
 moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// The MX kernels address one expert's weight codes ([N][K] bytes) with 31-bit
+// byte offsets from the expert's base (the weight-streaming kernel walks all
+// N rows from it, the SwiGLU tile pairs gate row c with up row N/2 + c), so
+// an expert's codes must stay below that range.
+constexpr int64_t kMaxMxExpertBytes = 0x7FFF0000;
+
 // An MX tensor's scale rows: at least ceil(K/32) bytes, padded to 16.
 bool mx_ld_ok(int64_t ld_s, int64_t K) { return ld_s >= (K + 31) / 32 && ld_s % 16 == 0; }
 
@@ -32,7 +38,7 @@ moe_status check_gmm_mx(const void* xq, const void* xs, int64_t ld_xs, const voi
                         int64_t K, int64_t N) {
     if (!gl || !wq || !ws || (M_cap > 0 && (!xq || !xs))) return MOE_ERR_NULL;
     if (E < 1 || E > kMaxE || M_cap < 0 || M_cap > kMaxRows || !dim_ok(K) || !dim_ok(N) ||
-        K % 32 != 0 || K > kMaxGmmDim || N > kMaxGmmDim)
+        K % 32 != 0 || K > kMaxGmmDim || N > kMaxGmmDim || N * K > kMaxMxExpertBytes)
         return MOE_ERR_INVALID;
     if (!mx_ld_ok(ld_xs, K) || !mx_ld_ok(ld_ws, K)) return MOE_ERR_INVALID;
     if (!aligned(xq, 16) || !aligned(xs, 16) || !aligned(wq, 16) || !aligned(ws, 16) ||
@@ -84,7 +90,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 6; }
+int moegmm_abi_version(void) { return 7; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;

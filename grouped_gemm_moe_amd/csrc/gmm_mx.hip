@@ -566,7 +566,13 @@ __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
 }  // namespace
 
 // Decode-shaped calls (a few rows per expert on average) stream the weights.
-static bool gmm_mx_stream_applies(int64_t E, int64_t M_cap) { return M_cap <= 8 * E; }
+static bool gmm_mx_stream_applies(int64_t E, int64_t M_cap) {
+    switch (forced_gmm_variant()) {
+        case kVariantTile: return false;
+        case kVariantStream: return true;
+        default: return M_cap <= 8 * E;
+    }
+}
 
 hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
                              const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,

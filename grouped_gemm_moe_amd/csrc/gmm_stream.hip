@@ -6,6 +6,9 @@
 // expert's weights once from HBM; an MFMA tile would sit mostly idle on
 // padding rows, so the products run on the vector ALUs in fp32 while 16-byte
 // weight loads stream through every CU.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -191,10 +194,25 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
 
 }  // namespace
 
+GmmVariant forced_gmm_variant() {
+    const char* v = getenv("MOEGMM_FORCE_VARIANT");
+    if (v == nullptr) return kVariantAuto;
+    if (strcmp(v, "tile") == 0) return kVariantTile;
+    if (strcmp(v, "stream") == 0) return kVariantStream;
+    return kVariantAuto;
+}
+
 bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K) {
-    // a few rows per expert on average, and the staged x rows keep the
-    // kernel's total LDS (at most 24 KiB static) within 64 KiB
-    return M_cap <= 8 * E && K * kStreamRows * 2 <= 32 * 1024;
+    // the staged x rows keep the kernel's total LDS (at most 24 KiB static)
+    // within 64 KiB
+    const bool fits = K * kStreamRows * 2 <= 32 * 1024;
+    switch (forced_gmm_variant()) {
+        case kVariantTile: return false;
+        case kVariantStream: return fits;
+        default: break;
+    }
+    // a few rows per expert on average
+    return M_cap <= 8 * E && fits;
 }
 
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,

@@ -48,6 +48,14 @@ hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const in
                                  int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
                                  uint16_t* h, void* ws, int32_t* dev_err, hipStream_t stream);
 
+// Test-only kernel choice for the forward GMMs, from the environment
+// variable MOEGMM_FORCE_VARIANT, read at every call: "tile" runs the
+// row-tile kernels and "stream" the weight-streaming kernels (where their
+// staging fits) whatever the shape; unset or anything else, the library
+// chooses by shape.  Lets tests run both kernels on one input.
+enum GmmVariant { kVariantAuto = 0, kVariantTile = 1, kVariantStream = 2 };
+GmmVariant forced_gmm_variant();
+
 // gmm_stream.hip (decode-shaped forward)
 bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K);
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,

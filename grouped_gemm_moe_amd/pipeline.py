@@ -167,6 +167,30 @@ class MoeLayer:
             swiglu_bwd(self.da, self.h, g, out=self.dh)
         gmm_bwd(self.x_perm, self.dh, w1, g, dx_out=self.dx, dw_out=self.dw1, ws=ws, dev_err=err)
 
+    # -- one training step of the expert block, call by call ----------------
+    def training_step_calls(self, x, topk_ids, probs, dyp, w1, w2):
+        """The forward and the expert-block backward from dYp as (name, call)
+        pairs in launch order, so that a caller can time each call:
+        permute -> gate_up GMM + SwiGLU (H kept) -> down GMM -> unpermute ->
+        down pair with the SwiGLU backward (dH, dW2) -> gate_up pair (dX,
+        dW1).  The same launches as forward(fused=True, keep_h=True)
+        followed by backward(dyp) with the fused SwiGLU backward."""
+        if self.low_memory or not self.fuse_swiglu_bwd or not hasattr(self, "dw1"):
+            raise ValueError("training_step_calls needs with_backward=True, low_memory=False and "
+                             "fuse_swiglu_bwd=True")
+        g, ws, err = self.tokens_per_expert, self.ws_gmm, self.dev_err
+        return [
+            ("moe_permute", lambda: self.permute(x, topk_ids)),
+            ("gmm_fwd_swiglu", lambda: gmm_fwd_swiglu(self.x_perm, w1, g, out=self.a, h_out=self.h,
+                                                      ws=ws, dev_err=err)),
+            ("gmm_fwd_down", lambda: gmm_fwd(self.a, w2, g, out=self.yp, ws=ws, dev_err=err)),
+            ("moe_unpermute", lambda: self.unpermute(probs)),
+            ("gmm_bwd_swiglu_down", lambda: gmm_bwd_swiglu(self.a, dyp, w2, self.h, g, dh_out=self.dh,
+                                                           dw_out=self.dw2, ws=ws, dev_err=err)),
+            ("gmm_bwd_gate_up", lambda: gmm_bwd(self.x_perm, self.dh, w1, g, dx_out=self.dx,
+                                                dw_out=self.dw1, ws=ws, dev_err=err)),
+        ]
+
     # -- backward of the two ends and of the whole layer --------------------
     def unpermute_backward(self, dout, probs):
         moe_unpermute_bwd(dout, self.yp, self.row_id_map, probs, out=(self.dyp, self.dprobs),

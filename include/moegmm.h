@@ -126,6 +126,11 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
  *   y [M_cap, N] bf16 OUT (rows < R written; rows >= R untouched).
  * bf16 products accumulate in fp32; each output is rounded once (RNE).
  * w[e] of an empty expert is never read.
+ * The kernel is chosen by shape: weight streaming when experts own a few
+ * rows each (M_cap <= 8E), row tiles otherwise.  For tests only, the
+ * environment variable MOEGMM_FORCE_VARIANT = "tile" or "stream", read at
+ * every call, forces one of them (streaming where its staging fits,
+ * K <= 4096) for gmm_fwd, gmm_fwd_swiglu and the MX forward calls.
  * ---------------------------------------------------------------------- */
 /* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd_weight and gmm_bwd
  * need 1152 bytes (their tile queue: counters the kernel increments with
@@ -330,7 +335,10 @@ moe_status moe_permute_bwd(const uint16_t* dx_perm, const int32_t* row_id_map, i
  * ceil(K/32) are padding, never read as scales and never written.  K must be
  * a multiple of 32.  Codes and scale pointers must be 16-byte aligned.
  * Weights are stored reduction-contiguous: w[e] is [N, K] (N output
- * columns), so an expert's weight is an MX tensor of N rows.
+ * columns), so an expert's weight is an MX tensor of N rows.  One expert's
+ * codes must hold fewer than 2^31 - 2^16 bytes (N * K <= 0x7FFF0000; N = 2I
+ * for gmm_mx_fwd_swiglu): the kernels address them with 31-bit offsets from
+ * the expert's base.  Larger experts return MOE_ERR_INVALID.
  * ---------------------------------------------------------------------- */
 
 /* ------------------------------------------------------------------------
@@ -366,7 +374,7 @@ moe_status moe_permute_mx(const uint16_t* x, const int32_t* topk_ids, int64_t T,
  *   xq [M_cap, K] codes, xs [M_cap, ld_xs] scales;
  *   wq [E, N, K] codes, ws [E, N, ld_ws] scales;
  *   y [M_cap, N] bf16 OUT (rows >= R untouched).
- * Limits as for gmm_fwd, plus K % 32 == 0.
+ * Limits as for gmm_fwd, plus K % 32 == 0 and N * K <= 0x7FFF0000.
  * ---------------------------------------------------------------------- */
 moe_status gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,
                       const uint8_t* ws, int64_t ld_ws, const int64_t* group_list, int64_t E,
@@ -385,7 +393,8 @@ moe_status gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const
  *   xq [M_cap, K], xs [M_cap, ld_xs]; w1q [E, 2I, K], w1s [E, 2I, ld_w1s];
  *   aq [M_cap, I] codes OUT, as [M_cap, ld_as] scales OUT (rows >= R and
  *   scale padding untouched).
- * Limits as for gmm_fwd_swiglu, plus K % 32 == 0 and I % 32 == 0.
+ * Limits as for gmm_fwd_swiglu, plus K % 32 == 0, I % 32 == 0 and
+ * 2I * K <= 0x7FFF0000.
  * ---------------------------------------------------------------------- */
 moe_status gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
                              const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,

@@ -227,6 +227,8 @@ def test_mx_calls_reject_bad_arguments(lib):
     assert g(xs=MIS) == MOE_ERR_INVALID
     assert g(E=0) == MOE_ERR_INVALID
     assert g(N=1 << 22) == MOE_ERR_INVALID
+    # one expert's codes past 31-bit offsets (N * K > 0x7FFF0000), each dim in range
+    assert g(K=1 << 16, N=1 << 16, lx=2048, lw=2048) == MOE_ERR_INVALID
     # gmm_mx_fwd_swiglu(..., E, M_cap, K, I, aq, as, ld_as, dev_err, stream)
     sw = dict(good, I=32, aq=A16c, asc=A16, la=16)
 
@@ -240,6 +242,7 @@ def test_mx_calls_reject_bad_arguments(lib):
     assert s(la=8) == MOE_ERR_INVALID
     assert s(asc=None) == MOE_ERR_NULL
     assert s(aq=MIS) == MOE_ERR_INVALID
+    assert s(K=1 << 16, I=1 << 15, lx=2048, lw=2048, la=1024) == MOE_ERR_INVALID  # 2I * K = 2^32
     # moe_permute_mx(x, ids, T, k, H, E, xq, xs, ld_xs, rmap, ss, tpe, ws, ws_bytes, dev_err, stream)
     need = lib.moe_permute_workspace_size(64, 8, 256)
     ws = ctypes.c_void_p(0x50000)

@@ -253,18 +253,32 @@ def test_ep_full_size_sampled(dev):
     da = moe.gmm_bwd_input(dyp, w2, g, dev_err=err)   # [R, 1536]
     dx = moe.gmm_bwd_input(dh, w1, g, dev_err=err)    # [R, 4096]
     dw1 = moe.gmm_bwd_weight(x, dh, g, dev_err=err)   # [32, 4096, 3072]
+    # the fused launches at full size: gmm_bwd (input- and weight-gradient
+    # tiles from one queue) and the gate_up GMM fused with SwiGLU keeping H
+    # give the bits of the separate calls over every element
+    ws = torch.zeros(moe.gmm_workspace_size(E, R, H, 2 * I, moe.OP_BWD), dtype=torch.uint8, device=dev)
+    dx2, dw1b = moe.gmm_bwd(x, dh, w1, g, ws=ws, dev_err=err)
+    a_f, h_f = torch.empty((R, I), dtype=torch.bfloat16, device=dev), torch.empty_like(y)
+    moe.gmm_fwd_swiglu(x, w1, g, out=a_f, h_out=h_f, dev_err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "gmm_bwd dx != gmm_bwd_input"
+    assert torch.equal(dw1b.view(torch.int16), dw1.view(torch.int16)), "gmm_bwd dw != gmm_bwd_weight"
+    assert torch.equal(h_f.view(torch.int16), y.view(torch.int16)), "gmm_fwd_swiglu h != gmm_fwd"
+    assert int(ws.count_nonzero().item()) == 0, "gmm_bwd left its queue non-zero"
     rows = _sample_rows(gl, rng)
     eo = _expert_of(gl)
     xs, w1f, w2f = f64(x_b[rows]), wl["w1"], wl["w2"]
     y_s = dev_f64(y[torch.from_numpy(rows).to(dev)])
+    a_s = dev_f64(a_f[torch.from_numpy(rows).to(dev)])  # fused: from the unrounded accumulators
     da_s = dev_f64(da[torch.from_numpy(rows).to(dev)])
     dx_s = dev_f64(dx[torch.from_numpy(rows).to(dev)])
     dys, dhs = f64(dy_b[rows]), f64(dh_b[rows])
     for i, r in enumerate(rows):
         e = eo[r]
         assert_close(y_s[i], xs[i] @ f64(w1f[e]), f"ep fwd row {r}")
+        assert_close(a_s[i], oracle.gmm_swiglu(xs[i:i + 1], f64(w1f[e:e + 1]), [1])[0],
+                     f"ep fwd+swiglu row {r}")
         assert_close(da_s[i], dys[i] @ f64(w2f[e]).T, f"ep dX(W2) row {r}")
         assert_close(dx_s[i], dhs[i] @ f64(w1f[e]).T, f"ep dX(W1) row {r}")
     # weight gradient: sampled weight rows k of sampled experts, all columns
@@ -358,3 +372,47 @@ def test_bwd_swiglu(dev, M, K, N, gl, in_place):
     _bwd_swiglu_case(dev, workloads.normal_bf16(rng, (M, K)), workloads.normal_bf16(rng, (M, N)),
                      workloads.normal_bf16(rng, (E, K, N), std=0.05),
                      workloads.normal_bf16(rng, (M, 2 * K), std=1.5), gl, in_place, "sweep")
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_forced_variants_agree_on_decode(dev, swiglu):
+    """MOEGMM_FORCE_VARIANT (test-only) runs the row-tile and the
+    weight-streaming forward on one decode-shaped input (512 rows over 256
+    experts, hidden 2048, gate_up 1024 columns): both against the oracle,
+    rows >= R untouched."""
+    import os
+
+    wl = workloads.decode(with_weights=False)
+    gl = np.bincount(wl["topk_ids"].ravel(), minlength=256).astype(np.int64)
+    rng = np.random.default_rng(91)
+    M, K, I = 512 + 8, 2048, 512
+    x_b = workloads.normal_bf16(rng, (M, K))
+    w_b = workloads.normal_bf16(rng, (256, K, 2 * I), std=0.02)
+    R = int(gl.sum())
+    x, w, g = bf16_dev(x_b, dev), bf16_dev(w_b, dev), _gl(dev, gl)
+    ref_h = oracle.gmm(f64(x_b), f64(w_b), gl)[:R]
+    outs = {}
+    try:
+        for variant in ("tile", "stream"):
+            os.environ["MOEGMM_FORCE_VARIANT"] = variant
+            print(f"forced {variant}: swiglu={swiglu} R={R}", flush=True)
+            err = torch.zeros(1, dtype=torch.int32, device=dev)
+            if swiglu:
+                a, h = _sentinel(dev, (M, I)), _sentinel(dev, (M, 2 * I))
+                moe.gmm_fwd_swiglu(x, w, g, out=a, h_out=h, dev_err=err)
+                outs[variant] = (dev_bits(a), dev_bits(h))
+            else:
+                y = moe.gmm_fwd(x, w, g, out=_sentinel(dev, (M, 2 * I)), dev_err=err)
+                outs[variant] = (dev_bits(y),)
+            torch.cuda.synchronize()
+            assert int(err.item()) == 0
+    finally:
+        os.environ.pop("MOEGMM_FORCE_VARIANT", None)
+    for variant, res in outs.items():
+        assert all((r[R:] == SENT).all() for r in res), f"{variant}: rows >= R written"
+        if swiglu:
+            a, h = res
+            assert_close(f64(h)[:R], ref_h, f"forced {variant} h")
+            assert_close(f64(a)[:R], oracle.gmm_swiglu(f64(x_b), f64(w_b), gl)[:R], f"forced {variant} a")
+        else:
+            assert_close(f64(res[0])[:R], ref_h, f"forced {variant} y")

@@ -162,3 +162,78 @@ def test_ep_rank_forward_backward_sampled(dev, low_memory):
                      extra=chained_reduction_slack(a[:, ks2], dye))
     for e in np.nonzero(gl == 0)[0]:
         assert (dev_bits(layer.dw1[e]) == 0).all() and (dev_bits(layer.dw2[e]) == 0).all()
+
+
+def test_ep_bench_step_sampled(dev):
+    """The expert-parallel share's training step exactly as bench.py times it
+    (MoeLayer.training_step_calls: fused gate_up + SwiGLU keeping H, down
+    GMM, unpermute, the down pair with the SwiGLU backward, the gate_up pair
+    as one gmm_bwd launch), at full size.  Sampled rows of h, a, yp, out, dh
+    and dx against the oracle; dW1 and dW2 of the largest and the smallest
+    non-empty expert on one weight row in every 256-row k-tile, all columns,
+    so every tile rectangle of the weight-gradient schedule is hit."""
+    wl = workloads.ep_slice()
+    gl = wl["group_list"]
+    d = wl.dims
+    E, H, I, R = d["E"], d["H"], d["I"], d["R"]
+    print(f"ep bench step: E={E} H={H} I={I} R={R}", flush=True)
+    layer = MoeLayer(LayerShape(R, 1, E, H, I), dev, with_backward=True)
+    w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
+    calls = layer.training_step_calls(bf16_dev(wl["x"], dev), torch.from_numpy(wl["topk_ids"]).to(dev),
+                                      torch.from_numpy(wl["probs"]).to(dev), bf16_dev(wl["dyp"], dev),
+                                      w1, w2)
+    assert [n for n, _ in calls] == ["moe_permute", "gmm_fwd_swiglu", "gmm_fwd_down", "moe_unpermute",
+                                     "gmm_bwd_swiglu_down", "gmm_bwd_gate_up"]
+    for _, fn in calls:
+        fn()
+    torch.cuda.synchronize()
+    assert int(layer.dev_err.item()) == 0
+    ss, rmap, cnt = oracle.permute_maps(wl["topk_ids"], E)
+    np.testing.assert_array_equal(layer.tokens_per_expert.cpu().numpy(), gl)
+    np.testing.assert_array_equal(layer.row_id_map.cpu().numpy(), rmap)
+    np.testing.assert_array_equal(layer.sorted_slot.cpu().numpy(), ss)
+    off = oracle.expert_offsets(gl)
+    eo = np.repeat(np.arange(E), gl)
+    rng = np.random.default_rng(78)
+    x_perm_bits = wl["x"][ss]                       # top_k = 1: slot == token
+    rows = np.unique(np.concatenate([off[:-1][gl > 0], off[1:][gl > 0] - 1, rng.integers(0, R, 64)]))
+    idx = torch.from_numpy(rows).to(dev)
+    got = {k: dev_f64(getattr(layer, k)[idx]) for k in ("h", "a", "yp", "dh", "dx")}
+    out_tok = dev_f64(layer.out[torch.from_numpy(ss[rows]).to(dev)])
+    probs = wl["probs"].astype(np.float64)
+    one = np.array([1])
+    for i, r in enumerate(rows):
+        e = eo[r]
+        xr = f64(x_perm_bits[r:r + 1])
+        h_exact = oracle.gmm(xr, f64(wl["w1"][e:e + 1]), one)
+        h = oracle.round_bf16(h_exact)
+        a = oracle.round_bf16(oracle.gmm_swiglu(xr, f64(wl["w1"][e:e + 1]), one))  # from the accumulators
+        yp = oracle.round_bf16(oracle.gmm(a, f64(wl["w2"][e:e + 1]), one))
+        da = oracle.gmm_bwd_input(f64(wl["dyp"][r:r + 1]), f64(wl["w2"][e:e + 1]), one)  # fused: unrounded
+        dh = oracle.round_bf16(oracle.swiglu_bwd(da, h))
+        dx = oracle.gmm_bwd_input(dh, f64(wl["w1"][e:e + 1]), one)
+        for k, ref in (("h", h), ("a", a), ("yp", yp), ("dh", dh), ("dx", dx)):
+            assert_close(got[k][i], ref[0], f"ep step {k} row {r} (expert {e})")
+        assert_close(out_tok[i], probs[ss[r], 0] * yp[0], f"ep step out token {ss[r]}")
+    live = np.nonzero(gl > 0)[0]
+    for e in (int(live[np.argmax(gl[live])]), int(live[np.argmin(gl[live])])):
+        n = int(gl[e])
+        print(f"ep bench step: weight gradients of expert {e} ({n} rows)", flush=True)
+        xe = f64(x_perm_bits[off[e]:off[e + 1]])
+        w1e = f64(wl["w1"][e:e + 1])
+        h = oracle.round_bf16(oracle.gmm(xe, w1e, [n]))
+        a = oracle.round_bf16(oracle.gmm_swiglu(xe, w1e, [n]))
+        dye = f64(wl["dyp"][off[e]:off[e + 1]])
+        da = oracle.gmm_bwd_input(dye, f64(wl["w2"][e:e + 1]), [n])
+        dh = oracle.round_bf16(oracle.swiglu_bwd(da, h))
+        # one weight row in every 256-row k-tile, every column
+        ks1 = np.arange(0, H, 256) + rng.integers(0, 256, H // 256)
+        ks2 = np.arange(0, I, 256) + rng.integers(0, 256, I // 256)
+        ref1 = oracle.gmm_bwd_weight(xe[:, ks1], dh, [n])[0]
+        ref2 = oracle.gmm_bwd_weight(a[:, ks2], dye, [n])[0]
+        assert_close(dev_f64(layer.dw1[e, torch.from_numpy(ks1).to(dev)]), ref1, f"ep step dW1 expert {e}",
+                     extra=chained_reduction_slack(xe[:, ks1], dh))
+        assert_close(dev_f64(layer.dw2[e, torch.from_numpy(ks2).to(dev)]), ref2, f"ep step dW2 expert {e}",
+                     extra=chained_reduction_slack(a[:, ks2], dye))
+    for e in np.nonzero(gl == 0)[0]:
+        assert (dev_bits(layer.dw1[e]) == 0).all() and (dev_bits(layer.dw2[e]) == 0).all()

@@ -237,3 +237,21 @@ def mx_random(rng: np.random.Generator, shape, std: float = 0.02):
     base = 127 + int(np.rint(np.log2(std))) - 6
     scales = (base + rng.integers(-1, 2, size=tuple(shape[:-1]) + (K // 32,))).astype(np.uint8)
     return codes, scales
+
+
+def mx_small_integers(rng: np.random.Generator, shape, scale_exps=(-5, -4)):
+    """MX operands (E4M3 code bytes [..., K], E8M0 scale bytes [..., K/32])
+    whose elements are integers in [-8, 8], packed by PyTorch's CPU
+    float8_e4m3fn cast (exact for these), with one scale 2^u per row, u drawn
+    from scale_exps.  Any product of two such operands is an integer times a
+    power of two, so every sum of them is exact in an accumulator a few bits
+    wide: a product-sum then has one right answer on every implementation."""
+    import torch
+
+    K = shape[-1]
+    assert K % 32 == 0
+    v = rng.integers(-8, 9, size=tuple(shape)).astype(np.float32)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    u = rng.choice(np.asarray(scale_exps), size=tuple(shape[:-1]) + (1,))
+    scales = np.repeat(127 + u, K // 32, axis=-1).astype(np.uint8)
+    return codes, scales

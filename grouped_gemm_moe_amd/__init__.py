@@ -23,7 +23,7 @@ import torch
 from . import _lib as _L
 
 __all__ = [
-    "MoeError", "moe_permute", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
+    "MoeError", "moe_permute", "moe_permute_noalloc", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
     "gmm_bwd_swiglu",
     "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
@@ -130,6 +130,32 @@ def moe_permute(x, topk_ids, num_experts: int, *, out=None, ws=None, dev_err=Non
     _check(library().moe_permute(_ptr(x), _ptr(topk_ids), T, top_k, H, num_experts, _ptr(x_perm),
                                  _ptr(row_id_map), _ptr(sorted_slot), _ptr(tpe), _ptr(ws), ws_bytes,
                                  _ptr(dev_err), _stream(dev)), "moe_permute")
+    return x_perm, row_id_map, sorted_slot, tpe
+
+
+def moe_permute_noalloc(x, topk_ids, num_experts: int, *, out, dev_err=None):
+    """moe_permute whose scratch is the library's static device array: no
+    workspace, and nothing allocated here either -- every output comes in
+    through out = (x_perm, row_id_map, sorted_slot, tokens_per_expert).  See
+    moe_permute_noalloc in include/moegmm.h for the size limit and the rule
+    that calls on one device must not overlap."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, H = x.shape
+    top_k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise MoeError("topk_ids must be [T, top_k]")
+    if out is None or len(out) != 4 or any(o is None for o in out):
+        raise MoeError("moe_permute_noalloc takes every output through out=")
+    S = T * top_k
+    dev = x.device
+    x_perm = _out(out[0], (S, H), torch.bfloat16, dev, "x_perm")
+    row_id_map = _out(out[1], (S,), torch.int32, dev, "row_id_map")
+    sorted_slot = _out(out[2], (S,), torch.int32, dev, "sorted_slot")
+    tpe = _out(out[3], (num_experts,), torch.int64, dev, "tokens_per_expert")
+    _check(library().moe_permute_noalloc(_ptr(x), _ptr(topk_ids), T, top_k, H, num_experts, _ptr(x_perm),
+                                         _ptr(row_id_map), _ptr(sorted_slot), _ptr(tpe), _ptr(dev_err),
+                                         _stream(dev)), "moe_permute_noalloc")
     return x_perm, row_id_map, sorted_slot, tpe
 
 

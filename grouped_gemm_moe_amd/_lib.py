@@ -22,6 +22,7 @@ SIGNATURES = {
     "moegmm_abi_version": (_int, []),
     "moe_permute_workspace_size": (_sz, [_i64, _i64, _i64]),
     "moe_permute": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_permute_noalloc": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "gmm_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
     "gmm_fwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_fwd_swiglu": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
@@ -42,7 +43,7 @@ SIGNATURES = {
                                  _i64, _p, _p]),
 }
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lib = None
 

@@ -90,30 +90,63 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 7; }
+int moegmm_abi_version(void) { return 8; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
     return moegmm::permute_workspace_bytes(T * top_k, E);
 }
 
-moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
-                       int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
-                       int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
-                       size_t ws_bytes, int32_t* dev_err, void* stream) {
-    if (!tokens_per_expert || !ws) return MOE_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// Arguments of moe_permute other than the workspace.
+moe_status check_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                         int64_t H, int64_t E, const uint16_t* x_perm, const int32_t* row_id_map,
+                         const int32_t* sorted_slot, const int64_t* tokens_per_expert) {
+    if (!tokens_per_expert) return MOE_ERR_NULL;
     if (T > 0 && (!x || !topk_ids || !x_perm || !row_id_map || !sorted_slot)) return MOE_ERR_NULL;
     if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || !dim_ok(H))
         return MOE_ERR_INVALID;
     if (T * top_k > kMaxRows) return MOE_ERR_INVALID;
     if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(topk_ids, 4) ||
-        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) || !aligned(tokens_per_expert, 8) ||
-        !aligned(ws, 4))
+        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) || !aligned(tokens_per_expert, 8))
         return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                       int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                       int32_t* sorted_slot, int64_t* tokens_per_expert, void* ws,
+                       size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!ws) return MOE_ERR_NULL;
+    moe_status st = check_permute(x, topk_ids, T, top_k, H, E, x_perm, row_id_map, sorted_slot,
+                                  tokens_per_expert);
+    if (st != MOE_OK) return st;
+    if (!aligned(ws, 4)) return MOE_ERR_INVALID;
     if (ws_bytes < moegmm::permute_workspace_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
     return from_hip(moegmm::launch_permute(x, topk_ids, T, top_k, H, E, x_perm, nullptr, nullptr,
                                            0, row_id_map, sorted_slot, tokens_per_expert, ws,
                                            dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                               int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                               int32_t* sorted_slot, int64_t* tokens_per_expert, int32_t* dev_err,
+                               void* stream) {
+    moe_status st = check_permute(x, topk_ids, T, top_k, H, E, x_perm, row_id_map, sorted_slot,
+                                  tokens_per_expert);
+    if (st != MOE_OK) return st;
+    if (moegmm::permute_workspace_bytes(T * top_k, E) > moegmm::permute_static_scratch_bytes())
+        return MOE_ERR_WORKSPACE;
+    return from_hip(moegmm::launch_permute_noalloc(x, topk_ids, T, top_k, H, E, x_perm, row_id_map,
+                                                   sorted_slot, tokens_per_expert, dev_err,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op) {

@@ -18,6 +18,14 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                           int64_t* tokens_per_expert, void* ws, int32_t* dev_err,
                           hipStream_t stream);
 
+// moe_permute with its histograms in a static device array (no workspace);
+// the caller checks permute_workspace_bytes(S, E) <= permute_static_scratch_bytes().
+size_t permute_static_scratch_bytes();
+hipError_t launch_permute_noalloc(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                                  int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                                  int32_t* sorted_slot, int64_t* tokens_per_expert, int32_t* dev_err,
+                                  hipStream_t stream);
+
 // gmm.hip
 // Compute units of the current device (cached per device; 256 if the query fails).
 int num_cus();

@@ -26,11 +26,21 @@
 //                 scales).
 // For at most 4096 slots (decode-sized calls) steps 1-3 run as one
 // single-workgroup kernel, so the whole permute is two launches.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "mx.h"
 
 namespace moegmm {
+
+// The per-block histograms of moe_permute_noalloc live here instead of in a
+// caller workspace: 1 MiB, held by each device the library runs on until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol); it uses the device address that
+// static_scratch() looks up once per device.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -374,6 +384,38 @@ int gather_tokens_per_block(int64_t T, int64_t top_k) {
 
 }  // namespace
 
+size_t permute_static_scratch_bytes() { return kStaticScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (hipGetSymbolAddress; each device holds its own copy of the
+// array at its own address) and kept.  nullptr, with the error, on failure.
+static void* static_scratch(hipError_t* err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 size_t permute_workspace_bytes(int64_t S, int64_t E) {
     const int64_t chunk = permute_chunk(S);
     const int64_t nblk = (S + chunk - 1) / chunk;
@@ -415,6 +457,19 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                                stream, x, row_id_map, T, (int)top_k, H, tpb, x_perm);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_permute_noalloc(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                                  int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                                  int32_t* sorted_slot, int64_t* tokens_per_expert, int32_t* dev_err,
+                                  hipStream_t stream) {
+    hipError_t err = hipSuccess;
+    void* ws = static_scratch(&err);
+    if (ws == nullptr) return err;
+    // the histograms are written whole by every call before they are read:
+    // nothing in the scratch needs clearing
+    return launch_permute(x, ids, T, top_k, H, E, x_perm, nullptr, nullptr, 0, row_id_map, sorted_slot,
+                          tokens_per_expert, ws, dev_err, stream);
 }
 
 }  // namespace moegmm

@@ -118,6 +118,29 @@ moe_status moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, in
                        size_t ws_bytes, int32_t* dev_err, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute with no workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * outputs, ordering and errors as moe_permute; its scratch (the per-block
+ * expert histograms) is a static 1 MiB device array of the library, which
+ * each device it runs on holds until the process ends.
+ *
+ * Limit: moe_permute_workspace_size(T, top_k, E) <= 1 MiB (1048576 bytes),
+ * e.g. E = 1024 experts with up to 262144 slots, E = 128 with up to 2M;
+ * larger calls return MOE_ERR_WORKSPACE before anything is enqueued.
+ * Allocates nothing: no hipMalloc/hipFree; the first call on a device looks
+ * up the array's device address (hipGetSymbolAddress) and keeps it.
+ * Every call on one device shares that array and leaves its contents behind
+ * (each call writes the histograms whole before reading them): calls that
+ * may overlap in time on one device -- different streams, or different host
+ * threads -- race on it and must not be issued.
+ * ---------------------------------------------------------------------- */
+moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64_t T, int64_t top_k,
+                               int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
+                               int32_t* sorted_slot, int64_t* tokens_per_expert, int32_t* dev_err,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * gmm_fwd -- grouped matmul  y[off_e + i, :] = x[off_e + i, :] @ w[e]  for
  * every expert e and 0 <= i < n_e.   [GMM] 算子语义: the per-expert loop and
  * its input table; [MegaMoE] Expert Compute: H_e = X_e W1[e], Y_e = A_e W2[e].

@@ -439,6 +439,15 @@ def run_decode(torch, dev, args):
     gbs = nbytes / (ms * 1e-3) / 1e9
     gate_up = "gmm_fwd_swiglu" if fused else "gmm_fwd_gate_up"
     wbytes = {k: n_active * (H * 2 * I if k == gate_up else I * H) * 2 for k in (gate_up, "gmm_fwd_down")}
+    # the same layer with one hot expert (about 50 rows; the others 0-6)
+    sk = workloads.decode_skewed()
+    ms_s, per_s, gl_s, (_, _, fused_s, _) = layer_forward(torch, dev, sk, args.decode_steps)
+    roof_s = layer_roofline(gl_s, T, K, H, I, ms_s, fused_s)
+    skewed = dict(workload="decode layer forward, expert 7 routed 48 more tokens (max rows per expert "
+                           f"{int(np.max(gl_s))})",
+                  ms_per_layer=round(ms_s, 4),
+                  gb_per_s=round(roof_s["bytes_per_layer"] / (ms_s * 1e-3) / 1e9, 1),
+                  per_call_us={k: round(v * 1e3, 2) for k, v in per_s.items()})
     return dict(
         metric="decode MoE layer HBM GB/s",
         workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
@@ -448,6 +457,7 @@ def run_decode(torch, dev, args):
         active_experts=n_active, frac_of_attainable=roof["frac_of_attainable"],
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
         gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
+        skewed=skewed,
     )
 
 
@@ -732,6 +742,7 @@ def main():
     if not args.skip_decode:
         decode = run_decode(torch, dev, args)
         log(f"decode: {decode['ms_per_layer']:.4f} ms, {decode['value']:.0f} GB/s; {decode['per_call_us']}")
+        log(f"decode, one hot expert: {decode['skewed']}")
         prefill = run_prefill(torch, dev, args)
         log(f"prefill: {prefill['ms_per_layer']:.4f} ms, {prefill['value']:.1f} % of attainable "
             f"({prefill['bound']}-bound); {prefill['per_call_us']}")

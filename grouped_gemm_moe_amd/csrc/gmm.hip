@@ -193,22 +193,25 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_order[kMaxExperts];
-    __shared__ int s_next;
+    __shared__ uint32_t s_next;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const DwSched ds = dw_schedule(s_cnt, E, K, N, s_order);
     const int total = E * ds.per_e;
     const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
-    const int mine = (total - xcd + 7) / 8;  // tiles 8j + xcd, j < mine
+    const uint32_t mine = (uint32_t)((total - xcd + 7) / 8);  // tiles 8j + xcd, j < mine
     uint32_t* ctr = queue + xcd * kQueueStride;
-    int j = blockIdx.x >> 3;  // first tile static, later ones from the counter
+    // Queue positions are unsigned and bounded by `mine` before use: a
+    // workspace that was not zero-filled gives skipped or repeated tiles,
+    // never an index outside the tile grid.
+    uint32_t j = blockIdx.x >> 3;  // first tile static, later ones from the counter
     while (j < mine) {
-        int nj = 0;
-        if (threadIdx.x == 0) nj = wg_per_xcd + (int)atomicAdd(ctr, 1u);
-        dw_tile(8 * j + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
+        uint32_t nj = 0;
+        if (threadIdx.x == 0) nj = (uint32_t)wg_per_xcd + atomicAdd(ctr, 1u);
+        dw_tile(8 * (int)j + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
         if (threadIdx.x == 0) s_next = nj;
         __syncthreads();  // the ring and the output image are free again
-        j = __builtin_amdgcn_readfirstlane(s_next);
+        j = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_next);
     }
     if (threadIdx.x == 0) queue_release(queue);
 }
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_order[kMaxExperts], s_tst[kMaxExperts];
-    __shared__ int s_next;
+    __shared__ uint32_t s_next;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const DwSched ds = dw_schedule(s_cnt, E, K, N, s_order);
@@ -247,14 +250,15 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
     const XcdRange xr = xcd_range(xcd, nx);
     const int x0 = xr.first, nxx = xr.count;
     const int mine_w = (E * ds.per_e - xcd + 7) / 8;
-    const int items = nxx + mine_w;
+    const uint32_t items = (uint32_t)(nxx + mine_w);
     uint32_t* ctr = queue + xcd * kQueueStride;
-    int j = blockIdx.x >> 3;
+    // unsigned queue positions, bounded before use (see gmm_dw_kernel)
+    uint32_t j = blockIdx.x >> 3;
     while (j < items) {
-        int nj = 0;
-        if (threadIdx.x == 0) nj = wg_per_xcd + (int)atomicAdd(ctr, 1u);
-        if (j < nxx) {
-            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NTx, x0 + j);
+        uint32_t nj = 0;
+        if (threadIdx.x == 0) nj = (uint32_t)wg_per_xcd + atomicAdd(ctr, 1u);
+        if (j < (uint32_t)nxx) {
+            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NTx, x0 + (int)j);
             const int row0 = rt.row0, rows_valid = rt.rows_valid;
             const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kBN);
             const int cols_left = K - n0;
@@ -270,11 +274,11 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
                     }
                 });
         } else {
-            dw_tile(8 * (j - nxx) + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
+            dw_tile(8 * ((int)j - nxx) + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
         }
         if (threadIdx.x == 0) s_next = nj;
         __syncthreads();  // the ring and the output image are free again
-        j = __builtin_amdgcn_readfirstlane(s_next);
+        j = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_next);
     }
     if (threadIdx.x == 0) queue_release(queue);
 }

@@ -416,3 +416,4 @@ def test_forced_variants_agree_on_decode(dev, swiglu):
             assert_close(f64(a)[:R], oracle.gmm_swiglu(f64(x_b), f64(w_b), gl)[:R], f"forced {variant} a")
         else:
             assert_close(f64(res[0])[:R], ref_h, f"forced {variant} y")
+

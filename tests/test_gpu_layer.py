@@ -89,7 +89,7 @@ def test_tiny_forward_backward(dev, fuse_swiglu_bwd):
     assert (dev_bits(layer.dw1)[2] == 0).all() and (dev_bits(layer.dw2)[2] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["prefill", "decode"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "decode_skewed"])
 def test_layer_forward(dev, name):
     wl = getattr(workloads, name)()
     layer = _run_forward(dev, wl)

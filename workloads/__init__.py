@@ -140,6 +140,20 @@ def decode(**kw) -> Workload:
     return moe_layer("decode", 6, T=64, K=8, E=256, H=2048, I=512, **kw)
 
 
+def decode_skewed(hot: int = 7, extra_tokens: int = 48) -> Workload:
+    """The decode workload with one hot expert: tokens 0 .. extra_tokens-1
+    route their last slot to expert `hot` (unless it is already among their
+    experts), so it holds about 50 rows while the others hold 0-6."""
+    wl = decode()
+    ids = wl["topk_ids"].copy()
+    for t in range(extra_tokens):
+        if hot not in ids[t]:
+            ids[t, -1] = hot
+    arrays = dict(wl.arrays)
+    arrays["topk_ids"] = ids
+    return Workload("decode_skewed", dict(wl.dims), arrays)
+
+
 # ---------------------------------------------------------------------------
 # one expert-parallel rank's share: E=32 local experts, 16384 received rows
 # ---------------------------------------------------------------------------

@@ -611,40 +611,60 @@ def run_mx(torch, dev, args):
 # Achievable ceilings on this GPU, for context (outside every timed step)
 # ---------------------------------------------------------------------------
 
+def best_ms(torch, fn, iters=10):
+    """Best of 3 event-timed runs of `iters` back-to-back calls, ms per call."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    best = 1e9
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / iters)
+    return best
+
+
 def ceilings(torch, dev):
     """hipBLASLt (torch.matmul) on a dense bf16 product of the ep gate_up
     shape, and a 512 MiB device-to-device copy: what a vendor GEMM and a
     plain copy reach here, next to the published peaks."""
-    def best_ms(fn, iters=10):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        best = 1e9
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(iters):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) / iters)
-        return best
-
     M, K, N = 16384, 4096, 3072
     a = torch.randn((M, K), device=dev).to(torch.bfloat16)
     b = torch.randn((K, N), device=dev).to(torch.bfloat16)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    mm = best_ms(lambda: torch.matmul(a, b, out=c))
+    mm = best_ms(torch, lambda: torch.matmul(a, b, out=c))
     del a, b, c
     src = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
-    cp = best_ms(lambda: dst.copy_(src))
+    cp = best_ms(torch, lambda: dst.copy_(src))
     del src, dst
     torch.cuda.empty_cache()
     return dict(hipblaslt_bf16_tflops=round(2.0 * M * K * N / (mm * 1e-3) / 1e12, 1),
                 hipblaslt_shape=[M, K, N],
                 d2d_copy_gbs=round(2 * 512 * 2 ** 20 / (cp * 1e-3) / 1e9, 1),
                 note="copy GB/s counts bytes read + written")
+
+
+def run_dw_few_tiles(torch, dev):
+    """A weight gradient whose tile grid cannot fill the chip: one dense
+    expert, dW [2048, 1024] from 32768 rows (32 output tiles), which
+    gmm_bwd_weight splits along the rows."""
+    import grouped_gemm_moe_amd as moe
+
+    M, K, N = 32768, 2048, 1024
+    x = torch.randn((M, K), device=dev).to(torch.bfloat16)
+    dy = torch.randn((M, N), device=dev).to(torch.bfloat16)
+    g = torch.tensor([M], dtype=torch.int64, device=dev)
+    ws = torch.zeros(moe.gmm_workspace_size(1, M, K, N, moe.OP_BWD_WEIGHT), dtype=torch.uint8, device=dev)
+    dw = torch.empty((1, K, N), dtype=torch.bfloat16, device=dev)
+    ms = best_ms(torch, lambda: moe.gmm_bwd_weight(x, dy, g, out=dw, ws=ws))
+    return dict(shape=[M, K, N], us=round(ms * 1e3, 2),
+                tflops=round(2.0 * M * K * N / (ms * 1e-3) / 1e12, 1),
+                note="dW = x^T dy for one expert; 32 output tiles, the row reduction split in chunks")
 
 
 # ---------------------------------------------------------------------------
@@ -750,9 +770,12 @@ def main():
     if not args.skip_mx:
         mx = run_mx(torch, dev, args)
     ceil = None
+    dw_few = None
     if not args.skip_mx and not args.skip_decode:
         ceil = ceilings(torch, dev)
         log(f"ceilings: {ceil}")
+        dw_few = run_dw_few_tiles(torch, dev)
+        log(f"dW on few tiles (row reduction split): {dw_few}")
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(wl, args.cpu_budget)
@@ -790,6 +813,7 @@ def main():
         "prefill": prefill,
         "mxfp8": mx,
         "ceilings": ceil,
+        "dw_few_tiles": dw_few,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

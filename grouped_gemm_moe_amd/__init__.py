@@ -36,6 +36,7 @@ DEVERR_EXPERT_ID = 1
 DEVERR_GROUP_LIST = 2
 DEVERR_ROW_MAP = 4
 OP_FWD, OP_BWD_INPUT, OP_BWD_WEIGHT, OP_BWD = 0, 1, 2, 3
+GMM_QUEUE_BYTES = 1152  # the zero-filled prefix of a GMM workspace
 
 
 class MoeError(RuntimeError):
@@ -84,8 +85,9 @@ _ZEROED_WS = {}
 
 def _workspace(nbytes: int, device, ws, zeroed: bool = False):
     """The caller's workspace, else a new one.  A `zeroed` workspace (GMM tile
-    queues) must be zero-filled before its first use and is left zero-filled
-    by every call, so one per (device, stream) is kept and reused."""
+    queue at its start, then scratch) must start zero-filled and is left so
+    where the queue lies by every call, so one per (device, stream) is kept
+    and reused."""
     if nbytes == 0:
         return None, 0
     if ws is not None:

@@ -12,6 +12,7 @@
 // LDS ring, fragments, epilogues).
 #include "gmm_engine.h"
 #include "launch.h"
+#include "moegmm.h"
 
 namespace moegmm {
 
@@ -43,6 +44,7 @@ enum RowsMode { kFwd = 0, kDx = 1, kSwiGLU = 2 };
 // zero-filled again when the kernel ends.
 constexpr int kQueueStride = 32;  // uint32 per slot
 constexpr int kQueueWords = 9 * kQueueStride;
+static_assert(kQueueWords * sizeof(uint32_t) == MOE_GMM_QUEUE_BYTES, "queue size in the header");
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
@@ -217,6 +219,133 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_dw_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradient with the row reduction split, for calls whose tile grid
+// (E * KT * NT tiles) cannot fill the CUs -- one large dense expert, or a
+// few experts with small K and N.  Two launches:
+//   1. work item (tile t, chunk c) reduces chunk c of the expert's rows and
+//      stores its fp32 partial in the caller's workspace (a tile whose
+//      expert has one chunk writes its output directly);
+//   2. eight workgroups per split tile add the tile's partials in chunk
+//      order and write it as bf16 -- so the result does not depend on
+//      where or when the chunks ran.
+// Chunks have at least kMinChunkRows rows: an expert with few rows gets
+// fewer chunks.  Partials keep the accumulator layout (4 consecutive columns
+// of accumulator (i, j), group g, of wave w, lane l, as the float4 at
+// ((w * TM*TN + i * TN + j) * 4 + g) * 64 + l), so every load and store of
+// them moves 1 KiB per wave instruction.
+// ---------------------------------------------------------------------------
+constexpr int kTileFloats = kBM * kBN;
+constexpr int kMinChunkRows = 256;  // shorter chunks would be mostly prologue and epilogue
+constexpr int kReducePieces = 8;    // workgroups per tile in the reduction
+constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN, kTM = kWTM / 32, kTN = kWTN / 32;
+
+// Chunk rows and chunk count of an expert with cnt rows, split at most S ways.
+struct DwChunks {
+    int rows, count;
+};
+MOE_DEVICE DwChunks dw_chunks(int cnt, int S) {
+    int cr = (cnt + S - 1) / S;
+    cr = (cr + BK - 1) / BK * BK;
+    if (cr < kMinChunkRows) cr = kMinChunkRows;
+    return DwChunks{cr, (cnt + cr - 1) / cr};
+}
+
+__global__ __launch_bounds__(kThreads, 1) void gmm_dw_split_kernel(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ DY, const int64_t* __restrict__ group_list,
+    int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int S, float* __restrict__ part,
+    int32_t* dev_err) {
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
+    __shared__ int64_t s_scan[kThreads / 64];
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts];
+
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
+    const int t = blockIdx.x / S, c = blockIdx.x % S;
+    const int e = t / (KT * NT), rem = t % (KT * NT);
+    const int k0 = (rem / NT) * kBM, n0 = (rem % NT) * kBN;
+    const int off = s_off[e], cnt = s_cnt[e];
+    const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
+    const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
+    bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
+    if (cnt == 0) {  // exact zeros, written by chunk 0
+        if (c != 0) return;
+        constexpr int CPR = kBN / 8;
+        for (int u = threadIdx.x; u < kBM * CPR; u += kThreads) {
+            const int row = u / CPR, cc = u % CPR;
+            if (row < rows_valid && cc * 8 < cols_valid)
+                st16(out + (int64_t)row * N + cc * 8, u32x4_t{0u, 0u, 0u, 0u});
+        }
+        return;
+    }
+    const DwChunks ch = dw_chunks(cnt, S);
+    if (c >= ch.count) return;  // uniform
+    const int r0 = c * ch.rows, rl = cnt - r0 < ch.rows ? cnt - r0 : ch.rows;
+    float* slot = part + ((int64_t)t * S + c) * kTileFloats;
+    gemm_tile<kBM, kBN, kWM, kWN, false, false>(
+        X + (int64_t)(off + r0) * K + k0, K, rows_valid, DY + (int64_t)(off + r0) * N + n0, N, cols_valid, 0, rl,
+        rows_valid, cols_valid, smem, [&](const auto& eng) {
+            if (ch.count == 1) {
+                eng.store(out, N, rows_valid, cols_valid, smem);
+                return;
+            }
+            static_assert(std::remove_reference_t<decltype(eng)>::TM == kTM &&
+                              std::remove_reference_t<decltype(eng)>::TN == kTN, "tile shape");
+            const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+            f32x4_t* p = reinterpret_cast<f32x4_t*>(slot) + wid * (kTM * kTN * 4 * 64) + lane;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        p[((i * kTN + j) * 4 + g) * 64] = f32x4_t{eng.acc[i][j][4 * g], eng.acc[i][j][4 * g + 1],
+                                                                  eng.acc[i][j][4 * g + 2], eng.acc[i][j][4 * g + 3]};
+        });
+}
+
+// Reduction of the split tiles: workgroup (tile t, piece p) takes float4s
+// [p, p + 1) * 2048 of each of the tile's partials, adds them in chunk
+// order and writes its 4 bf16 columns per float4.
+constexpr int kReduceThreads = 256;
+__global__ __launch_bounds__(kReduceThreads) void gmm_dw_reduce_kernel(
+    const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ DW, int S,
+    const float* __restrict__ part) {
+    __shared__ int64_t s_scan[kReduceThreads / 64];
+    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts];
+    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, nullptr);
+    const int KT = (K + kBM - 1) / kBM, NT = (N + kBN - 1) / kBN;
+    const int t = blockIdx.x / kReducePieces, piece = blockIdx.x % kReducePieces;
+    const int e = t / (KT * NT), rem = t % (KT * NT);
+    const int cnt = s_cnt[e];
+    if (cnt == 0) return;
+    const DwChunks ch = dw_chunks(cnt, S);
+    if (ch.count == 1) return;  // written by its only chunk
+    const int k0 = (rem / NT) * kBM, n0 = (rem % NT) * kBN;
+    const int rows_valid = K - k0 < kBM ? K - k0 : kBM;
+    const int cols_valid = N - n0 < kBN ? N - n0 : kBN;
+    bf16_t* out = DW + ((int64_t)e * K + k0) * N + n0;
+    constexpr int kF4 = kTileFloats / 4, kPer = kF4 / kReducePieces / kReduceThreads;
+    const f32x4_t* base = reinterpret_cast<const f32x4_t*>(part + (int64_t)t * S * kTileFloats);
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+        const int u = piece * (kF4 / kReducePieces) + it * kReduceThreads + threadIdx.x;
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+        for (int cc = 0; cc < ch.count; ++cc) v += base[(int64_t)cc * kF4 + u];
+        // float4 u of the accumulator layout -> (row, 4 columns) of the tile
+        const int lane = u & 63, g = (u >> 6) & 3, ij = (u >> 8) % (kTM * kTN), w = (u >> 8) / (kTM * kTN);
+        const int i = ij / kTN, j = ij % kTN;
+        const int row = (w / kWN) * kWTM + i * 32 + (lane & 31);
+        const int col = (w % kWN) * kWTN + j * 32 + 8 * g + 4 * (lane >> 5);
+        if (row < rows_valid && col < cols_valid) {
+            u32x2_t pk;
+            pk[0] = pack_bf16x2(v[0], v[1]);
+            pk[1] = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<u32x2_t*>(out + (int64_t)row * N + col) = pk;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Both gradients of one grouped matmul in one launch: dx = dy @ w[e]^T (row
 // tiles, as gmm_rows_kernel<kDx>) and dw[e] = x^T @ dy (as gmm_dw_kernel).
 // Each XCD's queue hands out its share of the input-gradient tiles first (a
@@ -298,8 +427,33 @@ int num_cus() {
     return cache[dev];
 }
 
-size_t gmm_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int op) {
-    return op == MOE_GMM_OP_BWD_WEIGHT || op == MOE_GMM_OP_BWD ? kQueueWords * sizeof(uint32_t) : 0;
+// Chunks per tile of the split weight gradient: 1 (no split) when the tile
+// grid has at least half a workgroup per CU, else enough chunks to give
+// every CU about one work item -- at most 32, and no more than chunks of
+// kMinChunkRows rows that M_cap rows could fill.
+static int dw_split_chunks(int64_t E, int64_t M_cap, int64_t K, int64_t N) {
+    const int64_t tiles = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t cus = num_cus();
+    if (tiles * 2 > cus) return 1;
+    int64_t S = cus / tiles;
+    if (S > 32) S = 32;
+    const int64_t fill = (M_cap + kMinChunkRows - 1) / kMinChunkRows;
+    if (S > fill) S = fill;
+    return S < 2 ? 1 : (int)S;
+}
+
+// Workspace of the weight-gradient calls: the tile queue (kQueueWords; it
+// must start zero-filled and is left so), then, for gmm_bwd_weight on a
+// grid it splits, the fp32 partials (chunks x tiles x kBM x kBN) from byte
+// kPartOffset on, scratch whose contents do not matter between calls.
+constexpr size_t kPartOffset = 2048;
+size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op) {
+    if (op == MOE_GMM_OP_BWD) return kQueueWords * sizeof(uint32_t);
+    if (op != MOE_GMM_OP_BWD_WEIGHT) return 0;
+    const int S = dw_split_chunks(E, M_cap, K, N);
+    if (S == 1) return kQueueWords * sizeof(uint32_t);
+    const int64_t tiles = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    return kPartOffset + (size_t)tiles * S * kTileFloats * sizeof(float);
 }
 
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
@@ -328,6 +482,15 @@ hipError_t launch_gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const in
                                  int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw,
                                  void* ws, int32_t* dev_err, hipStream_t stream) {
     const int64_t tiles = E * ((K + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int S = dw_split_chunks(E, M_cap, K, N);
+    if (S > 1) {
+        float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + kPartOffset);
+        hipLaunchKernelGGL(gmm_dw_split_kernel, dim3((unsigned)(tiles * S)), dim3(kThreads), 0, stream, x, dy,
+                           group_list, (int)E, M_cap, (int)K, (int)N, dw, S, part, dev_err);
+        hipLaunchKernelGGL(gmm_dw_reduce_kernel, dim3((unsigned)(tiles * kReducePieces)), dim3(kReduceThreads), 0,
+                           stream, group_list, (int)E, M_cap, (int)K, (int)N, dw, S, part);
+        return hipGetLastError();
+    }
     const int64_t need = (tiles + 7) / 8 * 8;
     int64_t grid = num_cus() / 8 * 8;
     if (grid > need) grid = need;

@@ -155,19 +155,25 @@ moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64
  * every call, forces one of them (streaming where its staging fits,
  * K <= 4096) for gmm_fwd, gmm_fwd_swiglu and the MX forward calls.
  * ---------------------------------------------------------------------- */
-/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd_weight and gmm_bwd
- * need 1152 bytes (their tile queue: counters the kernel increments with
- * atomics); the other ops need none (0) and take NULL.  A workspace that is needed must be
- * 16-byte aligned (else MOE_ERR_INVALID) and zero-filled before its first
- * use; every call leaves it zero-filled again, so one workspace serves any
- * number of calls issued one after another.  Calls that may run at the same
- * time (on different streams) need distinct workspaces.  Too small or NULL:
- * MOE_ERR_WORKSPACE. */
+/* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd needs
+ * MOE_GMM_QUEUE_BYTES (1152): its tile queue, counters the kernel increments with atomics.  gmm_bwd_weight
+ * needs the same 1152, or, on a tile grid too small to fill the GPU (E * KT *
+ * NT tiles of 256 x 256 at most half the CUs) where it splits each expert's
+ * row reduction into S chunks, 2048 + tiles * S * 256 KiB: the queue, then
+ * the chunks' fp32 partial tiles from byte 2048 on (up to 64 MiB).  The other
+ * ops need none (0) and take NULL.  A workspace that is needed must be 16-byte
+ * aligned (else MOE_ERR_INVALID), and its first 1152 bytes (the queue)
+ * zero-filled before
+ * its first use; every call leaves them zero-filled again (the partial tiles
+ * are scratch), so one workspace serves any number of calls issued one after
+ * another.  Calls that may run at the same time (on different streams) need
+ * distinct workspaces.  Too small or NULL: MOE_ERR_WORKSPACE. */
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
 #define MOE_GMM_OP_FWD 0
 #define MOE_GMM_OP_BWD_INPUT 1
 #define MOE_GMM_OP_BWD_WEIGHT 2
 #define MOE_GMM_OP_BWD 3 /* gmm_bwd: both gradients in one launch */
+#define MOE_GMM_QUEUE_BYTES 1152 /* the zero-filled prefix of a GMM workspace */
 moe_status gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list, int64_t E,
                    int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
                    int32_t* dev_err, void* stream);
@@ -211,10 +217,15 @@ moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* g
  *
  *   x [M_cap, K] bf16, dy [M_cap, N] bf16, group_list [E] int64,
  *   dw [E, K, N] bf16 OUT -- every expert written; exact zeros for n_e == 0.
- * The reduction order of every output is fixed, so the result is
- * bit-reproducible whatever order the tiles run in.
+ * The reduction order of every output is fixed by the shape, so the result
+ * is bit-reproducible whatever order the tiles run in.  Where the tile grid
+ * cannot fill the GPU the rows of each expert are reduced in S chunks (S from
+ * the shape and the device's CU count, chunks of at least 256 rows) whose
+ * fp32 partials are then
+ * added in chunk order; elsewhere each output is one fp32 sum over the rows.
  * Workspace: gmm_workspace_size(E, M_cap, K, N, MOE_GMM_OP_BWD_WEIGHT) bytes,
- * zero-filled before the first call (left zero-filled by every call).
+ * its first 1152 bytes zero-filled before the first call (left so by every
+ * call).
  * ---------------------------------------------------------------------- */
 moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dw, void* ws,
@@ -225,8 +236,9 @@ moe_status gmm_bwd_weight(const uint16_t* x, const uint16_t* dy, const int64_t* 
  * launch:  dx[off_e + i, :] = dy[off_e + i, :] @ w[e]^T  and
  *          dw[e] = x[rows_e]^T @ dy[rows_e].
  * [GMM] 算子语义, backward (both gradients over the same group boundaries).
- * Every output is bit-identical to what the two separate calls write; one
- * launch lets the short weight-gradient tiles fill the CUs the input
+ * Every output is bit-identical to what the two separate calls write
+ * (gmm_bwd_weight where it does not split the row reduction: this call
+ * never splits it); one launch lets the short weight-gradient tiles fill the CUs the input
  * gradient's last round of tiles leaves idle.
  *
  *   x [M_cap, K] bf16, dy [M_cap, N] bf16, w [E, K, N] bf16, group_list [E],

@@ -68,6 +68,25 @@ def test_workspace_queries(lib):
     for op in range(2):
         assert lib.gmm_workspace_size(32, 16384, 4096, 3072, op) == 0
     assert lib.gmm_workspace_size(32, 16384, 4096, 3072, 2) == 1152
+    assert lib.gmm_workspace_size(32, 16384, 4096, 3072, 3) == 1152
+    # a grid of 32 tiles of 256 x 256 on 256 CUs (the count used where no
+    # device is visible): the rows split 8 ways, a 256 KiB fp32 partial per
+    # (tile, chunk) after the 2048-byte queue area
+    assert lib.gmm_workspace_size(1, 32768, 2048, 1024, 2) == 2048 + 32 * 8 * 256 * 256 * 4
+    # few rows cap the chunks (one per started 256 rows): 600 rows, 3 chunks;
+    # 256 rows, no split
+    assert lib.gmm_workspace_size(1, 600, 2048, 1024, 2) == 2048 + 32 * 3 * 256 * 256 * 4
+    assert lib.gmm_workspace_size(1, 256, 2048, 1024, 2) == 1152
+
+
+def test_queue_bytes_constant():
+    """The zero-filled prefix of a GMM workspace: the header's value, the
+    binding's, and what gmm_bwd asks for agree."""
+    import grouped_gemm_moe_amd as moe
+
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_GMM_QUEUE_BYTES (\d+)", text)
+    assert m and int(m.group(1)) == moe.GMM_QUEUE_BYTES == 1152
 
 
 # fake but aligned non-null device addresses: validation must reject the call

@@ -46,7 +46,13 @@ def run_all(dev, x_bits, w_bits, dy_bits, gl, tag):
                            dev_err=err)
     torch.cuda.synchronize()
     assert np.array_equal(dev_bits(dx2), dev_bits(dx)), f"{tag}: gmm_bwd dx differs from gmm_bwd_input"
-    assert np.array_equal(dev_bits(dw2), dev_bits(dw)), f"{tag}: gmm_bwd dw differs from gmm_bwd_weight"
+    if moe.gmm_workspace_size(E, M, K, N, moe.OP_BWD_WEIGHT) > moe.GMM_QUEUE_BYTES:
+        # few tiles: gmm_bwd_weight splits the row reduction (another fp32
+        # summation order than gmm_bwd's whole-range tiles); both vs the oracle
+        ref = oracle.gmm_bwd_weight(f64(x_bits), f64(dy_bits), gl)
+        assert_close(f64(dev_bits(dw2)), ref, f"{tag} gmm_bwd dW")
+    else:
+        assert np.array_equal(dev_bits(dw2), dev_bits(dw)), f"{tag}: gmm_bwd dw differs from gmm_bwd_weight"
     return dev_bits(y), dev_bits(dx), dev_bits(dw), int(err.item())
 
 
@@ -265,7 +271,7 @@ def test_ep_full_size_sampled(dev):
     assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "gmm_bwd dx != gmm_bwd_input"
     assert torch.equal(dw1b.view(torch.int16), dw1.view(torch.int16)), "gmm_bwd dw != gmm_bwd_weight"
     assert torch.equal(h_f.view(torch.int16), y.view(torch.int16)), "gmm_fwd_swiglu h != gmm_fwd"
-    assert int(ws.count_nonzero().item()) == 0, "gmm_bwd left its queue non-zero"
+    assert int(ws[:moe.GMM_QUEUE_BYTES].count_nonzero().item()) == 0, "gmm_bwd left its queue non-zero"
     rows = _sample_rows(gl, rng)
     eo = _expert_of(gl)
     xs, w1f, w2f = f64(x_b[rows]), wl["w1"], wl["w2"]
@@ -298,9 +304,10 @@ def test_ep_full_size_sampled(dev):
 
 
 def test_dw_tile_queue_workspace(dev):
-    """gmm_bwd_weight's tile queue lives in the caller's workspace: the call
-    leaves it zero-filled, so back-to-back calls of different shapes through
-    one workspace give the same bits as calls with fresh workspaces."""
+    """gmm_bwd_weight's tile queue (and, on split grids, its partial tiles)
+    lives in the caller's workspace: the call leaves the queue zero-filled,
+    so back-to-back calls of different shapes through one workspace give the
+    same bits as calls with fresh workspaces."""
     rng = np.random.default_rng(11)
     ws = torch.zeros(moe.gmm_workspace_size(8, 1000, 520, 264, moe.OP_BWD_WEIGHT), dtype=torch.uint8,
                      device=dev)
@@ -313,7 +320,7 @@ def test_dw_tile_queue_workspace(dev):
         g = _gl(dev, gl)
         shared = moe.gmm_bwd_weight(x, dy, g, ws=ws)
         torch.cuda.synchronize()
-        assert int(ws.count_nonzero().item()) == 0, "workspace not left zero-filled"
+        assert int(ws[:moe.GMM_QUEUE_BYTES].count_nonzero().item()) == 0, "queue not left zero-filled"
         fresh = moe.gmm_bwd_weight(x, dy, g, ws=torch.zeros_like(ws))
         torch.cuda.synchronize()
         assert np.array_equal(dev_bits(shared), dev_bits(fresh))
@@ -339,7 +346,14 @@ def _bwd_swiglu_case(dev, x_b, dy_b, w_b, h_b, gl, in_place, tag):
     assert_close(f64(dev_bits(dh))[:R], ref[:R], f"gmm_bwd_swiglu {tag} dH")
     tail = dev_bits(dh)[R:]
     assert (tail == (h_b[R:] if in_place else SENT)).all(), "rows >= R were written"
-    assert np.array_equal(dev_bits(dw), dw_ref_bits), "dW differs from gmm_bwd_weight"
+    E, N = len(gl), dy_b.shape[1]
+    if moe.gmm_workspace_size(E, M, K, N, moe.OP_BWD_WEIGHT) > moe.GMM_QUEUE_BYTES:
+        # few tiles: gmm_bwd_weight splits the row reduction; both vs the oracle
+        ref_w = oracle.gmm_bwd_weight(f64(x_b), f64(dy_b), gl)
+        assert_close(f64(dev_bits(dw)), ref_w, f"gmm_bwd_swiglu {tag} dW")
+        assert_close(f64(dw_ref_bits), ref_w, f"gmm_bwd_weight {tag} dW")
+    else:
+        assert np.array_equal(dev_bits(dw), dw_ref_bits), "dW differs from gmm_bwd_weight"
 
 
 def test_bwd_swiglu_limits(dev):
@@ -366,7 +380,9 @@ def test_bwd_swiglu_limits(dev):
 ])
 def test_bwd_swiglu(dev, M, K, N, gl, in_place):
     """gmm_bwd_swiglu: dH = swiglu_bwd(dy @ w[e]^T, h) with the product kept
-    in fp32, and dW bit-identical to gmm_bwd_weight; rows >= R untouched."""
+    in fp32, and dW bit-identical to gmm_bwd_weight (or, where that call
+    splits the row reduction of a few-tile grid, both against the oracle);
+    rows >= R untouched."""
     rng = np.random.default_rng(M + K + N)
     E = len(gl)
     _bwd_swiglu_case(dev, workloads.normal_bf16(rng, (M, K)), workloads.normal_bf16(rng, (M, N)),
@@ -417,3 +433,56 @@ def test_forced_variants_agree_on_decode(dev, swiglu):
         else:
             assert_close(f64(res[0])[:R], ref_h, f"forced {variant} y")
 
+
+
+def test_dw_split_few_tiles_dense(dev):
+    """A weight gradient whose tile grid cannot fill the CUs (one expert,
+    K = 2048, N = 1024: 32 tiles) splits each tile's row reduction into
+    chunks whose fp32 partials meet in the workspace.  Against the oracle on
+    one weight row per 256-row k-tile (all columns); bit-identical on a
+    repeat; the workspace's queue left zero-filled."""
+    rng = np.random.default_rng(21)
+    M, K, N = 32768, 2048, 1024
+    x_b = workloads.normal_bf16(rng, (M, K))
+    dy_b = workloads.normal_bf16(rng, (M, N))
+    gl = np.array([M], dtype=np.int64)
+    x, dy, g = bf16_dev(x_b, dev), bf16_dev(dy_b, dev), _gl(dev, gl)
+    nbytes = moe.gmm_workspace_size(1, M, K, N, moe.OP_BWD_WEIGHT)
+    assert nbytes > moe.GMM_QUEUE_BYTES, "this grid takes the split path"
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    print(f"dW split: M={M} K={K} N={N} workspace={nbytes}", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dw1 = moe.gmm_bwd_weight(x, dy, g, ws=ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(ws[:moe.GMM_QUEUE_BYTES].count_nonzero().item()) == 0, "queue not left zero-filled"
+    dw2 = moe.gmm_bwd_weight(x, dy, g, ws=ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(dev_bits(dw1), dev_bits(dw2)), "split dW not bit-reproducible"
+    ks = np.arange(0, K, 256) + rng.integers(0, 256, K // 256)
+    got = dev_f64(dw1[0, torch.from_numpy(ks).to(dev)])
+    assert_close(got, f64(x_b[:, ks]).T @ f64(dy_b), "split dW rows")
+
+
+def test_dw_split_few_tiles_ragged(dev):
+    """Few tiles over several experts: a long expert split into many chunks,
+    an empty one (exact zeros), a short one kept whole; whole-tensor parity
+    with the oracle, and the fused gmm_bwd (no split) within tolerance."""
+    rng = np.random.default_rng(22)
+    M, K, N = 5100, 512, 520
+    gl = np.array([5000, 0, 37], dtype=np.int64)
+    x_b = workloads.normal_bf16(rng, (M, K))
+    dy_b = workloads.normal_bf16(rng, (M, N))
+    w_b = workloads.normal_bf16(rng, (3, K, N), std=0.02)
+    x, dy, w, g = bf16_dev(x_b, dev), bf16_dev(dy_b, dev), bf16_dev(w_b, dev), _gl(dev, gl)
+    assert moe.gmm_workspace_size(3, M, K, N, moe.OP_BWD_WEIGHT) > moe.GMM_QUEUE_BYTES
+    print(f"dW split ragged: gl={gl.tolist()} K={K} N={N}", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    dw = moe.gmm_bwd_weight(x, dy, g, out=_sentinel(dev, (3, K, N)), dev_err=err)
+    _, dw_fused = moe.gmm_bwd(x, dy, w, g, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.gmm_bwd_weight(f64(x_b), f64(dy_b), gl)
+    assert_close(dev_f64(dw), ref, "split dW ragged")
+    assert_close(dev_f64(dw_fused), ref, "gmm_bwd dW ragged")
+    assert (dev_bits(dw)[1] == 0).all(), "empty expert's dW not exact zeros"

@@ -25,7 +25,9 @@
 //                 variant quantises the row as it goes (E4M3 codes + E8M0
 //                 scales).
 // For at most 4096 slots (decode-sized calls) steps 1-3 run as one
-// single-workgroup kernel, so the whole permute is two launches.
+// single-workgroup kernel, so the whole permute is two launches.  Where the
+// per-block histograms fit LDS (blocks x experts <= 12288) every scatter
+// block repeats the scan itself, so steps 2 and 3 are one launch.
 #include <mutex>
 
 #include "common.h"
@@ -137,37 +139,50 @@ MOE_DEVICE void wave_counts(const int32_t* __restrict__ ids, int64_t w0, int64_t
     }
 }
 
+// Stable rank of one group of 64 consecutive slots (g .. g+63, lane l holds
+// slot g+l with expert `id`, -1 if masked or past w1) within its expert.
+// next_row[e] holds the wave's next row for expert e and is advanced.
+MOE_DEVICE void rank_group(int64_t g, int64_t w1, int32_t id, int E, int nbits, int32_t* next_row,
+                           int32_t* __restrict__ row_id_map, int32_t* __restrict__ sorted_slot) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t s = g + lane;
+    const bool ok = valid_id(id, E);
+    const int key = ok ? id : 0;
+    // peers = lanes with the same expert (match-any built from ballots)
+    uint64_t peers = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    int32_t row = -1;
+    if (ok) row = next_row[key] + __popcll(peers & lt_mask);
+    // all lanes have read next_row before the leaders update it
+    __builtin_amdgcn_wave_barrier();
+    if (ok && (peers & lt_mask) == 0) next_row[key] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (s < w1) {
+        row_id_map[s] = row;
+        if (ok) sorted_slot[row] = (int32_t)s;
+    }
+}
+
+MOE_DEVICE int id_bits(int E) {
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    return nbits;
+}
+
 // Stable rank of every slot within its expert, groups of 64 slots in order.
-// next_row[e] holds the wave's first row for expert e and is advanced.
 MOE_DEVICE void wave_rank_scatter(const int32_t* __restrict__ ids, int64_t w0, int64_t w1, int E,
                                   int32_t* next_row, int32_t* __restrict__ row_id_map,
                                   int32_t* __restrict__ sorted_slot) {
     const int lane = threadIdx.x & 63;
-    int nbits = 1;
-    while ((1 << nbits) < E) ++nbits;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nbits = id_bits(E);
     for (int64_t g = w0; g < w1; g += 64) {
         const int64_t s = g + lane;
-        const int32_t id = (s < w1) ? ids[s] : -1;
-        const bool ok = valid_id(id, E);
-        const int key = ok ? id : 0;
-        // peers = lanes with the same expert (match-any built from ballots)
-        uint64_t peers = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (key >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        int32_t row = -1;
-        if (ok) row = next_row[key] + __popcll(peers & lt_mask);
-        // all lanes have read next_row before the leaders update it
-        __builtin_amdgcn_wave_barrier();
-        if (ok && (peers & lt_mask) == 0) next_row[key] += __popcll(peers);
-        __builtin_amdgcn_wave_barrier();
-        if (s < w1) {
-            row_id_map[s] = row;
-            if (ok) sorted_slot[row] = (int32_t)s;
-        }
+        rank_group(g, w1, (s < w1) ? ids[s] : -1, E, nbits, next_row, row_id_map, sorted_slot);
     }
 }
 
@@ -200,6 +215,77 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     }
     __syncthreads();
     wave_rank_scatter(ids, w0, w1, E, next_row[wid], row_id_map, sorted_slot);
+}
+
+// Scan and scatter in one launch, for chunks of kFusedChunk slots whose
+// per-block table fits LDS: every block stages the whole table, finds each
+// expert's total and its own blocks-before prefix, scans the totals over
+// experts (block 0 writes tokens_per_expert) and ranks its slots as
+// permute_scatter_kernel does.  The blocks repeat the scan instead of
+// waiting for one block to do it; each wave loads its 4 x 64 expert ids once,
+// together with the table, and keeps them in registers.
+constexpr int64_t kFusedChunk = 1024;
+constexpr int kFusedGroups = kFusedChunk / kWaves / 64;  // 64-slot groups per wave
+
+__global__ __launch_bounds__(kPermThreads) void permute_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t nblk, const int32_t* __restrict__ blk_hist,
+    int64_t* __restrict__ tokens_per_expert, int32_t* __restrict__ row_id_map,
+    int32_t* __restrict__ sorted_slot) {
+    __shared__ int32_t s_hist[kScanLdsInts];
+    __shared__ int32_t next_row[kWaves][kMaxExperts];
+    __shared__ int64_t scan_tmp[kPermThreads / 64];
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t w0 = (int64_t)blockIdx.x * kFusedChunk + wid * (kFusedChunk / kWaves);
+    const int64_t w1 = w0 + kFusedChunk / kWaves < S ? w0 + kFusedChunk / kWaves : S;
+    int32_t id[kFusedGroups];
+#pragma unroll
+    for (int q = 0; q < kFusedGroups; ++q) {
+        const int64_t s = w0 + q * 64 + lane;
+        id[q] = s < w1 ? ids[s] : -1;
+    }
+    const int64_t n = nblk * E;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s_hist[i] = blk_hist[i];
+    for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kFusedGroups; ++q)
+        if (valid_id(id[q], E)) atomicAdd(&next_row[wid][id[q]], 1);
+    // per expert (thread owns <= 4, in expert order): the total over blocks
+    // and the part in blocks before this one
+    const int per = (E + kPermThreads - 1) / kPermThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    int64_t mine = 0;
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        for (int64_t b = 0; b < nblk; ++b) {
+            const int32_t c = s_hist[b * E + e];
+            tot[i] += c;
+            pre[i] += b < (int64_t)blockIdx.x ? c : 0;
+        }
+        mine += tot[i];
+    }
+    int64_t total;
+    int64_t off = block_exclusive_scan<int64_t>(mine, scan_tmp, &total);  // its barriers also order the counts
+    for (int i = 0; i < per && i < 4; ++i) {
+        const int e = e0 + i;
+        if (e >= E) break;
+        if (blockIdx.x == 0) tokens_per_expert[e] = tot[i];
+        int32_t run = (int32_t)(off + pre[i]);
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = next_row[w][e];
+            next_row[w][e] = run;
+            run += c;
+        }
+        off += tot[i];
+    }
+    __syncthreads();
+    const int nbits = id_bits(E);
+#pragma unroll
+    for (int q = 0; q < kFusedGroups; ++q)
+        rank_group(w0 + q * 64, w1, id[q], E, nbits, next_row[wid], row_id_map, sorted_slot);
 }
 
 // All of histogram, expert offsets and ranking in one workgroup, for inputs
@@ -440,11 +526,17 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
         if (nblk > 0)
             hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
                                stream, ids, S, (int)E, chunk, blk, dev_err);
-        hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
-                           (int)E, tokens_per_expert);
-        if (nblk > 0)
-            hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
-                               stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
+        if (nblk > 0 && chunk == kFusedChunk && nblk * E <= kScanLdsInts) {
+            hipLaunchKernelGGL(permute_scan_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
+                               stream, ids, S, (int)E, nblk, blk, tokens_per_expert, row_id_map,
+                               sorted_slot);
+        } else {
+            hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
+                               (int)E, tokens_per_expert);
+            if (nblk > 0)
+                hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
+                                   stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
+        }
     }
     if (nblk > 0) {
         const int tpb = gather_tokens_per_block(T, top_k);

@@ -14,6 +14,7 @@
 // (its second pass mostly from L2) instead of one block walking its groups
 // in turn: with one block per (expert, slice), a decode step where one
 // expert held 48 more rows than the rest took 2.5x as long.
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -242,7 +243,7 @@ bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K) {
     const bool fits = K * kStreamRows * 2 <= 32 * 1024;
     switch (forced_gmm_variant()) {
         case kVariantTile: return false;
-        case kVariantStream: return fits;
+        case kVariantStream: return fits && M_cap <= (int64_t(1) << 16);  // grid well within 2^31 blocks
         default: break;
     }
     // a few rows per expert on average
@@ -253,8 +254,10 @@ static hipError_t launch_stream(bool swiglu, const uint16_t* x, const uint16_t* 
                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, uint16_t* h,
                                 int32_t* dev_err, hipStream_t stream) {
     const size_t shmem = (size_t)K * kStreamRows * 2;
+    const int64_t blocks = max_sub_units(E, M_cap, N);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
     // blocks past the call's sub-units exit at once
-    const dim3 grid((unsigned)max_sub_units(E, M_cap, N));
+    const dim3 grid((unsigned)blocks);
     if (swiglu)
         hipLaunchKernelGGL(gmm_stream_kernel<true>, grid, dim3(kThreads), shmem, stream, x, w, group_list,
                            (int)E, M_cap, (int)K, (int)N, y, h, dev_err);

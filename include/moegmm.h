@@ -153,7 +153,8 @@ moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64
  * rows each (M_cap <= 8E), row tiles otherwise.  For tests only, the
  * environment variable MOEGMM_FORCE_VARIANT = "tile" or "stream", read at
  * every call, forces one of them (streaming where its staging fits,
- * K <= 4096) for gmm_fwd, gmm_fwd_swiglu and the MX forward calls.
+ * K <= 4096, and M_cap <= 2^16) for gmm_fwd, gmm_fwd_swiglu and the MX
+ * forward calls.
  * ---------------------------------------------------------------------- */
 /* Workspace bytes of GMM op `op` (MOE_GMM_OP_*).  gmm_bwd needs
  * MOE_GMM_QUEUE_BYTES (1152): its tile queue, counters the kernel increments with atomics.  gmm_bwd_weight

@@ -23,7 +23,8 @@ def dev():
 
 
 def _case(name):
-    rng = np.random.default_rng({"tiny": 41, "ragged_I": 42, "decode": 43, "prefill": 44}.get(name, 45))
+    rng = np.random.default_rng({"tiny": 41, "ragged_I": 42, "decode": 43, "prefill": 44,
+                                 "stream_fine": 46}.get(name, 45))
     if name.startswith("sweep"):
         wl = workloads.sweep(int(name[-1]))
         return wl["x"], wl["w"], wl["group_list"], wl.dims["M"]
@@ -31,6 +32,9 @@ def _case(name):
         "tiny": (5, 64, 32, [1, 2, 0, 2]),
         "ragged_I": (700, 200, 520, [0, 300, 0, 250, 100]),   # I not a multiple of the 128-column tile
         "decode": (512, 2048, 512, None),                        # weight-streaming path
+        # weight streaming with a long reduction (K = 1024), I not a multiple of the
+        # 128-column slice, 0-12 rows per expert (up to three row groups)
+        "stream_fine": (100, 1024, 504, [12, 0, 9, 1, 2, 3, 5, 0, 12, 4, 7, 11, 6, 8, 10, 10]),
         "prefill": (32768, 2048, 512, None),
     }
     M, K, I, gl = shapes[name]
@@ -44,7 +48,7 @@ def _case(name):
     return x, w1, gl, M_cap
 
 
-@pytest.mark.parametrize("name", ["tiny", "sweep0", "sweep2", "ragged_I", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tiny", "sweep0", "sweep2", "ragged_I", "decode", "stream_fine", "prefill"])
 def test_fused_gate_up_swiglu(dev, name):
     x, w1, gl, M_cap = _case(name)
     R = int(gl.sum())

@@ -29,12 +29,12 @@ Also in the line:
   mxfp8        -- the A8W8-FP (MXFP8) forward on the decode and prefill layers
                   and the ep rank: GB/s, TFLOP/s against the fp8 MFMA peak,
                   fraction of the attainable roofline;
-  *_ms_events  -- p10 / p50 / p90 of per-step (per-layer) spans from HIP events,
-                  first call's start to last call's end; they come from a pass
-                  that records an event pair around every call (also the source
-                  of per_call_us), so they sit a few percent above ms_per_step /
-                  ms_per_layer, which are timed with events around the dominant
-                  kernel's launches only (its roofline) or none;
+  *_ms_events  -- p10 / p50 / p90 of per-step (per-layer) device time from one
+                  HIP event pair around each whole step (layer), in a pass of
+                  its own; per_call_us comes from another pass with an event
+                  pair around every call, and ms_per_step / ms_per_layer from
+                  wall time with events around the dominant kernel's launches
+                  only (its roofline) or none;
   ceilings     -- hipBLASLt on a dense bf16 product of the ep gate_up shape and
                   a 512 MiB device copy, measured here for context;
   cpu_baseline -- the CPU oracle timed on a bounded sample of the same step.
@@ -100,12 +100,20 @@ class KernelTimer:
         self.pending = []
         return out
 
-    def spans(self, calls_per_step):
-        """ms from the first call's start to the last call's end of every
-        step (call before collect())."""
-        n = len(self.pending) // calls_per_step
-        return [self.pending[i * calls_per_step][1].elapsed_time(
-                    self.pending[(i + 1) * calls_per_step - 1][2]) for i in range(n)]
+
+def step_spans(torch, step, n):
+    """ms per step from one HIP event pair around each whole step (no event
+    between its calls), over n steps enqueued back to back."""
+    ev = []
+    for _ in range(n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 
 def percentiles(ms):
@@ -223,13 +231,14 @@ def run_ep(torch, dev, args):
         step(plain)
     torch.cuda.synchronize()
     # 1. an instrumented pass (an event pair around every call): the per-call
-    #    breakdown, the per-step spans and which kernel dominates
+    #    breakdown and which kernel dominates
     timer.collect()
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
-    step_ms = timer.spans(6)
     per = timer.collect()
+    # per-step spans from one event pair around each whole step
+    step_ms = step_spans(torch, lambda: step(plain), args.steps)
     flops = ep_gemm_flops(wl["group_list"], H, I)
     total_flops = sum(flops.values())
     mean_ms = {k: float(np.mean(v)) for k, v in per.items()}
@@ -366,8 +375,8 @@ def layer_forward(torch, dev, wl, steps):
     for _ in range(min(50, steps)):
         step(timer)
     torch.cuda.synchronize()
-    spans = percentiles(timer.spans(5 if not fused else 4))
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
+    spans = percentiles(step_spans(torch, lambda: step(plain), min(50, steps)))
     gl = layer.tokens_per_expert.cpu().numpy()
     return ms, per, gl, (layer, probs, fused, spans)
 
@@ -552,8 +561,8 @@ def mx_layer_forward(torch, dev, wl, steps):
     for _ in range(min(50, steps)):
         step(timer)
     torch.cuda.synchronize()
-    spans = percentiles(timer.spans(4))
     per = {k: float(np.mean(v)) for k, v in timer.collect().items()}
+    spans = percentiles(step_spans(torch, lambda: step(plain), min(50, steps)))
     assert int(err.item()) == 0, "device error word set during the MX bench"
     return ms, per, g.cpu().numpy(), spans
 

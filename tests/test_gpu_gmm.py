@@ -464,12 +464,15 @@ def test_dw_split_few_tiles_dense(dev):
     assert_close(got, f64(x_b[:, ks]).T @ f64(dy_b), "split dW rows")
 
 
-def test_dw_split_few_tiles_ragged(dev):
+@pytest.mark.parametrize("K,N", [(512, 520), (520, 264)])
+def test_dw_split_few_tiles_ragged(dev, K, N):
     """Few tiles over several experts: a long expert split into many chunks,
     an empty one (exact zeros), a short one kept whole; whole-tensor parity
-    with the oracle, and the fused gmm_bwd (no split) within tolerance."""
+    with the oracle, and the fused gmm_bwd (no split) within tolerance.  The
+    last tile column (N = 520) or the last tile row and column (K = 520,
+    N = 264) hold 8 of their 256 outputs."""
     rng = np.random.default_rng(22)
-    M, K, N = 5100, 512, 520
+    M = 5100
     gl = np.array([5000, 0, 37], dtype=np.int64)
     x_b = workloads.normal_bf16(rng, (M, K))
     dy_b = workloads.normal_bf16(rng, (M, N))

@@ -11,10 +11,9 @@
 //
 // Kernels (all deterministic; the only atomics are integer counts in LDS):
 //   1. hist    -- one block per chunk of slots: per-block expert histogram.
-//   2. scan    -- one block: per expert, an exclusive prefix over blocks, then
-//                 the expert offsets (exclusive scan over experts); writes
-//                 tokens_per_expert and turns the histogram into per-block
-//                 starting rows.
+//   2. scan    -- per expert, an exclusive prefix over blocks, then the
+//                 expert offsets (exclusive scan over experts); writes
+//                 tokens_per_expert and the per-block starting rows.
 //   3. scatter -- one block per chunk: each wave ranks its slots within the
 //                 expert in slot order (wave ballots emulate a match-any on
 //                 the expert id) and writes row_id_map and sorted_slot.
@@ -27,7 +26,8 @@
 // For at most 4096 slots (decode-sized calls) steps 1-3 run as one
 // single-workgroup kernel, so the whole permute is two launches.  Where the
 // per-block histograms fit LDS (blocks x experts <= 12288) every scatter
-// block repeats the scan itself, so steps 2 and 3 are one launch.
+// block repeats the scan itself, so steps 2 and 3 are one launch; larger
+// tables are scanned by segments of block rows over many workgroups.
 #include <mutex>
 
 #include "common.h"
@@ -81,23 +81,41 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(
     for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
 }
 
-// One block.  Thread i owns experts [i*per, i*per + per) so that the scan
-// over threads runs in ascending expert order.  The per-block histograms are
-// first staged in LDS with one coalesced pass when they fit (so the column
-// sums below read LDS instead of walking global memory one load at a time).
+// Tables too large for the fused scan (blocks x experts > kScanLdsInts) are
+// scanned in two launches.  1: segments of kSegBlocks block rows, one thread
+// per (expert, segment): the entries become exclusive prefixes within the
+// segment, the segment's total goes to seg[segment][expert].  2: one block
+// turns the segment totals into each segment's first row (the expert's
+// offset over all experts plus the segments before) and writes
+// tokens_per_expert.  The scatter then starts block b of expert e at
+// table[b][e] + seg[b / kSegBlocks][e].
 constexpr int64_t kScanLdsInts = 12288;  // 48 KiB
+constexpr int64_t kSegBlocks = 64;
 
-__global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
-    int32_t* __restrict__ blk_hist, int64_t nblk, int E, int64_t* __restrict__ tokens_per_expert) {
-    __shared__ int64_t scan_tmp[kPermThreads / 64];
-    __shared__ int32_t s_hist[kScanLdsInts];
-    const int64_t n = nblk * E;
-    const bool staged = n <= kScanLdsInts;  // uniform
-    if (staged) {
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s_hist[i] = blk_hist[i];
-        __syncthreads();
+int64_t scan_segments(int64_t nblk) { return (nblk + kSegBlocks - 1) / kSegBlocks; }
+
+__global__ __launch_bounds__(kPermThreads) void permute_segscan_kernel(int32_t* __restrict__ blk_hist,
+                                                                     int64_t nblk, int E,
+                                                                     int32_t* __restrict__ seg) {
+    const int e = blockIdx.x * kPermThreads + threadIdx.x;
+    if (e >= E) return;
+    const int64_t b0 = (int64_t)blockIdx.y * kSegBlocks;
+    const int64_t b1 = b0 + kSegBlocks < nblk ? b0 + kSegBlocks : nblk;
+    int32_t run = 0;
+    for (int64_t b = b0; b < b1; ++b) {
+        const int32_t v = blk_hist[b * E + e];
+        blk_hist[b * E + e] = run;
+        run += v;
     }
-    auto count = [&](int64_t i) { return staged ? s_hist[i] : blk_hist[i]; };
+    seg[(int64_t)blockIdx.y * E + e] = run;
+}
+
+// One block.  Thread i owns experts [i*per, i*per + per) so that the scan
+// over threads runs in ascending expert order.
+__global__ __launch_bounds__(kPermThreads) void permute_segbase_kernel(int32_t* __restrict__ seg,
+                                                                     int64_t nseg, int E,
+                                                                     int64_t* __restrict__ tokens_per_expert) {
+    __shared__ int64_t scan_tmp[kPermThreads / 64];
     const int per = (E + blockDim.x - 1) / blockDim.x;
     const int e0 = threadIdx.x * per;
     int64_t cnt[4] = {0, 0, 0, 0};
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
         const int e = e0 + i;
         if (e >= E) break;
         int64_t c = 0;
-        for (int64_t b = 0; b < nblk; ++b) c += count(b * E + e);
+        for (int64_t q = 0; q < nseg; ++q) c += seg[q * E + e];
         cnt[i] = c;
         mine += c;
     }
@@ -117,9 +135,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(
         if (e >= E) break;
         tokens_per_expert[e] = cnt[i];
         int64_t run = off;
-        for (int64_t b = 0; b < nblk; ++b) {
-            const int32_t v = count(b * E + e);
-            blk_hist[b * E + e] = (int32_t)run;
+        for (int64_t q = 0; q < nseg; ++q) {
+            const int32_t v = seg[q * E + e];
+            seg[q * E + e] = (int32_t)run;
             run += v;
         }
         off += cnt[i];
@@ -188,8 +206,8 @@ MOE_DEVICE void wave_rank_scatter(const int32_t* __restrict__ ids, int64_t w0, i
 
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t S, int E, int64_t chunk,
-    const int32_t* __restrict__ blk_base, int32_t* __restrict__ row_id_map,
-    int32_t* __restrict__ sorted_slot) {
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ seg_base,
+    int32_t* __restrict__ row_id_map, int32_t* __restrict__ sorted_slot) {
     __shared__ int32_t next_row[kWaves][kMaxExperts];
     const int wid = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
@@ -204,8 +222,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
     __syncthreads();
     // starting row of every wave for every expert
     const int32_t* base = blk_base + (int64_t)blockIdx.x * E;
+    const int32_t* sbase = seg_base + (int64_t)blockIdx.x / kSegBlocks * E;
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int32_t run = base[e];
+        int32_t run = base[e] + sbase[e];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const int32_t c = next_row[w][e];
@@ -502,11 +521,16 @@ static void* static_scratch(hipError_t* err) {
     return addr[dev];
 }
 
+// The per-block table, then (for the two-launch scan) the segment table.
+static size_t table_bytes(int64_t nblk, int64_t E) {
+    return ((size_t)(nblk * E) * sizeof(int32_t) + 255) / 256 * 256;
+}
 size_t permute_workspace_bytes(int64_t S, int64_t E) {
     const int64_t chunk = permute_chunk(S);
     const int64_t nblk = (S + chunk - 1) / chunk;
-    size_t bytes = (size_t)(nblk * E) * sizeof(int32_t);
-    bytes = (bytes + 255) / 256 * 256;
+    size_t bytes = table_bytes(nblk, E);
+    if (!(chunk == kFusedChunk && nblk * E <= kScanLdsInts))
+        bytes += ((size_t)(scan_segments(nblk) * E) * sizeof(int32_t) + 255) / 256 * 256;
     return bytes < 256 ? 256 : bytes;
 }
 
@@ -531,11 +555,18 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                                stream, ids, S, (int)E, nblk, blk, tokens_per_expert, row_id_map,
                                sorted_slot);
         } else {
-            hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, blk, nblk,
+            // also for no slots at all: then only tokens_per_expert (zeros) is written
+            int32_t* seg = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + table_bytes(nblk, E));
+            const int64_t nseg = scan_segments(nblk);
+            if (nblk > 0)
+                hipLaunchKernelGGL(permute_segscan_kernel,
+                                   dim3((unsigned)((E + kPermThreads - 1) / kPermThreads), (unsigned)nseg),
+                                   dim3(kPermThreads), 0, stream, blk, nblk, (int)E, seg);
+            hipLaunchKernelGGL(permute_segbase_kernel, dim3(1), dim3(kPermThreads), 0, stream, seg, nseg,
                                (int)E, tokens_per_expert);
             if (nblk > 0)
-                hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0,
-                                   stream, ids, S, (int)E, chunk, blk, row_id_map, sorted_slot);
+                hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)nblk), dim3(kPermThreads), 0, stream,
+                                   ids, S, (int)E, chunk, blk, seg, row_id_map, sorted_slot);
         }
     }
     if (nblk > 0) {

@@ -85,7 +85,8 @@ def test_ep_slice_routing(dev):
     (5, 3, 700, 24, 0.0),         # most experts empty
     (64, 8, 256, 2048, 1.0),      # every slot masked
     (1536, 8, 1024, 8, 0.0),      # 12 chunks x 1024 experts: the largest table scanned per block
-    (4000, 8, 1024, 8, 0.1),      # 32 chunks x 1024 experts: the separate scan launch
+    (4000, 8, 1024, 8, 0.1),      # 32 chunks x 1024 experts: the two-launch segmented scan
+    (20000, 8, 1024, 8, 0.05),    # 157 chunks x 1024 experts: three scan segments
 ])
 def test_random_routings(dev, T, K, E, H, mask):
     rng = np.random.default_rng(T * 31 + K)

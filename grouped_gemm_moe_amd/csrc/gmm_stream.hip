@@ -33,8 +33,10 @@ constexpr int kLanes = kStreamCols / 8;      // column lanes of one k-group (8 c
 constexpr int kGroupsPerWave = 64 / kLanes;  // k-groups per wave
 constexpr int kGroups = kGroupsPerWave * kWaves;
 
+// k-chunk iterations per unrolled loop body: 1 measured fastest (decode
+// gate_up 180 us; 2: 189 us; 3 and 4: 181-183 us)
 #ifndef MOEGMM_STREAM_UNROLL
-#define MOEGMM_STREAM_UNROLL 2
+#define MOEGMM_STREAM_UNROLL 1
 #endif
 
 // acc += x rows (LDS, [kStreamRows][K]) times the lane's 8 weight columns;

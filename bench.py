@@ -685,7 +685,7 @@ def cpu_baseline(wl, budget_s):
 
     # The host cores this process may run on; the BLAS pool is pinned to
     # them, or to the thread limit the environment sets if that is lower
-    # (a GPU machine shares its host: OMP_NUM_THREADS states this process's share).
+    # (on a shared host OMP_NUM_THREADS states this process's share).
     affinity = len(os.sched_getaffinity(0))
     threads = affinity
     env_limit = os.environ.get("OMP_NUM_THREADS", "")
@@ -751,7 +751,7 @@ def cpu_baseline(wl, budget_s):
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -30,7 +30,7 @@ Sources (web pages, cited by title and section):
              (rows of all groups concatenated, weight [groups, k, n], a list of
              per-group row counts).
 
-Readings where the pages are silent or ambiguous (each listed in the design doc):
+Readings where the pages are silent or ambiguous:
 
 * group_list holds per-expert COUNTS (int64), not a cumulative sum.
 * A slot (token t, choice k) has flat index s = t*top_k + k; id -1 = masked.

@@ -25,7 +25,7 @@ definition, restated here:
     to even, saturating at +-448 (E4M3 "FN" has no infinity; 0x7F / 0xFF are
     NaN and are produced only for NaN input).
 Where the pages leave the rounding and saturation of the element conversion
-open, this is the reading taken (listed in the design doc).
+open, this is the reading taken.
 
 Everything here works in float64 on exactly representable values.
 """

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests must run on a GPU machine; never silently pass without one.
+    # GPU tests must run on a GPU; never silently pass without one.
     pass
 
 

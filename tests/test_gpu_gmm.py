@@ -190,15 +190,20 @@ def test_decode_shaped_forward(dev, skew):
     assert (dev_bits(y)[R:] == SENT).all()
 
 
-def test_group_list_errors_reported(dev):
+@pytest.mark.parametrize("M", [256, 1024])
+def test_group_list_errors_reported(dev, M):
     """sum(group_list) > M_cap and negative counts set the error bit; the
-    kernels clamp to the buffer, so the call itself is safe."""
+    kernels clamp to the buffer, so the call itself is safe.  At M = 1024 the
+    weight gradient's 3 tiles take the split-row path (4 chunks)."""
     rng = np.random.default_rng(7)
-    M, K, N = 256, 64, 64
+    K, N = 64, 64
     x = bf16_dev(workloads.normal_bf16(rng, (M, K)), dev)
     dy = bf16_dev(workloads.normal_bf16(rng, (M, N)), dev)
     w = bf16_dev(workloads.normal_bf16(rng, (3, K, N)), dev)
-    for gl in ([200, 100, 10], [-5, 100, 10], [0, 0, 1000]):
+    split = moe.gmm_workspace_size(3, M, K, N, moe.OP_BWD_WEIGHT) > moe.GMM_QUEUE_BYTES
+    assert split == (M == 1024)
+    over = [M - 56, 100, 10]  # sum past M_cap
+    for gl in (over, [-5, 100, 10], [0, 0, 4 * M]):
         print(f"group_list error case {gl}", flush=True)
         for fn in ("fwd", "dx", "dw"):
             err = torch.zeros(1, dtype=torch.int32, device=dev)

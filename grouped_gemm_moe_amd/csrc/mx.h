@@ -47,6 +47,15 @@ MOE_DEVICE uint32_t e4m3_rne_sat(float f) {
     return sign | (uint32_t)(((e + 7) << 3) + m - 8);
 }
 
+// Largest of v over the 4 lanes of a quad (lanes 4q .. 4q+3), every lane of
+// the quad getting it: two DPP quad permutes (lane ^ 1, then lane ^ 2) on
+// the vector ALU instead of LDS-routed shuffles.  All lanes must be active.
+MOE_DEVICE float quad_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));  // [2,3,0,1]
+    return v;
+}
+
 // Four values (already scaled) -> four codes packed little-endian.
 MOE_DEVICE uint32_t e4m3_pack4(float a, float b, float c, float d) {
     return e4m3_rne_sat(a) | (e4m3_rne_sat(b) << 8) | (e4m3_rne_sat(c) << 16) |

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kQThreads) void mx_quantize_kernel(const uint16_t* 
                                                                 uint8_t* __restrict__ s) {
     const int64_t cpr = K / 8;  // 16-byte pieces per row (4 per group)
     const int64_t total = rows * cpr;
-    // every lane runs the same number of iterations (shuffles need the quad)
+    // every lane runs the same number of iterations (the quad maximum needs all four lanes)
     const int64_t stride = (int64_t)gridDim.x * kQThreads;
     const int64_t iters = (total + stride - 1) / stride;
     int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
@@ -37,8 +37,7 @@ __global__ __launch_bounds__(kQThreads) void mx_quantize_kernel(const uint16_t* 
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        amax = quad_max(amax);
         const uint32_t sb = mx_scale_byte(amax);
         const float inv = mx_inv_scale(sb);
         if (ok) {

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
 // The same gather with MX quantisation of each token row on the way (row-wise
 // Q_MX commutes with the gather, so a top-k token is quantised once): four
 // lanes own one group of 32 (16 bytes of bf16 each) and meet on its maximum
-// with two xor shuffles; each lane stores 8 codes, and the quad's first lane
+// with two DPP quad permutes (quad_max); each lane stores 8 codes, and the quad's first lane
 // the scale byte, to every slot row of the token.
 __global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t T, int top_k,
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
     const int64_t cpr = H / 8;  // 16-byte pieces per row, a multiple of 4
     const int64_t tok = T - t0 < tpb ? T - t0 : tpb;
     const int64_t total = tok * cpr;
-    // every lane runs the same number of iterations (shuffles need the quad)
+    // every lane runs the same number of iterations (the quad maximum needs all four lanes)
     constexpr int64_t kStep = (int64_t)kPermThreads * kGatherUnroll;
     const int64_t iters = (total + kStep - 1) / kStep;
     for (int64_t it = 0; it < iters; ++it) {
@@ -455,8 +455,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
             float amax = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            amax = quad_max(amax);
             if (i < total) {  // whole quads agree: total % 4 == 0
                 const uint32_t sb = mx_scale_byte(amax);
                 const float inv = mx_inv_scale(sb);

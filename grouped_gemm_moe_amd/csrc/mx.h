@@ -56,6 +56,12 @@ MOE_DEVICE float quad_max(float v) {
     return v;
 }
 
+// Largest of v over lane pairs (2p, 2p+1), both lanes getting it (one DPP
+// quad permute).  All lanes must be active.
+MOE_DEVICE float pair_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));  // [1,0,3,2]
+}
+
 // Four values (already scaled) -> four codes packed little-endian.
 MOE_DEVICE uint32_t e4m3_pack4(float a, float b, float c, float d) {
     return e4m3_rne_sat(a) | (e4m3_rne_sat(b) << 8) | (e4m3_rne_sat(c) << 16) |

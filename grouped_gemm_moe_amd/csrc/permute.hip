@@ -365,6 +365,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
 #define MOEGMM_GATHER_SLOTS 16
 #endif
 constexpr int kGatherMaxSlots = MOEGMM_GATHER_SLOTS;  // tpb * top_k <= max(this, top_k)
+static_assert(kGatherMaxSlots <= 64, "32-bit piece indices: tokens per block x 2^18 pieces < 2^31");
 constexpr int kGatherUnroll = 4;     // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
@@ -380,24 +381,26 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
         rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
     }
     __syncthreads();
-    const int64_t cpr = H / 8;  // 16-byte chunks per row
-    const int64_t tok = T - t0 < tpb ? T - t0 : tpb;
-    const int64_t total = tok * cpr;
-    for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)kPermThreads * kGatherUnroll) {
+    // 32-bit piece indices: at most 16 tokens of 2^18 pieces per block
+    const int cpr = (int)(H / 8);  // 16-byte chunks per row
+    const int tok = (int)(T - t0 < tpb ? T - t0 : tpb);
+    const int total = tok * cpr;
+    const uint16_t* xb = x + t0 * H;
+    for (int i0 = (int)threadIdx.x; i0 < total; i0 += kPermThreads * kGatherUnroll) {
         u32x4_t v[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            const int i = i0 + u * kPermThreads;
             if (i < total) {
-                const int64_t tt = i / cpr, c = i - tt * cpr;
-                v[u] = ld16(x + (t0 + tt) * H + c * 8);
+                const int tt = i / cpr, c = i - tt * cpr;
+                v[u] = ld16(xb + (int64_t)tt * H + c * 8);
             }
         }
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kPermThreads;
+            const int i = i0 + u * kPermThreads;
             if (i < total) {
-                const int64_t tt = i / cpr, c = i - tt * cpr;
+                const int tt = i / cpr, c = i - tt * cpr;
                 for (int k = 0; k < top_k; ++k) {
                     const int32_t r = rows[tt * top_k + k];
                     if (r >= 0) st16(x_perm + (int64_t)r * H + c * 8, v[u]);
@@ -408,10 +411,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_kernel(
 }
 
 // The same gather with MX quantisation of each token row on the way (row-wise
-// Q_MX commutes with the gather, so a top-k token is quantised once): four
-// lanes own one group of 32 (16 bytes of bf16 each) and meet on its maximum
-// with two DPP quad permutes (quad_max); each lane stores 8 codes, and the quad's first lane
-// the scale byte, to every slot row of the token.
+// Q_MX commutes with the gather, so a top-k token is quantised once): a lane
+// owns 32 bytes of a row (16 bf16, two loads), a lane pair one group of 32,
+// and the pair meets on the group's maximum with one DPP permute
+// (pair_max); each lane stores its 16 codes as one 16-byte store, and the
+// pair's first lane the scale byte, to every slot row of the token.
 __global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ row_id_map, int64_t T, int top_k,
     int64_t H, int tpb, int64_t ld_s, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
@@ -425,49 +429,56 @@ __global__ __launch_bounds__(kPermThreads) void permute_gather_mx_kernel(
         rows[threadIdx.x] = (r >= 0 && r < S) ? r : -1;
     }
     __syncthreads();
-    const int64_t cpr = H / 8;  // 16-byte pieces per row, a multiple of 4
-    const int64_t tok = T - t0 < tpb ? T - t0 : tpb;
-    const int64_t total = tok * cpr;
-    // every lane runs the same number of iterations (the quad maximum needs all four lanes)
-    constexpr int64_t kStep = (int64_t)kPermThreads * kGatherUnroll;
-    const int64_t iters = (total + kStep - 1) / kStep;
-    for (int64_t it = 0; it < iters; ++it) {
-        const int64_t i0 = it * kStep + threadIdx.x;
-        u32x4_t v[kGatherUnroll];
+    const int cpr = (int)(H / 16);  // 32-byte pieces per row, even (H is a multiple of 32)
+    const int tok = (int)(T - t0 < tpb ? T - t0 : tpb);
+    const int total = tok * cpr;    // even; at most 16 tokens x 2^17 pieces
+    const uint16_t* xb = x + t0 * H;
+    // every lane runs the same number of iterations (the pair maximum needs both lanes)
+    constexpr int kU = kGatherUnroll / 2;  // pieces per lane per iteration (two loads each)
+    constexpr int kStep = kPermThreads * kU;
+    const int iters = (total + kStep - 1) / kStep;
+    for (int it = 0; it < iters; ++it) {
+        const int i0 = it * kStep + (int)threadIdx.x;
+        u32x4_t v[kU][2];
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kPermThreads;
-            v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int u = 0; u < kU; ++u) {
+            const int i = i0 + u * kPermThreads;
+            v[u][0] = v[u][1] = u32x4_t{0u, 0u, 0u, 0u};
             if (i < total) {
-                const int64_t tt = i / cpr, c = i - tt * cpr;
-                v[u] = ld16(x + (t0 + tt) * H + c * 8);
+                const int tt = i / cpr, c = i - tt * cpr;
+                const uint16_t* p = xb + (int64_t)tt * H + c * 16;
+                v[u][0] = ld16(p);
+                v[u][1] = ld16(p + 8);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t i = i0 + (int64_t)u * kPermThreads;
-            float f[8];
+        for (int u = 0; u < kU; ++u) {
+            const int i = i0 + u * kPermThreads;
+            float f[16];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                f[2 * c] = bf16_lo(v[u][c]);
-                f[2 * c + 1] = bf16_hi(v[u][c]);
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    f[8 * h + 2 * c] = bf16_lo(v[u][h][c]);
+                    f[8 * h + 2 * c + 1] = bf16_hi(v[u][h][c]);
+                }
             float amax = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(f[c]));
-            amax = quad_max(amax);
-            if (i < total) {  // whole quads agree: total % 4 == 0
+            for (int c = 0; c < 16; ++c) amax = fmaxf(amax, fabsf(f[c]));
+            amax = pair_max(amax);
+            if (i < total) {  // whole pairs agree: total and i0 - threadIdx.x are even
                 const uint32_t sb = mx_scale_byte(amax);
                 const float inv = mx_inv_scale(sb);
-                u32x2_t o;
-                o[0] = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
-                o[1] = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
-                const int64_t tt = i / cpr, c = i - tt * cpr;
+                u32x4_t o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    o[q] = e4m3_pack4(f[4 * q] * inv, f[4 * q + 1] * inv, f[4 * q + 2] * inv, f[4 * q + 3] * inv);
+                const int tt = i / cpr, c = i - tt * cpr;
                 for (int k = 0; k < top_k; ++k) {
                     const int32_t r = rows[tt * top_k + k];
                     if (r >= 0) {
-                        *reinterpret_cast<u32x2_t*>(xq + (int64_t)r * H + c * 8) = o;
-                        if ((c & 3) == 0) xs[(int64_t)r * ld_s + (c >> 2)] = (uint8_t)sb;
+                        st16(xq + (int64_t)r * H + c * 16, o);
+                        if ((c & 1) == 0) xs[(int64_t)r * ld_s + (c >> 1)] = (uint8_t)sb;
                     }
                 }
             }

@@ -314,16 +314,16 @@ def run_ep(torch, dev, args):
 # decode-shaped layer forward: HBM GB/s
 # ---------------------------------------------------------------------------
 
-def decode_bytes(gl, T, K, H, I, fused=True):
+def decode_bytes(gl, T, K, H, I, fused=True, gathered=False):
     """Algorithmic bytes of one layer forward: weights of experts with rows,
     once; every activation tensor the path materialises written once and read
-    once (x_perm, A, Yp; H too when gate_up and SwiGLU run unfused);
-    indices."""
+    once (x_perm unless the gate_up GMM gathers token rows itself, A, Yp; H
+    too when gate_up and SwiGLU run unfused); indices."""
     n_active = int(np.sum(np.asarray(gl) > 0))
     S = int(np.sum(gl))
     w = n_active * (H * 2 * I + I * H) * 2
-    act = (T * H * 2            # x read by permute
-           + S * H * 2 * 2      # x_perm written, read
+    act = (T * H * 2            # x read (by the permute's gather, or by the gate_up GMM)
+           + (0 if gathered else S * H * 2 * 2)  # x_perm written, read
            + (0 if fused else S * 2 * I * 2 * 2)  # h written, read
            + S * I * 2 * 2      # a written, read
            + S * H * 2 * 2      # yp written, read
@@ -332,11 +332,13 @@ def decode_bytes(gl, T, K, H, I, fused=True):
     return w + act + idx, n_active
 
 
-def layer_forward(torch, dev, wl, steps):
+def layer_forward(torch, dev, wl, steps, gather=False):
     """Time the layer forward on workload `wl` -- permute -> gate_up GMM and
     SwiGLU (fused into one call, no H, except for decode-shaped calls where
     the weight-streaming gate_up + swiglu pair is faster) -> down GMM ->
-    unpermute: wall ms per layer, per-call means, and whether it fused."""
+    unpermute: wall ms per layer, per-call means, and whether it fused.
+    gather: the permute computes the maps only and the gate_up GMM reads the
+    token rows through sorted_slot (no x_perm)."""
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
 
     d = wl.dims
@@ -346,18 +348,19 @@ def layer_forward(torch, dev, wl, steps):
     w2 = bf16_dev(torch, wl["w2"], dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     probs = torch.from_numpy(wl["probs"]).to(dev)
-    layer = MoeLayer(LayerShape(T, K, E, H, I), dev)
+    layer = MoeLayer(LayerShape(T, K, E, H, I), dev, gather_rows=gather)
     timer = KernelTimer(torch)
-    from grouped_gemm_moe_amd import gmm_fwd, gmm_fwd_swiglu, moe_unpermute, swiglu
+    from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu
     g = layer.tokens_per_expert
     fused = layer.use_fused("auto")
+    sfx = "_gather" if gather else ""
 
     def step(t):
-        t("moe_permute", lambda: layer.permute(x, ids))
+        t("moe_permute_index" if gather else "moe_permute", lambda: layer.permute(x, ids))
         if fused:
-            t("gmm_fwd_swiglu", lambda: gmm_fwd_swiglu(layer.x_perm, w1, g, out=layer.a))
+            t("gmm_fwd_swiglu" + sfx, lambda: layer.gate_up(w1, True, keep_h=False))
         else:
-            t("gmm_fwd_gate_up", lambda: gmm_fwd(layer.x_perm, w1, g, out=layer.h))
+            t("gmm_fwd_gate_up" + sfx, lambda: layer.gate_up(w1, False))
             t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
         t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out))
@@ -421,11 +424,11 @@ def end_backward(torch, dev, layer, probs, steps=20):
     return res
 
 
-def layer_roofline(gl, T, K, H, I, ms, fused=True):
+def layer_roofline(gl, T, K, H, I, ms, fused=True, gathered=False):
     """Algorithmic bytes and FLOPs of one layer forward and the fraction of
     the attainable roofline max(FLOPs / MFMA peak, bytes / HBM peak) that the
     measured time reaches."""
-    nbytes, n_active = decode_bytes(gl, T, K, H, I, fused)
+    nbytes, n_active = decode_bytes(gl, T, K, H, I, fused, gathered)
     S = int(np.sum(gl))
     flops = 2.0 * S * H * 2 * I + 2.0 * S * I * H
     t_mem = nbytes / (HBM_PEAK_GBS * 1e9)
@@ -457,6 +460,7 @@ def run_decode(torch, dev, args):
                   ms_per_layer=round(ms_s, 4),
                   gb_per_s=round(roof_s["bytes_per_layer"] / (ms_s * 1e-3) / 1e9, 1),
                   per_call_us={k: round(v * 1e3, 2) for k, v in per_s.items()})
+    gathered = gathered_layer(torch, dev, wl, args.decode_steps, T, K, H, I)
     return dict(
         metric="decode MoE layer HBM GB/s",
         workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
@@ -467,7 +471,22 @@ def run_decode(torch, dev, args):
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
         gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
         skewed=skewed,
+        gathered=gathered,
     )
+
+
+def gathered_layer(torch, dev, wl, steps, T, K, H, I):
+    """The same layer forward with the dispatch fused into the gate_up GMM
+    (moe_permute_index, then the gate_up GMM gathers token rows itself): its
+    time, and its fraction of its own roofline, whose bytes no longer hold
+    the x_perm write and read."""
+    ms, per, gl, (_, _, fused, spans) = layer_forward(torch, dev, wl, steps, gather=True)
+    roof = layer_roofline(gl, T, K, H, I, ms, fused, gathered=True)
+    return dict(ms_per_layer=round(ms, 4), layer_ms_events=spans,
+                gb_per_s=round(roof["bytes_per_layer"] / (ms * 1e-3) / 1e9, 1),
+                bytes_per_layer=roof["bytes_per_layer"], roofline_ms=roof["roofline_ms"],
+                frac_of_attainable=roof["frac_of_attainable"],
+                per_call_us={k: round(v * 1e3, 2) for k, v in per.items()})
 
 
 def run_prefill(torch, dev, args):
@@ -491,6 +510,7 @@ def run_prefill(torch, dev, args):
         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **roof,
         per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
         end_backward=ends,
+        gathered=gathered_layer(torch, dev, wl, args.prefill_steps, T, K, H, I),
     )
 
 

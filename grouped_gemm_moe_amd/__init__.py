@@ -23,18 +23,20 @@ import torch
 from . import _lib as _L
 
 __all__ = [
-    "MoeError", "moe_permute", "moe_permute_noalloc", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
+    "MoeError", "moe_permute", "moe_permute_noalloc", "moe_permute_index", "gmm_fwd", "gmm_fwd_swiglu",
+    "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
     "gmm_bwd_swiglu",
     "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
     "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu",
-    "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP",
+    "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP", "DEVERR_SLOT",
 ]
 
 DEVERR_EXPERT_ID = 1
 DEVERR_GROUP_LIST = 2
 DEVERR_ROW_MAP = 4
+DEVERR_SLOT = 8
 OP_FWD, OP_BWD_INPUT, OP_BWD_WEIGHT, OP_BWD = 0, 1, 2, 3
 GMM_QUEUE_BYTES = 1152  # the zero-filled prefix of a GMM workspace
 
@@ -159,6 +161,75 @@ def moe_permute_noalloc(x, topk_ids, num_experts: int, *, out, dev_err=None):
                                          _ptr(row_id_map), _ptr(sorted_slot), _ptr(tpe), _ptr(dev_err),
                                          _stream(dev)), "moe_permute_noalloc")
     return x_perm, row_id_map, sorted_slot, tpe
+
+
+def moe_permute_index(topk_ids, num_experts: int, *, out=None, ws=None, dev_err=None):
+    """moe_permute without the row gather.  Returns (row_id_map, sorted_slot,
+    tokens_per_expert); see moe_permute_index in include/moegmm.h."""
+    _dev(topk_ids, "topk_ids", torch.int32)
+    if topk_ids.dim() != 2:
+        raise MoeError("topk_ids must be [T, top_k]")
+    T, top_k = topk_ids.shape
+    S = T * top_k
+    dev = topk_ids.device
+    if out is None:
+        out = (None, None, None)
+    row_id_map = _out(out[0], (S,), torch.int32, dev, "row_id_map")
+    sorted_slot = _out(out[1], (S,), torch.int32, dev, "sorted_slot")
+    tpe = _out(out[2], (num_experts,), torch.int64, dev, "tokens_per_expert")
+    nbytes = moe_permute_workspace_size(T, top_k, num_experts)
+    ws, ws_bytes = _workspace(nbytes, dev, ws)
+    _check(library().moe_permute_index(_ptr(topk_ids), T, top_k, num_experts, _ptr(row_id_map),
+                                       _ptr(sorted_slot), _ptr(tpe), _ptr(ws), ws_bytes, _ptr(dev_err),
+                                       _stream(dev)), "moe_permute_index")
+    return row_id_map, sorted_slot, tpe
+
+
+def _gather_args(x, sorted_slot, top_k):
+    _dev(x, "x", torch.bfloat16)
+    _dev(sorted_slot, "sorted_slot", torch.int32)
+    if x.dim() != 2 or sorted_slot.dim() != 1:
+        raise MoeError("x must be [T, K] and sorted_slot [M_cap]")
+    return x.shape[0], x.shape[1], sorted_slot.shape[0], int(top_k)
+
+
+def gmm_fwd_gather(x, sorted_slot, top_k: int, w, group_list, *, out=None, ws=None, dev_err=None):
+    """gmm_fwd on the rows x[sorted_slot[r] // top_k] without a permuted copy
+    (x holds the token rows); y is [len(sorted_slot), N] in grouped row order."""
+    T, K, M, top_k = _gather_args(x, sorted_slot, top_k)
+    _dev(w, "w", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    E, K2, N = w.shape
+    if K2 != K or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: x [T, K], w [E, K, N], group_list [E]")
+    y = _out(out, (M, N), torch.bfloat16, x.device, "y")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N, OP_FWD), x.device, ws, zeroed=True)
+    _check(library().gmm_fwd_gather(_ptr(x), _ptr(sorted_slot), T, top_k, _ptr(w), _ptr(group_list), E,
+                                    M, K, N, _ptr(y), _ptr(ws), ws_bytes, _ptr(dev_err),
+                                    _stream(x.device)), "gmm_fwd_gather")
+    return y
+
+
+def gmm_fwd_swiglu_gather(x, sorted_slot, top_k: int, w1, group_list, *, out=None, h_out=None, ws=None,
+                          dev_err=None):
+    """gmm_fwd_swiglu on the rows x[sorted_slot[r] // top_k] without a
+    permuted copy; a is [len(sorted_slot), I] in grouped row order."""
+    T, K, M, top_k = _gather_args(x, sorted_slot, top_k)
+    _dev(w1, "w1", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    E, K2, N2 = w1.shape
+    if K2 != K or N2 % 2 or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: x [T, K], w1 [E, K, 2I], group_list [E]")
+    I = N2 // 2
+    a = _out(out, (M, I), torch.bfloat16, x.device, "a")
+    if h_out is not None:
+        _out(h_out, (M, N2), torch.bfloat16, x.device, "h_out")
+    ws, ws_bytes = _workspace(gmm_workspace_size(E, M, K, N2, OP_FWD), x.device, ws, zeroed=True)
+    _check(library().gmm_fwd_swiglu_gather(_ptr(x), _ptr(sorted_slot), T, top_k, _ptr(w1),
+                                           _ptr(group_list), E, M, K, I, _ptr(a), _ptr(h_out), _ptr(ws),
+                                           ws_bytes, _ptr(dev_err), _stream(x.device)),
+           "gmm_fwd_swiglu_gather")
+    return a
 
 
 def gmm_fwd(x, w, group_list, *, out=None, ws=None, dev_err=None):

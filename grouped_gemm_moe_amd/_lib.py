@@ -23,9 +23,13 @@ SIGNATURES = {
     "moe_permute_workspace_size": (_sz, [_i64, _i64, _i64]),
     "moe_permute": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_permute_noalloc": (_int, [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "moe_permute_index": (_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p, _p]),
     "gmm_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
     "gmm_fwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_fwd_swiglu": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
+    "gmm_fwd_gather": (_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
+    "gmm_fwd_swiglu_gather": (_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p,
+                                     _sz, _p, _p]),
     "gmm_bwd_input": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd_weight": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),
@@ -43,7 +47,7 @@ SIGNATURES = {
                                  _i64, _p, _p]),
 }
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _lib = None
 

@@ -75,6 +75,19 @@ moe_status check_gmm_common(const void* a, const void* b, const void* gl, const 
     return MOE_OK;
 }
 
+// The token-row arguments of the gathered forward calls: x [T, K] holds the
+// tokens, sorted_slot [M_cap] (M_cap <= T * top_k) the slot of each grouped
+// row.  Every byte offset into x must fit 31 bits: T * K < 2^30 elements.
+moe_status check_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T, int64_t top_k,
+                        int64_t M_cap, int64_t K) {
+    if (M_cap > 0 && (!x || !sorted_slot)) return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || T * top_k > kMaxRows || M_cap > T * top_k)
+        return MOE_ERR_INVALID;
+    if (K > 0 && T * K >= (int64_t(1) << 30)) return MOE_ERR_INVALID;
+    if (!aligned(sorted_slot, 4)) return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,7 +103,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 8; }
+int moegmm_abi_version(void) { return 9; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -149,6 +162,23 @@ moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64
                                                    static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_permute_index(const int32_t* topk_ids, int64_t T, int64_t top_k, int64_t E,
+                             int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                             void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
+    if (!ws || !tokens_per_expert) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_ids || !row_id_map || !sorted_slot)) return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || T * top_k > kMaxRows)
+        return MOE_ERR_INVALID;
+    if (!aligned(topk_ids, 4) || !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) ||
+        !aligned(tokens_per_expert, 8) || !aligned(ws, 4))
+        return MOE_ERR_INVALID;
+    if (ws_bytes < moegmm::permute_workspace_bytes(T * top_k, E)) return MOE_ERR_WORKSPACE;
+    // no x and no x_perm: the launcher runs the index kernels only
+    return from_hip(moegmm::launch_permute(nullptr, topk_ids, T, top_k, 8, E, nullptr, nullptr, nullptr,
+                                           0, row_id_map, sorted_slot, tokens_per_expert, ws, dev_err,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t gmm_workspace_size(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op) {
     return moegmm::gmm_workspace_bytes(E, M_cap, K, N, op);
 }
@@ -176,6 +206,43 @@ moe_status gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* 
     if (!aligned(h, 16)) return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_gmm_fwd_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, ws,
                                                   dev_err, static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_fwd_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T, int64_t top_k,
+                          const uint16_t* w, const int64_t* group_list, int64_t E, int64_t M_cap,
+                          int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
+                          int32_t* dev_err, void* stream) {
+    moe_status st = check_gather(x, sorted_slot, T, top_k, M_cap, K);
+    if (st != MOE_OK) return st;
+    st = check_gmm_common(x, w, group_list, y, E, M_cap, K, N,
+                          moegmm::gmm_workspace_bytes(E, M_cap, K, N, MOE_GMM_OP_FWD), ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    moegmm::GatherRows g;
+    g.slot = sorted_slot;
+    g.top_k = top_k;
+    g.nslots = T * top_k;
+    return from_hip(moegmm::launch_gmm_fwd(x, w, group_list, E, M_cap, K, N, y, ws, dev_err,
+                                           static_cast<hipStream_t>(stream), g));
+}
+
+moe_status gmm_fwd_swiglu_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T,
+                                 int64_t top_k, const uint16_t* w1, const int64_t* group_list,
+                                 int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
+                                 uint16_t* h, void* ws, size_t ws_bytes, int32_t* dev_err,
+                                 void* stream) {
+    if (!dim_ok(I)) return MOE_ERR_INVALID;
+    moe_status st = check_gather(x, sorted_slot, T, top_k, M_cap, K);
+    if (st != MOE_OK) return st;
+    st = check_gmm_common(x, w1, group_list, a, E, M_cap, K, 2 * I,
+                          moegmm::gmm_workspace_bytes(E, M_cap, K, 2 * I, MOE_GMM_OP_FWD), ws_bytes, ws);
+    if (st != MOE_OK) return st;
+    if (!aligned(h, 16)) return MOE_ERR_INVALID;
+    moegmm::GatherRows g;
+    g.slot = sorted_slot;
+    g.top_k = top_k;
+    g.nslots = T * top_k;
+    return from_hip(moegmm::launch_gmm_fwd_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, ws, dev_err,
+                                                  static_cast<hipStream_t>(stream), g));
 }
 
 moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,

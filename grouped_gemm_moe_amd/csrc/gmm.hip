@@ -46,11 +46,14 @@ constexpr int kQueueStride = 32;  // uint32 per slot
 constexpr int kQueueWords = 9 * kQueueStride;
 static_assert(kQueueWords * sizeof(uint32_t) == MOE_GMM_QUEUE_BYTES, "queue size in the header");
 
-template <int MODE>
+// GATHER (kFwd, kSwiGLU): A is the token matrix [nslots / top_k, K] and row r
+// of the grouped operand is token slot[r] / top_k (RowGather); a separate
+// instantiation, so the plain kernels carry none of it.
+template <int MODE, bool GATHER = false>
 __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
-    int32_t* dev_err) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr bool IS_DX = MODE == kDx;
     constexpr int kCols = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
@@ -59,6 +62,17 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     const int Ncols = IS_DX ? K : (MODE == kSwiGLU ? N / 2 : N);  // output columns
     const int Kred = IS_DX ? N : K;                                 // reduction length
     const int NT = (Ncols + kCols - 1) / kCols;
+    // the gather arguments pass through LDS so that they are read at each
+    // tile's start rather than held in scalar registers across its steps
+    __shared__ const int32_t* s_slot;
+    __shared__ int32_t* s_err;
+    __shared__ int s_gather[2];
+    if (GATHER && threadIdx.x == 0) {
+        s_slot = slot;
+        s_err = dev_err;
+        s_gather[0] = top_k;
+        s_gather[1] = nslots;
+    }
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
     const XcdRange xr = xcd_range(blockIdx.x & 7, ntiles);
@@ -70,21 +84,23 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
         const int64_t lda = IS_DX ? N : K;
         const bf16_t* We = W + (int64_t)e * K * N;
         const int cols_left = Ncols - n0;
+        const bf16_t* a_base = GATHER ? A : A + (int64_t)row0 * lda;
+        const RowGather ga{GATHER ? s_slot + row0 : nullptr, GATHER ? s_gather[0] : 1, GATHER ? s_gather[1] : 0,
+                           GATHER ? s_err : nullptr};
         if constexpr (MODE == kSwiGLU) {
             bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
             bf16_t* h = Hout ? Hout + (int64_t)row0 * N + n0 : nullptr;
             const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
             gemm_tile<kBM, kBN, kWM, kWN, true, false>(
-                A + (int64_t)row0 * lda, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid,
-                tile_cols, smem, [&](const auto& eng) {
-                    eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem);
-                });
+                a_base, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid, tile_cols, smem,
+                [&](const auto& eng) { eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem); },
+                ga);
         } else {
             bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
             gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
-                A + (int64_t)row0 * lda, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N,
-                cols_left, 0, Kred, rows_valid, cols_left, smem,
-                [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); });
+                a_base, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N, cols_left, 0, Kred,
+                rows_valid, cols_left, smem,
+                [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); }, ga);
         }
         __syncthreads();  // every wave is done with its epilogue image before the next tile's copies
     }
@@ -458,13 +474,18 @@ size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int o
 
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void*,
-                          int32_t* dev_err, hipStream_t stream) {
+                          int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
     if (M_cap == 0) return hipSuccess;
     if (gmm_stream_applies(E, M_cap, K))
-        return launch_gmm_stream(x, w, group_list, E, M_cap, K, N, y, dev_err, stream);
+        return launch_gmm_stream(x, w, group_list, E, M_cap, K, N, y, dev_err, stream, g);
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
-    hipLaunchKernelGGL(gmm_rows_kernel<kFwd>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
-                       group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err);
+    if (g.slot)
+        hipLaunchKernelGGL((gmm_rows_kernel<kFwd, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, x,
+                           w, group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err, g.slot,
+                           (int)g.top_k, (int)g.nslots);
+    else
+        hipLaunchKernelGGL(gmm_rows_kernel<kFwd>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, w,
+                           group_list, (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err, nullptr, 1, 0);
     return hipGetLastError();
 }
 
@@ -474,7 +495,7 @@ hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int
     if (M_cap == 0) return hipSuccess;
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
     hipLaunchKernelGGL(gmm_rows_kernel<kDx>, dim3((unsigned)grid), dim3(kThreads), 0, stream, dy, w,
-                       group_list, (int)E, M_cap, (int)K, (int)N, dx, nullptr, dev_err);
+                       group_list, (int)E, M_cap, (int)K, (int)N, dx, nullptr, dev_err, nullptr, 1, 0);
     return hipGetLastError();
 }
 
@@ -521,13 +542,19 @@ hipError_t launch_gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const ui
 
 hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
                                  int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
-                                 uint16_t* h, void*, int32_t* dev_err, hipStream_t stream) {
+                                 uint16_t* h, void*, int32_t* dev_err, hipStream_t stream,
+                                 const GatherRows& g) {
     if (M_cap == 0) return hipSuccess;
     if (gmm_stream_applies(E, M_cap, K))
-        return launch_gmm_stream_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, dev_err, stream);
+        return launch_gmm_stream_swiglu(x, w1, group_list, E, M_cap, K, I, a, h, dev_err, stream, g);
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_rows_kernel
-    hipLaunchKernelGGL(gmm_rows_kernel<kSwiGLU>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x,
-                       w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h, dev_err);
+    if (g.slot)
+        hipLaunchKernelGGL((gmm_rows_kernel<kSwiGLU, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           x, w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h, dev_err, g.slot,
+                           (int)g.top_k, (int)g.nslots);
+    else
+        hipLaunchKernelGGL(gmm_rows_kernel<kSwiGLU>, dim3((unsigned)grid), dim3(kThreads), 0, stream, x,
+                           w1, group_list, (int)E, M_cap, (int)K, (int)(2 * I), a, h, dev_err, nullptr, 1, 0);
     return hipGetLastError();
 }
 

@@ -88,6 +88,17 @@ MOE_DEVICE int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 
 MOE_DEVICE int swz_k(int o) { return BK == 64 ? ((o ^ (o >> 3)) & 7) : ((o >> 2) & 3); }
 MOE_DEVICE int swz_mn(int k) { return (k & 3) << 2; }         // [64][outer] tiles
 
+// Rows of a reduction-contiguous operand taken from a token matrix instead of
+// a permuted copy of it: tile row o is token slot[o] / top_k, where slot (the
+// permute's sorted_slot, advanced to the tile's first row) holds a slot index
+// in [0, nslots).  A row whose entry is outside that range loads zeros and
+// sets MOE_DEVERR_SLOT.  slot == nullptr: no gather.
+struct RowGather {
+    const int32_t* slot;
+    int top_k, nslots;
+    int32_t* dev_err;
+};
+
 // ---------------------------------------------------------------------------
 // HBM -> LDS copies of one operand tile per reduction step.  A wave
 // instruction moves 1 KiB: lane l's 16 bytes land at LDS byte 16*l of it, so
@@ -127,6 +138,32 @@ struct Dma<BO, true> {
             red[i] = c * 8;
             if (vo < outer_lim) ok_mask |= 1u << i;
         }
+    }
+    // Gathered rows (no pair): row o of the tile is token g.slot[o] / g.top_k
+    // of a token matrix with row stride ld, whose T * ld elements span less
+    // than 2^30, so every offset fits the 31-bit buffer range.
+    MOE_DEVICE void init_gather(int64_t ld, int outer_lim, const RowGather& g) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int o = (wid * kInst + i) * kRowsPerInst + lane / kCPR;
+            const int c = (lane % kCPR) ^ swz_k(o);
+            int tok = 0;
+            if (o < outer_lim) {
+                const int s = g.slot[o];
+                if (s >= 0 && s < g.nslots) {
+                    tok = s / g.top_k;
+                    ok_mask |= 1u << i;
+                } else {
+                    bad = true;
+                }
+            }
+            off[i] = (uint32_t)(((int64_t)tok * ld + c * 8) * 2);
+            red[i] = c * 8;
+        }
+        if (bad && g.dev_err) atomicOr(g.dev_err, MOE_DEVERR_SLOT);
     }
     // stage_base: element (0, s*BK); red_left: valid reduction length from there
     MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
@@ -601,14 +638,20 @@ struct Engine {
 template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Store>
 MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
                           int64_t ldb, int b_olim, int b_pair, int red_len, int rows_valid,
-                          int cols_valid, bf16_t* smem, const Store& store) {
+                          int cols_valid, bf16_t* smem, const Store& store,
+                          const RowGather& gather = RowGather{nullptr, 1, 0, nullptr}) {
     using DA = Dma<BM, A_KMAJOR>;
     using DB = Dma<BN, B_KMAJOR>;
     constexpr int kStage = (BM + BN) * BK;       // elements per stage
     constexpr int kPer = DA::kInst + DB::kInst;  // loads per wave per stage
     DA da;
     DB db;
-    da.init(lda, a_olim);
+    if constexpr (A_KMAJOR) {
+        if (gather.slot) da.init_gather(lda, a_olim, gather);
+        else da.init(lda, a_olim);
+    } else {
+        da.init(lda, a_olim);
+    }
     db.init(ldb, b_olim, b_pair);
     Engine<BM, BN, WM, WN, A_KMAJOR, B_KMAJOR> eng;
     eng.zero();

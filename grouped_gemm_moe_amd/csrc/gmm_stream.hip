@@ -98,11 +98,15 @@ MOE_DEVICE int sub_unit_starts(const int* s_cnt, int E, int NB, int* s_su, int64
 // c0 .. c0+127, the second the up columns I+c0 .. of the same outputs, and
 // the epilogue writes a = SiLU(G) * U for 128 output columns (and, when h is
 // given, G and U too).
+//
+// slot (nullable): X is the token matrix [nslots / top_k, K] and row r of the
+// grouped operand is token slot[r] / top_k; an entry outside [0, nslots)
+// stages a zero row and sets MOE_DEVERR_SLOT.
 template <bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
-    int32_t* dev_err) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr int kOutCols = SWIGLU ? kStreamCols / 2 : kStreamCols;  // output columns per sub-unit
     extern __shared__ __attribute__((aligned(16))) char dsmem[];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_su[kMaxExperts];
@@ -136,11 +140,25 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bool col_ok = ocol < Nout;
     const bf16_t* We = W + (int64_t)e * K * N + col;
 
+    // source row of each staged row (-1: zeros)
+    int src[kStreamRows];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kStreamRows; ++r) {
+        src[r] = r < rows ? off + r : -1;
+        if (slot && r < rows) {
+            const int s = slot[off + r];
+            const bool ok = s >= 0 && s < nslots;
+            src[r] = ok ? s / top_k : -1;
+            bad |= !ok;
+        }
+    }
+    if (bad && tid == 0 && dev_err) atomicOr(dev_err, MOE_DEVERR_SLOT);
     const int cpr = K / 8;
     for (int u = tid; u < kStreamRows * cpr; u += kThreads) {
         const int r = u / cpr, c = u % cpr;
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (r < rows) v = ld16(X + (int64_t)(off + r) * K + c * 8);
+        if (src[r] >= 0) v = ld16(X + (int64_t)src[r] * K + c * 8);
         *reinterpret_cast<u32x4_t*>(xs + r * K + c * 8) = v;
     }
     __syncthreads();
@@ -254,7 +272,7 @@ bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K) {
 
 static hipError_t launch_stream(bool swiglu, const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, uint16_t* h,
-                                int32_t* dev_err, hipStream_t stream) {
+                                int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
     const size_t shmem = (size_t)K * kStreamRows * 2;
     const int64_t blocks = max_sub_units(E, M_cap, N);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
@@ -262,24 +280,26 @@ static hipError_t launch_stream(bool swiglu, const uint16_t* x, const uint16_t* 
     const dim3 grid((unsigned)blocks);
     if (swiglu)
         hipLaunchKernelGGL(gmm_stream_kernel<true>, grid, dim3(kThreads), shmem, stream, x, w, group_list,
-                           (int)E, M_cap, (int)K, (int)N, y, h, dev_err);
+                           (int)E, M_cap, (int)K, (int)N, y, h, dev_err, g.slot, (int)g.top_k,
+                           (int)g.nslots);
     else
         hipLaunchKernelGGL(gmm_stream_kernel<false>, grid, dim3(kThreads), shmem, stream, x, w, group_list,
-                           (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err);
+                           (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err, g.slot, (int)g.top_k,
+                           (int)g.nslots);
     return hipGetLastError();
 }
 
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                              int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y,
-                             int32_t* dev_err, hipStream_t stream) {
-    return launch_stream(false, x, w, group_list, E, M_cap, K, N, y, nullptr, dev_err, stream);
+                             int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
+    return launch_stream(false, x, w, group_list, E, M_cap, K, N, y, nullptr, dev_err, stream, g);
 }
 
 hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,
                                     const int64_t* group_list, int64_t E, int64_t M_cap,
                                     int64_t K, int64_t I, uint16_t* a, uint16_t* h,
-                                    int32_t* dev_err, hipStream_t stream) {
-    return launch_stream(true, x, w1, group_list, E, M_cap, K, 2 * I, a, h, dev_err, stream);
+                                    int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
+    return launch_stream(true, x, w1, group_list, E, M_cap, K, 2 * I, a, h, dev_err, stream, g);
 }
 
 }  // namespace moegmm

@@ -30,10 +30,20 @@ hipError_t launch_permute_noalloc(const uint16_t* x, const int32_t* ids, int64_t
 // Compute units of the current device (cached per device; 256 if the query fails).
 int num_cus();
 
+// Forward GMM operand rows gathered from token rows: with slot given, x is the
+// token matrix [nslots / top_k, K] and row r of the grouped operand is token
+// slot[r] / top_k (slot entries in [0, nslots), else zeros and
+// MOE_DEVERR_SLOT).  slot == nullptr: x is the grouped operand itself.
+struct GatherRows {
+    const int32_t* slot = nullptr;
+    int64_t top_k = 1;
+    int64_t nslots = 0;
+};
+
 size_t gmm_workspace_bytes(int64_t E, int64_t M_cap, int64_t K, int64_t N, int op);
 hipError_t launch_gmm_fwd(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                           int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, void* ws,
-                          int32_t* dev_err, hipStream_t stream);
+                          int32_t* dev_err, hipStream_t stream, const GatherRows& g = GatherRows{});
 hipError_t launch_gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx,
                                 void* ws, int32_t* dev_err, hipStream_t stream);
@@ -54,7 +64,8 @@ hipError_t launch_gmm_bwd_swiglu(const uint16_t* x, const uint16_t* dy, const ui
 
 hipError_t launch_gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* group_list,
                                  int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
-                                 uint16_t* h, void* ws, int32_t* dev_err, hipStream_t stream);
+                                 uint16_t* h, void* ws, int32_t* dev_err, hipStream_t stream,
+                                 const GatherRows& g = GatherRows{});
 
 // Test-only kernel choice for the forward GMMs, from the environment
 // variable MOEGMM_FORCE_VARIANT, read at every call: "tile" runs the
@@ -68,11 +79,11 @@ GmmVariant forced_gmm_variant();
 bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K);
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                              int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y,
-                             int32_t* dev_err, hipStream_t stream);
+                             int32_t* dev_err, hipStream_t stream, const GatherRows& g);
 hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,
                                     const int64_t* group_list, int64_t E, int64_t M_cap,
                                     int64_t K, int64_t I, uint16_t* a, uint16_t* h,
-                                    int32_t* dev_err, hipStream_t stream);
+                                    int32_t* dev_err, hipStream_t stream, const GatherRows& g);
 
 // gmm_mx.hip (MXFP8)
 hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,

@@ -579,7 +579,7 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int6
                                    ids, S, (int)E, chunk, blk, seg, row_id_map, sorted_slot);
         }
     }
-    if (nblk > 0) {
+    if (nblk > 0 && (xq || x_perm)) {  // neither: the index kernels only
         const int tpb = gather_tokens_per_block(T, top_k);
         const int64_t gblk = (T + tpb - 1) / tpb;
         if (xq)

@@ -3,7 +3,11 @@
 Forward ("NPU Training Operators - GMM", section "Qwen3.5 MoE 路径"):
     moe_permute -> gmm_fwd(W1) -> swiglu -> gmm_fwd(W2) -> moe_unpermute
 or, fused, moe_permute -> gmm_fwd_swiglu(W1) -> gmm_fwd(W2) -> moe_unpermute
-(H written only when a backward will need it)
+(H written only when a backward will need it).  A forward-only layer can
+also skip the permuted copy of x (gather_rows=True; "MegaMoE", 功能说明:
+dispatch fused with the first linear layer): moe_permute_index computes the
+maps only and the gate_up GMM reads token rows through sorted_slot
+(gmm_fwd_gather / gmm_fwd_swiglu_gather), with bit-identical results.
 Backward of the expert block, from the gradient dYp at the down-GMM output
 (permuted row order):
     dA = gmm_bwd_input(dYp, W2); dW2 = gmm_bwd_weight(A, dYp);
@@ -39,10 +43,10 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_swiglu, gmm_mx_fwd, gmm_mx_fwd_swiglu,
-               gmm_workspace_size, moe_permute, moe_permute_bwd, moe_permute_mx,
-               moe_permute_workspace_size, moe_unpermute, moe_unpermute_bwd, mx_quantize, mx_scale_ld,
-               swiglu, swiglu_bwd)
+from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_gather, gmm_fwd_swiglu,
+               gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_workspace_size, moe_permute,
+               moe_permute_bwd, moe_permute_index, moe_permute_mx, moe_permute_workspace_size, moe_unpermute,
+               moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd)
 
 
 @dataclass
@@ -63,9 +67,15 @@ class MoeLayer:
     current torch stream and never synchronise."""
 
     def __init__(self, shape: LayerShape, device, with_backward: bool = False,
-                 low_memory: bool = False, fuse_swiglu_bwd: bool = True):
+                 low_memory: bool = False, fuse_swiglu_bwd: bool = True, gather_rows: bool = False):
         s = shape
         self.shape = s
+        # forward only: the gate_up GMM reads token rows through sorted_slot
+        # and no permuted copy of x is made (the W1 gradient would need one)
+        self.gather_rows = bool(gather_rows)
+        if self.gather_rows and with_backward:
+            raise ValueError("gather_rows is forward-only: the W1 weight gradient reads X_perm")
+        self.x_tokens = None
         self.low_memory = bool(low_memory and with_backward)
         # dH straight from the down GMM's backward (gmm_bwd_swiglu): dA is
         # neither rounded nor stored, and no separate swiglu_bwd runs
@@ -73,7 +83,7 @@ class MoeLayer:
         d = device
         bf = torch.bfloat16
         S = s.S
-        self.x_perm = torch.empty((S, s.H), dtype=bf, device=d)
+        self.x_perm = None if self.gather_rows else torch.empty((S, s.H), dtype=bf, device=d)
         self.row_id_map = torch.empty(S, dtype=torch.int32, device=d)
         self.sorted_slot = torch.empty(S, dtype=torch.int32, device=d)
         self.tokens_per_expert = torch.empty(s.E, dtype=torch.int64, device=d)
@@ -107,8 +117,29 @@ class MoeLayer:
 
     # -- forward ---------------------------------------------------------
     def permute(self, x, topk_ids):
+        if self.gather_rows:
+            self.x_tokens = x
+            moe_permute_index(topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
+                              out=(self.row_id_map, self.sorted_slot, self.tokens_per_expert))
+            return
         moe_permute(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
                     out=(self.x_perm, self.row_id_map, self.sorted_slot, self.tokens_per_expert))
+
+    def gate_up(self, w1, fused, keep_h=True):
+        """The gate_up GMM of the rows permute() grouped: A (and H when
+        keep_h) if fused, else H only."""
+        g, ws, err = self.tokens_per_expert, self.ws_gmm, self.dev_err
+        h = self.h if keep_h else None
+        if self.gather_rows:
+            x, slot, k = self.x_tokens, self.sorted_slot, self.shape.top_k
+            if fused:
+                gmm_fwd_swiglu_gather(x, slot, k, w1, g, out=self.a, h_out=h, ws=ws, dev_err=err)
+            else:
+                gmm_fwd_gather(x, slot, k, w1, g, out=self.h, ws=ws, dev_err=err)
+        elif fused:
+            gmm_fwd_swiglu(self.x_perm, w1, g, out=self.a, h_out=h, ws=ws, dev_err=err)
+        else:
+            gmm_fwd(self.x_perm, w1, g, out=self.h, ws=ws, dev_err=err)
 
     def use_fused(self, fused) -> bool:
         """fused="auto": the fused gate_up + SwiGLU call unless the shape is
@@ -124,10 +155,9 @@ class MoeLayer:
         swiglu -> A.  fused may be "auto" (see use_fused)."""
         g = self.tokens_per_expert
         if self.use_fused(fused):
-            gmm_fwd_swiglu(self.x_perm, w1, g, out=self.a, h_out=self.h if keep_h else None,
-                           ws=self.ws_gmm, dev_err=self.dev_err)
+            self.gate_up(w1, True, keep_h)
         else:
-            gmm_fwd(self.x_perm, w1, g, out=self.h, ws=self.ws_gmm, dev_err=self.dev_err)
+            self.gate_up(w1, False)
             swiglu(self.h, g, out=self.a)
         gmm_fwd(self.a, w2, g, out=self.yp, ws=self.ws_gmm, dev_err=self.dev_err)
 

@@ -83,6 +83,8 @@ typedef enum {
 #define MOE_DEVERR_EXPERT_ID 1  /* an expert id outside [-1, E)               */
 #define MOE_DEVERR_GROUP_LIST 2 /* a negative count, or sum(group_list) > M_cap */
 #define MOE_DEVERR_ROW_MAP 4    /* a row_id_map entry outside [-1, T*top_k)   */
+#define MOE_DEVERR_SLOT 8       /* a sorted_slot entry outside [0, T*top_k) for
+                                   a row below sum(group_list) (gathered GMMs) */
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status s);
@@ -139,6 +141,18 @@ moe_status moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64
                                int64_t H, int64_t E, uint16_t* x_perm, int32_t* row_id_map,
                                int32_t* sorted_slot, int64_t* tokens_per_expert, int32_t* dev_err,
                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_index -- moe_permute without the row gather: the histogram,
+ * the stable ranks and the maps only, for a forward that reads the token rows
+ * through gmm_fwd_gather / gmm_fwd_swiglu_gather instead of a permuted copy.
+ * Same citations, ordering, workspace (moe_permute_workspace_size) and
+ * errors as moe_permute; row_id_map, sorted_slot and tokens_per_expert come
+ * out bit-identical to moe_permute's.  x and x_perm do not exist here.
+ * ---------------------------------------------------------------------- */
+moe_status moe_permute_index(const int32_t* topk_ids, int64_t T, int64_t top_k, int64_t E,
+                             int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                             void* ws, size_t ws_bytes, int32_t* dev_err, void* stream);
 
 /* ------------------------------------------------------------------------
  * gmm_fwd -- grouped matmul  y[off_e + i, :] = x[off_e + i, :] @ w[e]  for
@@ -198,6 +212,37 @@ moe_status gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* 
                           int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
                           uint16_t* h, void* ws, size_t ws_bytes, int32_t* dev_err,
                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * gmm_fwd_gather / gmm_fwd_swiglu_gather -- gmm_fwd / gmm_fwd_swiglu whose
+ * grouped operand is read straight from the token rows instead of from a
+ * permuted copy: grouped row r is x[sorted_slot[r] / top_k].  The dispatch
+ * (token rows stacked per expert) is fused into the first matmul's operand
+ * loads.  [MegaMoE] 功能说明 (dispatch, the first linear layer, activation,
+ * second linear layer and combine as one operator) and A16W16 Dispatch (X_e
+ * stacks the rows x_i of the tokens routed to expert e); the product itself
+ * is gmm_fwd's ([GMM] 算子语义).
+ *
+ *   x           [T, K] bf16       token rows (moe_permute's x)
+ *   sorted_slot [M_cap] int32     row -> slot, from moe_permute or
+ *                                 moe_permute_index over the same ids
+ *   T, top_k                      as given to the permute; M_cap <= T*top_k
+ *   w, group_list, E, K, N, y / w1, I, a, h, ws: as gmm_fwd / gmm_fwd_swiglu.
+ * Outputs are bit-identical to gmm_fwd(_swiglu) on moe_permute's x_perm.
+ * Entries of sorted_slot for rows r < sum(group_list) must lie in
+ * [0, T*top_k); others read a zero row and set MOE_DEVERR_SLOT.  Rows at or
+ * past sum(group_list) are not read.  Limit: T*K < 2^30 (x spans less than
+ * 2 GiB), else MOE_ERR_INVALID.
+ * ---------------------------------------------------------------------- */
+moe_status gmm_fwd_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T, int64_t top_k,
+                          const uint16_t* w, const int64_t* group_list, int64_t E, int64_t M_cap,
+                          int64_t K, int64_t N, uint16_t* y, void* ws, size_t ws_bytes,
+                          int32_t* dev_err, void* stream);
+moe_status gmm_fwd_swiglu_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T,
+                                 int64_t top_k, const uint16_t* w1, const int64_t* group_list,
+                                 int64_t E, int64_t M_cap, int64_t K, int64_t I, uint16_t* a,
+                                 uint16_t* h, void* ws, size_t ws_bytes, int32_t* dev_err,
+                                 void* stream);
 
 /* ------------------------------------------------------------------------
  * gmm_bwd_input -- dx[off_e + i, :] = dy[off_e + i, :] @ w[e]^T.

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     for n in ["moe_permute", "moe_permute_workspace_size", "gmm_fwd", "gmm_fwd_swiglu", "gmm_bwd_input",
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
-              "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu"]:
+              "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu",
+              "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather"]:
         assert n in names, n
 
 
@@ -274,3 +275,43 @@ def test_mx_calls_reject_bad_arguments(lib):
     assert p(H=2056) == MOE_ERR_INVALID  # H % 32
     assert p(ld=48) == MOE_ERR_INVALID   # ld < H/32
     assert p(wsb=need - 1) == MOE_ERR_WORKSPACE
+
+
+def test_gathered_calls_reject_bad_arguments(lib):
+    """moe_permute_index and the gathered forward GMMs validate their token
+    arguments on the host: nulls, top_k, M_cap beyond T*top_k, a token matrix
+    of 2^30 or more elements (byte offsets must fit 31 bits), misalignment,
+    a short permute workspace."""
+    ws = ctypes.c_void_p(0x40000)
+    S4 = ctypes.c_void_p(0x50000)  # sorted_slot (int32)
+    # gmm_fwd_gather(x, sorted_slot, T, top_k, w, group_list, E, M_cap, K, N, y, ws, ws_bytes, err, stream)
+    g = lambda x_=A16, s_=S4, T=16, k=4, M=64, K=64, y_=A16c: lib.gmm_fwd_gather(  # noqa: E731
+        x_, s_, T, k, A16b, A16, 4, M, K, 64, y_, ws, 0, None, None)
+    assert g(x_=None) == MOE_ERR_NULL
+    assert g(s_=None) == MOE_ERR_NULL
+    assert g(y_=None) == MOE_ERR_NULL
+    assert g(k=0) == MOE_ERR_INVALID
+    assert g(k=33) == MOE_ERR_INVALID
+    assert g(T=-1) == MOE_ERR_INVALID
+    assert g(M=65) == MOE_ERR_INVALID            # more grouped rows than slots
+    assert g(T=1 << 17, M=64, K=8192) == MOE_ERR_INVALID  # T*K == 2^30
+    assert g(x_=MIS) == MOE_ERR_INVALID
+    assert g(s_=ctypes.c_void_p(0x50002)) == MOE_ERR_INVALID
+    # gmm_fwd_swiglu_gather(x, sorted_slot, T, top_k, w1, group_list, E, M_cap, K, I, a, h, ws, ws_bytes, ...)
+    gs = lambda I=32, h_=None, k=4: lib.gmm_fwd_swiglu_gather(  # noqa: E731
+        A16, S4, 16, k, A16b, A16, 4, 64, 64, I, A16c, h_, ws, 0, None, None)
+    assert gs(I=30) == MOE_ERR_INVALID
+    assert gs(h_=MIS) == MOE_ERR_INVALID
+    assert gs(k=0) == MOE_ERR_INVALID
+    # moe_permute_index(ids, T, top_k, E, row_id_map, sorted_slot, tpe, ws, ws_bytes, err, stream)
+    need = lib.moe_permute_workspace_size(64, 8, 128)
+    pi = lambda ids=A16, rm=A16b, ss=A16c, tpe=S4, w=ws, n=need, T=64, k=8, E=128: lib.moe_permute_index(  # noqa: E731
+        ids, T, k, E, rm, ss, tpe, w, n, None, None)
+    assert pi(w=None) == MOE_ERR_NULL
+    assert pi(tpe=None) == MOE_ERR_NULL
+    assert pi(ids=None) == MOE_ERR_NULL
+    assert pi(ss=None) == MOE_ERR_NULL
+    assert pi(n=need - 1) == MOE_ERR_WORKSPACE
+    assert pi(E=0) == MOE_ERR_INVALID
+    assert pi(k=33) == MOE_ERR_INVALID
+    assert pi(tpe=ctypes.c_void_p(0x50004)) == MOE_ERR_INVALID

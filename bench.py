@@ -530,24 +530,28 @@ def mx_weights(torch, dev, wl):
     return MoeLayerMX.prepare_weights(bf16_dev(torch, wl["w1"], dev), bf16_dev(torch, wl["w2"], dev))
 
 
-def mx_layer_bytes(gl, T, K, H, I):
+def mx_layer_bytes(gl, T, K, H, I, gathered=False):
     """Algorithmic bytes of one A8W8-FP layer forward: MX weights (codes and
     one scale byte per 32) of experts with rows, once; x read; the MX
-    activations (xq/xs, aq/as) and Yp written once and read once; out
-    written; indices."""
+    activations (xq/xs of every slot row -- or of the T token rows when GMM1
+    gathers them --, aq/as) and Yp written once and read once; out written;
+    indices."""
     n_active = int(np.sum(np.asarray(gl) > 0))
     S = int(np.sum(gl))
     mx = 1.0 + 1.0 / 32
     w = n_active * (H * 2 * I + I * H) * mx
-    act = (T * H * 2 + S * H * mx * 2 + S * I * mx * 2 + S * H * 2 * 2 + T * H * 2)
+    xrows = T if gathered else S
+    act = (T * H * 2 + xrows * H * mx * 2 + S * I * mx * 2 + S * H * 2 * 2 + T * H * 2)
     idx = T * K * 4 * 3 + T * K * 4 + len(gl) * 8
     return int(w + act + idx), n_active
 
 
-def mx_layer_forward(torch, dev, wl, steps):
-    """Time permute_mx -> gmm_mx_fwd_swiglu -> gmm_mx_fwd -> unpermute."""
-    from grouped_gemm_moe_amd import (gmm_mx_fwd, gmm_mx_fwd_swiglu, moe_permute_mx,
-                                      moe_unpermute)
+def mx_layer_forward(torch, dev, wl, steps, gather=False):
+    """Time permute_mx -> gmm_mx_fwd_swiglu -> gmm_mx_fwd -> unpermute, or
+    with gather: mx_quantize of the token rows -> moe_permute_index ->
+    gmm_mx_fwd_swiglu_gather -> gmm_mx_fwd -> unpermute."""
+    from grouped_gemm_moe_amd import (gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
+                                      moe_permute_index, moe_permute_mx, moe_unpermute, mx_quantize)
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
 
     d = wl.dims
@@ -556,16 +560,23 @@ def mx_layer_forward(torch, dev, wl, steps):
     x = bf16_dev(torch, wl["x"], dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     probs = torch.from_numpy(wl["probs"]).to(dev)
-    L = MoeLayerMX(LayerShape(T, K, E, H, I), dev)
+    L = MoeLayerMX(LayerShape(T, K, E, H, I), dev, gather_rows=gather)
     g, err = L.tokens_per_expert, L.dev_err
     timer = KernelTimer(torch)
 
     def step(t):
-        t("moe_permute_mx", lambda: moe_permute_mx(x, ids, E, out=(L.xq, L.xs, L.row_id_map,
-                                                                  L.sorted_slot, g),
-                                                   ws=L.ws_perm, dev_err=err))
-        t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu(L.xq, L.xs, w1q, w1s, g, out=(L.aq, L.as_),
-                                                         dev_err=err))
+        if gather:
+            t("mx_quantize", lambda: mx_quantize(x, out=(L.xq, L.xs)))
+            t("moe_permute_index", lambda: moe_permute_index(ids, E, out=(L.row_id_map, L.sorted_slot, g),
+                                                             ws=L.ws_perm, dev_err=err))
+            t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu_gather(L.xq, L.xs, L.sorted_slot, K, w1q, w1s, g,
+                                                                    out=(L.aq, L.as_), dev_err=err))
+        else:
+            t("moe_permute_mx", lambda: moe_permute_mx(x, ids, E, out=(L.xq, L.xs, L.row_id_map,
+                                                                      L.sorted_slot, g),
+                                                       ws=L.ws_perm, dev_err=err))
+            t("gmm_mx_fwd_swiglu", lambda: gmm_mx_fwd_swiglu(L.xq, L.xs, w1q, w1s, g, out=(L.aq, L.as_),
+                                                             dev_err=err))
         t("gmm_mx_fwd_down", lambda: gmm_mx_fwd(L.aq, L.as_, w2q, w2s, g, out=L.yp, dev_err=err))
         t("moe_unpermute", lambda: moe_unpermute(L.yp, L.row_id_map, probs, out=L.out, dev_err=err))
 
@@ -623,8 +634,17 @@ def run_mx(torch, dev, args):
                                    "gmm_mx_fwd_down": round(wbytes2 / g2 / 1e9, 1)},
             per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
         )
+        # the same layer with GMM1 gathering the quantised token rows (no
+        # per-slot copy): its time and its fraction of its own roofline
+        ms_g, per_g, gl_g, spans_g = mx_layer_forward(torch, dev, wl, steps, gather=True)
+        nbytes_g, _ = mx_layer_bytes(gl_g, T, K, H, I, gathered=True)
+        roof_g = max(nbytes_g / (HBM_PEAK_GBS * 1e9), t_mfma) * 1e3
+        res[name]["gathered"] = dict(ms_per_layer=round(ms_g, 4), layer_ms_events=spans_g,
+                                     gb_per_s=round(nbytes_g / (ms_g * 1e-3) / 1e9, 1), bytes_per_layer=nbytes_g,
+                                     roofline_ms=round(roof_g, 4), frac_of_attainable=round(roof_g / ms_g, 4),
+                                     per_call_us={k: round(v * 1e3, 2) for k, v in per_g.items()})
         log(f"mx {name}: {ms:.4f} ms/layer; {res[name]['gb_per_s']} GB/s; {res[name]['tflops']} TFLOP/s; "
-            f"per call {res[name]['per_call_us']}")
+            f"per call {res[name]['per_call_us']}; gathered {ms_g:.4f} ms/layer")
         del wl
         torch.cuda.empty_cache()
     res["workload"] = ("A8W8-FP (MXFP8) forward: permute_mx (gather + MX quantisation) -> gate_up GMM "

@@ -29,7 +29,7 @@ __all__ = [
     "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
-    "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu",
+    "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_mx_fwd_swiglu_gather",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP", "DEVERR_SLOT",
 ]
 
@@ -524,4 +524,32 @@ def gmm_mx_fwd_swiglu(xq, xs, w1q, w1s, group_list, *, out=None, dev_err=None):
     _check(library().gmm_mx_fwd_swiglu(_ptr(xq), _ptr(xs), ld_x, _ptr(w1q), _ptr(w1s), ld_w,
                                        _ptr(group_list), E, M, K, I, _ptr(aq), _ptr(asc), ld_a,
                                        _ptr(dev_err), _stream(xq.device)), "gmm_mx_fwd_swiglu")
+    return aq, asc
+
+
+def gmm_mx_fwd_swiglu_gather(xq, xs, sorted_slot, top_k: int, w1q, w1s, group_list, *, out=None,
+                             dev_err=None):
+    """gmm_mx_fwd_swiglu on the token rows (xq, xs) [T, ...] read through
+    sorted_slot (grouped row r = token sorted_slot[r] // top_k); returns
+    (aq [M, I], as [M, mx_scale_ld(I)]) with M = len(sorted_slot)."""
+    K, ld_x = _mx_pair(xq, xs, "x")
+    K2, ld_w = _mx_pair(w1q, w1s, "w1")
+    _dev(sorted_slot, "sorted_slot", torch.int32)
+    _dev(group_list, "group_list", torch.int64)
+    if sorted_slot.dim() != 1:
+        raise MoeError("sorted_slot must be [M_cap]")
+    T, M = xq.shape[0], sorted_slot.shape[0]
+    E, N2, _ = w1q.shape
+    if K2 != K or group_list.shape[0] != E or N2 % 2:
+        raise MoeError("shape mismatch: x [T, K], w1 [E, 2I, K], group_list [E]")
+    I = N2 // 2
+    ld_a = mx_scale_ld(I)
+    if out is None:
+        out = (None, None)
+    aq = _out(out[0], (M, I), torch.uint8, xq.device, "aq")
+    asc = _out(out[1], (M, ld_a), torch.uint8, xq.device, "as")
+    _check(library().gmm_mx_fwd_swiglu_gather(_ptr(xq), _ptr(xs), ld_x, _ptr(sorted_slot), T, int(top_k),
+                                              _ptr(w1q), _ptr(w1s), ld_w, _ptr(group_list), E, M, K, I,
+                                              _ptr(aq), _ptr(asc), ld_a, _ptr(dev_err), _stream(xq.device)),
+           "gmm_mx_fwd_swiglu_gather")
     return aq, asc

@@ -45,6 +45,8 @@ SIGNATURES = {
     "gmm_mx_fwd": (_int, [_p, _p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p, _p]),
     "gmm_mx_fwd_swiglu": (_int, [_p, _p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _p,
                                  _i64, _p, _p]),
+    "gmm_mx_fwd_swiglu_gather": (_int, [_p, _p, _i64, _p, _i64, _i64, _p, _p, _i64, _p, _i64, _i64, _i64,
+                                        _i64, _p, _p, _i64, _p, _p]),
 }
 
 ABI_VERSION = 9

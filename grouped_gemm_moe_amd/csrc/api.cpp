@@ -78,7 +78,7 @@ moe_status check_gmm_common(const void* a, const void* b, const void* gl, const 
 // The token-row arguments of the gathered forward calls: x [T, K] holds the
 // tokens, sorted_slot [M_cap] (M_cap <= T * top_k) the slot of each grouped
 // row.  Every byte offset into x must fit 31 bits: T * K < 2^30 elements.
-moe_status check_gather(const uint16_t* x, const int32_t* sorted_slot, int64_t T, int64_t top_k,
+moe_status check_gather(const void* x, const int32_t* sorted_slot, int64_t T, int64_t top_k,
                         int64_t M_cap, int64_t K) {
     if (M_cap > 0 && (!x || !sorted_slot)) return MOE_ERR_NULL;
     if (T < 0 || top_k < 1 || top_k > kMaxTopK || T * top_k > kMaxRows || M_cap > T * top_k)
@@ -429,6 +429,30 @@ moe_status gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
     return from_hip(moegmm::launch_gmm_mx_fwd_swiglu(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list,
                                                      E, M_cap, K, I, aq, as, ld_as, dev_err,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status gmm_mx_fwd_swiglu_gather(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                                    const int32_t* sorted_slot, int64_t T, int64_t top_k,
+                                    const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                                    const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                                    int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                                    int32_t* dev_err, void* stream) {
+    if (!dim_ok(I) || I % 32 != 0 || !mx_ld_ok(ld_as, I)) return MOE_ERR_INVALID;
+    moe_status st = check_gather(xq, sorted_slot, T, top_k, M_cap, K);
+    if (st != MOE_OK) return st;
+    // the token rows' sizes (T rows) are bounded by the gather's T * K < 2^30
+    st = check_gmm_mx(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, E, M_cap, K, 2 * I);
+    if (st != MOE_OK) return st;
+    if (M_cap > 0 && (!aq || !as)) return MOE_ERR_NULL;
+    if (!aligned(aq, 16) || !aligned(as, 16) || M_cap * ld_as > (int64_t(1) << 40))
+        return MOE_ERR_INVALID;
+    moegmm::GatherRows g;
+    g.slot = sorted_slot;
+    g.top_k = top_k;
+    g.nslots = T * top_k;
+    return from_hip(moegmm::launch_gmm_mx_fwd_swiglu(xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list,
+                                                     E, M_cap, K, I, aq, as, ld_as, dev_err,
+                                                     static_cast<hipStream_t>(stream), g));
 }
 
 }  // extern "C"

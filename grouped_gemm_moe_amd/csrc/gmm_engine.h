@@ -75,8 +75,11 @@ MOE_DEVICE __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 
 // Non-temporal 16-byte store of lane data to base + byte offset `off`
 // (base wave-uniform); an offset of kOOB drops the lane's store.
+#ifndef MOEGMM_STORE_AUX
+#define MOEGMM_STORE_AUX 2  // cache policy bits of the epilogue stores: nt
+#endif
 MOE_DEVICE void store_nt16(u32x4_t v, const void* base, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(base), off, 0, 2 /* nt */);
+    __builtin_amdgcn_raw_buffer_store_b128(v, make_rsrc(base), off, 0, MOEGMM_STORE_AUX);
 }
 
 // Wave index as a scalar (the LDS-DMA destination must be wave-uniform).

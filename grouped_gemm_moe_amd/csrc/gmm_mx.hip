@@ -52,11 +52,19 @@ struct ScaleDma {
     uint32_t off;
     bool ok;
 
-    MOE_DEVICE void init(int64_t ld_a, int a_olim, int64_t ld_b, int b_olim, int b_pair) {
+    // gather.slot: A row t is token gather.slot[t] / top_k (RowGather; the
+    // code DMA reports bad entries, this one just loads no scales for them)
+    MOE_DEVICE void init(int64_t ld_a, int a_olim, int64_t ld_b, int b_olim, int b_pair,
+                         const RowGather& gather) {
         const int t = threadIdx.x;
         if (t < kBM) {
             off = (uint32_t)(t * ld_a);
             ok = t < a_olim;
+            if (gather.slot && ok) {
+                const int sl = gather.slot[t];
+                ok = sl >= 0 && sl < gather.nslots;
+                off = ok ? (uint32_t)((int64_t)(sl / gather.top_k) * ld_a) : 0u;
+            }
         } else {
             const int o = t - kBM;
             int vo = o, go = o;
@@ -227,7 +235,8 @@ template <int BM, int BN, int WM, int WN, class Store>
 MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a_sc, int64_t ld_as,
                              const uint8_t* b_base, int b_olim, int b_pair, const uint8_t* b_sc,
                              int64_t ld_bs, int K, int rows_valid, int cols_valid, bf16_t* smem,
-                             uint8_t* ssc, const Store& store) {
+                             uint8_t* ssc, const Store& store,
+                             const RowGather& gather = RowGather{nullptr, 1, 0, nullptr}) {
     using DA = Dma<BM, true>;
     using DB = Dma<BN, true>;
     constexpr int kStage = (BM + BN) * BK;
@@ -240,9 +249,10 @@ MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a
     DA da;
     DB db;
     ScaleDma sd;
-    da.init(ld16, a_olim);
+    if (gather.slot) da.init_gather(ld16, a_olim, gather);
+    else da.init(ld16, a_olim);
     db.init(ld16, b_olim, b_pair);
-    sd.init(ld_as, a_olim, ld_bs, b_olim, b_pair);
+    sd.init(ld_as, a_olim, ld_bs, b_olim, b_pair, gather);
     EngineMx<BM, BN, WM, WN> eng;
     eng.zero();
     const int nk = (red + BK - 1) / BK;
@@ -313,13 +323,15 @@ MOE_DEVICE void gemm_tile_mx(const uint8_t* a_base, int a_olim, const uint8_t* a
 //   SWIGLU true:  N = 2I weight rows; a tile covers kBN/2 output columns c,
 //                 reading gate rows c and up rows I + c; writes (aq, as).
 // ---------------------------------------------------------------------------
-template <bool SWIGLU>
+//   GATHER:      X / XS hold token rows and grouped row r is token
+//                slot[r] / top_k (RowGather), as in gmm_rows_kernel.
+template <bool SWIGLU, bool GATHER = false>
 __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, int64_t ld_xs,
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ WS, int64_t ld_ws,
     const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
     bf16_t* __restrict__ Y, uint8_t* __restrict__ AQ, uint8_t* __restrict__ AS, int64_t ld_as,
-    int32_t* dev_err) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr int kCols = SWIGLU ? kBN / 2 : kBN;  // output columns per tile
     __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
     __shared__ __attribute__((aligned(16))) uint8_t ssc[2 * kScaleSlot];
@@ -327,6 +339,16 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_tst[kMaxExperts];
     const int Ncols = SWIGLU ? N / 2 : N;
     const int NT = (Ncols + kCols - 1) / kCols;
+    // gather arguments through LDS, read at each tile's start (see gmm_rows_kernel)
+    __shared__ const int32_t* s_slot;
+    __shared__ int32_t* s_err;
+    __shared__ int s_gather[2];
+    if (GATHER && threadIdx.x == 0) {
+        s_slot = slot;
+        s_err = dev_err;
+        s_gather[0] = top_k;
+        s_gather[1] = nslots;
+    }
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
     const XcdRange xr = xcd_range(blockIdx.x & 7, ntiles);
@@ -337,8 +359,10 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
         const int cols_left = Ncols - n0;
         const uint8_t* We = W + ((int64_t)e * N + n0) * K;
         const uint8_t* Se = WS + ((int64_t)e * N + n0) * ld_ws;
-        const uint8_t* Xt = X + (int64_t)row0 * K;
-        const uint8_t* XSt = XS + (int64_t)row0 * ld_xs;
+        const uint8_t* Xt = GATHER ? X : X + (int64_t)row0 * K;
+        const uint8_t* XSt = GATHER ? XS : XS + (int64_t)row0 * ld_xs;
+        const RowGather ga{GATHER ? s_slot + row0 : nullptr, GATHER ? s_gather[0] : 1, GATHER ? s_gather[1] : 0,
+                           GATHER ? s_err : nullptr};
         if constexpr (SWIGLU) {
             const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
             gemm_tile_mx<kBM, kBN, kWM, kWN>(
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_mx_rows_kernel(
                     eng.store_swiglu_mx(AQ + (int64_t)row0 * Ncols + n0, Ncols,
                                         AS + (int64_t)row0 * ld_as, ld_as, n0 / kMxGroup, rows_valid,
                                         cols_left);
-                });
+                }, ga);
         } else {
             bf16_t* y = Y + (int64_t)row0 * N + n0;
             gemm_tile_mx<kBM, kBN, kWM, kWN>(
@@ -396,13 +420,15 @@ struct ScaleBatch {
     }
 };
 
-template <bool SWIGLU>
+// GATHER: X / XS hold token rows; grouped row r is token slot[r] / top_k
+// (a bad entry loads a zero row and sets MOE_DEVERR_SLOT).
+template <bool SWIGLU, bool GATHER = false>
 __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, int64_t ld_xs,
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ WS, int64_t ld_ws,
     const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
     bf16_t* __restrict__ Y, uint8_t* __restrict__ AQ, uint8_t* __restrict__ AS, int64_t ld_as,
-    int32_t* dev_err) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr int kWaves = kStreamThreads / 64;
     constexpr int kColsPerWave = SWIGLU ? 32 : 64;
     __shared__ int s_off[kMaxExperts];
@@ -461,9 +487,17 @@ __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
 
     for (int rg = 0; rg < cnt; rg += 32) {  // uniform across the wave
         const int xr = rg + r32;           // this lane's expert row
-        const bool xok = xr < cnt;
-        const uint8_t* xrow = X + (int64_t)(off + xr) * K;
-        const uint8_t* xsrow = XS + (int64_t)(off + xr) * ld_xs;
+        const bool xok = xr < cnt;         // the row exists (and is written)
+        bool xld = xok;                    // its operand row is loaded (else zeros)
+        int src = off + xr;                // its source row: grouped row, or token (slot)
+        if (GATHER && xok) {
+            const int sl = slot[off + xr];
+            xld = sl >= 0 && sl < nslots;
+            if (!xld && dev_err) atomicOr(dev_err, MOE_DEVERR_SLOT);
+            src = xld ? sl / top_k : 0;
+        }
+        const uint8_t* xrow = X + (int64_t)src * K;
+        const uint8_t* xsrow = XS + (int64_t)src * ld_xs;
         f32x16_t acc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -484,9 +518,9 @@ __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int k = 64 * (s0 + s) + 32 * h + 16 * c;
-                    xa[s][h] = xok && k < K ? ld16(xrow + k) : u32x4_t{0u, 0u, 0u, 0u};
+                    xa[s][h] = xld && k < K ? ld16(xrow + k) : u32x4_t{0u, 0u, 0u, 0u};
                 }
-            if (xok && sb < nblocks) xsc.load(xsrow + sb);
+            if (xld && sb < nblocks) xsc.load(xsrow + sb);
             else xsc.unit();
             // this batch's DMA (and every load above) has landed; read the
             // weights in the MFMA layout, then refill the stage with the
@@ -583,13 +617,14 @@ hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
         const int64_t NB = (N + 64 * 4 - 1) / (64 * 4);
         hipLaunchKernelGGL(gmm_mx_stream_kernel<false>, dim3((unsigned)(E * NB)),
                            dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, wq, ws, ld_ws, group_list,
-                           (int)E, M_cap, (int)K, (int)N, y, nullptr, nullptr, (int64_t)0, dev_err);
+                           (int)E, M_cap, (int)K, (int)N, y, nullptr, nullptr, (int64_t)0, dev_err, nullptr,
+                           1, 0);
         return hipGetLastError();
     }
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
     hipLaunchKernelGGL(gmm_mx_rows_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        xq, xs, ld_xs, wq, ws, ld_ws, group_list, (int)E, M_cap, (int)K, (int)N, y,
-                       nullptr, nullptr, (int64_t)0, dev_err);
+                       nullptr, nullptr, (int64_t)0, dev_err, nullptr, 1, 0);
     return hipGetLastError();
 }
 
@@ -597,20 +632,32 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
                                     const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
                                     const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
                                     int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
-                                    int32_t* dev_err, hipStream_t stream) {
+                                    int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
     if (M_cap == 0) return hipSuccess;
     if (gmm_mx_stream_applies(E, M_cap)) {
         const int64_t NB = (I + 32 * 4 - 1) / (32 * 4);
-        hipLaunchKernelGGL(gmm_mx_stream_kernel<true>, dim3((unsigned)(E * NB)),
-                           dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
-                           group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
-                           dev_err);
+        if (g.slot)
+            hipLaunchKernelGGL((gmm_mx_stream_kernel<true, true>), dim3((unsigned)(E * NB)),
+                               dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
+                               group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
+                               dev_err, g.slot, (int)g.top_k, (int)g.nslots);
+        else
+            hipLaunchKernelGGL(gmm_mx_stream_kernel<true>, dim3((unsigned)(E * NB)),
+                               dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
+                               group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
+                               dev_err, nullptr, 1, 0);
         return hipGetLastError();
     }
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
-    hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
-                       (int)(2 * I), nullptr, aq, as, ld_as, dev_err);
+    if (g.slot)
+        hipLaunchKernelGGL((gmm_mx_rows_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                           stream, xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
+                           (int)(2 * I), nullptr, aq, as, ld_as, dev_err, g.slot, (int)g.top_k,
+                           (int)g.nslots);
+    else
+        hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                           xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
+                           (int)(2 * I), nullptr, aq, as, ld_as, dev_err, nullptr, 1, 0);
     return hipGetLastError();
 }
 

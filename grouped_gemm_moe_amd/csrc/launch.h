@@ -94,7 +94,8 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
                                     const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
                                     const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
                                     int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
-                                    int32_t* dev_err, hipStream_t stream);
+                                    int32_t* dev_err, hipStream_t stream,
+                                    const GatherRows& g = GatherRows{});
 
 // mx_quant.hip
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ld_s, uint8_t* q,

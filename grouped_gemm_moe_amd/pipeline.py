@@ -32,6 +32,9 @@ elements fewer, for one extra swiglu pass.
 The A8W8-FP (MXFP8) forward ("MegaMoE", A8W8-FP scenario), MoeLayerMX:
     moe_permute_mx (gather + Q_MX) -> gmm_mx_fwd_swiglu(W1; GMM1, SwiGLU and
     Q_MX of A in one call) -> gmm_mx_fwd(W2) -> moe_unpermute
+or, with gather_rows=True, mx_quantize of the T token rows -> moe_permute_index
+-> gmm_mx_fwd_swiglu_gather (GMM1 reads the quantised token rows through
+sorted_slot) -> gmm_mx_fwd(W2) -> moe_unpermute, bit-identical.
 
 Every step runs in the HIP kernels of libmoegmm; this module only owns the
 buffers and the call order.  group_list (tokens_per_expert) stays on the
@@ -44,7 +47,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_gather, gmm_fwd_swiglu,
-               gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_workspace_size, moe_permute,
+               gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
+               gmm_workspace_size, moe_permute,
                moe_permute_bwd, moe_permute_index, moe_permute_mx, moe_permute_workspace_size, moe_unpermute,
                moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd)
 
@@ -243,14 +247,19 @@ class MoeLayerMX:
     rows, then up rows), W2 as [E, H, I]; prepare_weights builds them from
     the bf16 [E, H, 2I] / [E, I, H] weights."""
 
-    def __init__(self, shape: LayerShape, device):
+    def __init__(self, shape: LayerShape, device, gather_rows: bool = False):
         s = shape
         self.shape = s
         d = device
         u8 = dict(dtype=torch.uint8, device=d)
         S = s.S
-        self.xq = torch.empty((S, s.H), **u8)
-        self.xs = torch.empty((S, mx_scale_ld(s.H)), **u8)
+        # gather_rows: the token rows are quantised once ([T, H]) and GMM1
+        # reads them through sorted_slot; else the permute writes the
+        # quantised rows of every slot ([S, H])
+        self.gather_rows = bool(gather_rows)
+        rows = s.T if self.gather_rows else S
+        self.xq = torch.empty((rows, s.H), **u8)
+        self.xs = torch.empty((rows, mx_scale_ld(s.H)), **u8)
         self.aq = torch.empty((S, s.I), **u8)
         self.as_ = torch.empty((S, mx_scale_ld(s.I)), **u8)
         self.row_id_map = torch.empty(S, dtype=torch.int32, device=d)
@@ -273,10 +282,17 @@ class MoeLayerMX:
     def forward(self, x, topk_ids, probs, w1mx, w2mx):
         (w1q, w1s), (w2q, w2s) = w1mx, w2mx
         g = self.tokens_per_expert
-        moe_permute_mx(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
-                       out=(self.xq, self.xs, self.row_id_map, self.sorted_slot, g))
-        gmm_mx_fwd_swiglu(self.xq, self.xs, w1q, w1s, g, out=(self.aq, self.as_),
-                          dev_err=self.dev_err)
+        if self.gather_rows:
+            mx_quantize(x, out=(self.xq, self.xs))
+            moe_permute_index(topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
+                              out=(self.row_id_map, self.sorted_slot, g))
+            gmm_mx_fwd_swiglu_gather(self.xq, self.xs, self.sorted_slot, self.shape.top_k, w1q, w1s, g,
+                                     out=(self.aq, self.as_), dev_err=self.dev_err)
+        else:
+            moe_permute_mx(x, topk_ids, self.shape.E, ws=self.ws_perm, dev_err=self.dev_err,
+                           out=(self.xq, self.xs, self.row_id_map, self.sorted_slot, g))
+            gmm_mx_fwd_swiglu(self.xq, self.xs, w1q, w1s, g, out=(self.aq, self.as_),
+                              dev_err=self.dev_err)
         gmm_mx_fwd(self.aq, self.as_, w2q, w2s, g, out=self.yp, dev_err=self.dev_err)
         moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
         return self.out

@@ -483,6 +483,28 @@ moe_status gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
                              int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
                              int32_t* dev_err, void* stream);
 
+/* ------------------------------------------------------------------------
+ * gmm_mx_fwd_swiglu_gather -- gmm_mx_fwd_swiglu whose grouped operand rows
+ * are read from token rows instead of a permuted copy: grouped row r is row
+ * sorted_slot[r] / top_k of (xq, xs), the MX quantisation of the T token rows
+ * (mx_quantize of x).  Q_MX works row by row, so these are the bytes that
+ * moe_permute_mx would have written for row r, and the outputs are
+ * bit-identical to gmm_mx_fwd_swiglu on them.  [MX] (tokens gathered per
+ * expert are MX-quantised); [MegaMoE] 功能说明 (dispatch fused with the
+ * expert computation), as gmm_fwd_gather.
+ *
+ *   xq [T, K] codes, xs [T, ld_xs] scales; sorted_slot [M_cap] int32 from
+ *   moe_permute_index (or moe_permute) over the same ids; M_cap <= T*top_k;
+ *   everything else as gmm_mx_fwd_swiglu.
+ * Bad sorted_slot entries and limits as gmm_fwd_gather (T*K < 2^30).
+ * ---------------------------------------------------------------------- */
+moe_status gmm_mx_fwd_swiglu_gather(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs,
+                                    const int32_t* sorted_slot, int64_t T, int64_t top_k,
+                                    const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                                    const int64_t* group_list, int64_t E, int64_t M_cap, int64_t K,
+                                    int64_t I, uint8_t* aq, uint8_t* as, int64_t ld_as,
+                                    int32_t* dev_err, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

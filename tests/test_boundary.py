@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
               "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu",
-              "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather"]:
+              "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_mx_fwd_swiglu_gather"]:
         assert n in names, n
 
 
@@ -315,3 +315,12 @@ def test_gathered_calls_reject_bad_arguments(lib):
     assert pi(E=0) == MOE_ERR_INVALID
     assert pi(k=33) == MOE_ERR_INVALID
     assert pi(tpe=ctypes.c_void_p(0x50004)) == MOE_ERR_INVALID
+    # gmm_mx_fwd_swiglu_gather(xq, xs, ld_xs, sorted_slot, T, top_k, w1q, w1s, ld_w1s, group_list,
+    #                          E, M_cap, K, I, aq, as, ld_as, err, stream)
+    mxg = lambda s_=S4, T=16, k=4, M=64, K=64, I=32: lib.gmm_mx_fwd_swiglu_gather(  # noqa: E731
+        A16, A16b, 16, s_, T, k, A16c, A16, 16, A16b, 4, M, K, I, A16c, A16, 16, None, None)
+    assert mxg(s_=None) == MOE_ERR_NULL
+    assert mxg(M=65) == MOE_ERR_INVALID
+    assert mxg(k=0) == MOE_ERR_INVALID
+    assert mxg(I=48) == MOE_ERR_INVALID          # I % 32
+    assert mxg(T=1 << 17, K=8192) == MOE_ERR_INVALID

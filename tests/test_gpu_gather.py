@@ -220,3 +220,68 @@ def test_gather_rows_is_forward_only(dev):
 
     with pytest.raises(ValueError):
         MoeLayer(LayerShape(8, 2, 4, 64, 32), dev, with_backward=True, gather_rows=True)
+
+
+# --- the A8W8-FP (MXFP8) GMM1 reading quantised token rows -------------------
+
+MX_SHAPES = [
+    (600, 8, 16, 512, 384, 0.1, None),   # row tiles
+    (600, 8, 16, 512, 384, 0.0, "stream"),
+    (24, 4, 32, 1024, 256, 0.2, None),   # weight streaming
+    (24, 4, 32, 1024, 256, 0.0, "tile"),
+]
+
+
+@pytest.mark.parametrize("T,K,E,H,I,mask,variant", MX_SHAPES)
+def test_gmm_mx_fwd_swiglu_gather(dev, T, K, E, H, I, mask, variant):
+    """Q_MX is row-wise, so the token rows quantised once hold the bytes
+    moe_permute_mx writes for each slot row; GMM1 through sorted_slot on them
+    is bit-identical to GMM1 on the permuted rows."""
+    print(f"gmm_mx_fwd_swiglu_gather T={T} K={K} E={E} H={H} I={I} variant={variant}", flush=True)
+    rng = np.random.default_rng(T + I)
+    x = bf16_dev(workloads.normal_bf16(rng, (T, H)), dev)
+    w1 = bf16_dev(workloads.normal_bf16(rng, (E, H, 2 * I), std=0.02), dev)
+    ids = torch.from_numpy(_ids(rng, T, K, E, mask)).to(dev)
+    w1q, w1s = moe.mx_quantize(w1.transpose(1, 2).contiguous())
+    xq_p, xs_p, _, ss, tpe = moe.moe_permute_mx(x, ids, E)
+    xq_t, xs_t = moe.mx_quantize(x)
+    torch.cuda.synchronize()
+    R = int(tpe.sum().item())
+    tok = ss[:R].long() // K
+    assert torch.equal(xq_t[tok], xq_p[:R])
+    nb = H // 32
+    assert torch.equal(xs_t[tok][:, :nb], xs_p[:R, :nb])
+    S, ld_a = T * K, moe.mx_scale_ld(I)
+    aq = torch.full((S, I), 0xA5, dtype=torch.uint8, device=dev)
+    asc = torch.full((S, ld_a), 0xA5, dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    with force_variant(variant):
+        moe.gmm_mx_fwd_swiglu_gather(xq_t, xs_t, ss, K, w1q, w1s, tpe, out=(aq, asc), dev_err=err)
+        aq_ref, as_ref = moe.gmm_mx_fwd_swiglu(xq_p, xs_p, w1q, w1s, tpe)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(aq[:R], aq_ref[:R])
+    assert torch.equal(asc[:R, :I // 32], as_ref[:R, :I // 32])
+    assert (aq[R:] == 0xA5).all() and (asc[R:] == 0xA5).all()
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_layer_mx_gathered_is_bit_identical(dev, name):
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
+
+    print(f"MX layer forward gathered {name}", flush=True)
+    wl = getattr(workloads, name)()
+    d = wl.dims
+    shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
+    x = bf16_dev(wl["x"], dev)
+    wmx = MoeLayerMX.prepare_weights(bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev))
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    plain = MoeLayerMX(shape, dev)
+    gath = MoeLayerMX(shape, dev, gather_rows=True)
+    assert gath.xq.shape[0] == d["T"]
+    out_p = plain.forward(x, ids, probs, *wmx).clone()
+    out_g = gath.forward(x, ids, probs, *wmx).clone()
+    torch.cuda.synchronize()
+    assert int(gath.dev_err.item()) == 0
+    np.testing.assert_array_equal(dev_bits(out_g), dev_bits(out_p))

@@ -74,12 +74,37 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
         s_gather[1] = nslots;
     }
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
-    const int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
+    // the plain forward and the input gradient run half-height tiles for an
+    // expert's last <= 128 rows (MixedTile); the SwiGLU epilogue assumes
+    // 256 x 256 tiles
+    // 256 x 256 tiles, and only where that lowers the tile count of the
+    // busiest workgroup (this schedule is static: a somewhat dearer half
+    // tile that does not remove a tile round only lengthens it)
+    constexpr bool kHalfTiles = MODE != kSwiGLU;
+    const int NTH = (Ncols + kHN - 1) / kHN;
+    int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
+    bool use_half = false;
+    if constexpr (kHalfTiles) {
+        const int per_wg = gridDim.x >> 3;
+        const auto rounds = [&](int n) { return ((n + 7) / 8 + per_wg - 1) / per_wg; };
+        const int nmixed = mixed_tile_count(s_cnt, E, NT, NTH, s_scan);
+        if (rounds(nmixed) < rounds(ntiles)) {
+            use_half = true;
+            ntiles = mixed_tile_starts(s_cnt, E, NT, NTH, s_tst, s_scan);
+        }
+    }
     const XcdRange xr = xcd_range(blockIdx.x & 7, ntiles);
     for (int j = blockIdx.x >> 3; j < xr.count; j += gridDim.x >> 3) {
-        const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
-        const int e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid;
-        const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kCols);
+        int e, row0, rows_valid, nt;
+        bool half = false;
+        if (kHalfTiles && use_half) {
+            const MixedTile mt = mixed_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j);
+            e = mt.e, row0 = mt.row0, rows_valid = mt.rows_valid, nt = mt.nt, half = mt.half;
+        } else {
+            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
+            e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid, nt = rt.nt;
+        }
+        const int n0 = __builtin_amdgcn_readfirstlane(nt * (half ? kHN : kCols));
 
         const int64_t lda = IS_DX ? N : K;
         const bf16_t* We = W + (int64_t)e * K * N;
@@ -97,10 +122,14 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
                 ga);
         } else {
             bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
-            gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(
-                a_base, lda, rows_valid, IS_DX ? We + (int64_t)n0 * N : We + n0, N, cols_left, 0, Kred,
-                rows_valid, cols_left, smem,
-                [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); }, ga);
+            const bf16_t* b_base = IS_DX ? We + (int64_t)n0 * N : We + n0;
+            auto st = [&](const auto& eng) { eng.store(y, Ncols, rows_valid, cols_left, smem); };
+            if (half)
+                gemm_tile<kHM, kHN, kHWM, kHWN, true, IS_DX, kHNST>(a_base, lda, rows_valid, b_base, N, cols_left,
+                                                                    0, Kred, rows_valid, cols_left, smem, st, ga);
+            else
+                gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(a_base, lda, rows_valid, b_base, N, cols_left, 0, Kred,
+                                                          rows_valid, cols_left, smem, st, ga);
         }
         __syncthreads();  // every wave is done with its epilogue image before the next tile's copies
     }
@@ -387,9 +416,8 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const DwSched ds = dw_schedule(s_cnt, E, K, N, s_order);
-    const int total_mt = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan);
     const int NTx = (K + kBN - 1) / kBN;  // dx has K columns
-    const int nx = total_mt * NTx;
+    const int nx = mixed_tile_starts(s_cnt, E, NTx, (K + kHN - 1) / kHN, s_tst, s_scan);
     const int xcd = blockIdx.x & 7, wg_per_xcd = gridDim.x >> 3;
     // this XCD's input-gradient tiles: [x0, x0 + nxx) of the row-tile order
     const XcdRange xr = xcd_range(xcd, nx);
@@ -403,21 +431,27 @@ __global__ __launch_bounds__(kThreads, 1) void gmm_bwd_kernel(
         uint32_t nj = 0;
         if (threadIdx.x == 0) nj = (uint32_t)wg_per_xcd + atomicAdd(ctr, 1u);
         if (j < (uint32_t)nxx) {
-            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NTx, x0 + (int)j);
-            const int row0 = rt.row0, rows_valid = rt.rows_valid;
-            const int n0 = __builtin_amdgcn_readfirstlane(rt.nt * kBN);
+            const MixedTile mt = mixed_tile_at(s_off, s_cnt, s_tst, E, NTx, x0 + (int)j);
+            const int row0 = mt.row0, rows_valid = mt.rows_valid;
+            const int n0 = __builtin_amdgcn_readfirstlane(mt.nt * (mt.half ? kHN : kBN));
             const int cols_left = K - n0;
-            const bf16_t* We = W + (int64_t)rt.e * K * N;
-            gemm_tile<kBM, kBN, kWM, kWN, true, true>(
-                DY + (int64_t)row0 * N, N, rows_valid, We + (int64_t)n0 * N, N, cols_left, 0, N,
-                rows_valid, cols_left, smem, [&](const auto& eng) {
-                    if constexpr (SWIGLU_BWD) {
-                        const int64_t o = (int64_t)row0 * 2 * K + n0;
-                        eng.store_swiglu_bwd(DH + o, Hin + o, 2 * K, K, rows_valid, cols_left, smem);
-                    } else {
-                        eng.store(DX + (int64_t)row0 * K + n0, K, rows_valid, cols_left, smem);
-                    }
-                });
+            const bf16_t* We = W + (int64_t)mt.e * K * N;
+            auto st = [&](const auto& eng) {
+                if constexpr (SWIGLU_BWD) {
+                    const int64_t o = (int64_t)row0 * 2 * K + n0;
+                    eng.store_swiglu_bwd(DH + o, Hin + o, 2 * K, K, rows_valid, cols_left, smem);
+                } else {
+                    eng.store(DX + (int64_t)row0 * K + n0, K, rows_valid, cols_left, smem);
+                }
+            };
+            if (mt.half)
+                gemm_tile<kHM, kHN, kHWM, kHWN, true, true, kHNST>(DY + (int64_t)row0 * N, N, rows_valid,
+                                                                   We + (int64_t)n0 * N, N, cols_left, 0, N,
+                                                                   rows_valid, cols_left, smem, st);
+            else
+                gemm_tile<kBM, kBN, kWM, kWN, true, true>(DY + (int64_t)row0 * N, N, rows_valid,
+                                                          We + (int64_t)n0 * N, N, cols_left, 0, N, rows_valid,
+                                                          cols_left, smem, st);
         } else {
             dw_tile(8 * ((int)j - nxx) + xcd, ds, s_off, s_cnt, s_order, X, DY, K, N, DW, smem);
         }

@@ -57,6 +57,10 @@ constexpr int kWaves = kThreads / 64;
 #endif
 constexpr int BK = MOEGMM_BK;     // reduction depth of one LDS stage
 constexpr int kNST = MOEGMM_NST;  // LDS stages in the ring
+// The LDS array of a GMM workgroup: kNST stages of a 256 x 256 tile.  Other
+// tile shapes run rings of their own stage count in the same array, and the
+// epilogues use it for their images.
+constexpr int kRingElems = kNST * (256 + 256) * BK;
 static_assert((BK == 32 && kNST == 4) || (BK == 64 && kNST == 2), "ring of 128 KiB");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -455,7 +459,7 @@ struct Engine {
         constexpr int kRows = 32;       // rows per pass
         constexpr int kIt = kRows / 8;  // 8 rows of 128 bytes per instruction
         constexpr int kRegion = 2 * kRows * WTN;  // G and U of one pass, bf16 elements
-        static_assert(kWaves * 2 * kRegion <= (BM + BN) * BK * kNST, "regions fit the ring");
+        static_assert(kWaves * 2 * kRegion <= kRingElems, "regions fit the LDS array");
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
         const int lane = tid & 63;
@@ -555,7 +559,7 @@ struct Engine {
                                  bf16_t* smem) const {
         static_assert(TN == 2, "one gate and one up fragment per wave");
         constexpr int kCols = BN / 2, kChunks = kCols / 8;  // one output row: kChunks 16-byte chunks
-        static_assert(kChunks == 16 && 2 * BM * kCols <= (BM + BN) * BK * kNST, "images fit the ring");
+        static_assert(kChunks == 16 && 2 * BM * kCols <= kRingElems, "images fit the LDS array");
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
         const int lane = tid & 63;
@@ -627,18 +631,18 @@ struct Engine {
     }
 };
 
-// One output tile over a ring of kNST LDS stages.  Per step s: wait for this
-// wave's copies of step s (the kNST-2 later steps stay in flight), barrier
+// One output tile over a ring of NST LDS stages.  Per step s: wait for this
+// wave's copies of step s (the NST-2 later steps stay in flight), barrier
 // (all copies of step s landed; step s-1 fully read), then run step s while
-// refilling the stage read at step s-1 with step s+kNST-1, one load after
+// refilling the stage read at step s-1 with step s+NST-1, one load after
 // every few MFMAs so the memory pipe and the MFMA pipe work side by side.
 // Steps past the end still "load", with every lane out of range: that only
 // writes zeros into a stage nobody reads again, and keeps the number of
 // loads in flight constant (no data-dependent wait counts, no branches).
-// `smem` holds kNST stages of [A tile | B tile].
+// `smem` holds NST stages of [A tile | B tile].
 // `store(eng)` writes the result; rows_valid / cols_valid (in tile columns)
 // decide which waves have any work.
-template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, class Store>
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, int NST = kNST, class Store>
 MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
                           int64_t ldb, int b_olim, int b_pair, int red_len, int rows_valid,
                           int cols_valid, bf16_t* smem, const Store& store,
@@ -647,6 +651,7 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     using DB = Dma<BN, B_KMAJOR>;
     constexpr int kStage = (BM + BN) * BK;       // elements per stage
     constexpr int kPer = DA::kInst + DB::kInst;  // loads per wave per stage
+    static_assert(NST >= 2 && NST * kStage <= kRingElems, "ring within the LDS array");
     DA da;
     DB db;
     if constexpr (A_KMAJOR) {
@@ -660,7 +665,7 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     eng.zero();
     const int nk = (red_len + BK - 1) / BK;
     auto issue = [&](int step) {
-        bf16_t* st = smem + (step % kNST) * kStage;
+        bf16_t* st = smem + (step % NST) * kStage;
         da.issue(DA::stage(a_base, lda, step), st, red_len - step * BK);
         db.issue(DB::stage(b_base, ldb, step), st + BM * BK, red_len - step * BK);
     };
@@ -668,16 +673,16 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
     constexpr int kMfmaPerStep = (BK / 16) * (BM / WM / 32) * (BN / WN / 32);
     static_assert(kMfmaPerStep >= kPer, "load spacing");
 #pragma unroll
-    for (int p = 0; p < kNST - 1; ++p) issue(p);
+    for (int p = 0; p < NST - 1; ++p) issue(p);
     // this wave's corner of the output tile; two copies of the step loop
     // (active and idle wave), so the common one carries no branch
     const int wrow0 = (wave_id() / WN) * (BM / WM), wcol0 = (wave_id() % WN) * (BN / WN);
     auto run_steps = [&](auto active_tag) {
     for (int s = 0; s < nk; ++s) {
-        wait_vmcnt<(kNST - 2) * kPer>();
+        wait_vmcnt<(NST - 2) * kPer>();
         __builtin_amdgcn_s_barrier();
-        const int nxt = s + kNST - 1;
-        bf16_t* nst = smem + (nxt % kNST) * kStage;
+        const int nxt = s + NST - 1;
+        bf16_t* nst = smem + (nxt % NST) * kStage;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(DA::stage(a_base, lda, nxt));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(DB::stage(b_base, ldb, nxt));
         const int left = red_len - nxt * BK;
@@ -691,7 +696,7 @@ MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const b
             }
         };
         if constexpr (decltype(active_tag)::value > 0) {
-            const bf16_t* st = smem + (s % kNST) * kStage;
+            const bf16_t* st = smem + (s % NST) * kStage;
             eng.template compute<decltype(active_tag)::value>(st, st + BM * BK, hook);
         } else {
 #pragma unroll
@@ -730,7 +735,12 @@ MOE_DEVICE XcdRange xcd_range(int xcd, int n) {
 // 256x256 output tiles, 8 waves of 128x64: the copy split, the epilogue
 // images and the SwiGLU passes assume this shape (see their static_asserts).
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
-constexpr int kSmemElems = kNST * (kBM + kBN) * BK;
+// Half-height tiles for an expert's last rows when they number at most 128
+// (MixedTile): 128 x 512, 8 waves of 128 x 64 in one row, a 3-stage ring of
+// 40 KiB stages.
+constexpr int kHM = 128, kHN = 512, kHWM = 1, kHWN = 8, kHNST = 3;
+constexpr int kSmemElems = kRingElems;
+static_assert(kSmemElems == kNST * (kBM + kBN) * BK, "the ring of full tiles fills the LDS array");
 // two workgroups per CU when the LDS ring and the accumulators allow it: one
 // workgroup's epilogue and first loads then overlap the other's MFMAs
 constexpr int kAccRegs = (kBM / kWM) * (kBN / kWN) / 64;
@@ -783,6 +793,86 @@ MOE_DEVICE RowTile row_tile_at(const int* s_off, const int* s_cnt, const int* s_
     rt.rows_valid = row_end - rt.row0 < BM ? row_end - rt.row0 : BM;
     rt.nt = lt % NT;
     return rt;
+}
+
+// ---------------------------------------------------------------------------
+// Row tiles with half-height remainders.  An expert's rows go in kBM-row
+// tiles of NT column tiles each, and when its last r rows number at most
+// kBM/2, in one row of NTH half-height tiles of kBM/2 rows and 2*kBN columns
+// instead.  Those tiles use the same 128 x 64 wave tiles (one row of 8
+// waves), so every output takes the same MFMAs in the same order; but a tile
+// of few rows costs nearly as much as a full one (it streams the whole
+// weight panel), and there are half as many of them.
+// ---------------------------------------------------------------------------
+struct MixedTile {
+    int e, row0, rows_valid, nt;
+    bool half;
+};
+
+MOE_DEVICE int expert_tiles(int cnt, int NT, int NTH) {
+    const int full = cnt / kBM, rem = cnt - full * kBM;
+    return full * NT + (rem == 0 ? 0 : (2 * rem <= kBM ? NTH : NT));
+}
+
+// The total of mixed_tile_starts without the per-expert starts.  All
+// threads of the block; ends with a barrier.
+MOE_DEVICE int mixed_tile_count(const int* s_cnt, int E, int NT, int NTH, int64_t* s_scan) {
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += expert_tiles(s_cnt[e0 + i], NT, NTH);
+    int64_t total;
+    block_exclusive_scan<int64_t>(mine, s_scan, &total);
+    __syncthreads();
+    return (int)total;
+}
+
+// s_tst[e] = first tile of expert e; returns the total.  All threads of the
+// block; ends with a barrier.
+MOE_DEVICE int mixed_tile_starts(const int* s_cnt, int E, int NT, int NTH, int* s_tst, int64_t* s_scan) {
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += expert_tiles(s_cnt[e0 + i], NT, NTH);
+    int64_t total;
+    int64_t run = block_exclusive_scan<int64_t>(mine, s_scan, &total);
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) {
+            s_tst[e0 + i] = (int)run;
+            run += expert_tiles(s_cnt[e0 + i], NT, NTH);
+        }
+    __syncthreads();
+    return (int)total;
+}
+
+// Logical tile lt: expert-major, then row tile, then column tile.
+MOE_DEVICE MixedTile mixed_tile_at(const int* s_off, const int* s_cnt, const int* s_tst, int E, int NT,
+                                   int lt) {
+    int lo = 0, hi = E - 1;  // last expert whose first tile is <= lt
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tst[mid] <= lt) lo = mid; else hi = mid - 1;
+    }
+    MixedTile mt;
+    mt.e = __builtin_amdgcn_readfirstlane(lo);
+    const int local = __builtin_amdgcn_readfirstlane(lt - s_tst[mt.e]);
+    const int off = __builtin_amdgcn_readfirstlane(s_off[mt.e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[mt.e]);
+    const int full = cnt / kBM;
+    if (local < full * NT) {
+        mt.row0 = off + (local / NT) * kBM;
+        mt.rows_valid = kBM;
+        mt.nt = local % NT;
+        mt.half = false;
+    } else {
+        mt.row0 = off + full * kBM;
+        mt.rows_valid = cnt - full * kBM;
+        mt.nt = local - full * NT;
+        mt.half = 2 * mt.rows_valid <= kBM;
+    }
+    return mt;
 }
 
 }  // namespace

@@ -248,6 +248,44 @@ def _expert_of(gl):
     return np.repeat(np.arange(len(gl)), gl)
 
 
+def test_half_height_tiles_prefill_groups(dev):
+    """The prefill routing (128 experts of ~256 rows): an expert's last <= 128
+    rows run as half-height tiles (128 x 512) in the forward and input-gradient
+    launches wherever that removes a tile round -- here the [32768, 512] x
+    [512, 2048] forward and the input gradient with 2048 output columns.
+    Sampled rows (every expert's first and last rows among them) against the
+    oracle, and bit-equality with gmm_bwd, whose queue always uses them."""
+    wl = workloads.prefill(with_weights=False)
+    gl = oracle.tokens_per_expert(wl["topk_ids"], 128)
+    R, E, K, N = int(gl.sum()), 128, 512, 2048
+    rng = np.random.default_rng(77)
+    a_b = workloads.normal_bf16(rng, (R, K))
+    w_b = workloads.normal_bf16(rng, (E, K, N), std=0.02)
+    g = _gl(dev, gl)
+    a, w = bf16_dev(a_b, dev), bf16_dev(w_b, dev)
+    # [E, N, K]: the input gradient a @ wt[e]^T has N = 2048 output columns
+    # over a reduction of K = 512, and equals a @ w[e]
+    wt = w.transpose(1, 2).contiguous()
+    print("half-height tiles: fwd [32768,512]x[512,2048], dX with 2048 output columns", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = moe.gmm_fwd(a, w, g, dev_err=err)                 # [R, 2048]
+    dx = moe.gmm_bwd_input(a, wt, g, dev_err=err)         # [R, 2048]
+    ws = torch.zeros(moe.gmm_workspace_size(E, R, N, K, moe.OP_BWD), dtype=torch.uint8, device=dev)
+    dx2, _ = moe.gmm_bwd(y, a, wt, g, ws=ws, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "gmm_bwd dx != gmm_bwd_input"
+    rows = _sample_rows(gl, rng, per_expert=1)
+    eo = _expert_of(gl)
+    ridx = torch.from_numpy(rows).to(dev)
+    y_s, dx_s = dev_f64(y[ridx]), dev_f64(dx[ridx])
+    wf = f64(w_b)
+    for i, r in enumerate(rows):
+        ref = f64(a_b[r]) @ wf[eo[r]]
+        assert_close(y_s[i], ref, f"fwd row {r}")
+        assert_close(dx_s[i], ref, f"dX row {r}")
+
+
 def test_ep_full_size_sampled(dev):
     wl = workloads.ep_slice()
     gl = wl["group_list"]

@@ -193,8 +193,8 @@ def ep_gemm_bytes(gl, H, I):
 
 # libmoegmm kernel behind each call of the step (kernel symbol -> calls)
 EP_KERNELS = {
-    "gmm_rows_kernel<2>": ["gmm_fwd_swiglu"],
-    "gmm_rows_kernel<0>": ["gmm_fwd_down"],
+    "gmm_rows_kernel<2, false>": ["gmm_fwd_swiglu"],
+    "gmm_rows_kernel<0, false>": ["gmm_fwd_down"],
     "gmm_bwd_kernel<true>": ["gmm_bwd_swiglu_down"],
     "gmm_bwd_kernel<false>": ["gmm_bwd_gate_up"],
 }

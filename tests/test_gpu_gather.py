@@ -113,6 +113,11 @@ SHAPES = [
     (24, 4, 32, 1024, 512, 0.2, None),
     (24, 4, 32, 1024, 512, 0.0, "tile"),
     (1000, 1, 8, 520, 264, 0.0, None),
+    # many experts, most of them empty; reduction and column tails
+    (300, 3, 1024, 520, 264, 0.1, None),
+    (300, 3, 1024, 520, 264, 0.1, "tile"),
+    # the largest top_k
+    (40, 32, 64, 256, 512, 0.05, None),
 ]
 
 
@@ -160,6 +165,18 @@ def test_gmm_fwd_swiglu_gather(dev, T, K, E, H, N, mask, variant, with_h):
     ref_ss, _, cnt = oracle.permute_maps(ids, E)
     ref = oracle.gmm_swiglu(f64(x_bits[ref_ss // K]), f64(w_bits), cnt)
     assert_close(f64(got[:R]), ref, "gmm_fwd_swiglu_gather vs oracle")
+
+
+def test_gather_empty_call(dev):
+    """No tokens: the gathered calls enqueue nothing and return."""
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    ss = torch.empty((0,), dtype=torch.int32, device=dev)
+    w = torch.zeros((4, 64, 128), dtype=torch.bfloat16, device=dev)
+    g = torch.zeros(4, dtype=torch.int64, device=dev)
+    y = moe.gmm_fwd_gather(x, ss, 2, w, g)
+    a = moe.gmm_fwd_swiglu_gather(x, ss, 2, w, g)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128) and a.shape == (0, 64)
 
 
 @pytest.mark.parametrize("variant", ["tile", "stream"])

@@ -317,15 +317,17 @@ def run_ep(torch, dev, args):
 def decode_bytes(gl, T, K, H, I, fused=True, gathered=False):
     """Algorithmic bytes of one layer forward: weights of experts with rows,
     once; every activation tensor the path materialises written once and read
-    once (x_perm unless the gate_up GMM gathers token rows itself, A, Yp; H
-    too when gate_up and SwiGLU run unfused); indices."""
+    once (x_perm unless the gate_up GMM gathers token rows itself, Yp; A
+    when the gate_up GMM is fused with SwiGLU; H when it is not, and then A
+    written only, by swiglu_gmm_fwd, whose streaming kernel reads H); out
+    written; indices."""
     n_active = int(np.sum(np.asarray(gl) > 0))
     S = int(np.sum(gl))
     w = n_active * (H * 2 * I + I * H) * 2
     act = (T * H * 2            # x read (by the permute's gather, or by the gate_up GMM)
            + (0 if gathered else S * H * 2 * 2)  # x_perm written, read
            + (0 if fused else S * 2 * I * 2 * 2)  # h written, read
-           + S * I * 2 * 2      # a written, read
+           + S * I * 2 * (2 if fused else 1)     # a written (and read by the down GMM when fused)
            + S * H * 2 * 2      # yp written, read
            + T * H * 2)         # out written
     idx = T * K * 4 * 3 + T * K * 4 + len(gl) * 8
@@ -350,7 +352,7 @@ def layer_forward(torch, dev, wl, steps, gather=False):
     probs = torch.from_numpy(wl["probs"]).to(dev)
     layer = MoeLayer(LayerShape(T, K, E, H, I), dev, gather_rows=gather)
     timer = KernelTimer(torch)
-    from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu
+    from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu_gmm_fwd
     g = layer.tokens_per_expert
     fused = layer.use_fused("auto")
     sfx = "_gather" if gather else ""
@@ -359,10 +361,10 @@ def layer_forward(torch, dev, wl, steps, gather=False):
         t("moe_permute_index" if gather else "moe_permute", lambda: layer.permute(x, ids))
         if fused:
             t("gmm_fwd_swiglu" + sfx, lambda: layer.gate_up(w1, True, keep_h=False))
+            t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp))
         else:
             t("gmm_fwd_gate_up" + sfx, lambda: layer.gate_up(w1, False))
-            t("swiglu", lambda: swiglu(layer.h, g, out=layer.a))
-        t("gmm_fwd_down", lambda: gmm_fwd(layer.a, w2, g, out=layer.yp))
+            t("swiglu_gmm_fwd_down", lambda: swiglu_gmm_fwd(layer.h, w2, g, out=(layer.a, layer.yp)))
         t("moe_unpermute", lambda: moe_unpermute(layer.yp, layer.row_id_map, probs, out=layer.out))
 
     plain = lambda name, fn: fn()  # noqa: E731
@@ -450,7 +452,8 @@ def run_decode(torch, dev, args):
     nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
     gbs = nbytes / (ms * 1e-3) / 1e9
     gate_up = "gmm_fwd_swiglu" if fused else "gmm_fwd_gate_up"
-    wbytes = {k: n_active * (H * 2 * I if k == gate_up else I * H) * 2 for k in (gate_up, "gmm_fwd_down")}
+    down = "gmm_fwd_down" if fused else "swiglu_gmm_fwd_down"
+    wbytes = {k: n_active * (H * 2 * I if k == gate_up else I * H) * 2 for k in (gate_up, down)}
     # the same layer with one hot expert (about 50 rows; the others 0-6)
     sk = workloads.decode_skewed()
     ms_s, per_s, gl_s, (_, _, fused_s, _) = layer_forward(torch, dev, sk, args.decode_steps)

@@ -24,7 +24,7 @@ from . import _lib as _L
 
 __all__ = [
     "MoeError", "moe_permute", "moe_permute_noalloc", "moe_permute_index", "gmm_fwd", "gmm_fwd_swiglu",
-    "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
+    "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "swiglu_gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
     "gmm_bwd_swiglu",
     "swiglu",
     "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
@@ -230,6 +230,25 @@ def gmm_fwd_swiglu_gather(x, sorted_slot, top_k: int, w1, group_list, *, out=Non
                                            ws_bytes, _ptr(dev_err), _stream(x.device)),
            "gmm_fwd_swiglu_gather")
     return a
+
+
+def swiglu_gmm_fwd(h, w2, group_list, *, out=None, dev_err=None):
+    """a = SiLU(G) * U of h = [G | U], then y[rows_e] = a[rows_e] @ w2[e]:
+    the activation and the down GMM in one call.  Returns (a, y)."""
+    _dev(h, "h", torch.bfloat16)
+    _dev(w2, "w2", torch.bfloat16)
+    _dev(group_list, "group_list", torch.int64)
+    M, I2 = h.shape
+    E, I, N = w2.shape
+    if I2 != 2 * I or group_list.shape[0] != E:
+        raise MoeError("shape mismatch: h [M, 2I], w2 [E, I, N], group_list [E]")
+    if out is None:
+        out = (None, None)
+    a = _out(out[0], (M, I), torch.bfloat16, h.device, "a")
+    y = _out(out[1], (M, N), torch.bfloat16, h.device, "y")
+    _check(library().swiglu_gmm_fwd(_ptr(h), _ptr(w2), _ptr(group_list), E, M, I, N, _ptr(a), _ptr(y),
+                                    _ptr(dev_err), _stream(h.device)), "swiglu_gmm_fwd")
+    return a, y
 
 
 def gmm_fwd(x, w, group_list, *, out=None, ws=None, dev_err=None):

@@ -30,6 +30,7 @@ SIGNATURES = {
     "gmm_fwd_gather": (_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_fwd_swiglu_gather": (_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p,
                                      _sz, _p, _p]),
+    "swiglu_gmm_fwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p]),
     "gmm_bwd_input": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd_weight": (_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p, _p]),
     "gmm_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p, _p]),

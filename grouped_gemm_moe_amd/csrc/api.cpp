@@ -245,6 +245,25 @@ moe_status gmm_fwd_swiglu_gather(const uint16_t* x, const int32_t* sorted_slot, 
                                                   static_cast<hipStream_t>(stream), g));
 }
 
+moe_status swiglu_gmm_fwd(const uint16_t* h, const uint16_t* w2, const int64_t* group_list, int64_t E,
+                          int64_t M_cap, int64_t I, int64_t N, uint16_t* a, uint16_t* y, int32_t* dev_err,
+                          void* stream) {
+    if (!dim_ok(I)) return MOE_ERR_INVALID;
+    moe_status st = check_gmm_common(h, w2, group_list, y, E, M_cap, I, N, 0, 0, nullptr);
+    if (st != MOE_OK) return st;
+    if (M_cap > 0 && !a) return MOE_ERR_NULL;
+    if (!aligned(a, 16) || M_cap * 2 * I > (int64_t(1) << 40)) return MOE_ERR_INVALID;
+    const size_t bh = (size_t)(M_cap * 2 * I) * 2, ba = (size_t)(M_cap * I) * 2, by = (size_t)(M_cap * N) * 2;
+    if (overlaps(a, ba, h, bh) || overlaps(a, ba, y, by) || overlaps(y, by, h, bh)) return MOE_ERR_INVALID;
+    if (M_cap == 0) return MOE_OK;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (moegmm::gmm_stream_applies(E, M_cap, I))
+        return from_hip(moegmm::launch_stream_swiglu_in(h, w2, group_list, E, M_cap, I, N, a, y, dev_err, hs));
+    hipError_t e = moegmm::launch_swiglu(h, group_list, E, M_cap, I, a, hs);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(moegmm::launch_gmm_fwd(a, w2, group_list, E, M_cap, I, N, y, nullptr, dev_err, hs));
+}
+
 moe_status gmm_bwd_input(const uint16_t* dy, const uint16_t* w, const int64_t* group_list,
                          int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* dx, void* ws,
                          size_t ws_bytes, int32_t* dev_err, void* stream) {

@@ -25,6 +25,7 @@
 // All are HBM-bound streams: 16-byte loads and stores, fp32 math.
 #include "common.h"
 #include "launch.h"
+#include "swiglu.h"
 
 namespace moegmm {
 
@@ -48,16 +49,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const bf16_t* __restri
          u += (int64_t)gridDim.x * kThreads) {
         const int64_t r = u / cpr, c = u - r * cpr;
         const bf16_t* hr = h + r * 2 * I;
-        const u32x4_t g = ld16(hr + c * 8);
-        const u32x4_t up = ld16(hr + I + c * 8);
-        u32x4_t o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const float g0 = bf16_lo(g[d]), g1 = bf16_hi(g[d]);
-            const float u0 = bf16_lo(up[d]), u1 = bf16_hi(up[d]);
-            o[d] = pack_bf16x2(g0 * silu_sigmoid(g0) * u0, g1 * silu_sigmoid(g1) * u1);
-        }
-        st16(a + r * I + c * 8, o);
+        st16(a + r * I + c * 8, swiglu8(ld16(hr + c * 8), ld16(hr + I + c * 8)));
     }
 }
 

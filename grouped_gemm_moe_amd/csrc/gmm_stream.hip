@@ -20,6 +20,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "swiglu.h"
 
 namespace moegmm {
 
@@ -102,7 +103,12 @@ MOE_DEVICE int sub_unit_starts(const int* s_cnt, int E, int NB, int* s_su, int64
 // slot (nullable): X is the token matrix [nslots / top_k, K] and row r of the
 // grouped operand is token slot[r] / top_k; an entry outside [0, nslots)
 // stages a zero row and sets MOE_DEVERR_SLOT.
-template <bool SWIGLU>
+//
+// SWIGLU_IN: the down GMM on SwiGLU(X): X is H [M_cap, 2K] and the staged
+// rows are A = SiLU(G) * U of its halves, rounded as the swiglu kernel
+// rounds them; Hout, when given, receives A [M_cap, K] (from the sub-units
+// of the first column slice).
+template <bool SWIGLU, bool SWIGLU_IN = false>
 __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
@@ -158,7 +164,15 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     for (int u = tid; u < kStreamRows * cpr; u += kThreads) {
         const int r = u / cpr, c = u % cpr;
         u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (src[r] >= 0) v = ld16(X + (int64_t)src[r] * K + c * 8);
+        if constexpr (SWIGLU_IN) {
+            if (src[r] >= 0) {
+                const bf16_t* hr = X + (int64_t)src[r] * 2 * K;
+                v = swiglu8(ld16(hr + c * 8), ld16(hr + K + c * 8));
+                if (Hout && nb == 0) st16(Hout + (int64_t)src[r] * K + c * 8, v);
+            }
+        } else {
+            if (src[r] >= 0) v = ld16(X + (int64_t)src[r] * K + c * 8);
+        }
         *reinterpret_cast<u32x4_t*>(xs + r * K + c * 8) = v;
     }
     __syncthreads();
@@ -293,6 +307,17 @@ hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t
                              int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y,
                              int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
     return launch_stream(false, x, w, group_list, E, M_cap, K, N, y, nullptr, dev_err, stream, g);
+}
+
+hipError_t launch_stream_swiglu_in(const uint16_t* h, const uint16_t* w2, const int64_t* group_list,
+                                   int64_t E, int64_t M_cap, int64_t I, int64_t N, uint16_t* a, uint16_t* y,
+                                   int32_t* dev_err, hipStream_t stream) {
+    const size_t shmem = (size_t)I * kStreamRows * 2;
+    const int64_t blocks = max_sub_units(E, M_cap, N);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gmm_stream_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), shmem, stream,
+                       h, w2, group_list, (int)E, M_cap, (int)I, (int)N, y, a, dev_err, nullptr, 1, 0);
+    return hipGetLastError();
 }
 
 hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,

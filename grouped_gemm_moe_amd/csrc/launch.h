@@ -77,6 +77,10 @@ GmmVariant forced_gmm_variant();
 
 // gmm_stream.hip (decode-shaped forward)
 bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K);
+// y = SwiGLU(h) @ w2[e] in one weight-streaming launch (a = SwiGLU(h) too)
+hipError_t launch_stream_swiglu_in(const uint16_t* h, const uint16_t* w2, const int64_t* group_list,
+                                   int64_t E, int64_t M_cap, int64_t I, int64_t N, uint16_t* a, uint16_t* y,
+                                   int32_t* dev_err, hipStream_t stream);
 hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                              int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y,
                              int32_t* dev_err, hipStream_t stream, const GatherRows& g);

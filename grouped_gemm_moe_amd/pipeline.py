@@ -50,7 +50,7 @@ from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, 
                gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
                gmm_workspace_size, moe_permute,
                moe_permute_bwd, moe_permute_index, moe_permute_mx, moe_permute_workspace_size, moe_unpermute,
-               moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd)
+               moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd, swiglu_gmm_fwd)
 
 
 @dataclass
@@ -155,15 +155,17 @@ class MoeLayer:
 
     def experts_forward(self, w1, w2, fused=False, keep_h=True):
         """fused: one gate_up GMM + SwiGLU call writes A (and H only when
-        keep_h, as the backward needs it); otherwise gate_up GMM -> H ->
-        swiglu -> A.  fused may be "auto" (see use_fused)."""
+        keep_h, as the backward needs it); otherwise gate_up GMM -> H, then
+        SwiGLU and the down GMM in one swiglu_gmm_fwd call (A written too).
+        fused may be "auto" (see use_fused)."""
         g = self.tokens_per_expert
         if self.use_fused(fused):
             self.gate_up(w1, True, keep_h)
+            gmm_fwd(self.a, w2, g, out=self.yp, ws=self.ws_gmm, dev_err=self.dev_err)
         else:
             self.gate_up(w1, False)
-            swiglu(self.h, g, out=self.a)
-        gmm_fwd(self.a, w2, g, out=self.yp, ws=self.ws_gmm, dev_err=self.dev_err)
+            # SwiGLU and the down GMM: one launch on weight-streaming shapes
+            swiglu_gmm_fwd(self.h, w2, g, out=(self.a, self.yp), dev_err=self.dev_err)
 
     def unpermute(self, probs):
         moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)

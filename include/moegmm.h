@@ -214,6 +214,24 @@ moe_status gmm_fwd_swiglu(const uint16_t* x, const uint16_t* w1, const int64_t* 
                           void* stream);
 
 /* ------------------------------------------------------------------------
+ * swiglu_gmm_fwd -- the activation and the down grouped matmul in one call:
+ *   a[r, :] = SiLU(G) * U  with G = h[r, :I], U = h[r, I:]   (as swiglu)
+ *   y[off_e + i, :] = a[off_e + i, :] @ w2[e]                (as gmm_fwd)
+ * [MegaMoE] activation formulas and Expert Compute (A_e W2[e]); [GMM]
+ * "Qwen3.5 MoE 路径" (SwiGLU, then the down GMM).  Where experts own a few
+ * rows each (the weight-streaming shapes of gmm_fwd) one kernel applies
+ * SwiGLU while it stages the rows and also writes a; otherwise swiglu then
+ * gmm_fwd.  a and y are bit-identical to those two calls.
+ *
+ *   h [M_cap, 2I] bf16, w2 [E, I, N] bf16, group_list [E] int64,
+ *   a [M_cap, I] bf16 OUT, y [M_cap, N] bf16 OUT (rows >= R untouched).
+ * a, y and h must not overlap.  Limits as gmm_fwd with K = I.
+ * ---------------------------------------------------------------------- */
+moe_status swiglu_gmm_fwd(const uint16_t* h, const uint16_t* w2, const int64_t* group_list, int64_t E,
+                          int64_t M_cap, int64_t I, int64_t N, uint16_t* a, uint16_t* y, int32_t* dev_err,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
  * gmm_fwd_gather / gmm_fwd_swiglu_gather -- gmm_fwd / gmm_fwd_swiglu whose
  * grouped operand is read straight from the token rows instead of from a
  * permuted copy: grouped row r is x[sorted_slot[r] / top_k].  The dispatch

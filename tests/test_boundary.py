@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
               "gmm_bwd_weight", "gmm_workspace_size", "swiglu", "swiglu_bwd", "moe_unpermute",
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
               "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu",
-              "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_mx_fwd_swiglu_gather"]:
+              "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_mx_fwd_swiglu_gather",
+              "swiglu_gmm_fwd"]:
         assert n in names, n
 
 
@@ -324,3 +325,15 @@ def test_gathered_calls_reject_bad_arguments(lib):
     assert mxg(k=0) == MOE_ERR_INVALID
     assert mxg(I=48) == MOE_ERR_INVALID          # I % 32
     assert mxg(T=1 << 17, K=8192) == MOE_ERR_INVALID
+
+
+def test_swiglu_gmm_fwd_rejects_bad_arguments(lib):
+    """swiglu_gmm_fwd(h, w2, group_list, E, M_cap, I, N, a, y, dev_err, stream)."""
+    D1, D2, D3 = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    f = lambda h=D1, a=D2, y=D3, I=64, M=64: lib.swiglu_gmm_fwd(h, A16b, A16, 4, M, I, 64, a, y, None, None)  # noqa: E731
+    assert f(a=None) == MOE_ERR_NULL
+    assert f(y=None) == MOE_ERR_NULL
+    assert f(I=60) == MOE_ERR_INVALID
+    assert f(a=MIS) == MOE_ERR_INVALID
+    assert f(a=ctypes.c_void_p(0x100000 + 64 * 128 * 2 - 16)) == MOE_ERR_INVALID  # a overlaps h
+    assert f(y=D2) == MOE_ERR_INVALID                                           # y overlaps a

@@ -302,3 +302,38 @@ def test_layer_mx_gathered_is_bit_identical(dev, name):
     torch.cuda.synchronize()
     assert int(gath.dev_err.item()) == 0
     np.testing.assert_array_equal(dev_bits(out_g), dev_bits(out_p))
+
+
+# --- SwiGLU and the down GMM in one call --------------------------------------
+
+@pytest.mark.parametrize("T,K,E,I,N,mask,variant", [
+    (64, 8, 256, 512, 2048, 0.0, None),      # decode shape: one streaming launch
+    (64, 8, 256, 512, 2048, 0.1, "tile"),    # forced: swiglu, then the row tiles
+    (600, 8, 16, 256, 520, 0.0, None),       # row tiles
+    (24, 4, 32, 264, 264, 0.2, "stream"),    # a reduction tail
+])
+def test_swiglu_gmm_fwd(dev, T, K, E, I, N, mask, variant):
+    """a and y bit-identical to swiglu then gmm_fwd; rows >= R untouched."""
+    print(f"swiglu_gmm_fwd T={T} K={K} E={E} I={I} N={N} variant={variant}", flush=True)
+    rng = np.random.default_rng(T + I + N)
+    ids = _ids(rng, T, K, E, mask)
+    g = torch.from_numpy(oracle.tokens_per_expert(ids, E)).to(dev)
+    S = T * K
+    R = int(g.sum().item())
+    h_b = workloads.normal_bf16(rng, (S, 2 * I))
+    w_b = workloads.normal_bf16(rng, (E, I, N), std=0.02)
+    h, w2 = bf16_dev(h_b, dev), bf16_dev(w_b, dev)
+    a = bf16_dev(np.full((S, I), SENT, dtype=np.uint16), dev)
+    y = bf16_dev(np.full((S, N), SENT, dtype=np.uint16), dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    with force_variant(variant):
+        moe.swiglu_gmm_fwd(h, w2, g, out=(a, y), dev_err=err)
+        a_ref = moe.swiglu(h, g)
+        y_ref = moe.gmm_fwd(a_ref, w2, g)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    np.testing.assert_array_equal(dev_bits(a)[:R], dev_bits(a_ref)[:R])
+    np.testing.assert_array_equal(dev_bits(y)[:R], dev_bits(y_ref)[:R])
+    assert (dev_bits(a)[R:] == SENT).all() and (dev_bits(y)[R:] == SENT).all()
+    ref = oracle.gmm(f64(dev_bits(a_ref)[:R]), f64(w_b), oracle.tokens_per_expert(ids, E))
+    assert_close(f64(dev_bits(y)[:R]), ref, "swiglu_gmm_fwd vs oracle")

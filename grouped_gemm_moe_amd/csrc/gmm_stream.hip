@@ -40,6 +40,16 @@ constexpr int kGroups = kGroupsPerWave * kWaves;
 #define MOEGMM_STREAM_UNROLL 1
 #endif
 
+// Bytes of the staged rows' LDS region, which the k-group partial sums
+// reuse (so at least their size), rounded to 16; then the expert tables.
+constexpr size_t kRedBytes = (size_t)kWaves * kStreamRows * kStreamCols * sizeof(float);
+__host__ __device__ inline size_t stream_rows_bytes(int64_t K) {
+    const size_t rows = (size_t)K * kStreamRows * 2;
+    const size_t b = rows > kRedBytes ? rows : kRedBytes;
+    return (b + 15) / 16 * 16;
+}
+size_t stream_lds_bytes(int64_t K, int64_t E) { return stream_rows_bytes(K) + 3 * (size_t)E * sizeof(int); }
+
 // acc += x rows (LDS, [kStreamRows][K]) times the lane's 8 weight columns;
 // k-group kg takes reduction rows 8*kg + 64*i .. +7.
 template <int ROWS>
@@ -114,11 +124,17 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
     int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr int kOutCols = SWIGLU ? kStreamCols / 2 : kStreamCols;  // output columns per sub-unit
+    // Dynamic LDS (stream_lds_bytes): the staged rows, whose space the
+    // k-group partial sums reuse once every wave has left the streaming loop,
+    // then the per-expert tables, sized by E -- so that four workgroups fit
+    // a CU even for K = 2048.
     extern __shared__ __attribute__((aligned(16))) char dsmem[];
-    __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_su[kMaxExperts];
     __shared__ int64_t s_scan[kThreads / 64];
-    __shared__ float red[kWaves][kStreamRows][kStreamCols];
     bf16_t* xs = reinterpret_cast<bf16_t*>(dsmem);  // [kStreamRows][K]
+    float(*red)[kStreamRows][kStreamCols] = reinterpret_cast<float(*)[kStreamRows][kStreamCols]>(dsmem);
+    int* s_off = reinterpret_cast<int*>(dsmem + stream_rows_bytes(K));
+    int* s_cnt = s_off + E;
+    int* s_su = s_cnt + E;
 
     load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
     const int Nout = SWIGLU ? N / 2 : N;
@@ -194,6 +210,7 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
         for (int r = 0; r < kStreamRows; ++r)
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[r][c] += __shfl_xor(acc[r][c], o, 64);
+    __syncthreads();  // every wave is done reading the staged rows, whose space red takes
     if (lane < kLanes) {
 #pragma unroll
         for (int r = 0; r < kStreamRows; ++r)
@@ -287,7 +304,7 @@ bool gmm_stream_applies(int64_t E, int64_t M_cap, int64_t K) {
 static hipError_t launch_stream(bool swiglu, const uint16_t* x, const uint16_t* w, const int64_t* group_list,
                                 int64_t E, int64_t M_cap, int64_t K, int64_t N, uint16_t* y, uint16_t* h,
                                 int32_t* dev_err, hipStream_t stream, const GatherRows& g) {
-    const size_t shmem = (size_t)K * kStreamRows * 2;
+    const size_t shmem = stream_lds_bytes(K, E);
     const int64_t blocks = max_sub_units(E, M_cap, N);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     // blocks past the call's sub-units exit at once
@@ -312,7 +329,7 @@ hipError_t launch_gmm_stream(const uint16_t* x, const uint16_t* w, const int64_t
 hipError_t launch_stream_swiglu_in(const uint16_t* h, const uint16_t* w2, const int64_t* group_list,
                                    int64_t E, int64_t M_cap, int64_t I, int64_t N, uint16_t* a, uint16_t* y,
                                    int32_t* dev_err, hipStream_t stream) {
-    const size_t shmem = (size_t)I * kStreamRows * 2;
+    const size_t shmem = stream_lds_bytes(I, E);
     const int64_t blocks = max_sub_units(E, M_cap, N);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gmm_stream_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), shmem, stream,

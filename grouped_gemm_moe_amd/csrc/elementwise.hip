@@ -120,15 +120,26 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        for (int k = 0; k < top_k; ++k) {
-            const int32_t r = s_row[k];
-            if (r < 0) continue;
-            const float p = s_p[k];
-            const u32x4_t v = ld16(y_perm + (int64_t)r * H + c0);
+        // the rows of up to 8 slots in flight together, then added in
+        // ascending k (a few tokens per call leave most CUs idle, so the
+        // load latency is what a token costs)
+        for (int k0 = 0; k0 < top_k; k0 += 8) {
+            u32x4_t v[8];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                acc[2 * d] = __builtin_fmaf(p, bf16_lo(v[d]), acc[2 * d]);
-                acc[2 * d + 1] = __builtin_fmaf(p, bf16_hi(v[d]), acc[2 * d + 1]);
+            for (int j = 0; j < 8; ++j) {
+                const int32_t r = k0 + j < top_k ? s_row[k0 + j] : -1;
+                v[j] = r >= 0 ? ld16(y_perm + (int64_t)r * H + c0) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int32_t r = k0 + j < top_k ? s_row[k0 + j] : -1;
+                if (r < 0) continue;
+                const float p = s_p[k0 + j];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    acc[2 * d] = __builtin_fmaf(p, bf16_lo(v[j][d]), acc[2 * d]);
+                    acc[2 * d + 1] = __builtin_fmaf(p, bf16_hi(v[j][d]), acc[2 * d + 1]);
+                }
             }
         }
         u32x4_t o;

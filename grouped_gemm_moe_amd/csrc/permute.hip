@@ -321,13 +321,21 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
     const int64_t sub = (S + kWaves * 64 - 1) / (kWaves * 64) * 64;  // multiple of 64
     const int64_t w0 = wid * sub < S ? wid * sub : S;
     const int64_t w1 = w0 + sub < S ? w0 + sub : S;
+    // the wave's ids, loaded once (at most kSmallSlots / kWaves per wave)
+    constexpr int kPerLane = (int)(kSmallSlots / (kWaves * 64));
+    int32_t id[kPerLane];
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const int64_t s = w0 + q * 64 + lane;
+        id[q] = s < w1 ? ids[s] : -1;
+    }
     int bad = 0;
-    for (int64_t s = w0 + lane; s < w1; s += 64) {
-        const int32_t id = ids[s];
-        if (!valid_id(id, E) && id != -1) bad = 1;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        if (valid_id(id[q], E)) atomicAdd(&next_row[wid][id[q]], 1);
+        else if (id[q] != -1) bad = 1;
     }
     if (bad && dev_err) atomicOr(dev_err, MOE_DEVERR_EXPERT_ID);
-    wave_counts(ids, w0, w1, E, next_row[wid]);
     __syncthreads();
     // per-expert totals, scanned in expert order (thread owns <= 4 experts)
     const int per = (E + kPermThreads - 1) / kPermThreads;
@@ -355,7 +363,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_small_kernel(
         off += tot[i];
     }
     __syncthreads();
-    wave_rank_scatter(ids, w0, w1, E, next_row[wid], row_id_map, sorted_slot);
+    const int nbits = id_bits(E);
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q)
+        if (w0 + q * 64 < w1) rank_group(w0 + q * 64, w1, id[q], E, nbits, next_row[wid], row_id_map, sorted_slot);
 }
 
 // Gather, token by token: a block owns tpb consecutive tokens, loads each

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr bool IS_DX = MODE == kDx;
     constexpr int kCols = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemElems];
+    // the SwiGLU forward runs tall tiles (tall_tile_at), whose ring is larger
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[MODE == kSwiGLU ? kSmemTallElems : kSmemElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_tst[kMaxExperts];
     const int Ncols = IS_DX ? K : (MODE == kSwiGLU ? N / 2 : N);  // output columns
@@ -82,7 +83,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     // tile that does not remove a tile round only lengthens it)
     constexpr bool kHalfTiles = MODE != kSwiGLU;
     const int NTH = (Ncols + kHN - 1) / kHN;
-    int ntiles = row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan) * NT;
+    int ntiles = (MODE == kSwiGLU ? tall_tile_starts(s_cnt, E, s_tst, s_scan)
+                                  : row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan)) * NT;
     bool use_half = false;
     if constexpr (kHalfTiles) {
         const int per_wg = gridDim.x >> 3;
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
             const MixedTile mt = mixed_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j);
             e = mt.e, row0 = mt.row0, rows_valid = mt.rows_valid, nt = mt.nt, half = mt.half;
         } else {
-            const RowTile rt = row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
+            const RowTile rt = MODE == kSwiGLU ? tall_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j)
+                                               : row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
             e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid, nt = rt.nt;
         }
         const int n0 = __builtin_amdgcn_readfirstlane(nt * (half ? kHN : kCols));
@@ -116,10 +119,13 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
             bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
             bf16_t* h = Hout ? Hout + (int64_t)row0 * N + n0 : nullptr;
             const int tile_cols = 2 * cols_left < kBN ? 2 * cols_left : kBN;
-            gemm_tile<kBM, kBN, kWM, kWN, true, false>(
-                a_base, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid, tile_cols, smem,
-                [&](const auto& eng) { eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem); },
-                ga);
+            auto st = [&](const auto& eng) { eng.store_swiglu(y, Ncols, h, N, Ncols, rows_valid, cols_left, smem); };
+            if (rows_valid > kBM)
+                gemm_tile<kTallM, kBN, kWM, kWN, true, false, kNST, kSmemTallElems>(
+                    a_base, lda, rows_valid, We + n0, N, cols_left, Ncols, Kred, rows_valid, tile_cols, smem, st, ga);
+            else
+                gemm_tile<kBM, kBN, kWM, kWN, true, false>(a_base, lda, rows_valid, We + n0, N, cols_left, Ncols,
+                                                          Kred, rows_valid, tile_cols, smem, st, ga);
         } else {
             bf16_t* y = Y + (int64_t)row0 * Ncols + n0;
             const bf16_t* b_base = IS_DX ? We + (int64_t)n0 * N : We + n0;

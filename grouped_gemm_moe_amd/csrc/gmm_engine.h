@@ -247,6 +247,77 @@ struct Dma<BO, false> {
     }
 };
 
+// Reduction-contiguous operand whose rows do not split evenly over the waves
+// (BO = 320: 20 copies of 16 rows per stage for 8 waves).  Copy g = w +
+// kWaves * i of wave w fills rows 16g .. 16g+15 at LDS slot g, the same
+// layout as Dma<BO, true>; a wave's copies past the last one go, with every
+// lane out of range, to a spare 1 KiB slot (`spare`), so that every wave
+// issues the same number of copies and the in-order wait counts hold.
+template <int BO>
+struct DmaTallA {
+    static constexpr int kCPR = BK / 8;
+    static constexpr int kRowsPerInst = 64 / kCPR;
+    static constexpr int kInstTotal = BO / kRowsPerInst;
+    static constexpr int kInst = (kInstTotal + kWaves - 1) / kWaves;  // per wave
+    static_assert(BO % kRowsPerInst == 0, "whole copies");
+    uint32_t off[kInst];
+    int red[kInst];
+    uint32_t ok_mask;
+    bf16_t* spare;
+
+    MOE_DEVICE int slot(int i) const { return wave_id() + kWaves * i; }
+    MOE_DEVICE void init(int64_t ld, int outer_lim, int pair = 0) {
+        (void)pair;
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int g = wid + kWaves * i;
+            const int o = g * kRowsPerInst + lane / kCPR;
+            const int c = (lane % kCPR) ^ swz_k(o);
+            off[i] = (uint32_t)(((int64_t)o * ld + c * 8) * 2);
+            red[i] = c * 8;
+            if (g < kInstTotal && o < outer_lim) ok_mask |= 1u << i;
+        }
+    }
+    MOE_DEVICE void init_gather(int64_t ld, int outer_lim, const RowGather& gt) {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        ok_mask = 0;
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) {
+            const int g = wid + kWaves * i;
+            const int o = g * kRowsPerInst + lane / kCPR;
+            const int c = (lane % kCPR) ^ swz_k(o);
+            int tok = 0;
+            if (g < kInstTotal && o < outer_lim) {
+                const int sl = gt.slot[o];
+                if (sl >= 0 && sl < gt.nslots) {
+                    tok = sl / gt.top_k;
+                    ok_mask |= 1u << i;
+                } else {
+                    bad = true;
+                }
+            }
+            off[i] = (uint32_t)(((int64_t)tok * ld + c * 8) * 2);
+            red[i] = c * 8;
+        }
+        if (bad && gt.dev_err) atomicOr(gt.dev_err, MOE_DEVERR_SLOT);
+    }
+    MOE_DEVICE void issue_one(int i, __amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, int red_left) const {
+        const uint32_t v = ((ok_mask >> i) & 1u) && red[i] < red_left ? off[i] : kOOB;
+        const int g = slot(i);
+        bf16_t* dst = g < kInstTotal ? lds + g * 512 : spare;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, v, 0, 0, 0);
+    }
+    MOE_DEVICE void issue(const bf16_t* stage_base, bf16_t* lds, int red_left) const {
+        const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(stage_base);
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) issue_one(i, rsrc, lds, red_left);
+    }
+    static MOE_DEVICE const bf16_t* stage(const bf16_t* base, int64_t, int s) { return base + s * BK; }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA operand fragments: lane l gets T[o0 + l%32][k0 + 8*(l/32) + 0..7].
 //
@@ -559,14 +630,17 @@ struct Engine {
                                  bf16_t* smem) const {
         static_assert(TN == 2, "one gate and one up fragment per wave");
         constexpr int kCols = BN / 2, kChunks = kCols / 8;  // one output row: kChunks 16-byte chunks
-        static_assert(kChunks == 16 && 2 * BM * kCols <= kRingElems, "images fit the LDS array");
+        // A and G side by side when both images fit the LDS array, else one
+        // image at a time (A, then G, then U)
+        constexpr bool kTwo = 2 * BM * kCols <= kRingElems;
+        static_assert(kChunks == 16 && BM * kCols <= kRingElems, "images fit the LDS array");
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
         const int lane = tid & 63;
         const int wid = wave_id();
         const int wm = wid / WN, wn = wid % WN;
         bf16_t* img_a = smem;
-        bf16_t* img_g = smem + BM * kCols;
+        bf16_t* img_g = kTwo ? smem + BM * kCols : smem;
         auto put = [&](bf16_t* img, int r, int c, uint32_t lo, uint32_t hi) {
             u32x2_t pk;
             pk[0] = lo;
@@ -608,7 +682,7 @@ struct Engine {
                     av[q] = gv * silu_sigmoid(gv) * uv;
                 }
                 put(img_a, r, c, pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
-                if (h)
+                if (kTwo && h)
                     put(img_g, r, c, pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]),
                         pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]));
             }
@@ -616,8 +690,20 @@ struct Engine {
         __syncthreads();
         copy_out(img_a, a, lda);
         if (!h) return;
+        if constexpr (!kTwo) {
+            __syncthreads();  // image A is read out; G takes its place
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    put(img_g, r, wn * 4 + g, pack_bf16x2(acc[i][0][4 * g], acc[i][0][4 * g + 1]),
+                        pack_bf16x2(acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]));
+            }
+            __syncthreads();
+        }
         copy_out(img_g, h, ldh);
-        __syncthreads();  // image A is read out; U takes its place
+        __syncthreads();  // the image is read out; U takes its place
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm * WTM + i * 32 + (lane & 31);
@@ -642,18 +728,23 @@ struct Engine {
 // `smem` holds NST stages of [A tile | B tile].
 // `store(eng)` writes the result; rows_valid / cols_valid (in tile columns)
 // decide which waves have any work.
-template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, int NST = kNST, class Store>
+// LDS_ELEMS: size of `smem`.  An A tile whose rows do not split evenly over
+// the waves (DmaTallA) also uses 512 elements after the ring.
+template <int BM, int BN, int WM, int WN, bool A_KMAJOR, bool B_KMAJOR, int NST = kNST,
+          int LDS_ELEMS = kRingElems, class Store>
 MOE_DEVICE void gemm_tile(const bf16_t* a_base, int64_t lda, int a_olim, const bf16_t* b_base,
                           int64_t ldb, int b_olim, int b_pair, int red_len, int rows_valid,
                           int cols_valid, bf16_t* smem, const Store& store,
                           const RowGather& gather = RowGather{nullptr, 1, 0, nullptr}) {
-    using DA = Dma<BM, A_KMAJOR>;
+    constexpr bool kTallA = A_KMAJOR && BM % (Dma<256, true>::kRowsPerInst * kWaves) != 0;
+    using DA = std::conditional_t<kTallA, DmaTallA<BM>, Dma<BM, A_KMAJOR>>;
     using DB = Dma<BN, B_KMAJOR>;
     constexpr int kStage = (BM + BN) * BK;       // elements per stage
     constexpr int kPer = DA::kInst + DB::kInst;  // loads per wave per stage
-    static_assert(NST >= 2 && NST * kStage <= kRingElems, "ring within the LDS array");
+    static_assert(NST >= 2 && NST * kStage + (kTallA ? 512 : 0) <= LDS_ELEMS, "ring within the LDS array");
     DA da;
     DB db;
+    if constexpr (kTallA) da.spare = smem + NST * kStage;
     if constexpr (A_KMAJOR) {
         if (gather.slot) da.init_gather(lda, a_olim, gather);
         else da.init(lda, a_olim);
@@ -791,6 +882,62 @@ MOE_DEVICE RowTile row_tile_at(const int* s_off, const int* s_cnt, const int* s_
     rt.row0 = __builtin_amdgcn_readfirstlane(s_off[rt.e] + (mt - s_tst[rt.e]) * BM);
     const int row_end = __builtin_amdgcn_readfirstlane(s_off[rt.e] + s_cnt[rt.e]);
     rt.rows_valid = row_end - rt.row0 < BM ? row_end - rt.row0 : BM;
+    rt.nt = lt % NT;
+    return rt;
+}
+
+// ---------------------------------------------------------------------------
+// Row tiles with tall last tiles (the SwiGLU forward).  When an expert's rows
+// past its last full kBM-row tile number at most kTallM - kBM, that tile
+// takes them too (a kTallM x kBN tile: 8 waves of 160 x 64) instead of a
+// tile of their own, which would stream the whole weight panel again for a
+// few rows.  Every output still takes the same MFMAs in the same order.
+// ---------------------------------------------------------------------------
+constexpr int kTallM = 320;
+// LDS of a workgroup that runs tall tiles: a 4-stage ring of 320 x 256
+// tiles and the spare slot of DmaTallA.
+constexpr int kSmemTallElems = kNST * (kTallM + kBN) * BK + 512;
+
+MOE_DEVICE int tall_mtiles(int n) {
+    const int full = n / kBM, rem = n - full * kBM;
+    return (full >= 1 && rem > 0 && rem <= kTallM - kBM) ? full : (n + kBM - 1) / kBM;
+}
+
+// s_tst[e] = first row tile of expert e (tall_mtiles of each); returns the
+// total.  All threads of the block; ends with a barrier.
+MOE_DEVICE int tall_tile_starts(const int* s_cnt, int E, int* s_tst, int64_t* s_scan) {
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += tall_mtiles(s_cnt[e0 + i]);
+    int64_t total;
+    int64_t run = block_exclusive_scan<int64_t>(mine, s_scan, &total);
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) {
+            s_tst[e0 + i] = (int)run;
+            run += tall_mtiles(s_cnt[e0 + i]);
+        }
+    __syncthreads();
+    return (int)total;
+}
+
+// Logical tile lt (row tile lt / NT, column tile lt % NT); an expert's last
+// row tile holds all of its remaining rows (up to kTallM).
+MOE_DEVICE RowTile tall_tile_at(const int* s_off, const int* s_cnt, const int* s_tst, int E, int NT, int lt) {
+    const int mt = lt / NT;
+    int lo = 0, hi = E - 1;  // last expert whose first tile is <= mt
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tst[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    RowTile rt;
+    rt.e = __builtin_amdgcn_readfirstlane(lo);
+    const int local = __builtin_amdgcn_readfirstlane(mt - s_tst[rt.e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[rt.e]);
+    rt.row0 = __builtin_amdgcn_readfirstlane(s_off[rt.e] + local * kBM);
+    const int left = cnt - local * kBM;
+    rt.rows_valid = local == tall_mtiles(cnt) - 1 ? left : (left < kBM ? left : kBM);
     rt.nt = lt % NT;
     return rt;
 }

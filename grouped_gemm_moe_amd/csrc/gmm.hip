@@ -56,8 +56,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
     constexpr bool IS_DX = MODE == kDx;
     constexpr int kCols = MODE == kSwiGLU ? kBN / 2 : kBN;  // output columns per tile
-    // the SwiGLU forward runs tall tiles (tall_tile_at), whose ring is larger
-    __shared__ __attribute__((aligned(1024))) bf16_t smem[MODE == kSwiGLU ? kSmemTallElems : kSmemElems];
+    // room for the ring of tall tiles (tall_tile_at)
+    __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmemTallElems];
     __shared__ int64_t s_scan[kThreads / 64];
     __shared__ int s_off[kMaxExperts], s_cnt[kMaxExperts], s_tst[kMaxExperts];
     const int Ncols = IS_DX ? K : (MODE == kSwiGLU ? N / 2 : N);  // output columns
@@ -81,16 +81,22 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
     // 256 x 256 tiles, and only where that lowers the tile count of the
     // busiest workgroup (this schedule is static: a somewhat dearer half
     // tile that does not remove a tile round only lengthens it)
+    // (and, like the SwiGLU forward, tall last tiles), whichever lowers the
+    // round count more; tall tiles first where both tie
     constexpr bool kHalfTiles = MODE != kSwiGLU;
     const int NTH = (Ncols + kHN - 1) / kHN;
     int ntiles = (MODE == kSwiGLU ? tall_tile_starts(s_cnt, E, s_tst, s_scan)
                                   : row_tile_starts<kBM>(s_cnt, E, s_tst, s_scan)) * NT;
-    bool use_half = false;
+    bool use_half = false, use_tall = MODE == kSwiGLU;
     if constexpr (kHalfTiles) {
         const int per_wg = gridDim.x >> 3;
         const auto rounds = [&](int n) { return ((n + 7) / 8 + per_wg - 1) / per_wg; };
         const int nmixed = mixed_tile_count(s_cnt, E, NT, NTH, s_scan);
-        if (rounds(nmixed) < rounds(ntiles)) {
+        const int ntall = tall_tile_count(s_cnt, E, s_scan) * NT;
+        if (rounds(ntall) < rounds(ntiles) && rounds(ntall) <= rounds(nmixed)) {
+            use_tall = true;
+            ntiles = tall_tile_starts(s_cnt, E, s_tst, s_scan) * NT;
+        } else if (rounds(nmixed) < rounds(ntiles)) {
             use_half = true;
             ntiles = mixed_tile_starts(s_cnt, E, NT, NTH, s_tst, s_scan);
         }
@@ -103,8 +109,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
             const MixedTile mt = mixed_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j);
             e = mt.e, row0 = mt.row0, rows_valid = mt.rows_valid, nt = mt.nt, half = mt.half;
         } else {
-            const RowTile rt = MODE == kSwiGLU ? tall_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j)
-                                               : row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
+            const RowTile rt = use_tall ? tall_tile_at(s_off, s_cnt, s_tst, E, NT, xr.first + j)
+                                        : row_tile_at<kBM>(s_off, s_cnt, s_tst, E, NT, xr.first + j);
             e = rt.e, row0 = rt.row0, rows_valid = rt.rows_valid, nt = rt.nt;
         }
         const int n0 = __builtin_amdgcn_readfirstlane(nt * (half ? kHN : kCols));
@@ -133,6 +139,9 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void gmm_rows_kernel(
             if (half)
                 gemm_tile<kHM, kHN, kHWM, kHWN, true, IS_DX, kHNST>(a_base, lda, rows_valid, b_base, N, cols_left,
                                                                     0, Kred, rows_valid, cols_left, smem, st, ga);
+            else if (rows_valid > kBM)
+                gemm_tile<kTallM, kBN, kWM, kWN, true, IS_DX, kNST, kSmemTallElems>(
+                    a_base, lda, rows_valid, b_base, N, cols_left, 0, Kred, rows_valid, cols_left, smem, st, ga);
             else
                 gemm_tile<kBM, kBN, kWM, kWN, true, IS_DX>(a_base, lda, rows_valid, b_base, N, cols_left, 0, Kred,
                                                           rows_valid, cols_left, smem, st, ga);

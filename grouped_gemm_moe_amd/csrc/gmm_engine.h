@@ -382,6 +382,15 @@ MOE_DEVICE void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
+// f(integral_constant<int, i>) for i = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+MOE_DEVICE void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The tile engine: C[BM][BN] = A[BM][red] * B[red][BN], fp32 accumulation.
 // ---------------------------------------------------------------------------
@@ -468,45 +477,54 @@ struct Engine {
     MOE_DEVICE void store(bf16_t* __restrict__ out, int64_t ld, int rows_valid, int cols_valid,
                           bf16_t* smem) const {
         static_assert(WTN == 64, "one 128-byte row segment per wave row");
+        // at most 4 fragments (128 rows) per pass through the wave's image:
+        // taller wave tiles (160 rows) take a second pass through the same
+        // image (each wave reads back its own writes first)
+        constexpr int kPassFr = TM < 4 ? TM : 4;
+        static_assert(kWaves * kPassFr * 32 * WTN <= kRingElems, "images fit the LDS array");
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));  // keeps this address math out of an enclosing tile loop
         const int lane = tid & 63;
         const int wid = wave_id();
         const int wm = wid / WN, wn = wid % WN;
         __syncthreads();  // every wave is done reading the ring
-        bf16_t* img = smem + wid * (WTM * WTN);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = i * 32 + (lane & 31);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
-                    u32x2_t pk;
-                    pk[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-                    pk[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                    *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
-                }
-        }
-        // Each wave reads back only its own image (no barrier): all reads
-        // first, then one unconditional store per 8 rows, masked lanes
-        // getting an out-of-range offset, so the reads overlap each other.
-        constexpr int kIt = WTM / 8;
-        u32x4_t v[kIt];
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int r = it * 8 + (lane >> 3), c = lane & 7;
-            v[it] = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
-        }
+        bf16_t* img = smem + wid * (kPassFr * 32 * WTN);
         const int c = lane & 7;
         const uint32_t lane_off = (uint32_t)(((int64_t)(lane >> 3) * ld + c * 8) * 2);
+        static_for<0, (TM + kPassFr - 1) / kPassFr>([&](auto pc_) {
+            constexpr int p0 = decltype(pc_)::value * kPassFr;
+            constexpr int np = TM - p0 < kPassFr ? TM - p0 : kPassFr;
 #pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-            const int row = wm * WTM + it * 8 + (lane >> 3), col = wn * WTN + c * 8;
-            const bool ok = row < rows_valid && col < cols_valid;
-            store_nt16(v[it], out + (int64_t)(wm * WTM + it * 8) * ld + wn * WTN, ok ? lane_off : kOOB);
-        }
+            for (int i = 0; i < np; ++i) {
+                const int r = i * 32 + (lane & 31);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int pc = (j * 4 + g) ^ ((r >> 1) & 7);
+                        u32x2_t pk;
+                        pk[0] = pack_bf16x2(acc[p0 + i][j][4 * g + 0], acc[p0 + i][j][4 * g + 1]);
+                        pk[1] = pack_bf16x2(acc[p0 + i][j][4 * g + 2], acc[p0 + i][j][4 * g + 3]);
+                        *reinterpret_cast<u32x2_t*>(img + r * 64 + pc * 8 + (lane >> 5) * 4) = pk;
+                    }
+            }
+            // Each wave reads back only its own image (no barrier): all reads
+            // first, then one unconditional store per 8 rows, masked lanes
+            // getting an out-of-range offset, so the reads overlap each other.
+            constexpr int kIt = np * 4;
+            u32x4_t v[kIt];
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int r = it * 8 + (lane >> 3);
+                v[it] = *reinterpret_cast<const u32x4_t*>(img + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+            }
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int r0 = wm * WTM + p0 * 32 + it * 8;
+                const bool ok = r0 + (lane >> 3) < rows_valid && wn * WTN + c * 8 < cols_valid;
+                store_nt16(v[it], out + (int64_t)r0 * ld + wn * WTN, ok ? lane_off : kOOB);
+            }
+        });
     }
 
     // Input-gradient tile of the down GMM fused with the SwiGLU backward.
@@ -918,6 +936,20 @@ MOE_DEVICE int tall_tile_starts(const int* s_cnt, int E, int* s_tst, int64_t* s_
             s_tst[e0 + i] = (int)run;
             run += tall_mtiles(s_cnt[e0 + i]);
         }
+    __syncthreads();
+    return (int)total;
+}
+
+// The total of tall_tile_starts without the per-expert starts.  All
+// threads of the block; ends with a barrier.
+MOE_DEVICE int tall_tile_count(const int* s_cnt, int E, int64_t* s_scan) {
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += tall_mtiles(s_cnt[e0 + i]);
+    int64_t total;
+    block_exclusive_scan<int64_t>(mine, s_scan, &total);
     __syncthreads();
     return (int)total;
 }

@@ -249,12 +249,13 @@ def _expert_of(gl):
 
 
 def test_half_height_tiles_prefill_groups(dev):
-    """The prefill routing (128 experts of ~256 rows): an expert's last <= 128
-    rows run as half-height tiles (128 x 512) in the forward and input-gradient
-    launches wherever that removes a tile round -- here the [32768, 512] x
-    [512, 2048] forward and the input gradient with 2048 output columns.
-    Sampled rows (every expert's first and last rows among them) against the
-    oracle, and bit-equality with gmm_bwd, whose queue always uses them."""
+    """The prefill routing (128 experts of ~256 rows): the forward and
+    input-gradient launches take an expert's last rows into its last full
+    tile (tall tiles, at most 64 rows past it) where that removes a tile
+    round -- here the [32768, 512] x [512, 2048] forward and the input
+    gradient with 2048 output columns -- while gmm_bwd's queue runs them as
+    half-height tiles.  Sampled rows (every expert's first and last rows among
+    them) against the oracle, and bit-equality of the two shapes' dX."""
     wl = workloads.prefill(with_weights=False)
     gl = oracle.tokens_per_expert(wl["topk_ids"], 128)
     R, E, K, N = int(gl.sum()), 128, 512, 2048
@@ -284,6 +285,68 @@ def test_half_height_tiles_prefill_groups(dev):
         ref = f64(a_b[r]) @ wf[eo[r]]
         assert_close(y_s[i], ref, f"fwd row {r}")
         assert_close(dx_s[i], ref, f"dX row {r}")
+
+
+def _check_rows(dev, a_b, w_b, gl, outs, rng, tag):
+    """Sampled rows of each output in outs (name -> (tensor, weight bits
+    [E, K, N] it multiplies by)) against the oracle's row products."""
+    rows = _sample_rows(gl, rng, per_expert=1)
+    eo = _expert_of(gl)
+    ridx = torch.from_numpy(rows).to(dev)
+    for name, (t, wb) in outs.items():
+        got = dev_f64(t[ridx])
+        wf = f64(wb)
+        for i, r in enumerate(rows):
+            assert_close(got[i], f64(a_b[r]) @ wf[eo[r]], f"{tag} {name} row {r}")
+
+
+@pytest.mark.parametrize("shape", ["tall", "half"])
+def test_tall_and_half_tile_schedules(dev, shape):
+    """The static forward / input-gradient schedules at their boundaries.
+    tall: 256 experts of 257 .. 320 rows (1 .. 64 past a full tile) with
+    256 output columns: tall last tiles halve the tile count (2 rounds -> 1),
+    half-height tiles do not.  half: 356 rows each (100 past a full tile:
+    no tall tile) with 1024 output columns: half-height tiles take 8 rounds to
+    6.  The SwiGLU forward (always tall) on the same rows, its H bit-equal to
+    gmm_fwd with the same weights; dX bit-equal to gmm_bwd's (always
+    half-height tiles)."""
+    E = 256
+    if shape == "tall":
+        gl = np.array([(257, 280, 300, 320)[e % 4] for e in range(E)], dtype=np.int64)
+        K, N = 256, 256
+    else:
+        gl = np.full(E, 356, dtype=np.int64)
+        K, N = 256, 1024
+    R = int(gl.sum())
+    rng = np.random.default_rng(91)
+    a_b = workloads.normal_bf16(rng, (R, K))
+    w_b = workloads.normal_bf16(rng, (E, K, N), std=0.02)
+    g = _gl(dev, gl)
+    a, w = bf16_dev(a_b, dev), bf16_dev(w_b, dev)
+    wt = w.transpose(1, 2).contiguous()  # [E, N, K]: a @ wt[e]^T = a @ w[e]
+    print(f"tile schedules {shape}: E={E} R={R} K={K} N={N}", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = moe.gmm_fwd(a, w, g, dev_err=err)
+    dx = moe.gmm_bwd_input(a, wt, g, dev_err=err)
+    ws = torch.zeros(moe.gmm_workspace_size(E, R, N, K, moe.OP_BWD), dtype=torch.uint8, device=dev)
+    dx2, _ = moe.gmm_bwd(y, a, wt, g, ws=ws, dev_err=err)
+    h = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    a_sw = moe.gmm_fwd_swiglu(a, w, g, h_out=h, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dx2.view(torch.int16), dx.view(torch.int16)), "gmm_bwd dx != gmm_bwd_input"
+    assert torch.equal(h.view(torch.int16), y.view(torch.int16)), "gmm_fwd_swiglu H != gmm_fwd"
+    _check_rows(dev, a_b, w_b, gl, {"fwd": (y, w_b), "dX": (dx, w_b)}, rng, shape)
+    # A = SiLU(G) * U from the same rows
+    rows = _sample_rows(gl, rng, per_expert=1)
+    eo = _expert_of(gl)
+    got = dev_f64(a_sw[torch.from_numpy(rows).to(dev)])
+    I = N // 2
+    wf = f64(w_b)
+    for i, r in enumerate(rows):
+        gu = f64(a_b[r]) @ wf[eo[r]]
+        ref = gu[:I] / (1.0 + np.exp(-gu[:I])) * gu[I:]
+        assert_close(got[i], ref, f"{shape} swiglu row {r}")
 
 
 def test_ep_full_size_sampled(dev):

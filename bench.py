@@ -334,13 +334,15 @@ def decode_bytes(gl, T, K, H, I, fused=True, gathered=False):
     return w + act + idx, n_active
 
 
-def layer_forward(torch, dev, wl, steps, gather=False):
+def layer_forward(torch, dev, wl, steps, gather=False, routed=False):
     """Time the layer forward on workload `wl` -- permute -> gate_up GMM and
     SwiGLU (fused into one call, no H, except for decode-shaped calls where
     the weight-streaming gate_up + swiglu pair is faster) -> down GMM ->
     unpermute: wall ms per layer, per-call means, and whether it fused.
     gather: the permute computes the maps only and the gate_up GMM reads the
-    token rows through sorted_slot (no x_perm)."""
+    token rows through sorted_slot (no x_perm).  routed: the whole forward
+    as moe_decode_fwd (the routing fused into the gate_up GMM: no permute
+    launch)."""
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayer
 
     d = wl.dims
@@ -350,14 +352,17 @@ def layer_forward(torch, dev, wl, steps, gather=False):
     w2 = bf16_dev(torch, wl["w2"], dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     probs = torch.from_numpy(wl["probs"]).to(dev)
-    layer = MoeLayer(LayerShape(T, K, E, H, I), dev, gather_rows=gather)
+    layer = MoeLayer(LayerShape(T, K, E, H, I), dev, gather_rows=gather or routed)
     timer = KernelTimer(torch)
     from grouped_gemm_moe_amd import gmm_fwd, moe_unpermute, swiglu_gmm_fwd
     g = layer.tokens_per_expert
-    fused = layer.use_fused("auto")
+    fused = layer.use_fused("auto") and not routed
     sfx = "_gather" if gather else ""
 
     def step(t):
+        if routed:
+            t("moe_decode_fwd", lambda: layer.forward_decode(x, ids, probs, w1, w2))
+            return
         t("moe_permute_index" if gather else "moe_permute", lambda: layer.permute(x, ids))
         if fused:
             t("gmm_fwd_swiglu" + sfx, lambda: layer.gate_up(w1, True, keep_h=False))
@@ -442,6 +447,12 @@ def layer_roofline(gl, T, K, H, I, ms, fused=True, gathered=False):
 
 
 def run_decode(torch, dev, args):
+    """The decode layer forward as the library runs it for decode shapes,
+    moe_decode_fwd (the headline: routing fused into the weight-streaming
+    gate_up GMM, SwiGLU into the down GMM's row staging, then unpermute),
+    with the five-call chain (x_perm materialised, as a training forward
+    needs) and the gathered chain beside it, each on the normal and the
+    skewed routing."""
     import workloads
 
     wl = workloads.decode()
@@ -449,8 +460,7 @@ def run_decode(torch, dev, args):
     T, K, H, I = d["T"], d["K"], d["H"], d["I"]
     ms, per, gl, (_, _, fused, spans) = layer_forward(torch, dev, wl, args.decode_steps)
     roof = layer_roofline(gl, T, K, H, I, ms, fused)
-    nbytes, n_active = roof["bytes_per_layer"], roof["active_experts"]
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    n_active = roof["active_experts"]
     gate_up = "gmm_fwd_swiglu" if fused else "gmm_fwd_gate_up"
     down = "gmm_fwd_down" if fused else "swiglu_gmm_fwd_down"
     wbytes = {k: n_active * (H * 2 * I if k == gate_up else I * H) * 2 for k in (gate_up, down)}
@@ -458,22 +468,33 @@ def run_decode(torch, dev, args):
     sk = workloads.decode_skewed()
     ms_s, per_s, gl_s, (_, _, fused_s, _) = layer_forward(torch, dev, sk, args.decode_steps)
     roof_s = layer_roofline(gl_s, T, K, H, I, ms_s, fused_s)
-    skewed = dict(workload="decode layer forward, expert 7 routed 48 more tokens (max rows per expert "
-                           f"{int(np.max(gl_s))})",
-                  ms_per_layer=round(ms_s, 4),
-                  gb_per_s=round(roof_s["bytes_per_layer"] / (ms_s * 1e-3) / 1e9, 1),
-                  per_call_us={k: round(v * 1e3, 2) for k, v in per_s.items()})
+    chain = dict(workload="the same layer as five calls: moe_permute (x_perm materialised) -> gmm_fwd "
+                          "(gate_up) -> swiglu_gmm_fwd -> moe_unpermute",
+                 ms_per_layer=round(ms, 4), layer_ms_events=spans,
+                 gb_per_s=round(roof["bytes_per_layer"] / (ms * 1e-3) / 1e9, 1),
+                 bytes_per_layer=roof["bytes_per_layer"], frac_of_attainable=roof["frac_of_attainable"],
+                 per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
+                 gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
+                 skewed=dict(ms_per_layer=round(ms_s, 4),
+                             gb_per_s=round(roof_s["bytes_per_layer"] / (ms_s * 1e-3) / 1e9, 1),
+                             per_call_us={k: round(v * 1e3, 2) for k, v in per_s.items()}))
     gathered = gathered_layer(torch, dev, wl, args.decode_steps, T, K, H, I)
+    routed = routed_layer(torch, dev, wl, args.decode_steps, T, K, H, I)
+    routed_s = routed_layer(torch, dev, sk, args.decode_steps, T, K, H, I)
+    gbs = routed["gb_per_s"]
     return dict(
         metric="decode MoE layer HBM GB/s",
-        workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, "
-                 "intermediate 512; permute -> gate_up (weight streaming) -> SwiGLU -> down -> unpermute",
-        value=round(gbs, 1), unit="GB/s", ms_per_layer=round(ms, 4), layer_ms_events=spans,
-        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=nbytes,
-        active_experts=n_active, frac_of_attainable=roof["frac_of_attainable"],
-        per_call_us={k: round(v * 1e3, 2) for k, v in per.items()},
-        gmm_weight_stream_gbs={k: round(wbytes[k] / (per[k] * 1e-3) / 1e9, 1) for k in wbytes},
-        skewed=skewed,
+        workload="decode layer forward: T=64 tokens, top-8 of E=256, hidden 2048, intermediate 512; "
+                 "moe_decode_fwd: permute fused into the weight-streaming gate_up GMM -> SwiGLU fused into "
+                 "the down GMM -> unpermute",
+        value=gbs, unit="GB/s", ms_per_layer=routed["ms_per_layer"], layer_ms_events=routed["layer_ms_events"],
+        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), bytes_per_layer=routed["bytes_per_layer"],
+        active_experts=n_active, frac_of_attainable=routed["frac_of_attainable"],
+        per_call_us=routed["per_call_us"],
+        skewed=dict(workload="decode layer forward, expert 7 routed 48 more tokens (max rows per expert "
+                             f"{int(np.max(gl_s))})",
+                    ms_per_layer=routed_s["ms_per_layer"], gb_per_s=routed_s["gb_per_s"]),
+        chain=chain,
         gathered=gathered,
     )
 
@@ -485,6 +506,18 @@ def gathered_layer(torch, dev, wl, steps, T, K, H, I):
     the x_perm write and read."""
     ms, per, gl, (_, _, fused, spans) = layer_forward(torch, dev, wl, steps, gather=True)
     roof = layer_roofline(gl, T, K, H, I, ms, fused, gathered=True)
+    return dict(ms_per_layer=round(ms, 4), layer_ms_events=spans,
+                gb_per_s=round(roof["bytes_per_layer"] / (ms * 1e-3) / 1e9, 1),
+                bytes_per_layer=roof["bytes_per_layer"], roofline_ms=roof["roofline_ms"],
+                frac_of_attainable=roof["frac_of_attainable"],
+                per_call_us={k: round(v * 1e3, 2) for k, v in per.items()})
+
+
+def routed_layer(torch, dev, wl, steps, T, K, H, I):
+    """The decode layer forward as moe_decode_fwd: the gathered path's
+    tensors (same algorithmic bytes) without its permute launch."""
+    ms, per, gl, (_, _, _, spans) = layer_forward(torch, dev, wl, steps, routed=True)
+    roof = layer_roofline(gl, T, K, H, I, ms, False, gathered=True)
     return dict(ms_per_layer=round(ms, 4), layer_ms_events=spans,
                 gb_per_s=round(roof["bytes_per_layer"] / (ms * 1e-3) / 1e9, 1),
                 bytes_per_layer=roof["bytes_per_layer"], roofline_ms=roof["roofline_ms"],
@@ -814,7 +847,7 @@ def main():
     if not args.skip_decode:
         decode = run_decode(torch, dev, args)
         log(f"decode: {decode['ms_per_layer']:.4f} ms, {decode['value']:.0f} GB/s; {decode['per_call_us']}")
-        log(f"decode, one hot expert: {decode['skewed']}")
+        log(f"decode, one hot expert: {decode['skewed']}; five-call chain: {decode['chain']}")
         prefill = run_prefill(torch, dev, args)
         log(f"prefill: {prefill['ms_per_layer']:.4f} ms, {prefill['value']:.1f} % of attainable "
             f"({prefill['bound']}-bound); {prefill['per_call_us']}")

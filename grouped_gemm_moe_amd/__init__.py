@@ -27,7 +27,7 @@ __all__ = [
     "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "swiglu_gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
     "gmm_bwd_swiglu",
     "swiglu",
-    "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd",
+    "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd", "moe_decode_fwd",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
     "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_mx_fwd_swiglu_gather",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP", "DEVERR_SLOT",
@@ -407,6 +407,43 @@ def moe_unpermute(y_perm, row_id_map, probs, *, out=None, dev_err=None):
     _check(library().moe_unpermute(_ptr(y_perm), _ptr(row_id_map), _ptr(probs), T, top_k, H,
                                    _ptr(o), _ptr(dev_err), _stream(y_perm.device)), "moe_unpermute")
     return o
+
+
+def moe_decode_fwd(x, topk_ids, probs, w1, w2, *, out=None, dev_err=None):
+    """The decode-shaped layer forward with the routing fused into the
+    gate_up GMM (three launches, no permute launch).  Returns (out,
+    row_id_map, sorted_slot, tokens_per_expert, h, a, y_perm), all
+    bit-identical to moe_permute_index -> gmm_fwd_gather -> swiglu_gmm_fwd ->
+    moe_unpermute; out= takes a tuple of the same seven (None entries are
+    allocated)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    _dev(w1, "w1", torch.bfloat16)
+    _dev(w2, "w2", torch.bfloat16)
+    T, H = x.shape
+    E, H1, I2 = w1.shape
+    I = I2 // 2
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T or tuple(probs.shape) != tuple(topk_ids.shape):
+        raise MoeError("topk_ids and probs must be [T, top_k] for x [T, H]")
+    if H1 != H or tuple(w2.shape) != (E, I, H) or I2 != 2 * I:
+        raise MoeError("shape mismatch: x [T, H], w1 [E, H, 2I], w2 [E, I, H]")
+    top_k = topk_ids.shape[1]
+    S = T * top_k
+    dev = x.device
+    o = tuple(out) if out is not None else (None,) * 7
+    if len(o) != 7:
+        raise MoeError("out= takes (out, row_id_map, sorted_slot, tokens_per_expert, h, a, y_perm)")
+    res = (_out(o[0], (T, H), torch.bfloat16, dev, "out"),
+           _out(o[1], (S,), torch.int32, dev, "row_id_map"),
+           _out(o[2], (S,), torch.int32, dev, "sorted_slot"),
+           _out(o[3], (E,), torch.int64, dev, "tokens_per_expert"),
+           _out(o[4], (S, 2 * I), torch.bfloat16, dev, "h"),
+           _out(o[5], (S, I), torch.bfloat16, dev, "a"),
+           _out(o[6], (S, H), torch.bfloat16, dev, "y_perm"))
+    _check(library().moe_decode_fwd(_ptr(x), _ptr(topk_ids), _ptr(probs), _ptr(w1), _ptr(w2), T, top_k, H, I,
+                                    E, *[_ptr(t) for t in res], _ptr(dev_err), _stream(dev)), "moe_decode_fwd")
+    return res
 
 
 def moe_unpermute_bwd(dout, y_perm, row_id_map, probs, *, out=None, dev_err=None):

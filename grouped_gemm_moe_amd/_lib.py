@@ -38,6 +38,8 @@ SIGNATURES = {
     "swiglu": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
     "swiglu_bwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "moe_unpermute": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "moe_decode_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p,
+                              _p, _p]),
     "moe_unpermute_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "moe_permute_bwd": (_int, [_p, _p, _i64, _i64, _i64, _p, _p, _p]),
     "mx_quantize": (_int, [_p, _i64, _i64, _i64, _p, _p, _p]),
@@ -50,7 +52,7 @@ SIGNATURES = {
                                         _i64, _p, _p, _i64, _p, _p]),
 }
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _lib = None
 

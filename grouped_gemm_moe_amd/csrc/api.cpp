@@ -103,7 +103,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 9; }
+int moegmm_abi_version(void) { return 10; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -359,6 +359,38 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, cons
         return MOE_ERR_INVALID;
     return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err,
                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_decode_fwd(const uint16_t* x, const int32_t* topk_ids, const float* probs,
+                          const uint16_t* w1, const uint16_t* w2, int64_t T, int64_t top_k, int64_t H,
+                          int64_t I, int64_t E, uint16_t* out, int32_t* row_id_map, int32_t* sorted_slot,
+                          int64_t* tokens_per_expert, uint16_t* h, uint16_t* a, uint16_t* y_perm,
+                          int32_t* dev_err, void* stream) {
+    if (!w1 || !w2 || !tokens_per_expert) return MOE_ERR_NULL;
+    if (T > 0 && (!x || !topk_ids || !probs || !out || !row_id_map || !sorted_slot || !h || !a || !y_perm))
+        return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || !dim_ok(H) || !dim_ok(I) ||
+        T * top_k > kMaxRows || !moegmm::decode_fwd_applies(T, top_k, H, I, E))
+        return MOE_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) || !aligned(h, 16) ||
+        !aligned(a, 16) || !aligned(y_perm, 16) || !aligned(topk_ids, 4) || !aligned(probs, 4) ||
+        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4) || !aligned(tokens_per_expert, 8))
+        return MOE_ERR_INVALID;
+    const size_t S = (size_t)(T * top_k);
+    const void* buf[] = {x, topk_ids, probs, out, row_id_map, sorted_slot, tokens_per_expert, h, a, y_perm};
+    const size_t len[] = {(size_t)(T * H) * 2, S * 4, S * 4, (size_t)(T * H) * 2, S * 4, S * 4,
+                          (size_t)E * 8, S * 2 * (size_t)I * 2, S * (size_t)I * 2, S * (size_t)H * 2};
+    // every output (index 3 on) apart from every other buffer
+    for (int i = 3; i < 10; ++i)
+        for (int j = 0; j < 10; ++j)
+            if (i != j && overlaps(buf[i], len[i], buf[j], len[j])) return MOE_ERR_INVALID;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = moegmm::launch_gmm_stream_route(x, topk_ids, T, top_k, w1, E, H, 2 * I, h, row_id_map,
+                                                   sorted_slot, tokens_per_expert, dev_err, hs);
+    if (e != hipSuccess || T == 0) return from_hip(e);
+    e = moegmm::launch_stream_swiglu_in(h, w2, tokens_per_expert, E, (int64_t)S, I, H, a, y_perm, dev_err, hs);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err, hs));
 }
 
 moe_status moe_unpermute_bwd(const uint16_t* dout, const uint16_t* y_perm,

@@ -14,6 +14,10 @@
 // (its second pass mostly from L2) instead of one block walking its groups
 // in turn: with one block per (expert, slice), a decode step where one
 // expert held 48 more rows than the rest took 2.5x as long.
+//
+// The decode layer forward of moe_decode_fwd uses a routed form of the
+// gate_up launch: every block counts the expert histogram of topk_ids and
+// ranks its own expert's slots, so no permute launch runs before it.
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -97,6 +101,84 @@ MOE_DEVICE int sub_unit_starts(const int* s_cnt, int E, int NB, int* s_su, int64
     return (int)total;
 }
 
+// The routed gate_up (moe_decode_fwd): routing inputs and the maps it writes.
+struct RouteArgs {
+    const int32_t* ids = nullptr;          // [T * top_k] expert of each slot, or -1
+    int32_t* row_id_map = nullptr;         // [T * top_k] slot -> row (OUT)
+    int32_t* sorted_slot = nullptr;        // [T * top_k] row -> slot (OUT)
+    int64_t* tokens_per_expert = nullptr;  // [E] (OUT)
+};
+
+// Slots [s0, s1) of this thread: S slots in contiguous chunks, so that
+// ranks in slot order follow from one block scan of per-thread counts.
+MOE_DEVICE void slot_chunk(int S, int& s0, int& s1) {
+    const int C = (S + kThreads - 1) / kThreads;
+    s0 = threadIdx.x * C < S ? threadIdx.x * C : S;
+    s1 = s0 + C < S ? s0 + C : S;
+}
+
+// The routed gate_up's group ranges: every block counts the histogram of the
+// slots' expert ids itself (ids outside [-1, E) count nowhere and, from the
+// block with `report`, set MOE_DEVERR_EXPERT_ID), then takes the exclusive
+// offsets -- the tokens_per_expert and row offsets that moe_permute_index
+// produces.  All threads; ends with a barrier.
+MOE_DEVICE void route_group_ranges(const int32_t* __restrict__ ids, int S, int E, int* s_off, int* s_cnt,
+                                   int64_t* s_scan, int32_t* dev_err, bool report) {
+    for (int e = threadIdx.x; e < E; e += kThreads) s_cnt[e] = 0;
+    __syncthreads();
+    int s0, s1;
+    slot_chunk(S, s0, s1);
+    bool bad = false;
+    for (int s = s0; s < s1; ++s) {
+        const int id = ids[s];
+        if (id >= 0 && id < E) atomicAdd(&s_cnt[id], 1);
+        else bad |= id != -1;
+    }
+    if (bad && report && dev_err) atomicOr(dev_err, MOE_DEVERR_EXPERT_ID);
+    __syncthreads();
+    const int per = (E + kThreads - 1) / kThreads;
+    const int e0 = threadIdx.x * per;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) mine += s_cnt[e0 + i];
+    int64_t total;
+    int64_t run = block_exclusive_scan<int64_t>(mine, s_scan, &total);
+    for (int i = 0; i < per; ++i)
+        if (e0 + i < E) {
+            s_off[e0 + i] = (int)run;
+            run += s_cnt[e0 + i];
+        }
+    __syncthreads();
+}
+
+// The slots of expert e ranked rank0 .. rank0 + rows - 1 in slot order, into
+// s_rows.  All threads; ends with a barrier.
+MOE_DEVICE void route_rows(const int32_t* __restrict__ ids, int S, int e, int rank0, int rows, int* s_rows,
+                           int64_t* s_scan) {
+    int s0, s1;
+    slot_chunk(S, s0, s1);
+    int64_t mine = 0;
+    for (int s = s0; s < s1; ++s) mine += ids[s] == e;
+    int64_t total;
+    int64_t rank = block_exclusive_scan<int64_t>(mine, s_scan, &total);
+    for (int s = s0; s < s1 && rank < rank0 + rows; ++s)
+        if (ids[s] == e) {
+            if (rank >= rank0) s_rows[rank - rank0] = s;
+            ++rank;
+        }
+    __syncthreads();
+}
+
+// The routed gate_up's whole-call outputs, by one block: tokens_per_expert,
+// and row_id_map = -1 for the slots that take no part.
+MOE_DEVICE void route_call_outputs(const RouteArgs& ra, int E, int S, const int* s_cnt) {
+    for (int e = threadIdx.x; e < E; e += kThreads) ra.tokens_per_expert[e] = s_cnt[e];
+    for (int s = threadIdx.x; s < S; s += kThreads) {
+        const int id = ra.ids[s];
+        if (!(id >= 0 && id < E)) ra.row_id_map[s] = -1;
+    }
+}
+
 // Block = one sub-unit.  A wave holds kGroupsPerWave k-groups of kLanes
 // column lanes; a lane owns 8 columns and walks k-chunks of 8 rows, so each
 // step is eight 16-byte weight loads feeding 8 x 8 x ROWS fp32 FMAs.  The
@@ -118,11 +200,19 @@ MOE_DEVICE int sub_unit_starts(const int* s_cnt, int E, int NB, int* s_su, int64
 // rows are A = SiLU(G) * U of its halves, rounded as the swiglu kernel
 // rounds them; Hout, when given, receives A [M_cap, K] (from the sub-units
 // of the first column slice).
-template <bool SWIGLU, bool SWIGLU_IN = false>
+//
+// ROUTE (plain gate_up, X the token matrix): the group ranges and the rows'
+// slots come from ra.ids (route_group_ranges, route_rows) instead of
+// group_list and slot; the blocks of the first column slice write
+// sorted_slot and row_id_map for their rows, and the grid's last block the
+// call outputs (route_call_outputs).
+template <bool SWIGLU, bool SWIGLU_IN = false, bool ROUTE = false>
 __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const int64_t* __restrict__ group_list,
     int E, int64_t M_cap, int K, int N, bf16_t* __restrict__ Y, bf16_t* __restrict__ Hout,
-    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots, const RouteArgs ra) {
+    static_assert(!ROUTE || (!SWIGLU && !SWIGLU_IN), "the routed form is the plain gate_up");
+    __shared__ int s_rows[kStreamRows];
     constexpr int kOutCols = SWIGLU ? kStreamCols / 2 : kStreamCols;  // output columns per sub-unit
     // Dynamic LDS (stream_lds_bytes): the staged rows, whose space the
     // k-group partial sums reuse once every wave has left the streaming loop,
@@ -136,7 +226,13 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     int* s_cnt = s_off + E;
     int* s_su = s_cnt + E;
 
-    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    if constexpr (ROUTE) {
+        const bool last = blockIdx.x == gridDim.x - 1;
+        route_group_ranges(ra.ids, nslots, E, s_off, s_cnt, s_scan, dev_err, last);
+        if (last) route_call_outputs(ra, E, nslots, s_cnt);
+    } else {
+        load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    }
     const int Nout = SWIGLU ? N / 2 : N;
     const int NB = (Nout + kOutCols - 1) / kOutCols;
     const int SU = sub_unit_starts(s_cnt, E, NB, s_su, s_scan);
@@ -162,12 +258,21 @@ __global__ __launch_bounds__(kThreads) void gmm_stream_kernel(
     const bool col_ok = ocol < Nout;
     const bf16_t* We = W + (int64_t)e * K * N + col;
 
+    if constexpr (ROUTE) {
+        route_rows(ra.ids, nslots, e, g * kStreamRows, rows, s_rows, s_scan);
+        if (nb == 0 && tid < rows) {
+            ra.sorted_slot[off + tid] = s_rows[tid];
+            ra.row_id_map[s_rows[tid]] = off + tid;
+        }
+    }
+
     // source row of each staged row (-1: zeros)
     int src[kStreamRows];
     bool bad = false;
 #pragma unroll
     for (int r = 0; r < kStreamRows; ++r) {
         src[r] = r < rows ? off + r : -1;
+        if constexpr (ROUTE) src[r] = r < rows ? s_rows[r] / top_k : -1;
         if (slot && r < rows) {
             const int s = slot[off + r];
             const bool ok = s >= 0 && s < nslots;
@@ -312,11 +417,11 @@ static hipError_t launch_stream(bool swiglu, const uint16_t* x, const uint16_t* 
     if (swiglu)
         hipLaunchKernelGGL(gmm_stream_kernel<true>, grid, dim3(kThreads), shmem, stream, x, w, group_list,
                            (int)E, M_cap, (int)K, (int)N, y, h, dev_err, g.slot, (int)g.top_k,
-                           (int)g.nslots);
+                           (int)g.nslots, RouteArgs{});
     else
         hipLaunchKernelGGL(gmm_stream_kernel<false>, grid, dim3(kThreads), shmem, stream, x, w, group_list,
                            (int)E, M_cap, (int)K, (int)N, y, nullptr, dev_err, g.slot, (int)g.top_k,
-                           (int)g.nslots);
+                           (int)g.nslots, RouteArgs{});
     return hipGetLastError();
 }
 
@@ -333,7 +438,33 @@ hipError_t launch_stream_swiglu_in(const uint16_t* h, const uint16_t* w2, const 
     const int64_t blocks = max_sub_units(E, M_cap, N);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gmm_stream_kernel<false, true>), dim3((unsigned)blocks), dim3(kThreads), shmem, stream,
-                       h, w2, group_list, (int)E, M_cap, (int)I, (int)N, y, a, dev_err, nullptr, 1, 0);
+                       h, w2, group_list, (int)E, M_cap, (int)I, (int)N, y, a, dev_err, nullptr, 1, 0,
+                       RouteArgs{});
+    return hipGetLastError();
+}
+
+bool decode_fwd_applies(int64_t T, int64_t top_k, int64_t H, int64_t I, int64_t E) {
+    const int64_t S = T * top_k;
+    // both GMMs stage 4 rows of their reduction dim in at most 32 KiB; the
+    // routing scans every slot in each block, so the slots stay few
+    return S <= 8 * E && S <= 16384 && H * kStreamRows * 2 <= 32 * 1024 && I * kStreamRows * 2 <= 32 * 1024;
+}
+
+hipError_t launch_gmm_stream_route(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                                   const uint16_t* w1, int64_t E, int64_t K, int64_t N, uint16_t* h,
+                                   int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                                   int32_t* dev_err, hipStream_t stream) {
+    const int64_t S = T * top_k;
+    RouteArgs ra;
+    ra.ids = ids;
+    ra.row_id_map = row_id_map;
+    ra.sorted_slot = sorted_slot;
+    ra.tokens_per_expert = tokens_per_expert;
+    const int64_t blocks = max_sub_units(E, S, N);
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gmm_stream_kernel<false, false, true>), dim3((unsigned)blocks), dim3(kThreads),
+                       stream_lds_bytes(K, E), stream, x, w1, nullptr, (int)E, S, (int)K, (int)N, h, nullptr,
+                       dev_err, nullptr, (int)top_k, (int)S, ra);
     return hipGetLastError();
 }
 

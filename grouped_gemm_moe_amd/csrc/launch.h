@@ -88,6 +88,15 @@ hipError_t launch_gmm_stream_swiglu(const uint16_t* x, const uint16_t* w1,
                                     const int64_t* group_list, int64_t E, int64_t M_cap,
                                     int64_t K, int64_t I, uint16_t* a, uint16_t* h,
                                     int32_t* dev_err, hipStream_t stream, const GatherRows& g);
+// The decode layer forward (moe_decode_fwd): the shapes it takes, and its
+// gate_up launch, which routes its own rows from ids (moe_permute_index and
+// gmm_fwd_gather in one weight-streaming launch: h, the maps and
+// tokens_per_expert as those two calls write them).
+bool decode_fwd_applies(int64_t T, int64_t top_k, int64_t H, int64_t I, int64_t E);
+hipError_t launch_gmm_stream_route(const uint16_t* x, const int32_t* ids, int64_t T, int64_t top_k,
+                                   const uint16_t* w1, int64_t E, int64_t K, int64_t N, uint16_t* h,
+                                   int32_t* row_id_map, int32_t* sorted_slot, int64_t* tokens_per_expert,
+                                   int32_t* dev_err, hipStream_t stream);
 
 // gmm_mx.hip (MXFP8)
 hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const uint8_t* wq,

@@ -48,7 +48,7 @@ import torch
 
 from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_gather, gmm_fwd_swiglu,
                gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
-               gmm_workspace_size, moe_permute,
+               gmm_workspace_size, moe_decode_fwd, moe_permute,
                moe_permute_bwd, moe_permute_index, moe_permute_mx, moe_permute_workspace_size, moe_unpermute,
                moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd, swiglu_gmm_fwd)
 
@@ -169,6 +169,23 @@ class MoeLayer:
 
     def unpermute(self, probs):
         moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
+
+    def decode_applies(self) -> bool:
+        """Whether forward_decode takes this shape: a few rows per expert
+        (at most 8 slots per expert, at most 16384 slots) and H, I <= 4096."""
+        s = self.shape
+        return s.S <= 8 * s.E and s.S <= 16384 and s.H <= 4096 and s.I <= 4096
+
+    def forward_decode(self, x, topk_ids, probs, w1, w2):
+        """The same forward with the routing fused into the gate_up GMM
+        (moe_decode_fwd: no permute launch).  Fills the same buffers as
+        forward(..., fused=False) with a gather_rows layer, bit for bit."""
+        self.x_tokens = x
+        moe_decode_fwd(x, topk_ids, probs, w1, w2,
+                       out=(self.out, self.row_id_map, self.sorted_slot, self.tokens_per_expert, self.h,
+                            self.a, self.yp),
+                       dev_err=self.dev_err)
+        return self.out
 
     def forward(self, x, topk_ids, probs, w1, w2, fused=False, keep_h=True):
         self.permute(x, topk_ids)

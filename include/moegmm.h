@@ -385,6 +385,38 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, cons
                          void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_decode_fwd -- the whole routed-expert layer forward for decode-shaped
+ * calls (a few rows per expert), in three launches: the gate_up GMM routes
+ * its own rows (every workgroup of the weight-streaming kernel counts the
+ * expert histogram of topk_ids and ranks its own expert's slots, so no
+ * permute launch runs first: moe_permute_index and gmm_fwd_gather in one),
+ * then swiglu_gmm_fwd (the down GMM on SwiGLU(h)) and moe_unpermute.
+ * [MegaMoE] 功能说明 (dispatch fused into the first linear layer) and Token
+ * Combine; [GMM] "Qwen3.5 MoE 路径" (permute, gate_up GMM, SwiGLU, down GMM,
+ * unpermute).
+ *
+ *   x [T, H] bf16, topk_ids [T, top_k] int32 (or -1), probs [T, top_k] fp32,
+ *   w1 [E, H, 2I] bf16, w2 [E, I, H] bf16,
+ *   out [T, H] bf16 OUT             the layer output, as moe_unpermute
+ *   row_id_map, sorted_slot [T*top_k] int32, tokens_per_expert [E] int64 OUT
+ *                                   as moe_permute_index
+ *   h [T*top_k, 2I], a [T*top_k, I], y_perm [T*top_k, H] bf16 OUT
+ *                                   as gmm_fwd_gather / swiglu_gmm_fwd
+ *                                   (rows >= R untouched)
+ * Every output is bit-identical to the chain moe_permute_index ->
+ * gmm_fwd_gather -> swiglu_gmm_fwd -> moe_unpermute on the same inputs.
+ * Shapes: T*top_k <= 8*E and <= 16384, H <= 4096, I <= 4096 (else
+ * MOE_ERR_INVALID: use that chain).  Outputs must not overlap each other or
+ * the inputs.  Ids outside [-1, E) set MOE_DEVERR_EXPERT_ID and are masked.
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+moe_status moe_decode_fwd(const uint16_t* x, const int32_t* topk_ids, const float* probs,
+                          const uint16_t* w1, const uint16_t* w2, int64_t T, int64_t top_k, int64_t H,
+                          int64_t I, int64_t E, uint16_t* out, int32_t* row_id_map, int32_t* sorted_slot,
+                          int64_t* tokens_per_expert, uint16_t* h, uint16_t* a, uint16_t* y_perm,
+                          int32_t* dev_err, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_unpermute_bwd -- gradients of moe_unpermute with respect to y_perm and
  * probs, given dout = d(loss)/d(out):
  *   dy_perm[row(t,k), :] = probs[t, k] * dout[t, :]        (rounded once, RNE)

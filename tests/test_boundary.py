@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
               "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu",
               "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_mx_fwd_swiglu_gather",
-              "swiglu_gmm_fwd"]:
+              "swiglu_gmm_fwd", "moe_decode_fwd"]:
         assert n in names, n
 
 
@@ -337,3 +337,30 @@ def test_swiglu_gmm_fwd_rejects_bad_arguments(lib):
     assert f(a=MIS) == MOE_ERR_INVALID
     assert f(a=ctypes.c_void_p(0x100000 + 64 * 128 * 2 - 16)) == MOE_ERR_INVALID  # a overlaps h
     assert f(y=D2) == MOE_ERR_INVALID                                           # y overlaps a
+
+
+def test_decode_fwd_rejects_bad_arguments(lib):
+    """moe_decode_fwd(x, ids, probs, w1, w2, T, top_k, H, I, E, out, row_id_map,
+    sorted_slot, tokens_per_expert, h, a, y_perm, dev_err, stream): nothing
+    is enqueued for a call validation rejects."""
+    T, K, H, I, E = 16, 4, 256, 128, 32
+    base = [0x1000000 * (i + 1) for i in range(12)]
+    p = [ctypes.c_void_p(b) for b in base]
+
+    def call(*over, T=T, K=K, H=H, I=I, E=E):
+        a = list(p)
+        for i, v in over:
+            a[i] = v
+        x, ids, probs, w1, w2, out, rmap, ss, tpe, h, aa, yp = a
+        return lib.moe_decode_fwd(x, ids, probs, w1, w2, T, K, H, I, E, out, rmap, ss, tpe, h, aa, yp, None, None)
+
+    assert call((0, None)) == MOE_ERR_NULL          # x
+    assert call((8, None)) == MOE_ERR_NULL          # tokens_per_expert
+    assert call((11, None)) == MOE_ERR_NULL         # y_perm
+    assert call((0, MIS)) == MOE_ERR_INVALID        # misaligned x
+    assert call(K=0) == MOE_ERR_INVALID
+    assert call(H=60) == MOE_ERR_INVALID
+    assert call(T=80) == MOE_ERR_INVALID            # 320 slots > 8 per expert: not a decode shape
+    assert call(H=8192) == MOE_ERR_INVALID          # staged rows past 32 KiB
+    assert call((5, p[0])) == MOE_ERR_INVALID       # out on top of x
+    assert call((11, ctypes.c_void_p(base[10] + 16))) == MOE_ERR_INVALID  # y_perm overlapping a

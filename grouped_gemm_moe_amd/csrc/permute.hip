@@ -70,10 +70,21 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(
     const int64_t s0 = (int64_t)blockIdx.x * chunk;
     const int64_t s1 = s0 + chunk < S ? s0 + chunk : S;
     int bad = 0;
-    for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
-        int32_t id = ids[s];
-        if (valid_id(id, E)) atomicAdd(&hist[id], 1);
-        else if (id != -1) bad = 1;
+    // kHistLoads ids in flight per thread, then their counts (one load per
+    // iteration would wait out an L2 round trip each time)
+    constexpr int kHistLoads = 4;
+    for (int64_t s = s0 + threadIdx.x; s < s1; s += (int64_t)blockDim.x * kHistLoads) {
+        int32_t id[kHistLoads];
+#pragma unroll
+        for (int u = 0; u < kHistLoads; ++u) {
+            const int64_t su = s + (int64_t)u * blockDim.x;
+            id[u] = su < s1 ? ids[su] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kHistLoads; ++u) {
+            if (valid_id(id[u], E)) atomicAdd(&hist[id[u]], 1);
+            else if (id[u] != -1) bad = 1;
+        }
     }
     if (bad && dev_err) atomicOr(dev_err, MOE_DEVERR_EXPERT_ID);
     __syncthreads();
@@ -263,7 +274,22 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_scatter_kernel(
         id[q] = s < w1 ? ids[s] : -1;
     }
     const int64_t n = nblk * E;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) s_hist[i] = blk_hist[i];
+    // the table with kStageLoads loads in flight per thread (a plain copy loop
+    // waits out one L2 round trip per entry it stages)
+    constexpr int kStageLoads = 16;
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)blockDim.x * kStageLoads) {
+        int32_t v[kStageLoads];
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int64_t i = i0 + (int64_t)u * blockDim.x;
+            v[u] = i < n ? blk_hist[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int64_t i = i0 + (int64_t)u * blockDim.x;
+            if (i < n) s_hist[i] = v[u];
+        }
+    }
     for (int i = threadIdx.x; i < kWaves * E; i += blockDim.x) next_row[i / E][i % E] = 0;
     __syncthreads();
 #pragma unroll

@@ -67,6 +67,39 @@ def test_decode_forward_graph_replays(dev):
     assert int(layer.dev_err.item()) == 0
 
 
+def test_routed_decode_forward_graph_replays(dev):
+    """moe_decode_fwd (routing inside the gate_up GMM) captured and replayed
+    with new token rows and a new routing each time: every output, the maps
+    included, bit-identical to the same call run eagerly."""
+    wl = workloads.decode()
+    d = wl.dims
+    shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
+    print(f"graph: routed decode forward {shape}", flush=True)
+    w1, w2 = bf16_dev(wl["w1"], dev), bf16_dev(wl["w2"], dev)
+    ids = torch.from_numpy(wl["topk_ids"]).to(dev)
+    probs = torch.from_numpy(wl["probs"]).to(dev)
+    x = bf16_dev(wl["x"], dev)
+    layer = MoeLayer(shape, dev, gather_rows=True)
+    ref = MoeLayer(shape, dev, gather_rows=True)
+    g = _capture(lambda: layer.forward_decode(x, ids, probs, w1, w2))
+    gen = torch.Generator(device=dev).manual_seed(12)
+    for i in range(4):
+        x_i = torch.randn(x.shape, generator=gen, device=dev).to(torch.bfloat16)
+        ids_i = torch.stack([torch.randperm(d["E"], generator=gen, device=dev)[: d["K"]] for _ in range(d["T"])])
+        ids_i = ids_i.to(torch.int32)
+        x.copy_(x_i)
+        ids.copy_(ids_i)
+        g.replay()
+        ref.forward_decode(x_i, ids_i, probs, w1, w2)
+        torch.cuda.synchronize()
+        R = int(ref.tokens_per_expert.sum().item())
+        for name in ("out", "row_id_map", "tokens_per_expert"):
+            _same_bits(getattr(layer, name), getattr(ref, name), name, i)
+        for name in ("sorted_slot", "h", "a", "yp"):
+            _same_bits(getattr(layer, name)[:R], getattr(ref, name)[:R], name, i)
+    assert int(layer.dev_err.item()) == 0
+
+
 @pytest.mark.parametrize("fuse_swiglu_bwd", [True, False])
 def test_layer_forward_backward_graph_replays(dev, fuse_swiglu_bwd):
     # several row tiles per expert, ragged tails and both backward pairs on the

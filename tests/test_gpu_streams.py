@@ -62,3 +62,39 @@ def test_two_streams_match_sequential(dev):
                 assert torch.equal(a, b), f"rep {rep}, layer {k}: {name} differs from the sequential run"
             assert int(torch.count_nonzero(Lp.ws_gmm[:moe.GMM_QUEUE_BYTES]).item()) == 0
             assert int(Lp.dev_err.item()) == 0
+
+
+def test_routed_decode_on_two_streams_matches_sequential(dev):
+    """moe_decode_fwd takes no workspace, so two calls may overlap on two
+    streams with their own buffers; each must equal the same call run alone."""
+    wls = [workloads.decode(), workloads.decode_skewed()]
+    d = wls[0].dims
+    shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
+    print(f"two streams: routed decode {shape}", flush=True)
+    ins = [dict(x=bf16_dev(wl["x"], dev), ids=torch.from_numpy(wl["topk_ids"]).to(dev),
+                probs=torch.from_numpy(wl["probs"]).to(dev), w1=bf16_dev(wl["w1"], dev),
+                w2=bf16_dev(wl["w2"], dev)) for wl in wls]
+    seq = [MoeLayer(shape, dev, gather_rows=True) for _ in range(2)]
+    for L, a in zip(seq, ins):
+        L.forward_decode(a["x"], a["ids"], a["probs"], a["w1"], a["w2"])
+    torch.cuda.synchronize()
+    par = [MoeLayer(shape, dev, gather_rows=True) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    main = torch.cuda.current_stream()
+    for s in streams:
+        s.wait_stream(main)
+    for rep in range(3):
+        for L, a, s in zip(par, ins, streams):
+            with torch.cuda.stream(s):
+                L.forward_decode(a["x"], a["ids"], a["probs"], a["w1"], a["w2"])
+        torch.cuda.synchronize()
+        for k, (Lp, Ls) in enumerate(zip(par, seq)):
+            R = int(Ls.tokens_per_expert.sum().item())
+            for name in ("out", "row_id_map", "tokens_per_expert", "sorted_slot", "yp"):
+                a, b = getattr(Lp, name), getattr(Ls, name)
+                if name in ("sorted_slot", "yp"):
+                    a, b = a[:R], b[:R]
+                if a.dtype == torch.bfloat16:
+                    a, b = a.view(torch.int16), b.view(torch.int16)
+                assert torch.equal(a, b), f"rep {rep}, layer {k}: {name} differs from the sequential run"
+            assert int(Lp.dev_err.item()) == 0

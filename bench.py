@@ -582,10 +582,11 @@ def mx_layer_bytes(gl, T, K, H, I, gathered=False):
     return int(w + act + idx), n_active
 
 
-def mx_layer_forward(torch, dev, wl, steps, gather=False):
+def mx_layer_forward(torch, dev, wl, steps, gather=False, routed=False):
     """Time permute_mx -> gmm_mx_fwd_swiglu -> gmm_mx_fwd -> unpermute, or
     with gather: mx_quantize of the token rows -> moe_permute_index ->
-    gmm_mx_fwd_swiglu_gather -> gmm_mx_fwd -> unpermute."""
+    gmm_mx_fwd_swiglu_gather -> gmm_mx_fwd -> unpermute, or routed: mx_quantize
+    -> moe_decode_fwd_mx (the routing inside GMM1)."""
     from grouped_gemm_moe_amd import (gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
                                       moe_permute_index, moe_permute_mx, moe_unpermute, mx_quantize)
     from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
@@ -596,11 +597,14 @@ def mx_layer_forward(torch, dev, wl, steps, gather=False):
     x = bf16_dev(torch, wl["x"], dev)
     ids = torch.from_numpy(wl["topk_ids"]).to(dev)
     probs = torch.from_numpy(wl["probs"]).to(dev)
-    L = MoeLayerMX(LayerShape(T, K, E, H, I), dev, gather_rows=gather)
+    L = MoeLayerMX(LayerShape(T, K, E, H, I), dev, gather_rows=gather or routed)
     g, err = L.tokens_per_expert, L.dev_err
     timer = KernelTimer(torch)
 
     def step(t):
+        if routed:
+            t("moe_decode_fwd_mx", lambda: L.forward_decode(x, ids, probs, (w1q, w1s), (w2q, w2s)))
+            return
         if gather:
             t("mx_quantize", lambda: mx_quantize(x, out=(L.xq, L.xs)))
             t("moe_permute_index", lambda: moe_permute_index(ids, E, out=(L.row_id_map, L.sorted_slot, g),
@@ -679,6 +683,13 @@ def run_mx(torch, dev, args):
                                      gb_per_s=round(nbytes_g / (ms_g * 1e-3) / 1e9, 1), bytes_per_layer=nbytes_g,
                                      roofline_ms=round(roof_g, 4), frac_of_attainable=round(roof_g / ms_g, 4),
                                      per_call_us={k: round(v * 1e3, 2) for k, v in per_g.items()})
+        if name == "decode":
+            # GMM1 routing its own rows (moe_decode_fwd_mx): the gathered tensors, no permute launch
+            ms_r, per_r, _, spans_r = mx_layer_forward(torch, dev, wl, steps, routed=True)
+            res[name]["routed"] = dict(ms_per_layer=round(ms_r, 4), layer_ms_events=spans_r,
+                                       gb_per_s=round(nbytes_g / (ms_r * 1e-3) / 1e9, 1),
+                                       frac_of_attainable=round(roof_g / ms_r, 4),
+                                       per_call_us={k: round(v * 1e3, 2) for k, v in per_r.items()})
         log(f"mx {name}: {ms:.4f} ms/layer; {res[name]['gb_per_s']} GB/s; {res[name]['tflops']} TFLOP/s; "
             f"per call {res[name]['per_call_us']}; gathered {ms_g:.4f} ms/layer")
         del wl

@@ -27,7 +27,7 @@ __all__ = [
     "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "swiglu_gmm_fwd", "gmm_bwd_input", "gmm_bwd_weight", "gmm_bwd",
     "gmm_bwd_swiglu",
     "swiglu",
-    "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd", "moe_decode_fwd",
+    "swiglu_bwd", "moe_unpermute", "moe_unpermute_bwd", "moe_permute_bwd", "moe_decode_fwd", "moe_decode_fwd_mx",
     "moe_permute_workspace_size", "gmm_workspace_size", "mx_scale_ld", "mx_quantize",
     "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_mx_fwd_swiglu_gather",
     "library", "DEVERR_EXPERT_ID", "DEVERR_GROUP_LIST", "DEVERR_ROW_MAP", "DEVERR_SLOT",
@@ -443,6 +443,45 @@ def moe_decode_fwd(x, topk_ids, probs, w1, w2, *, out=None, dev_err=None):
            _out(o[6], (S, H), torch.bfloat16, dev, "y_perm"))
     _check(library().moe_decode_fwd(_ptr(x), _ptr(topk_ids), _ptr(probs), _ptr(w1), _ptr(w2), T, top_k, H, I,
                                     E, *[_ptr(t) for t in res], _ptr(dev_err), _stream(dev)), "moe_decode_fwd")
+    return res
+
+
+def moe_decode_fwd_mx(xq, xs, topk_ids, probs, w1q, w1s, w2q, w2s, *, out=None, dev_err=None):
+    """The A8W8-FP decode layer forward with the routing fused into GMM1:
+    (xq, xs) = mx_quantize(x) token rows, MX weights w1 [E, 2I, H], w2
+    [E, H, I].  Returns (out, row_id_map, sorted_slot, tokens_per_expert, aq,
+    as, y_perm), bit-identical to moe_permute_index -> gmm_mx_fwd_swiglu_gather
+    -> gmm_mx_fwd -> moe_unpermute; out= takes a tuple of the same seven."""
+    H, ld_x = _mx_pair(xq, xs, "x")
+    H1, ld_w1 = _mx_pair(w1q, w1s, "w1")
+    I, ld_w2 = _mx_pair(w2q, w2s, "w2")
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(probs, "probs", torch.float32)
+    T = xq.shape[0]
+    E, N2, _ = w1q.shape
+    if H1 != H or N2 != 2 * I or tuple(w2q.shape) != (E, H, I):
+        raise MoeError("shape mismatch: x [T, H], w1 [E, 2I, H], w2 [E, H, I]")
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T or tuple(probs.shape) != tuple(topk_ids.shape):
+        raise MoeError("topk_ids and probs must be [T, top_k] for x [T, H]")
+    top_k = topk_ids.shape[1]
+    S = T * top_k
+    ld_a = mx_scale_ld(I)
+    dev = xq.device
+    o = tuple(out) if out is not None else (None,) * 7
+    if len(o) != 7:
+        raise MoeError("out= takes (out, row_id_map, sorted_slot, tokens_per_expert, aq, as, y_perm)")
+    res = (_out(o[0], (T, H), torch.bfloat16, dev, "out"),
+           _out(o[1], (S,), torch.int32, dev, "row_id_map"),
+           _out(o[2], (S,), torch.int32, dev, "sorted_slot"),
+           _out(o[3], (E,), torch.int64, dev, "tokens_per_expert"),
+           _out(o[4], (S, I), torch.uint8, dev, "aq"),
+           _out(o[5], (S, ld_a), torch.uint8, dev, "as"),
+           _out(o[6], (S, H), torch.bfloat16, dev, "y_perm"))
+    r = [_ptr(t) for t in res]
+    _check(library().moe_decode_fwd_mx(_ptr(xq), _ptr(xs), ld_x, _ptr(topk_ids), _ptr(probs), _ptr(w1q),
+                                       _ptr(w1s), ld_w1, _ptr(w2q), _ptr(w2s), ld_w2, T, top_k, H, I, E,
+                                       r[0], r[1], r[2], r[3], r[4], r[5], ld_a, r[6], _ptr(dev_err),
+                                       _stream(dev)), "moe_decode_fwd_mx")
     return res
 
 

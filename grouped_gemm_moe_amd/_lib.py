@@ -38,6 +38,8 @@ SIGNATURES = {
     "swiglu": (_int, [_p, _p, _i64, _i64, _i64, _p, _p]),
     "swiglu_bwd": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "moe_unpermute": (_int, [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]),
+    "moe_decode_fwd_mx": (_int, [_p, _p, _i64, _p, _p, _p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                 _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p]),
     "moe_decode_fwd": (_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p,
                               _p, _p]),
     "moe_unpermute_bwd": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p]),
@@ -52,7 +54,7 @@ SIGNATURES = {
                                         _i64, _p, _p, _i64, _p, _p]),
 }
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _lib = None
 

@@ -103,7 +103,7 @@ const char* moe_status_string(moe_status s) {
     return "unknown moe_status";
 }
 
-int moegmm_abi_version(void) { return 10; }
+int moegmm_abi_version(void) { return 11; }
 
 size_t moe_permute_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
@@ -389,6 +389,45 @@ moe_status moe_decode_fwd(const uint16_t* x, const int32_t* topk_ids, const floa
                                                    sorted_slot, tokens_per_expert, dev_err, hs);
     if (e != hipSuccess || T == 0) return from_hip(e);
     e = moegmm::launch_stream_swiglu_in(h, w2, tokens_per_expert, E, (int64_t)S, I, H, a, y_perm, dev_err, hs);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err, hs));
+}
+
+moe_status moe_decode_fwd_mx(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const int32_t* topk_ids,
+                             const float* probs, const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                             const uint8_t* w2q, const uint8_t* w2s, int64_t ld_w2s, int64_t T, int64_t top_k,
+                             int64_t H, int64_t I, int64_t E, uint16_t* out, int32_t* row_id_map,
+                             int32_t* sorted_slot, int64_t* tokens_per_expert, uint8_t* aq, uint8_t* as,
+                             int64_t ld_as, uint16_t* y_perm, int32_t* dev_err, void* stream) {
+    if (!tokens_per_expert) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_ids || !probs || !out || !row_id_map || !sorted_slot || !aq || !as || !y_perm))
+        return MOE_ERR_NULL;
+    if (T < 0 || top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxE || !dim_ok(H) || !dim_ok(I) ||
+        T * top_k > kMaxRows || !moegmm::decode_fwd_applies(T, top_k, H, I, E) || I % 32 != 0)
+        return MOE_ERR_INVALID;
+    const int64_t S = T * top_k;
+    // GMM1 on T token rows ([T, H] codes), GMM2 on S rows of A ([S, I] codes)
+    moe_status st = check_gmm_mx(xq, xs, ld_xs, w1q, w1s, ld_w1s, tokens_per_expert, E, T, H, 2 * I);
+    if (st != MOE_OK) return st;
+    st = check_gmm_mx(aq, as, ld_as, w2q, w2s, ld_w2s, tokens_per_expert, E, S, I, H);
+    if (st != MOE_OK) return st;
+    if (!aligned(out, 16) || !aligned(y_perm, 16) || !aligned(topk_ids, 4) || !aligned(probs, 4) ||
+        !aligned(row_id_map, 4) || !aligned(sorted_slot, 4))
+        return MOE_ERR_INVALID;
+    const size_t bS = (size_t)S;
+    const void* buf[] = {xq, xs, topk_ids, probs, out, row_id_map, sorted_slot, tokens_per_expert, aq, as, y_perm};
+    const size_t len[] = {(size_t)(T * H), (size_t)(T * ld_xs), bS * 4, bS * 4, (size_t)(T * H) * 2, bS * 4,
+                          bS * 4, (size_t)E * 8, bS * (size_t)I, bS * (size_t)ld_as, bS * (size_t)H * 2};
+    // every output (index 4 on) apart from every other buffer
+    for (int i = 4; i < 11; ++i)
+        for (int j = 0; j < 11; ++j)
+            if (i != j && overlaps(buf[i], len[i], buf[j], len[j])) return MOE_ERR_INVALID;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = moegmm::launch_gmm_mx_stream_route(xq, xs, ld_xs, topk_ids, T, top_k, w1q, w1s, ld_w1s, E, H, I,
+                                                      aq, as, ld_as, row_id_map, sorted_slot, tokens_per_expert,
+                                                      dev_err, hs);
+    if (e != hipSuccess || T == 0) return from_hip(e);
+    e = moegmm::launch_gmm_mx_fwd(aq, as, ld_as, w2q, w2s, ld_w2s, tokens_per_expert, E, S, I, H, y_perm, dev_err, hs);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(moegmm::launch_unpermute(y_perm, row_id_map, probs, T, top_k, H, out, dev_err, hs));
 }

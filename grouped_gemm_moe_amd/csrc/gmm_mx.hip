@@ -25,6 +25,7 @@
 // and 256 B rows) into a two-slot ring beside the operand ring.
 #include "gmm_engine.h"
 #include "launch.h"
+#include "route.h"
 #include "mx.h"
 
 namespace moegmm {
@@ -422,27 +423,43 @@ struct ScaleBatch {
 
 // GATHER: X / XS hold token rows; grouped row r is token slot[r] / top_k
 // (a bad entry loads a zero row and sets MOE_DEVERR_SLOT).
-template <bool SWIGLU, bool GATHER = false>
+// ROUTE (GMM1 of moe_decode_fwd_mx, X / XS the token rows): the group ranges
+// and each row's slot come from ra.ids (route.h) instead of group_list and
+// slot, kRouteRows rows of the expert at a time; the blocks of the first
+// column group write sorted_slot and row_id_map for their expert's rows, and
+// the grid's last block the call outputs.
+constexpr int kRouteRows = 256;
+template <bool SWIGLU, bool GATHER = false, bool ROUTE = false>
 __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, int64_t ld_xs,
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ WS, int64_t ld_ws,
     const int64_t* __restrict__ group_list, int E, int64_t M_cap, int K, int N,
     bf16_t* __restrict__ Y, uint8_t* __restrict__ AQ, uint8_t* __restrict__ AS, int64_t ld_as,
-    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots) {
+    int32_t* dev_err, const int32_t* __restrict__ slot, int top_k, int nslots, const RouteArgs ra) {
+    static_assert(!(GATHER && ROUTE), "one way to find the rows");
+    static_assert(kStreamThreads == kRouteThreads, "the routing helpers assume this block size");
     constexpr int kWaves = kStreamThreads / 64;
     constexpr int kColsPerWave = SWIGLU ? 32 : 64;
     __shared__ int s_off[kMaxExperts];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int64_t s_scan[kStreamThreads / 64];
+    __shared__ int s_rows[ROUTE ? kRouteRows : 1];
     __shared__ __attribute__((aligned(1024))) uint8_t stage[kWaves][64 * kSeg];  // one batch per wave
-    load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    if constexpr (ROUTE) {
+        const bool last = blockIdx.x == gridDim.x - 1;
+        route_group_ranges(ra.ids, nslots, E, s_off, s_cnt, s_scan, dev_err, last);
+        if (last) route_call_outputs(ra, E, nslots, s_cnt);
+    } else {
+        load_group_ranges(group_list, E, M_cap, s_off, s_cnt, s_scan, dev_err);
+    }
     const int Nout = SWIGLU ? N / 2 : N;
     const int NB = (Nout + kColsPerWave * kWaves - 1) / (kColsPerWave * kWaves);
     const int e = blockIdx.x / NB, nb = blockIdx.x % NB;
     const int off = s_off[e], cnt = s_cnt[e];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int c0 = (nb * kWaves + wid) * kColsPerWave;  // first output column of the wave
-    if (cnt == 0 || c0 >= Nout) return;                  // uniform per wave; no barrier follows
+    const bool active = cnt > 0 && c0 < Nout;            // uniform per wave
+    if (!ROUTE && !active) return;                       // no barrier follows without ROUTE
     const int c = lane >> 5, r32 = lane & 31;
     // this lane's weight row in each of the two operands (for its scales)
     int wrow[2];
@@ -485,11 +502,23 @@ __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
         return wst + (t * 8 + (r >> 2)) * 1024 + (r & 3) * 256 + ((q ^ (r & 15)) << 4);
     };
 
-    for (int rg = 0; rg < cnt; rg += 32) {  // uniform across the wave
+    // rows [ch, ch + nrows) of the expert per chunk (one chunk unless ROUTE)
+    for (int ch = 0; ch < cnt; ch += ROUTE ? kRouteRows : cnt) {  // uniform across the block
+    const int nrows = ROUTE && cnt - ch > kRouteRows ? kRouteRows : cnt - ch;
+    if constexpr (ROUTE) {
+        route_rows(ra.ids, nslots, e, ch, nrows, s_rows, s_scan);
+        if (nb == 0)
+            for (int i = threadIdx.x; i < nrows; i += kStreamThreads) {
+                ra.sorted_slot[off + ch + i] = s_rows[i];
+                ra.row_id_map[s_rows[i]] = off + ch + i;
+            }
+    }
+    for (int rg = ch; active && rg < ch + nrows; rg += 32) {  // uniform across the wave
         const int xr = rg + r32;           // this lane's expert row
         const bool xok = xr < cnt;         // the row exists (and is written)
         bool xld = xok;                    // its operand row is loaded (else zeros)
         int src = off + xr;                // its source row: grouped row, or token (slot)
+        if constexpr (ROUTE) src = xok ? s_rows[xr - ch] / top_k : 0;
         if (GATHER && xok) {
             const int sl = slot[off + xr];
             xld = sl >= 0 && sl < nslots;
@@ -595,6 +624,8 @@ __global__ __launch_bounds__(kStreamThreads) void gmm_mx_stream_kernel(
                 }
         }
     }
+    if constexpr (ROUTE) __syncthreads();  // s_rows is refilled for the next chunk
+    }
 }
 
 }  // namespace
@@ -618,7 +649,7 @@ hipError_t launch_gmm_mx_fwd(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs
         hipLaunchKernelGGL(gmm_mx_stream_kernel<false>, dim3((unsigned)(E * NB)),
                            dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, wq, ws, ld_ws, group_list,
                            (int)E, M_cap, (int)K, (int)N, y, nullptr, nullptr, (int64_t)0, dev_err, nullptr,
-                           1, 0);
+                           1, 0, RouteArgs{});
         return hipGetLastError();
     }
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
@@ -640,12 +671,12 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
             hipLaunchKernelGGL((gmm_mx_stream_kernel<true, true>), dim3((unsigned)(E * NB)),
                                dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
                                group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
-                               dev_err, g.slot, (int)g.top_k, (int)g.nslots);
+                               dev_err, g.slot, (int)g.top_k, (int)g.nslots, RouteArgs{});
         else
             hipLaunchKernelGGL(gmm_mx_stream_kernel<true>, dim3((unsigned)(E * NB)),
                                dim3(kStreamThreads), 0, stream, xq, xs, ld_xs, w1q, w1s, ld_w1s,
                                group_list, (int)E, M_cap, (int)K, (int)(2 * I), nullptr, aq, as, ld_as,
-                               dev_err, nullptr, 1, 0);
+                               dev_err, nullptr, 1, 0, RouteArgs{});
         return hipGetLastError();
     }
     const int64_t grid = num_cus() / 8 * 8;  // persistent, see gmm_mx_rows_kernel
@@ -658,6 +689,24 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
         hipLaunchKernelGGL(gmm_mx_rows_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
                            xq, xs, ld_xs, w1q, w1s, ld_w1s, group_list, (int)E, M_cap, (int)K,
                            (int)(2 * I), nullptr, aq, as, ld_as, dev_err, nullptr, 1, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_gmm_mx_stream_route(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const int32_t* ids,
+                                      int64_t T, int64_t top_k, const uint8_t* w1q, const uint8_t* w1s,
+                                      int64_t ld_w1s, int64_t E, int64_t K, int64_t I, uint8_t* aq, uint8_t* as,
+                                      int64_t ld_as, int32_t* row_id_map, int32_t* sorted_slot,
+                                      int64_t* tokens_per_expert, int32_t* dev_err, hipStream_t stream) {
+    RouteArgs ra;
+    ra.ids = ids;
+    ra.row_id_map = row_id_map;
+    ra.sorted_slot = sorted_slot;
+    ra.tokens_per_expert = tokens_per_expert;
+    const int64_t S = T * top_k;
+    const int64_t NB = (I + 32 * 4 - 1) / (32 * 4);
+    hipLaunchKernelGGL((gmm_mx_stream_kernel<true, false, true>), dim3((unsigned)(E * NB)), dim3(kStreamThreads), 0,
+                       stream, xq, xs, ld_xs, w1q, w1s, ld_w1s, nullptr, (int)E, S, (int)K, (int)(2 * I), nullptr,
+                       aq, as, ld_as, dev_err, nullptr, (int)top_k, (int)S, ra);
     return hipGetLastError();
 }
 

@@ -110,6 +110,15 @@ hipError_t launch_gmm_mx_fwd_swiglu(const uint8_t* xq, const uint8_t* xs, int64_
                                     int32_t* dev_err, hipStream_t stream,
                                     const GatherRows& g = GatherRows{});
 
+// GMM1 of moe_decode_fwd_mx: the MX streaming gate_up + SwiGLU + requant
+// reading quantised token rows, routing its own rows from ids (h, the maps
+// and tokens_per_expert as moe_permute_index + gmm_mx_fwd_swiglu_gather).
+hipError_t launch_gmm_mx_stream_route(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const int32_t* ids,
+                                      int64_t T, int64_t top_k, const uint8_t* w1q, const uint8_t* w1s,
+                                      int64_t ld_w1s, int64_t E, int64_t K, int64_t I, uint8_t* aq, uint8_t* as,
+                                      int64_t ld_as, int32_t* row_id_map, int32_t* sorted_slot,
+                                      int64_t* tokens_per_expert, int32_t* dev_err, hipStream_t stream);
+
 // mx_quant.hip
 hipError_t launch_mx_quantize(const uint16_t* x, int64_t rows, int64_t K, int64_t ld_s, uint8_t* q,
                               uint8_t* s, hipStream_t stream);

@@ -48,7 +48,7 @@ import torch
 
 from . import (gmm_bwd, gmm_bwd_input, gmm_bwd_swiglu, gmm_bwd_weight, gmm_fwd, gmm_fwd_gather, gmm_fwd_swiglu,
                gmm_fwd_swiglu_gather, gmm_mx_fwd, gmm_mx_fwd_swiglu, gmm_mx_fwd_swiglu_gather,
-               gmm_workspace_size, moe_decode_fwd, moe_permute,
+               gmm_workspace_size, moe_decode_fwd, moe_decode_fwd_mx, moe_permute,
                moe_permute_bwd, moe_permute_index, moe_permute_mx, moe_permute_workspace_size, moe_unpermute,
                moe_unpermute_bwd, mx_quantize, mx_scale_ld, swiglu, swiglu_bwd, swiglu_gmm_fwd)
 
@@ -314,4 +314,17 @@ class MoeLayerMX:
                               dev_err=self.dev_err)
         gmm_mx_fwd(self.aq, self.as_, w2q, w2s, g, out=self.yp, dev_err=self.dev_err)
         moe_unpermute(self.yp, self.row_id_map, probs, out=self.out, dev_err=self.dev_err)
+        return self.out
+
+    def forward_decode(self, x, topk_ids, probs, w1mx, w2mx):
+        """The same forward (gather_rows=True buffers) with the routing fused
+        into GMM1 (moe_decode_fwd_mx: no permute launch), bit for bit."""
+        if not self.gather_rows:
+            raise ValueError("forward_decode reads the quantised token rows: build with gather_rows=True")
+        (w1q, w1s), (w2q, w2s) = w1mx, w2mx
+        mx_quantize(x, out=(self.xq, self.xs))
+        moe_decode_fwd_mx(self.xq, self.xs, topk_ids, probs, w1q, w1s, w2q, w2s,
+                          out=(self.out, self.row_id_map, self.sorted_slot, self.tokens_per_expert, self.aq,
+                               self.as_, self.yp),
+                          dev_err=self.dev_err)
         return self.out

@@ -410,6 +410,30 @@ moe_status moe_unpermute(const uint16_t* y_perm, const int32_t* row_id_map, cons
  * the inputs.  Ids outside [-1, E) set MOE_DEVERR_EXPERT_ID and are masked.
  * No workspace.
  * ---------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------
+ * moe_decode_fwd_mx -- the A8W8-FP (MXFP8) decode layer forward with the
+ * routing fused into GMM1, as moe_decode_fwd does for bf16: GMM1 + SwiGLU +
+ * requantisation reads the quantised token rows (mx_quantize of x) and
+ * routes its own rows, then gmm_mx_fwd (GMM2) and moe_unpermute.  [MegaMoE]
+ * A8W8-FP (GMM1 -> activation -> requantisation -> GMM2) and 功能说明
+ * (dispatch fused into the first linear layer).
+ *
+ *   xq [T, H] fp8 codes, xs [T, ld_xs] E8M0 scales: mx_quantize(x)
+ *   topk_ids, probs [T, top_k]; w1q/w1s, w2q/w2s as gmm_mx_fwd_swiglu / gmm_mx_fwd
+ *   out [T, H] bf16, row_id_map, sorted_slot [T*top_k], tokens_per_expert [E],
+ *   aq [T*top_k, I] + as [T*top_k, ld_as], y_perm [T*top_k, H] bf16 OUT
+ * Every output is bit-identical to moe_permute_index ->
+ * gmm_mx_fwd_swiglu_gather -> gmm_mx_fwd -> moe_unpermute on the same
+ * inputs.  Shapes as moe_decode_fwd (else MOE_ERR_INVALID), limits as the MX
+ * calls; I % 32 == 0.  No workspace.
+ * ---------------------------------------------------------------------- */
+moe_status moe_decode_fwd_mx(const uint8_t* xq, const uint8_t* xs, int64_t ld_xs, const int32_t* topk_ids,
+                             const float* probs, const uint8_t* w1q, const uint8_t* w1s, int64_t ld_w1s,
+                             const uint8_t* w2q, const uint8_t* w2s, int64_t ld_w2s, int64_t T, int64_t top_k,
+                             int64_t H, int64_t I, int64_t E, uint16_t* out, int32_t* row_id_map,
+                             int32_t* sorted_slot, int64_t* tokens_per_expert, uint8_t* aq, uint8_t* as,
+                             int64_t ld_as, uint16_t* y_perm, int32_t* dev_err, void* stream);
+
 moe_status moe_decode_fwd(const uint16_t* x, const int32_t* topk_ids, const float* probs,
                           const uint16_t* w1, const uint16_t* w2, int64_t T, int64_t top_k, int64_t H,
                           int64_t I, int64_t E, uint16_t* out, int32_t* row_id_map, int32_t* sorted_slot,

@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
               "moe_unpermute_bwd", "moe_permute_bwd", "moe_status_string", "moegmm_abi_version",
               "mx_quantize", "moe_permute_mx", "gmm_mx_fwd", "gmm_mx_fwd_swiglu", "gmm_bwd", "gmm_bwd_swiglu",
               "moe_permute_index", "gmm_fwd_gather", "gmm_fwd_swiglu_gather", "gmm_mx_fwd_swiglu_gather",
-              "swiglu_gmm_fwd", "moe_decode_fwd"]:
+              "swiglu_gmm_fwd", "moe_decode_fwd", "moe_decode_fwd_mx"]:
         assert n in names, n
 
 

@@ -172,3 +172,48 @@ def test_decode_fwd_empty_call_and_shape_limits(dev):
     probs = torch.zeros((40, 2), dtype=torch.float32, device=dev)
     with pytest.raises(moe.MoeError):
         moe.moe_decode_fwd(x, ids, probs, w1, w2)
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_skewed"])
+def test_decode_fwd_mx_bit_identical_to_gathered_chain(dev, name):
+    """moe_decode_fwd_mx against MoeLayerMX(gather_rows=True).forward (mx_quantize,
+    moe_permute_index, gmm_mx_fwd_swiglu_gather, gmm_mx_fwd, moe_unpermute):
+    every output bit for bit, twice in a row on the same buffers."""
+    from grouped_gemm_moe_amd.pipeline import LayerShape, MoeLayerMX
+
+    print(f"moe_decode_fwd_mx {name}", flush=True)
+    wl = getattr(workloads, name)()
+    d = wl.dims
+    shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
+    x, ids, probs, w1, w2 = _inputs(wl, dev)
+    w1mx, w2mx = MoeLayerMX.prepare_weights(w1, w2)
+    chain = MoeLayerMX(shape, dev, gather_rows=True)
+    routed = MoeLayerMX(shape, dev, gather_rows=True)
+    for rep in range(2):
+        chain.forward(x, ids, probs, w1mx, w2mx)
+        routed.forward_decode(x, ids, probs, w1mx, w2mx)
+        torch.cuda.synchronize()
+        R = int(chain.tokens_per_expert.sum().item())
+        for nm in ("out", "row_id_map", "tokens_per_expert"):
+            a, b = getattr(routed, nm), getattr(chain, nm)
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), (rep, nm)
+        for nm in ("sorted_slot", "aq", "as_", "yp"):
+            a, b = getattr(routed, nm)[:R], getattr(chain, nm)[:R]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), (rep, nm)
+        assert int(routed.dev_err.item()) == 0
+    # the masked / bad-id routing: maps and flags as the chain's
+    wl = _masked_workload(5, 24, 4, 16, 256, 128, bad_ids=True)
+    d = wl.dims
+    shape = LayerShape(d["T"], d["K"], d["E"], d["H"], d["I"])
+    x, ids, probs, w1, w2 = _inputs(wl, dev)
+    w1mx, w2mx = MoeLayerMX.prepare_weights(w1, w2)
+    chain = MoeLayerMX(shape, dev, gather_rows=True)
+    routed = MoeLayerMX(shape, dev, gather_rows=True)
+    chain.forward(x, ids, probs, w1mx, w2mx)
+    routed.forward_decode(x, ids, probs, w1mx, w2mx)
+    torch.cuda.synchronize()
+    assert torch.equal(routed.out.view(torch.int16), chain.out.view(torch.int16))
+    assert torch.equal(routed.row_id_map, chain.row_id_map)
+    assert int(routed.dev_err.item()) == int(chain.dev_err.item()) == moe.DEVERR_EXPERT_ID
